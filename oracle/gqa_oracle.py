@@ -1,0 +1,354 @@
+"""Plain CPU oracle for the forward pass of a grouped-query attention layer
+with an explicitly set head_dim.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check of ``__graft_entry__``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.
+The product path (the HIP library and its Python binding) never does, and it
+shares no code, table or constant with this file.
+
+What it computes, step by step, follows the sources below; each function
+names the passage it implements.
+
+* "Tutorial 07: Multi-Head and Grouped-Query Attention (Full Layer)",
+  section 4 (the ``Attention.__call__`` code, steps 1 to 7) for the order of
+  the steps: project, per-head QK-norm, RoPE on q and k, grouped attention in
+  float, flatten to the query width, output projection.  Section 3 says the
+  norm has dim = head_dim and runs per head.
+* GPT-NeoX issue "Support explicit attention head_dim independent of
+  hidden_size / num_attention_heads", sections "Proposed configuration
+  behavior", "Proposed implementation", "Fused QKV projection", "Attention
+  output flattening", "Output projection" and "Scaling and RoPE" for the
+  shapes, the quotient fallback, the divisibility rules and the scale.
+* "num_heads Is Not a Capacity Knob", section "Why the cost does not move",
+  for the weight and multiply-accumulate counts.
+
+Readings where the pages are silent (each also listed in the design doc):
+
+1. RMSNorm is the textbook ``v / sqrt(mean(v*v) + eps) * w`` over the d
+   entries of one head; one [d] weight for q and one for k, shared by all
+   heads.  The pages name RMSNorm(head_dim, weight, eps) but print no formula.
+2. k_norm is applied to k's own projection (the tutorial's code in section 4;
+   its prose in section 3 has k_norm(projection_q), read as a typo).
+3. RoPE is full-width rotate-half: entry i pairs with entry i + d/2 and turns
+   by angle ``p * theta**(-2i/d)``.  The pages name RoPE(head_dim,
+   max_position_embeddings, rope_theta) but print no pairing rule.  Angles
+   are formed in float64.
+4. The fused QKV weight is the row concatenation [q_proj; k_proj; v_proj].
+5. Query head h reads KV head h // (Hq / Hkv) (contiguous groups).
+6. No bias in any projection (``linear(x, W)`` = ``x @ W.T``).
+7. With a cache, query i of a chunk of L sits at position cache_len + i and
+   sees keys at positions <= its own (bottom-right causal alignment); new
+   k and v are appended before attending.
+8. The layer returns the o_proj output; the residual add is the caller's.
+
+parity unpinned: reading 1 (the exact RMSNorm formula: eps placement) and
+reading 3 (the RoPE pairing convention) are not fixed by the pages.  The
+tests pin them to library routines and mathematical invariants (norm
+preservation, relative-position property, identity at p = 0), not to page
+values.
+
+Arithmetic runs in float64 by default; ``dtype=np.float32`` runs the same
+code in float32, the precision the tutorial's step 6 names for the attention
+core.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Configuration
+# ---------------------------------------------------------------------------
+
+class ConfigError(ValueError):
+    """A configuration the pages say must be rejected."""
+
+
+@dataclass(frozen=True)
+class Resolved:
+    hidden: int        # residual width
+    hq: int            # query heads
+    hkv: int           # key/value heads
+    d: int             # effective head_dim
+    group: int         # query heads per KV head
+    q_width: int       # hq * d
+    kv_width: int      # hkv * d
+    n_qkv: int         # q_width + 2 * kv_width
+    scale: float       # d ** -0.5
+
+
+def resolve_config(hidden_size: int, num_heads: int,
+                   num_kv_heads: Optional[int] = None,
+                   head_dim: Optional[int] = None,
+                   require_even: bool = True) -> Resolved:
+    """Effective head_dim and widths.
+
+    GPT-NeoX issue "Support explicit attention head_dim ...":
+    - "Proposed configuration behavior": d = head_dim if set, else
+      hidden_size // num_attention_heads; hidden_size % num_attention_heads
+      is required only when d must be derived.
+    - "Proposed implementation": query width Hq*d, kv width Hkv*d with
+      Hkv defaulting to Hq.
+    - "Scaling and RoPE": scale d**-0.5; RoPE needs an even d.
+    "Attention head partitions: keep each head's dependencies intact": GQA
+    groups Hq/Hkv query heads per KV head when that ratio is integral.
+    """
+    if hidden_size <= 0 or num_heads <= 0:
+        raise ConfigError("hidden_size and num_heads must be positive")
+    if head_dim is None:
+        if hidden_size % num_heads != 0:
+            raise ConfigError(
+                f"head_dim unset and hidden_size {hidden_size} is not "
+                f"divisible by num_heads {num_heads}")
+        d = hidden_size // num_heads
+    else:
+        d = int(head_dim)
+        if d <= 0:
+            raise ConfigError("head_dim must be positive")
+    hkv = num_heads if num_kv_heads is None else int(num_kv_heads)
+    if hkv <= 0:
+        raise ConfigError("num_kv_heads must be positive")
+    if num_heads % hkv != 0:
+        raise ConfigError(
+            f"num_heads {num_heads} is not a multiple of num_kv_heads {hkv}")
+    if require_even and d % 2 != 0:
+        raise ConfigError(f"head_dim {d} is odd; RoPE needs an even head_dim")
+    return Resolved(hidden=hidden_size, hq=num_heads, hkv=hkv, d=d,
+                    group=num_heads // hkv, q_width=num_heads * d,
+                    kv_width=hkv * d, n_qkv=(num_heads + 2 * hkv) * d,
+                    scale=float(d) ** -0.5)
+
+
+def weight_shapes(res: Resolved) -> dict:
+    """Projection weight shapes, [out, in] as in the GPT-NeoX issue's
+    "Checkpoint conversion" section and the tutorial's section 2."""
+    return {
+        "q_proj": (res.q_width, res.hidden),
+        "k_proj": (res.kv_width, res.hidden),
+        "v_proj": (res.kv_width, res.hidden),
+        "o_proj": (res.hidden, res.q_width),
+        "query_key_value": (res.n_qkv, res.hidden),
+    }
+
+
+def attention_param_count(res: Resolved) -> int:
+    """Weights of the four projections ("num_heads Is Not a Capacity Knob",
+    "Why the cost does not move": four matrices, no biases)."""
+    s = weight_shapes(res)
+    return sum(a * b for k, (a, b) in s.items() if k != "query_key_value")
+
+
+def macs_per_token(res: Resolved, n_context: int) -> dict:
+    """Multiply-accumulates per token ("Why the cost does not move"): the
+    projections cost one MAC per weight, the scores cost d per visible key
+    per query head, and the value average d per key per head."""
+    proj = attention_param_count(res)
+    score = n_context * res.d * res.hq
+    value = n_context * res.d * res.hq
+    return {"projection": proj, "score_value": score + value}
+
+
+# ---------------------------------------------------------------------------
+# Steps of the layer
+# ---------------------------------------------------------------------------
+
+def project(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """linear(x, W) = x @ W.T (tutorial section 4, step 1; no bias)."""
+    return np.matmul(x, w.T)
+
+
+def split_heads(y: np.ndarray, res: Resolved):
+    """Split the fused projection on whole-head boundaries, Q | K | V, and
+    reshape each to [B, L, heads, d] (GPT-NeoX issue, "Fused QKV
+    projection"; tutorial section 4, step 1)."""
+    b, l, _ = y.shape
+    q = y[..., :res.q_width].reshape(b, l, res.hq, res.d)
+    k = y[..., res.q_width:res.q_width + res.kv_width].reshape(
+        b, l, res.hkv, res.d)
+    v = y[..., res.q_width + res.kv_width:].reshape(b, l, res.hkv, res.d)
+    return q, k, v
+
+
+def rms_norm_heads(v: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head RMSNorm over the last axis (tutorial section 3: the norm has
+    dim = head_dim and works within each head)."""
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * w
+
+
+def rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    """theta ** (-2i/d) for i < d/2, in float64."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * i / d)
+
+
+def apply_rope(v: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of v [B, L, heads, d] at integer positions [B, L]
+    (tutorial section 4, step 3; GPT-NeoX issue "Scaling and RoPE": built at
+    the effective head_dim)."""
+    d = v.shape[-1]
+    half = d // 2
+    ang = positions.astype(np.float64)[..., None] * rope_inv_freq(d, theta)
+    cos = np.cos(ang).astype(v.dtype)[:, :, None, :]
+    sin = np.sin(ang).astype(v.dtype)[:, :, None, :]
+    x1 = v[..., :half]
+    x2 = v[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def grouped_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                      q_pos: np.ndarray, kv_len: np.ndarray, scale: float,
+                      causal: bool = True) -> np.ndarray:
+    """softmax(q k^T * scale) v with each KV head serving Hq/Hkv query heads
+    (tutorial section 4, step 6; "Attention head partitions ...": the
+    head-to-KV-group map).
+
+    q [B, Hq, Lq, d]; k, v [B, Hkv, S, d] with S >= kv_len[b]; q_pos [B, Lq]
+    holds each query's position.  Query i of batch b sees keys j < kv_len[b],
+    and with ``causal`` only those with j <= q_pos[b, i].
+    Returns [B, Hq, Lq, d].
+    """
+    bsz, hq, lq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    out = np.zeros((bsz, hq, lq, v.shape[-1]), dtype=q.dtype)
+    for b in range(bsz):
+        n = int(kv_len[b])
+        key_idx = np.arange(n)
+        visible = np.ones((lq, n), dtype=bool)
+        if causal:
+            visible = key_idx[None, :] <= q_pos[b][:, None]
+        for h in range(hq):
+            g = h // group
+            s = np.matmul(q[b, h], k[b, g, :n].T) * q.dtype.type(scale)
+            s = np.where(visible, s, -np.inf)
+            m = np.max(s, axis=-1, keepdims=True)
+            p = np.exp(s - m)
+            p = p / np.sum(p, axis=-1, keepdims=True)
+            out[b, h] = np.matmul(p, v[b, g, :n])
+    return out
+
+
+def merge_heads(o: np.ndarray) -> np.ndarray:
+    """[B, Hq, L, d] -> [B, L, Hq*d] (GPT-NeoX issue, "Attention output
+    flattening": flatten to the query width, not the residual width)."""
+    b, h, l, d = o.shape
+    return o.transpose(0, 2, 1, 3).reshape(b, l, h * d)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+
+def qkv_normrope(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, positions,
+                 rope_theta, rms_eps, qk_norm=True, rope=True):
+    """Steps 1 to 4 of the tutorial's ``Attention.__call__``: project, QK-norm,
+    RoPE, transpose to head-major.  Returns q [B, Hq, L, d] and k, v
+    [B, Hkv, L, d] (k after norm and RoPE, v raw)."""
+    y = project(x, w_qkv)
+    q, k, v = split_heads(y, res)
+    if qk_norm:
+        q = rms_norm_heads(q, q_norm_w, rms_eps)
+        k = rms_norm_heads(k, k_norm_w, rms_eps)
+    if rope:
+        q = apply_rope(q, positions, rope_theta)
+        k = apply_rope(k, positions, rope_theta)
+    return (q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3),
+            v.transpose(0, 2, 1, 3))
+
+
+def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
+                  rope_theta: float, rms_eps: float, qk_norm: bool = True,
+                  causal: bool = True, rope: bool = True,
+                  k_cache=None, v_cache=None, cache_len=None,
+                  dtype=np.float64):
+    """The layer forward (tutorial section 4, steps 1 to 7).
+
+    x [B, L, hidden]; w_qkv [(Hq+2Hkv)d, hidden]; w_o [hidden, Hq*d].
+    Without a cache, positions are 0..L-1.  With ``k_cache``/``v_cache``
+    [B, Hkv, S, d] and ``cache_len`` [B], token i of sequence b sits at
+    position cache_len[b] + i, its k and v are written at that row of a copy
+    of the cache (step 5, update_and_fetch), and attention runs over rows
+    0 .. cache_len[b] + L - 1.
+
+    Returns (out [B, L, hidden], k_cache', v_cache') where the caches are the
+    updated copies (None without a cache).  ``rope=False`` drops step 3 and
+    exists only to reduce the layer to textbook multi-head attention in the
+    tests.
+    """
+    x = np.asarray(x, dtype=dtype)
+    w_qkv = np.asarray(w_qkv, dtype=dtype)
+    w_o = np.asarray(w_o, dtype=dtype)
+    qn = None if q_norm_w is None else np.asarray(q_norm_w, dtype=dtype)
+    kn = None if k_norm_w is None else np.asarray(k_norm_w, dtype=dtype)
+    bsz, seq, _ = x.shape
+    if cache_len is None:
+        start = np.zeros(bsz, dtype=np.int64)
+    else:
+        start = np.asarray(cache_len, dtype=np.int64)
+    positions = start[:, None] + np.arange(seq, dtype=np.int64)[None, :]
+    q, k, v = qkv_normrope(res, x, w_qkv, qn, kn, positions, rope_theta,
+                           rms_eps, qk_norm=qk_norm, rope=rope)
+    if k_cache is None:
+        kk, vv = k, v
+        kv_len = np.full(bsz, seq, dtype=np.int64)
+        k_out = v_out = None
+    else:
+        kk = np.array(k_cache, dtype=dtype, copy=True)
+        vv = np.array(v_cache, dtype=dtype, copy=True)
+        for b in range(bsz):
+            s0 = int(start[b])
+            kk[b, :, s0:s0 + seq] = k[b]
+            vv[b, :, s0:s0 + seq] = v[b]
+        kv_len = start + seq
+        k_out, v_out = kk, vv
+    o = grouped_attention(q, kk, vv, positions, kv_len, res.scale, causal)
+    out = project(merge_heads(o), w_o)
+    return out, k_out, v_out
+
+
+def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
+                       *, rope_theta: float, rms_eps: float,
+                       qk_norm: bool = True, dtype=np.float64):
+    """Exact causal prefill output (no cache, positions 0..L-1) for chosen
+    (b, t) rows only.
+
+    Row t of the output depends only on x[b, t] (through q) and x[b, :t+1]
+    (through k and v), because the causal mask hides later keys.  So the
+    same steps as ``layer_forward``, run on the prefix x[b, :t+1] and read
+    at its last position, give row t exactly.  Returns an array [len(rows),
+    hidden].
+    """
+    rows = list(rows)
+    out = np.zeros((len(rows), res.hidden), dtype=dtype)
+    by_b: dict = {}
+    for i, (b, t) in enumerate(rows):
+        by_b.setdefault(int(b), []).append((i, int(t)))
+    for b, items in by_b.items():
+        tmax = max(t for _, t in items)
+        xb = np.asarray(x[b:b + 1, :tmax + 1], dtype=dtype)
+        y_prefix = project(xb, np.asarray(w_qkv[res.q_width:], dtype=dtype))
+        k = y_prefix[..., :res.kv_width].reshape(1, tmax + 1, res.hkv, res.d)
+        v = y_prefix[..., res.kv_width:].reshape(1, tmax + 1, res.hkv, res.d)
+        pos_all = np.arange(tmax + 1, dtype=np.int64)[None, :]
+        if qk_norm:
+            k = rms_norm_heads(k, np.asarray(k_norm_w, dtype=dtype), rms_eps)
+        k = apply_rope(k, pos_all, rope_theta)
+        k = k.transpose(0, 2, 1, 3)
+        v = v.transpose(0, 2, 1, 3)
+        ts = np.array([t for _, t in items], dtype=np.int64)
+        xq = np.asarray(x[b:b + 1, ts], dtype=dtype)
+        q = project(xq, np.asarray(w_qkv[:res.q_width], dtype=dtype))
+        q = q.reshape(1, len(ts), res.hq, res.d)
+        if qk_norm:
+            q = rms_norm_heads(q, np.asarray(q_norm_w, dtype=dtype), rms_eps)
+        q = apply_rope(q, ts[None, :], rope_theta).transpose(0, 2, 1, 3)
+        o = grouped_attention(q, k, v, ts[None, :],
+                              np.array([tmax + 1]), res.scale, True)
+        o_rows = project(merge_heads(o), np.asarray(w_o, dtype=dtype))[0]
+        for j, (i, _) in enumerate(items):
+            out[i] = o_rows[j]
+    return out

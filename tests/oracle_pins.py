@@ -1,0 +1,495 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics
+fix, independent of the oracle's own formulas.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees.
+They are plain functions so that ``test_oracle_mutations`` can rerun them
+against an oracle with a planted mistake and show that some pin fails.
+All access to the oracle goes through the module object ``O`` so that a
+patched function is the one exercised.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from oracle import gqa_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def golden():
+    with open(os.path.join(HERE, "golden", "page_figures.json")) as f:
+        return json.load(f)
+
+
+def _rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+def _layer_case(seed=0, b=2, l=9, hidden=24, hq=4, hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    res = O.resolve_config(hidden, hq, hkv, d)
+    x = _rand(rng, b, l, hidden)
+    w_qkv = _rand(rng, res.n_qkv, hidden, scale=0.3)
+    qn = 1.0 + _rand(rng, d, scale=0.1)
+    kn = 1.0 + _rand(rng, d, scale=0.1)
+    w_o = _rand(rng, hidden, res.q_width, scale=0.3)
+    return res, x, w_qkv, qn, kn, w_o
+
+
+# ---------------------------------------------------------------------------
+# Configuration, shapes and counts (page figures)
+# ---------------------------------------------------------------------------
+
+def check_geometries():
+    g = golden()
+    q = g["qwen3_0_6b_geometry"]
+    r = O.resolve_config(q["hidden_size"], q["num_attention_heads"],
+                         q["num_kv_heads"], q["head_dim"])
+    assert r.d == q["head_dim"]
+    assert r.q_width == q["query_hidden_size"]
+    assert r.kv_width == q["kv_hidden_size"]
+    assert r.n_qkv == q["qkv_out"]
+    s = O.weight_shapes(r)
+    assert s["o_proj"] == (q["o_proj_out"], q["o_proj_in"])
+    assert s["query_key_value"] == (q["qkv_out"], q["hidden_size"])
+    qp = q["quotient_path"]
+    r0 = O.resolve_config(q["hidden_size"], q["num_attention_heads"],
+                          q["num_kv_heads"], None)
+    assert r0.d == qp["head_dim"] and r0.n_qkv == qp["qkv_out"]
+    assert r0.kv_width == qp["kv_hidden_size"] and r0.q_width == qp["o_proj_in"]
+
+    q4 = g["qwen3_4b_geometry"]
+    r = O.resolve_config(q4["hidden_size"], q4["num_attention_heads"], None,
+                         q4["head_dim"])
+    s = O.weight_shapes(r)
+    assert list(s["q_proj"]) == q4["q_proj_weight"]
+    assert list(s["o_proj"]) == q4["o_proj_weight"]
+    r0 = O.resolve_config(q4["hidden_size"], q4["num_attention_heads"])
+    assert r0.d == q4["quotient"]
+
+    q8 = g["qwen3_8b_geometry"]
+    r = O.resolve_config(q8["hidden_size"], q8["num_attention_heads"],
+                         q8["num_kv_heads"], q8["head_dim"])
+    s = O.weight_shapes(r)
+    assert list(s["q_proj"]) == q8["w_q"] and list(s["k_proj"]) == q8["w_k"]
+    assert list(s["v_proj"]) == q8["w_v"] and list(s["o_proj"]) == q8["w_o"]
+    assert O.resolve_config(q8["hidden_size"], q8["num_attention_heads"],
+                            q8["num_kv_heads"]).d == q8["head_dim"]
+    # the tutorial's reshape flow, run through the oracle's own steps
+    fl = q8["reshape_flow"]
+    res_small = O.resolve_config(q8["hidden_size"], q8["num_attention_heads"],
+                                 q8["num_kv_heads"], q8["head_dim"])
+    y = np.zeros(fl["x"][:2] + [res_small.n_qkv])
+    qh, kh, vh = O.split_heads(y, res_small)
+    assert list(qh.shape) == fl["heads"]
+    assert list(qh.transpose(0, 2, 1, 3).shape) == fl["transposed"]
+    assert list(O.merge_heads(qh.transpose(0, 2, 1, 3)).shape) == fl["flat"]
+
+    gm = g["gemma3_geometry"]
+    r = O.resolve_config(gm["hidden_size"], gm["num_attention_heads"], None,
+                         gm["head_dim"])
+    assert r.d == gm["head_dim"]
+    assert O.resolve_config(gm["hidden_size"], gm["num_attention_heads"]).d \
+        == gm["quotient"]
+
+
+def check_resolve_errors():
+    # divisibility is required only when head_dim must be derived
+    O.resolve_config(1000, 16, 8, 128)
+    try:
+        O.resolve_config(1000, 16, 8, None)
+    except O.ConfigError:
+        pass
+    else:
+        raise AssertionError("indivisible hidden_size accepted with head_dim unset")
+    for bad in [dict(num_kv_heads=3), dict(head_dim=127)]:
+        try:
+            O.resolve_config(1024, 16, bad.get("num_kv_heads", 8),
+                             bad.get("head_dim", 128))
+        except O.ConfigError:
+            pass
+        else:
+            raise AssertionError(f"{bad} accepted")
+    r = O.resolve_config(1024, 16)
+    assert r.hkv == 16 and r.group == 1
+    assert abs(O.resolve_config(256, 4, 2, 128).scale - 128 ** -0.5) < 1e-15
+
+
+def check_param_counts():
+    g = golden()
+    c = g["param_counts_d_model_512_quotient"]
+    for case in c["cases"]:
+        # d = 512/512 = 1 at the far end: odd, so no RoPE check here
+        r = O.resolve_config(c["d_model"], case["heads"], require_even=False)
+        assert O.attention_param_count(r) == case["params"], case
+    c = g["param_counts_d_model_512_head_dim_128"]
+    for case in c["cases"]:
+        r = O.resolve_config(c["d_model"], case["heads"], None, c["head_dim"])
+        assert O.attention_param_count(r) == case["params"], case
+
+
+def check_macs():
+    c = golden()["macs_per_token_d_model_512"]
+    for h in c["heads_checked"]:
+        r = O.resolve_config(c["d_model"], h, require_even=False)
+        for case in c["score_value_cases"]:
+            m = O.macs_per_token(r, case["n"])
+            assert m["score_value"] == case["macs"], (h, case)
+            assert m["projection"] == c["projection_macs"]
+
+
+# ---------------------------------------------------------------------------
+# Steps against brute force and library routines
+# ---------------------------------------------------------------------------
+
+def check_projection_bruteforce():
+    rng = np.random.default_rng(1)
+    x = _rand(rng, 2, 3, 5)
+    w = _rand(rng, 4, 5)
+    y = O.project(x, w)
+    for b in range(2):
+        for t in range(3):
+            for n in range(4):
+                acc = 0.0
+                for k in range(5):
+                    acc += x[b, t, k] * w[n, k]
+                assert abs(y[b, t, n] - acc) < 1e-12
+
+
+def _brute_attention(q, k, v, q_pos, kv_len, scale, causal):
+    """Pure-Python loops with math.exp (no numpy reductions)."""
+    bsz, hq, lq, d = q.shape
+    hkv = k.shape[1]
+    per = hq // hkv
+    out = np.zeros_like(q)
+    for b in range(bsz):
+        for h in range(hq):
+            g = h // per
+            for i in range(lq):
+                keys = [j for j in range(int(kv_len[b]))
+                        if (not causal) or j <= q_pos[b][i]]
+                scores = []
+                for j in keys:
+                    s = 0.0
+                    for e in range(d):
+                        s += q[b, h, i, e] * k[b, g, j, e]
+                    scores.append(s * scale)
+                mx = max(scores)
+                ws = [math.exp(s - mx) for s in scores]
+                tot = sum(ws)
+                for e in range(d):
+                    acc = 0.0
+                    for w_, j in zip(ws, keys):
+                        acc += w_ * v[b, g, j, e]
+                    out[b, h, i, e] = acc / tot
+    return out
+
+
+def check_attention_bruteforce():
+    rng = np.random.default_rng(2)
+    q = _rand(rng, 1, 4, 7, 8)
+    k = _rand(rng, 1, 2, 7, 8)
+    v = _rand(rng, 1, 2, 7, 8)
+    pos = np.arange(7)[None, :]
+    for causal in (True, False):
+        got = O.grouped_attention(q, k, v, pos, np.array([7]), 8 ** -0.5, causal)
+        ref = _brute_attention(q, k, v, pos, [7], 8 ** -0.5, causal)
+        assert np.max(np.abs(got - ref)) < 1e-12
+    # a chunk of 3 queries at the end of 7 cached keys (bottom-right aligned)
+    qc = q[:, :, :3]
+    pos = np.array([[4, 5, 6]])
+    got = O.grouped_attention(qc, k, v, pos, np.array([7]), 0.3, True)
+    ref = _brute_attention(qc, k, v, pos, [7], 0.3, True)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def check_attention_vs_torch_sdpa():
+    rng = np.random.default_rng(3)
+    for hq, hkv in [(4, 4), (4, 2), (8, 1)]:
+        q = _rand(rng, 2, hq, 11, 16)
+        k = _rand(rng, 2, hkv, 11, 16)
+        v = _rand(rng, 2, hkv, 11, 16)
+        pos = np.tile(np.arange(11), (2, 1))
+        got = O.grouped_attention(q, k, v, pos, np.array([11, 11]), 0.25, True)
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            is_causal=True, scale=0.25, enable_gqa=True).numpy()
+        assert np.max(np.abs(got - ref)) < 1e-12, (hq, hkv)
+    # queries at the tail of a longer key range: explicit bottom-right mask
+    q = _rand(rng, 1, 4, 3, 16)
+    k = _rand(rng, 1, 2, 10, 16)
+    v = _rand(rng, 1, 2, 10, 16)
+    pos = np.array([[7, 8, 9]])
+    mask = torch.from_numpy(np.arange(10)[None, :] <= pos[0][:, None])
+    got = O.grouped_attention(q, k, v, pos, np.array([10]), 0.25, True)
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=mask, scale=0.25, enable_gqa=True).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def check_layer_mha_reduces_to_torch_mha():
+    """Hkv = Hq, d = hidden/Hq, no QK-norm and no RoPE: the layer is the
+    Concat(head_i) W_O multi-head attention of "num_heads Is Not a Capacity
+    Knob", "Why the cost does not move"; torch's packed in_proj weight uses
+    the same q | k | v row order."""
+    rng = np.random.default_rng(4)
+    hidden, heads, L = 32, 4, 10
+    res = O.resolve_config(hidden, heads)
+    x = _rand(rng, 2, L, hidden)
+    w_qkv = _rand(rng, res.n_qkv, hidden, scale=0.3)
+    w_o = _rand(rng, hidden, res.q_width, scale=0.3)
+    got, _, _ = O.layer_forward(res, x, w_qkv, None, None, w_o, rope_theta=1e4,
+                                rms_eps=1e-6, qk_norm=False, rope=False)
+    xt = torch.from_numpy(x).transpose(0, 1)   # [L, B, E]
+    mask = torch.triu(torch.ones(L, L, dtype=torch.bool), diagonal=1)
+    ref, _ = F.multi_head_attention_forward(
+        xt, xt, xt, hidden, heads, torch.from_numpy(w_qkv), None, None, None,
+        False, 0.0, torch.from_numpy(w_o), None, training=False,
+        need_weights=False, attn_mask=mask)
+    ref = ref.transpose(0, 1).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def _torch_rope_complex(v, positions, theta):
+    """RoPE as complex multiplication: z_i = v_i + 1j*v_{i+d/2} times
+    exp(1j * p * theta**(-2i/d))."""
+    d = v.shape[-1]
+    half = d // 2
+    t = torch.from_numpy(v)
+    z = torch.complex(t[..., :half], t[..., half:])
+    i = torch.arange(half, dtype=torch.float64)
+    ang = torch.from_numpy(positions).double()[..., None] * \
+        torch.pow(torch.tensor(theta, dtype=torch.float64), -2.0 * i / d)
+    rot = torch.polar(torch.ones_like(ang), ang)[:, :, None, :]
+    z = z * rot
+    return torch.cat([z.real, z.imag], dim=-1).numpy()
+
+
+def check_layer_vs_torch_composition():
+    """The whole layer with Hq*d != hidden, QK-norm, RoPE, GQA and a causal
+    mask, composed from torch library routines (F.linear, F.rms_norm, RoPE as
+    complex multiplication, SDPA with enable_gqa), in float64."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=5, b=2, l=9, hidden=24,
+                                             hq=4, hkv=2, d=8)
+    theta, eps = 1e4, 1e-6
+    got, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_o, rope_theta=theta,
+                                rms_eps=eps)
+    b, l, _ = x.shape
+    y = F.linear(torch.from_numpy(x), torch.from_numpy(w_qkv))
+    q = y[..., :res.q_width].reshape(b, l, res.hq, res.d)
+    k = y[..., res.q_width:res.q_width + res.kv_width].reshape(b, l, res.hkv, res.d)
+    v = y[..., res.q_width + res.kv_width:].reshape(b, l, res.hkv, res.d)
+    q = F.rms_norm(q, (res.d,), torch.from_numpy(qn), eps)
+    k = F.rms_norm(k, (res.d,), torch.from_numpy(kn), eps)
+    pos = np.tile(np.arange(l), (b, 1))
+    q = torch.from_numpy(_torch_rope_complex(q.numpy(), pos, theta))
+    k = torch.from_numpy(_torch_rope_complex(k.numpy(), pos, theta))
+    o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2),
+                                       v.transpose(1, 2), is_causal=True,
+                                       enable_gqa=True)
+    ref = F.linear(o.transpose(1, 2).reshape(b, l, res.q_width),
+                   torch.from_numpy(w_o)).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-10
+
+
+def check_rmsnorm():
+    rng = np.random.default_rng(6)
+    v = _rand(rng, 3, 5, 4, 16, scale=3.0)
+    w = 1.0 + _rand(rng, 16, scale=0.1)
+    got = O.rms_norm_heads(v, w, 1e-6)
+    ref = F.rms_norm(torch.from_numpy(v), (16,), torch.from_numpy(w), 1e-6).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+    unit = O.rms_norm_heads(v, np.ones(16), 0.0)
+    assert np.max(np.abs(np.sqrt(np.mean(unit ** 2, axis=-1)) - 1.0)) < 1e-12
+    # scale invariance: norm(c * v) == norm(v) for c > 0 (eps = 0)
+    assert np.max(np.abs(O.rms_norm_heads(7.5 * v, w, 0.0)
+                         - O.rms_norm_heads(v, w, 0.0))) < 1e-12
+
+
+def check_rope():
+    rng = np.random.default_rng(7)
+    v = _rand(rng, 2, 6, 3, 16)
+    pos = np.array([[0, 1, 2, 100, 5000, 32768], [7, 7, 8, 9, 10, 65535]])
+    theta = 1e6
+    got = O.apply_rope(v, pos, theta)
+    # identity at position 0
+    z = O.apply_rope(v, np.zeros_like(pos), theta)
+    assert np.max(np.abs(z - v)) < 1e-15
+    # norm preserving per head
+    assert np.max(np.abs(np.linalg.norm(got, axis=-1)
+                         - np.linalg.norm(v, axis=-1))) < 1e-10
+    # complex-multiplication form
+    ref = _torch_rope_complex(v, pos, theta)
+    assert np.max(np.abs(got - ref)) < 1e-10
+    # relative position: <R(p) a, R(p') b> depends only on p' - p
+    a = _rand(rng, 1, 1, 1, 16)
+    bb = _rand(rng, 1, 1, 1, 16)
+    dots = []
+    for shift in (0, 13, 4096):
+        ra = O.apply_rope(a, np.array([[3 + shift]]), theta)
+        rb = O.apply_rope(bb, np.array([[11 + shift]]), theta)
+        dots.append(float(np.sum(ra * rb)))
+    assert max(dots) - min(dots) < 1e-10
+
+
+def check_position_shift_invariance():
+    """Shifting every position by the same offset leaves scores, and so the
+    attention output, unchanged (RoPE's relative-position property)."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=8)
+    b, l, _ = x.shape
+    outs = []
+    for shift in (0, 1000):
+        pos = np.tile(np.arange(l), (b, 1)) + shift
+        q, k, v = O.qkv_normrope(res, x, w_qkv, qn, kn, pos, 1e4, 1e-6)
+        o = O.grouped_attention(q, k, v, pos - shift, np.full(b, l), res.scale)
+        outs.append(o)
+    assert np.max(np.abs(outs[0] - outs[1])) < 1e-10
+
+
+def check_causality():
+    """Changing x at t' leaves rows t < t' unchanged (a nontrivial sequence
+    length, per "Attention head partitions ...": a single token cannot show
+    a future-token leak)."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=9, l=12)
+    base, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_o, rope_theta=1e4,
+                                 rms_eps=1e-6)
+    for tp in (3, 11):
+        x2 = x.copy()
+        x2[:, tp] += 5.0
+        pert, _, _ = O.layer_forward(res, x2, w_qkv, qn, kn, w_o,
+                                     rope_theta=1e4, rms_eps=1e-6)
+        assert np.max(np.abs(pert[:, :tp] - base[:, :tp])) < 1e-12
+        assert np.max(np.abs(pert[:, tp] - base[:, tp])) > 1e-3
+
+
+def check_gqa_equals_repeated_kv():
+    """GQA equals MHA with each KV head repeated for its Hq/Hkv query heads
+    (contiguous groups), on per-head-distinguishable values."""
+    rng = np.random.default_rng(10)
+    hq, hkv, L, d = 8, 2, 9, 6
+    q = _rand(rng, 1, hq, L, d)
+    k = _rand(rng, 1, hkv, L, d)
+    v = _rand(rng, 1, hkv, L, d) + np.arange(hkv)[None, :, None, None] * 10.0
+    pos = np.arange(L)[None, :]
+    got = O.grouped_attention(q, k, v, pos, np.array([L]), 0.4)
+    kr = np.repeat(k, hq // hkv, axis=1)
+    vr = np.repeat(v, hq // hkv, axis=1)
+    ref = O.grouped_attention(q, kr, vr, pos, np.array([L]), 0.4)
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # heads are distinguishable: query head h's output carries KV head h//4's offset
+    means = got.mean(axis=(2, 3))[0]
+    for h in range(hq):
+        assert abs(means[h] - 10.0 * (h // (hq // hkv))) < 3.0
+
+
+def check_rank_ceiling():
+    """rank(q k^T) <= d_head ("num_heads Is Not a Capacity Knob", "What a
+    head cannot express")."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=11, b=1, l=40, hidden=24,
+                                             hq=2, hkv=1, d=4)
+    pos = np.arange(40)[None, :]
+    q, k, v = O.qkv_normrope(res, x, w_qkv, qn, kn, pos, 1e4, 1e-6)
+    s = q[0, 0] @ k[0, 0].T
+    assert np.linalg.matrix_rank(s) <= res.d
+    assert np.linalg.matrix_rank(s) == res.d
+
+
+def check_one_dim_head():
+    """With d_head = 1 and no RoPE every query ranks the visible keys the
+    same way, reversed when its own coordinate is negative."""
+    rng = np.random.default_rng(12)
+    L = 16
+    a = _rand(rng, 1, 1, L, 1)
+    bk = _rand(rng, 1, 1, L, 1)
+    v = np.eye(L)[None, None]          # value j = one-hot(j): output = weights
+    pos = np.arange(L)[None, :]
+    w = O.grouped_attention(a, bk, v, pos, np.array([L]), 1.0)[0, 0]
+    for t in range(1, L):
+        order_keys = np.argsort(bk[0, 0, :t + 1, 0], kind="stable")
+        order_w = np.argsort(w[t, :t + 1], kind="stable")
+        if a[0, 0, t, 0] > 0:
+            assert list(order_w) == list(order_keys)
+        else:
+            assert list(order_w) == list(order_keys[::-1])
+
+
+def check_sum_over_heads():
+    """out = sum_h O_h W_o[:, h*d:(h+1)*d]^T; zeroing one head's W_o slice
+    removes exactly that head's term ("Why the cost does not move")."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=13)
+    b, l, _ = x.shape
+    pos = np.tile(np.arange(l), (b, 1))
+    q, k, v = O.qkv_normrope(res, x, w_qkv, qn, kn, pos, 1e4, 1e-6)
+    o = O.grouped_attention(q, k, v, pos, np.full(b, l), res.scale)
+    full, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_o, rope_theta=1e4,
+                                 rms_eps=1e-6)
+    terms = [o[:, h] @ w_o[:, h * res.d:(h + 1) * res.d].T for h in range(res.hq)]
+    assert np.max(np.abs(sum(terms) - full)) < 1e-12
+    w_pruned = w_o.copy()
+    w_pruned[:, 1 * res.d:2 * res.d] = 0.0
+    pruned, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_pruned,
+                                   rope_theta=1e4, rms_eps=1e-6)
+    assert np.max(np.abs(pruned - (full - terms[1]))) < 1e-12
+
+
+def check_prefill_equals_decode():
+    """Prefill over L tokens equals prefill of a prefix followed by cached
+    chunks (step 5, update_and_fetch, appends before attending)."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=14, b=2, l=10)
+    kw = dict(rope_theta=1e4, rms_eps=1e-6)
+    full, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_o, **kw)
+    cap = 10
+    kc = np.full((2, res.hkv, cap, res.d), np.nan)
+    vc = np.full((2, res.hkv, cap, res.d), np.nan)
+    o1, kc, vc = O.layer_forward(res, x[:, :6], w_qkv, qn, kn, w_o, k_cache=kc,
+                                 v_cache=vc, cache_len=np.array([0, 0]), **kw)
+    o2, kc, vc = O.layer_forward(res, x[:, 6:9], w_qkv, qn, kn, w_o, k_cache=kc,
+                                 v_cache=vc, cache_len=np.array([6, 6]), **kw)
+    o3, kc, vc = O.layer_forward(res, x[:, 9:], w_qkv, qn, kn, w_o, k_cache=kc,
+                                 v_cache=vc, cache_len=np.array([9, 9]), **kw)
+    got = np.concatenate([o1, o2, o3], axis=1)
+    assert np.max(np.abs(got - full)) < 1e-12
+
+
+def check_quotient_equals_explicit():
+    rng = np.random.default_rng(15)
+    r0 = O.resolve_config(32, 4, 2, None)
+    r1 = O.resolve_config(32, 4, 2, 8)
+    assert r0 == r1
+    x = _rand(rng, 1, 7, 32)
+    w_qkv = _rand(rng, r0.n_qkv, 32, scale=0.3)
+    w_o = _rand(rng, 32, r0.q_width, scale=0.3)
+    a, _, _ = O.layer_forward(r0, x, w_qkv, None, None, w_o, rope_theta=5e5,
+                              rms_eps=1e-6, qk_norm=False)
+    b, _, _ = O.layer_forward(r1, x, w_qkv, None, None, w_o, rope_theta=5e5,
+                              rms_eps=1e-6, qk_norm=False)
+    assert np.array_equal(a, b)
+
+
+def check_rows_mode():
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=16, b=2, l=11)
+    kw = dict(rope_theta=1e4, rms_eps=1e-6)
+    full, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_o, **kw)
+    rows = [(0, 0), (0, 5), (1, 10), (1, 3), (0, 10)]
+    got = O.layer_forward_rows(res, x, w_qkv, qn, kn, w_o, rows, **kw)
+    for i, (b, t) in enumerate(rows):
+        assert np.max(np.abs(got[i] - full[b, t])) < 1e-12
+
+
+ALL_CHECKS = [
+    check_geometries, check_resolve_errors, check_param_counts, check_macs,
+    check_projection_bruteforce, check_attention_bruteforce,
+    check_attention_vs_torch_sdpa, check_layer_mha_reduces_to_torch_mha,
+    check_layer_vs_torch_composition, check_rmsnorm, check_rope,
+    check_position_shift_invariance, check_causality,
+    check_gqa_equals_repeated_kv, check_rank_ceiling, check_one_dim_head,
+    check_sum_over_heads, check_prefill_equals_decode,
+    check_quotient_equals_explicit, check_rows_mode,
+]

@@ -1,0 +1,151 @@
+"""Plant plausible mistakes in the CPU oracle and show that at least one pin
+fails for each.  Every mistake is planted in the oracle, on the CPU, through
+pytest's monkeypatch (undone after each case)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle_pins as P  # noqa: E402
+from oracle import gqa_oracle as O  # noqa: E402
+
+_orig = {name: getattr(O, name) for name in (
+    "resolve_config", "attention_param_count", "macs_per_token", "project",
+    "split_heads", "rms_norm_heads", "rope_inv_freq", "apply_rope",
+    "grouped_attention", "merge_heads", "qkv_normrope")}
+
+
+def _k_norm_uses_q_weight(res, x, w_qkv, qn, kn, positions, theta, eps,
+                          qk_norm=True, rope=True):
+    return _orig["qkv_normrope"](res, x, w_qkv, qn, qn, positions, theta, eps,
+                                 qk_norm=qk_norm, rope=rope)
+
+
+def _attention_with(group_map=None, scale_fn=None, causal_shift=0,
+                    normalize=True, softmax_axis=-1):
+    def attn(q, k, v, q_pos, kv_len, scale, causal=True):
+        bsz, hq, lq, d = q.shape
+        hkv = k.shape[1]
+        group = hq // hkv
+        out = np.zeros((bsz, hq, lq, v.shape[-1]), dtype=q.dtype)
+        sc = scale if scale_fn is None else scale_fn(d)
+        for b in range(bsz):
+            n = int(kv_len[b])
+            vis = np.arange(n)[None, :] <= (q_pos[b][:, None] + causal_shift)
+            if not causal:
+                vis = np.ones_like(vis)
+            for h in range(hq):
+                g = h // group if group_map is None else group_map(h, hkv, group)
+                s = q[b, h] @ k[b, g, :n].T * sc
+                s = np.where(vis, s, -np.inf)
+                m = np.max(s, axis=-1, keepdims=True)
+                p = np.exp(s - m)
+                if normalize:
+                    p = p / np.sum(p, axis=softmax_axis, keepdims=True)
+                p = np.nan_to_num(p)
+                out[b, h] = p @ v[b, g, :n]
+        return out
+    return attn
+
+
+def _rope_with(sign=1.0, interleaved=False, freq_factor=2.0):
+    def rope(v, positions, theta):
+        d = v.shape[-1]
+        half = d // 2
+        i = np.arange(half, dtype=np.float64)
+        ang = positions.astype(np.float64)[..., None] * \
+            np.power(np.float64(theta), -freq_factor * i / d) * sign
+        cos = np.cos(ang)[:, :, None, :]
+        sin = np.sin(ang)[:, :, None, :]
+        if interleaved:
+            x1, x2 = v[..., 0::2], v[..., 1::2]
+            y = np.empty_like(v)
+            y[..., 0::2] = x1 * cos - x2 * sin
+            y[..., 1::2] = x2 * cos + x1 * sin
+            return y
+        x1, x2 = v[..., :half], v[..., half:]
+        return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], -1)
+    return rope
+
+
+def _split_kv_swapped(y, res):
+    q, k, v = _orig["split_heads"](y, res)
+    if k.shape == v.shape:
+        return q, v, k
+    return q, k, v
+
+
+def _resolve_always_quotient(hidden_size, num_heads, num_kv_heads=None,
+                             head_dim=None, require_even=True):
+    return _orig["resolve_config"](hidden_size, num_heads, num_kv_heads,
+                                   None if hidden_size % num_heads == 0 else head_dim,
+                                   require_even)
+
+
+def _params_without_o_proj(res):
+    s = O.weight_shapes(res)
+    return sum(a * b for k, (a, b) in s.items()
+               if k not in ("query_key_value", "o_proj"))
+
+
+def _macs_score_only(res, n):
+    m = _orig["macs_per_token"](res, n)
+    return {"projection": m["projection"], "score_value": m["score_value"] // 2}
+
+
+MUTATIONS = {
+    "k_norm_with_q_weight": ("qkv_normrope", _k_norm_uses_q_weight),
+    "group_map_modulo": ("grouped_attention",
+                         _attention_with(group_map=lambda h, hkv, g: h % hkv)),
+    "scale_one_over_d": ("grouped_attention",
+                         _attention_with(scale_fn=lambda d: 1.0 / d)),
+    "causal_sees_next_token": ("grouped_attention",
+                               _attention_with(causal_shift=1)),
+    "softmax_not_normalised": ("grouped_attention",
+                               _attention_with(normalize=False)),
+    "softmax_over_queries": ("grouped_attention",
+                             _attention_with(softmax_axis=0)),
+    "rope_sign_flipped": ("apply_rope", _rope_with(sign=-1.0)),
+    "rope_interleaved_pairs": ("apply_rope", _rope_with(interleaved=True)),
+    "rope_freq_dropped_factor_2": ("apply_rope", _rope_with(freq_factor=1.0)),
+    "rmsnorm_eps_outside_sqrt": (
+        "rms_norm_heads",
+        lambda v, w, eps: v / (np.sqrt(np.mean(v * v, -1, keepdims=True)) + eps) * w),
+    "rmsnorm_over_heads": (
+        "rms_norm_heads",
+        lambda v, w, eps: v / np.sqrt(np.mean(v * v, axis=(-2, -1), keepdims=True)
+                                      + eps) * w),
+    "flatten_without_transpose": (
+        "merge_heads", lambda o: o.reshape(o.shape[0], o.shape[2], -1)),
+    "k_v_swapped": ("split_heads", _split_kv_swapped),
+    "projection_transposed_operand": (
+        "project", lambda x, w: np.matmul(x, w.T) if w.shape[0] != w.shape[1]
+        else np.matmul(x, w)),
+    "head_dim_always_derived": ("resolve_config", _resolve_always_quotient),
+    "params_miss_o_proj": ("attention_param_count", _params_without_o_proj),
+    "macs_miss_value_term": ("macs_per_token", _macs_score_only),
+}
+
+
+def _run_all_checks():
+    failed = []
+    for chk in P.ALL_CHECKS:
+        try:
+            chk()
+        except Exception as e:  # AssertionError, or a crash from bad shapes
+            failed.append((chk.__name__, type(e).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = _run_all_checks()
+    assert failed, f"no pin caught the planted mistake {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _run_all_checks() == []
