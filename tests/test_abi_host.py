@@ -1,0 +1,144 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, resolves configurations by the pages' rules and rejects bad calls on
+the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+T = pytest.importorskip("transformer_attention_layer_amd")
+
+
+def _lib_or_skip():
+    if not os.path.exists(T.LIB_PATH):
+        pytest.skip("libgqa.so not built (run __graft_entry__.build())")
+    return T.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "gqa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for n in ["gqa_resolve", "gqa_workspace_bytes", "qkv_proj_normrope", "gqa_attn_core",
+              "gqa_o_proj", "gqa_layer_forward", "gqa_status_string", "gqa_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib_or_skip()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def cfg(**kw):
+    base = dict(hidden_size=1024, num_heads=16, num_kv_heads=8, head_dim=128)
+    base.update(kw)
+    return T.GQAConfig(**base)
+
+
+def test_resolve_explicit_and_quotient():
+    _lib_or_skip()
+    # Qwen3-0.6B geometry: explicit 128 although 1024 / 16 = 64
+    r = T.gqa_resolve(cfg())
+    assert (r["head_dim"], r["num_kv_heads"]) == (128, 8)
+    # quotient fallback (Qwen3-8B-like): 4096 / 32 = 128
+    r = T.gqa_resolve(cfg(hidden_size=4096, num_heads=32, head_dim=None))
+    assert r["head_dim"] == 128
+    # Hkv unset means plain multi-head attention
+    assert T.gqa_resolve(cfg(num_kv_heads=None))["num_kv_heads"] == 16
+    # explicit head_dim needs no divisibility (1000 % 16 != 0)
+    assert T.gqa_resolve(cfg(hidden_size=1000, dtype="f32"))["head_dim"] == 128
+
+
+@pytest.mark.parametrize("kw,name", [
+    (dict(hidden_size=1000, head_dim=None), "GQA_ERR_HEAD_DIM_INDIVISIBLE"),
+    (dict(num_kv_heads=5), "GQA_ERR_GROUP_INDIVISIBLE"),
+    (dict(head_dim=127, dtype="f32"), "GQA_ERR_ODD_HEAD_DIM"),
+    (dict(head_dim=64), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(head_dim=258, dtype="f32"), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(hidden_size=1004), "GQA_ERR_UNSUPPORTED_SHAPE"),
+    (dict(hidden_size=0), "GQA_ERR_INVALID_ARG"),
+    (dict(rope_theta=0.0), "GQA_ERR_INVALID_ARG"),
+    (dict(rms_eps=-1.0), "GQA_ERR_INVALID_ARG"),
+])
+def test_resolve_rejects(kw, name):
+    _lib_or_skip()
+    with pytest.raises(T.GQAError) as e:
+        T.gqa_resolve(cfg(**kw))
+    assert e.value.name == name
+    assert T.lib().gqa_last_error().decode()
+
+
+def test_unsupported_head_dim_message_names_the_dimension():
+    _lib_or_skip()
+    with pytest.raises(T.GQAError) as e:
+        T.gqa_resolve(cfg(hidden_size=2560, num_heads=32, head_dim=None))  # quotient 80
+    assert "80" in str(e.value)
+
+
+def test_workspace_sizes():
+    _lib_or_skip()
+    c = cfg()
+    assert T.gqa_workspace_bytes(c, 8, 2048, 2048, T.WS_ATTN) == 0          # prefill: none
+    assert T.gqa_workspace_bytes(c, 8, 2048, 2048, T.WS_QKV) >= 8 * 2048 * 64 * 8
+    lay = T.gqa_workspace_bytes(c, 8, 2048, 2048, T.WS_LAYER)
+    assert lay >= 2 * 8 * 2048 * 16 * 128 * 2
+    dec = T.gqa_workspace_bytes(cfg(hidden_size=2560, num_heads=32), 64, 1, 32769, T.WS_ATTN)
+    assert dec > 0
+    assert T.gqa_workspace_bytes(cfg(num_kv_heads=5), 1, 1, 1, T.WS_LAYER) == 0
+
+
+def _raw_call_layer(c, batch, q_len, cap, ptr=1, ws_bytes=1 << 40):
+    L = T.lib()
+    cc = c.c()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return L.gqa_layer_forward(ctypes.byref(cc), batch, q_len, p, p, p, p, p, p, p, cap, None, p,
+                               p, ws_bytes, None)
+
+
+def test_entry_points_validate_before_launch():
+    """Every rejected call returns before touching the device (no GPU here)."""
+    _lib_or_skip()
+    L = T.lib()
+    # empty batch / sequence: a no-op
+    assert _raw_call_layer(cfg(), 0, 16, 16) == 0
+    assert _raw_call_layer(cfg(), 2, 0, 16) == 0
+    # null tensors
+    assert T.STATUS_NAMES[_raw_call_layer(cfg(), 2, 16, 16, ptr=0)] == "GQA_ERR_INVALID_ARG"
+    # capacity below q_len
+    assert T.STATUS_NAMES[_raw_call_layer(cfg(), 2, 16, 8)] == "GQA_ERR_CAPACITY"
+    # workspace too small
+    assert T.STATUS_NAMES[_raw_call_layer(cfg(), 2, 16, 16, ws_bytes=16)] == \
+        "GQA_ERR_WORKSPACE_TOO_SMALL"
+    # bad config
+    assert T.STATUS_NAMES[_raw_call_layer(cfg(num_kv_heads=3), 2, 16, 16)] == \
+        "GQA_ERR_GROUP_INDIVISIBLE"
+    cc = cfg(qk_norm=True).c()
+    st = L.qkv_proj_normrope(ctypes.byref(cc), 1, 4, 1, 1, None, None, None, 1, 1, 1, 4, 1,
+                             1 << 30, None)
+    assert T.STATUS_NAMES[st] == "GQA_ERR_INVALID_ARG"   # qk_norm on, weights missing
+    st = L.gqa_attn_core(ctypes.byref(cc), -1, 4, 1, 1, 1, None, 4, 1, None, 0, None)
+    assert T.STATUS_NAMES[st] == "GQA_ERR_INVALID_ARG"
+    st = L.gqa_o_proj(ctypes.byref(cc), 5, None, 1, 1, None)
+    assert T.STATUS_NAMES[st] == "GQA_ERR_INVALID_ARG"
+    assert L.gqa_status_string(5) == b"GQA_ERR_UNSUPPORTED_HEAD_DIM"
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports the oracle or a CPU fallback."""
+    pkg = os.path.join(ROOT, "transformer_attention_layer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element, at sizes the oracle finishes in
+seconds; every case spans several tiles and a ragged tail."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gqa_inputs as GI  # noqa: E402
+from gpu_util import (announce, assert_close, cfg_of, oracle_layer, resolved,  # noqa: E402
+                      to_np)
+from oracle import gqa_oracle as O  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_attention_layer_amd as T
+    T.lib()  # fail loudly if the library is missing
+    yield
+
+
+def T_():
+    import transformer_attention_layer_amd as T
+    return T
+
+
+# reduced-size versions of every workload (same model shapes, shorter runs)
+SMALL = {
+    "tiny_f32": GI.WORKLOADS["tiny_f32"],
+    "prefill_h1024": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=200),
+    "quotient_h4096": GI.WORKLOADS["quotient_h4096"].with_(batch=1, seq=300),
+    "wide_h5120": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=130),
+    "decode_h2560_gqa": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000),
+    "decode_h2560_mqa": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777),
+}
+
+
+def run_layer(w, h, cache=None, cache_len=None, out_f32=True):
+    T = T_()
+    d = GI.to_device(h, w)
+    kw = {}
+    if cache is not None:
+        c = GI.to_device(cache, w)
+        kw = dict(k_cache=c["k_cache"], v_cache=c["v_cache"],
+                  cache_len=torch.tensor(cache_len, dtype=torch.int32, device="cuda"))
+    out, kc, vc = T.gqa_layer_forward(cfg_of(w, out_f32), d["x"], d["w_qkv"], d["q_norm_w"],
+                                      d["k_norm_w"], d["w_o"], **kw)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_forward_parity(name):
+    w = SMALL[name]
+    announce(f"[layer] {name} B={w.batch} L={w.seq} cache={w.cache_len}")
+    h = GI.host_layer_inputs(w)
+    if w.cache_len:
+        cache = GI.host_cache(w)
+        cl = np.full(w.batch, w.cache_len, dtype=np.int64)
+        out, kc, vc = run_layer(w, h, cache, cl)
+        ref, rk, rv = oracle_layer(w, h, cache, cl)
+        # the appended row of the cache
+        n = w.cache_len
+        assert_close(to_np(kc)[:, :, n:n + w.seq], rk[:, :, n:n + w.seq], w.dtype, "k append")
+        assert_close(to_np(vc)[:, :, n:n + w.seq], rv[:, :, n:n + w.seq], w.dtype, "v append")
+        # rows below are untouched
+        assert np.array_equal(to_np(kc)[:, :, :n], cache["k_cache"][:, :, :n])
+    else:
+        out, kc, vc = run_layer(w, h)
+        ref, _, _ = oracle_layer(w, h)
+    assert_close(to_np(out), ref, w.dtype, "out")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "prefill_h1024", "quotient_h4096"])
+def test_entry_points_parity(name):
+    """qkv_proj_normrope, gqa_attn_core and gqa_o_proj separately."""
+    T = T_()
+    w = SMALL[name]
+    announce(f"[entry points] {name}")
+    res = resolved(w)
+    h = GI.host_layer_inputs(w)
+    d = GI.to_device(h, w)
+    cfg = cfg_of(w)
+    q, kc, vc = T.qkv_proj_normrope(cfg, d["x"], d["w_qkv"], d["q_norm_w"], d["k_norm_w"])
+    pos = np.tile(np.arange(w.seq), (w.batch, 1))
+    rq, rk, rv = O.qkv_normrope(res, h["x"].astype(np.float64), h["w_qkv"].astype(np.float64),
+                                h["q_norm_w"].astype(np.float64),
+                                h["k_norm_w"].astype(np.float64), pos, w.rope_theta, w.rms_eps,
+                                qk_norm=w.qk_norm)
+    assert_close(to_np(q), rq, w.dtype, "q")
+    assert_close(to_np(kc), rk, w.dtype, "k")
+    assert_close(to_np(vc), rv, w.dtype, "v")
+    # attention core on the oracle's own q, k, v (rounded to the storage type)
+    qh = GI.round_bf16(rq.astype(np.float32)) if w.dtype == "bf16" else rq.astype(np.float32)
+    kh = GI.round_bf16(rk.astype(np.float32)) if w.dtype == "bf16" else rk.astype(np.float32)
+    vh = GI.round_bf16(rv.astype(np.float32)) if w.dtype == "bf16" else rv.astype(np.float32)
+    dd = GI.to_device({"q": qh, "k": kh, "v": vh}, w)
+    o = T.gqa_attn_core(cfg, dd["q"], dd["k"], dd["v"])
+    ro = O.merge_heads(O.grouped_attention(qh.astype(np.float64), kh.astype(np.float64),
+                                           vh.astype(np.float64), pos,
+                                           np.full(w.batch, w.seq), res.scale, w.causal))
+    assert_close(to_np(o), ro, w.dtype, "attention")
+    # o_proj on an oracle-side activation
+    oh = GI.round_bf16(ro.astype(np.float32)) if w.dtype == "bf16" else ro.astype(np.float32)
+    out = T.gqa_o_proj(cfg, GI.to_device({"o": oh}, w)["o"], d["w_o"])
+    assert_close(to_np(out), O.project(oh.astype(np.float64), h["w_o"].astype(np.float64)),
+                 w.dtype, "o_proj")
+
+
+@pytest.mark.parametrize("variant", [
+    dict(hq=16, hkv=16),            # plain MHA (group 1)
+    dict(hq=12, hkv=4),             # group 3
+    dict(hq=16, hkv=2),             # group 8 -> two workgroups per KV group
+    dict(hq=16, hkv=8, causal=False),
+    dict(hq=8, hkv=8, qk_norm=False, seq=67),
+])
+def test_prefill_variants(variant):
+    seq = variant.pop("seq", 150)
+    w = GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=seq, **variant)
+    announce(f"[variant] {variant} seq={seq}")
+    h = GI.host_layer_inputs(w)
+    out, _, _ = run_layer(w, h)
+    ref, _, _ = oracle_layer(w, h)
+    assert_close(to_np(out), ref, w.dtype, "out")
+
+
+def test_chunked_prefill_with_ragged_cache():
+    """A chunk of new tokens appended to caches of different lengths per
+    sequence (bottom-right causal alignment)."""
+    w = GI.WORKLOADS["prefill_h1024"].with_(batch=3, seq=70, cache_len=300)
+    announce("[chunked prefill] ragged cache lengths")
+    h = GI.host_layer_inputs(w)
+    cache = GI.host_cache(w)
+    cl = np.array([300, 0, 123], dtype=np.int64)
+    for b, n in enumerate(cl):
+        cache["k_cache"][b, :, n:] = np.nan
+        cache["v_cache"][b, :, n:] = np.nan
+    out, kc, vc = run_layer(w, h, cache, cl)
+    ref, rk, _ = oracle_layer(w, h, cache, cl)
+    assert_close(to_np(out), ref, w.dtype, "out")
+
+
+@pytest.mark.parametrize("q_len", [2, 4, 8])
+def test_multi_token_decode(q_len):
+    """A few new tokens per sequence (group * q_len <= 32 takes the split-KV
+    kernel)."""
+    w = GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, seq=q_len, cache_len=531)
+    announce(f"[multi-token decode] q_len={q_len}")
+    h = GI.host_layer_inputs(w)
+    cache = GI.host_cache(w)
+    cl = np.array([531, 200], dtype=np.int64)
+    cache["k_cache"][1, :, 200:] = np.nan
+    cache["v_cache"][1, :, 200:] = np.nan
+    out, _, _ = run_layer(w, h, cache, cl)
+    ref, _, _ = oracle_layer(w, h, cache, cl)
+    assert_close(to_np(out), ref, w.dtype, "out")
+
+
+def test_future_tokens_do_not_leak():
+    """Changing x at t' leaves rows t < t' bitwise unchanged on the GPU
+    (distinguishable heads, nontrivial length)."""
+    w = GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=190)
+    announce("[causality] future-token perturbation")
+    h = GI.host_layer_inputs(w)
+    base, _, _ = run_layer(w, h)
+    for tp in (64, 131, 189):
+        h2 = dict(h)
+        x2 = h["x"].copy()
+        x2[:, tp] += 3.0
+        h2["x"] = GI.round_bf16(x2)
+        pert, _, _ = run_layer(w, h2)
+        a, b = to_np(base), to_np(pert)
+        assert np.array_equal(a[:, :tp], b[:, :tp]), tp
+        assert not np.array_equal(a[:, tp], b[:, tp])
+
+
+@pytest.mark.parametrize("name", ["prefill_h1024", "decode_h2560_gqa"])
+def test_bf16_output_is_rounded_fp32_output(name):
+    """With out_f32 off the o_proj output is the fp32 accumulator rounded to
+    bf16 (nearest even), bit for bit."""
+    w = SMALL[name]
+    h = GI.host_layer_inputs(w)
+    cache, cl = None, None
+    if w.cache_len:
+        cache = GI.host_cache(w)
+        cl = np.full(w.batch, w.cache_len, dtype=np.int64)
+    a, _, _ = run_layer(w, h, cache, cl, out_f32=True)
+    b, _, _ = run_layer(w, h, cache, cl, out_f32=False)
+    assert b.dtype == torch.bfloat16 and a.dtype == torch.float32
+    assert torch.equal(a.to(torch.bfloat16), b)
+
+
+def test_deterministic():
+    w = SMALL["prefill_h1024"]
+    h = GI.host_layer_inputs(w)
+    a, _, _ = run_layer(w, h)
+    b, _, _ = run_layer(w, h)
+    assert torch.equal(a, b)
+
+
+def test_quotient_equals_explicit_head_dim():
+    """head_dim unset resolves to hidden/Hq and gives bitwise the same
+    output as that head_dim set explicitly."""
+    w0 = SMALL["quotient_h4096"]
+    w1 = w0.with_(head_dim=128)
+    h = GI.host_layer_inputs(w0)
+    a, _, _ = run_layer(w0, h)
+    b, _, _ = run_layer(w1, h)
+    assert torch.equal(a, b)
+
+
+def test_prefill_then_decode_matches_prefill():
+    """Prefill of L-1 tokens into a cache, then one decoded token, equals the
+    last row of a prefill over L tokens."""
+    w = GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=97)
+    h = GI.host_layer_inputs(w)
+    full, _, _ = run_layer(w, h)
+    T = T_()
+    d = GI.to_device(h, w)
+    cfg = cfg_of(w)
+    kc = torch.zeros((2, w.hkv, 97, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    T.gqa_layer_forward(cfg, d["x"][:, :96].contiguous(), d["w_qkv"], d["q_norm_w"],
+                        d["k_norm_w"], d["w_o"], k_cache=kc, v_cache=vc,
+                        cache_len=torch.zeros(2, dtype=torch.int32, device="cuda"))
+    last, _, _ = T.gqa_layer_forward(cfg, d["x"][:, 96:].contiguous(), d["w_qkv"],
+                                     d["q_norm_w"], d["k_norm_w"], d["w_o"], k_cache=kc,
+                                     v_cache=vc,
+                                     cache_len=torch.full((2,), 96, dtype=torch.int32,
+                                                          device="cuda"))
+    assert_close(to_np(last)[:, 0], to_np(full)[:, 96], "bf16", "decode vs prefill")
+
+
+def test_empty_calls_are_noops():
+    T = T_()
+    w = SMALL["prefill_h1024"]
+    cfg = cfg_of(w)
+    x = torch.zeros((0, 5, w.hidden), dtype=torch.bfloat16, device="cuda")
+    h = GI.to_device(GI.host_layer_inputs(w.with_(batch=1, seq=1)), w)
+    out, _, _ = T.gqa_layer_forward(cfg, x, h["w_qkv"], h["q_norm_w"], h["k_norm_w"], h["w_o"])
+    assert out.shape == (0, 5, w.hidden)

@@ -1,0 +1,395 @@
+// Grouped causal attention on the bf16 matrix cores of gfx950, head_dim 128.
+//
+// Computes softmax(q k^T * d^-0.5 + mask) v with query head h reading KV
+// head h / (Hq/Hkv) (tutorial "Multi-Head and Grouped-Query Attention (Full
+// Layer)", section 4 step 6; "Attention head partitions: keep each head's
+// dependencies intact" for the grouping; GPT-NeoX issue "Scaling and RoPE"
+// for the scale).  The softmax is exact: it is evaluated tile by tile over
+// the keys with a running maximum and sum ("num_heads Is Not a Capacity
+// Knob", "Why the cost does not move": a flash-style kernel changes the
+// memory traffic of the same products, not their result).
+//
+// Layout inside a wave.  A wave owns 32 query rows.  Scores are formed
+// transposed, S^T = K Q^T (keys are MFMA rows, queries MFMA columns), so
+// lane l holds one query (l % 32) and half of each 32-key block; the row max
+// and sum need a single exchange with lane l ^ 32, and the rescale factor is
+// one scalar per lane.  O^T = V^T P^T then takes P^T straight from the score
+// registers; V^T is built in LDS while the tile is stored, with the keys of
+// each 16-key group in the order the score registers hold them.
+//
+// Two kernels:
+//   prefill: a workgroup of 4 waves covers up to 4 query heads of one KV
+//            group at the same 32 positions (or 2 heads x 64 positions, or
+//            1 head x 128), so every wave walks the same causal key range and
+//            each K/V tile is staged in LDS once for the whole group.
+//   decode : one wave per (sequence, KV head, key split); its 32 rows are the
+//            group's query heads (x the few new tokens).  Partial (max, sum,
+//            unnormalised output) per split are merged by a second kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kD = 128;
+
+// K tile: rows = keys, 256 B = 16 chunks each; chunk c of row r at slot
+// c ^ (r & 15).
+__device__ __forceinline__ int kslot(int row, int chunk) { return (row << 4) + (chunk ^ (row & 15)); }
+
+// V^T tile: rows = the 128 value features, TK keys each (TK/8 chunks).  Key
+// 16g + 8a + 4h + i is stored at position 16g + 8h + 4a + i, so chunk 2g + h
+// holds exactly the eight keys lane-half h feeds to the PV product of key
+// group g.  Chunks are XOR-swizzled with (r ^ r>>2) to spread rows over banks.
+template <int TK>
+__device__ __forceinline__ int vslot(int row, int chunk) {
+  constexpr int NCH = TK / 8;
+  return row * NCH + (chunk ^ ((row ^ (row >> 2)) & (NCH - 1)));
+}
+
+template <int NT, int TK>
+struct KVRegs {
+  static constexpr int kK = TK * 16 / NT;  // 16-byte chunks of K per thread
+  static constexpr int kV = TK * 8 / NT;   // 4-key x 4-feature groups of V per thread
+  u32x4 k[kK];
+  u32x2 v[kV][4];
+};
+
+template <int NT, int TK>
+__device__ __forceinline__ void load_kv(KVRegs<NT, TK>& r, const bf16* __restrict__ kb,
+                                        const bf16* __restrict__ vb, int key0, int kend, int tid) {
+#pragma unroll
+  for (int i = 0; i < KVRegs<NT, TK>::kK; ++i) {
+    const int idx = tid + i * NT;
+    const int key = key0 + (idx >> 4);
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < kend) val = ld16(kb + (size_t)key * kD + (idx & 15) * 8);
+    r.k[i] = val;
+  }
+#pragma unroll
+  for (int i = 0; i < KVRegs<NT, TK>::kV; ++i) {
+    const int idx = tid + i * NT;
+    const int g4 = idx & 31;
+    const int kq = idx >> 5;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = key0 + 4 * kq + e;
+      u32x2 val = {0u, 0u};
+      if (key < kend) val = ld8(vb + (size_t)key * kD + 4 * g4);
+      r.v[i][e] = val;
+    }
+  }
+}
+
+template <int NT, int TK>
+__device__ __forceinline__ void store_kv(const KVRegs<NT, TK>& r, u32x4* sk, u32x4* sv, int tid) {
+#pragma unroll
+  for (int i = 0; i < KVRegs<NT, TK>::kK; ++i) {
+    const int idx = tid + i * NT;
+    sk[kslot(idx >> 4, idx & 15)] = r.k[i];
+  }
+  u32x2* sv2 = reinterpret_cast<u32x2*>(sv);
+#pragma unroll
+  for (int i = 0; i < KVRegs<NT, TK>::kV; ++i) {
+    const int idx = tid + i * NT;
+    const int g4 = idx & 31;
+    const int kq = idx >> 5;                 // keys 4kq .. 4kq+3 of the tile
+    const int chunk = 2 * (kq >> 2) + (kq & 1);
+    const int half = (kq >> 1) & 1;
+    const u32x2* v = r.v[i];
+    // 4 keys x 4 features -> 4 features x 4 keys
+    u32x2 t0, t1, t2, t3;
+    t0.x = (v[0].x & 0xffffu) | (v[1].x << 16);
+    t0.y = (v[2].x & 0xffffu) | (v[3].x << 16);
+    t1.x = (v[0].x >> 16) | (v[1].x & 0xffff0000u);
+    t1.y = (v[2].x >> 16) | (v[3].x & 0xffff0000u);
+    t2.x = (v[0].y & 0xffffu) | (v[1].y << 16);
+    t2.y = (v[2].y & 0xffffu) | (v[3].y << 16);
+    t3.x = (v[0].y >> 16) | (v[1].y & 0xffff0000u);
+    t3.y = (v[2].y >> 16) | (v[3].y & 0xffff0000u);
+    const int row = 4 * g4;
+    sv2[vslot<TK>(row + 0, chunk) * 2 + half] = t0;
+    sv2[vslot<TK>(row + 1, chunk) * 2 + half] = t1;
+    sv2[vslot<TK>(row + 2, chunk) * 2 + half] = t2;
+    sv2[vslot<TK>(row + 3, chunk) * 2 + half] = t3;
+  }
+}
+
+// Running state of one wave: 32 query rows, lane = row (l % 32).
+struct RowState {
+  floatx16 o[4];   // O^T: value feature 32*db + 8*(r/4) + 4*(l/32) + r%4
+  float m;         // running max (log2 units)
+  float l;         // running sum, this lane-half's keys only
+};
+
+__device__ __forceinline__ void init_state(RowState& st) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[d][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// One key tile: scores, online softmax, PV.  `kend_row` = one past the last
+// key this lane's query may see; `masked` = some key of the tile may be past
+// it for some row of the wave.
+template <int TK, int NCH_V>
+__device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], const u32x4* sk,
+                                            const u32x4* sv, int key0, int kend_row, bool masked,
+                                            float scale_log2, int l32, int hh) {
+  constexpr int KB = TK / 32;
+  floatx16 s[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[kb] = mfma32x32x16(sk[kslot(32 * kb + l32, 2 * c + hh)], qf[c], s[kb]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[kb][r] * scale_log2;
+      if (masked) {
+        const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        x = key < kend_row ? x : -INFINITY;
+      }
+      s[kb][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  mx = fmaxf(mx, wave_xor32(mx));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(s[kb][r] - m_use);
+      s[kb][r] = p;
+      rs += p;
+    }
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[d][r] *= alpha;
+  }
+#pragma unroll
+  for (int g = 0; g < TK / 16; ++g) {
+    const int kb = g >> 1;
+    const int rb = 8 * (g & 1);
+    u32x4 pf;
+    pf.x = pack_bf16x2(s[kb][rb + 0], s[kb][rb + 1]);
+    pf.y = pack_bf16x2(s[kb][rb + 2], s[kb][rb + 3]);
+    pf.z = pack_bf16x2(s[kb][rb + 4], s[kb][rb + 5]);
+    pf.w = pack_bf16x2(s[kb][rb + 6], s[kb][rb + 7]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) st.o[d] = mfma32x32x16(sv[vslot<TK>(32 * d + l32, 2 * g + hh)], pf, st.o[d]);
+  }
+}
+
+__device__ __forceinline__ int kv_len_of(const AttnArgs& a, int b) {
+  int n = (a.kv_base ? a.kv_base[b] : 0) + a.kv_add;
+  return n < 0 ? 0 : (n > a.cap ? a.cap : n);
+}
+
+__device__ __forceinline__ void load_q(u32x4 (&qf)[8], const bf16* qrow, bool valid, int hh) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (valid) v = ld16(qrow + 16 * c + 8 * hh);
+    qf[c] = v;
+  }
+}
+
+constexpr int kPrefillTK = 64;
+constexpr int kPrefillNT = 256;
+
+__global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a) {
+  constexpr int TK = kPrefillTK, NT = kPrefillNT;
+  __shared__ u32x4 sk[2][TK * 16];
+  __shared__ u32x4 sv[2][kD * TK / 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qt = a.n_qtiles - 1 - (int)blockIdx.z;  // heaviest query tiles first
+  const int b = blockIdx.y;
+  const int kvh = blockIdx.x / a.n_hsub;
+  const int hsub = blockIdx.x - kvh * a.n_hsub;
+  const int head_local = wave % a.hpw;
+  const int pblk = wave / a.hpw;
+  const int hq = kvh * a.G + hsub * a.hpw + head_local;
+
+  const int kvl = kv_len_of(a, b);
+  const int off = kvl - a.Lq;  // query i sits at position off + i
+  const int wg_t0 = qt * a.pb * 32;
+  const int wg_tlast = min(wg_t0 + a.pb * 32, a.Lq) - 1;
+  const int key_end_wg = a.causal ? min(kvl, off + wg_tlast + 1) : kvl;
+  const int n_tiles = key_end_wg > 0 ? (key_end_wg + TK - 1) / TK : 0;
+
+  const int t0 = wg_t0 + pblk * 32;
+  const bool wave_live = t0 < a.Lq;
+  const int w_tlast = min(t0 + 31, a.Lq - 1);
+  const int key_end_w = wave_live ? (a.causal ? min(kvl, off + w_tlast + 1) : kvl) : 0;
+  const int kmin_w = a.causal ? min(kvl, off + t0 + 1) : kvl;
+  const int tq = t0 + l32;
+  const bool row_valid = tq < a.Lq;
+  const int kend_row = row_valid ? (a.causal ? min(kvl, off + tq + 1) : kvl) : 0;
+
+  u32x4 qf[8];
+  load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + (row_valid ? tq : 0)) * kD, row_valid, hh);
+
+  const bf16* kb = a.k + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const bf16* vb = a.v + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+
+  RowState st;
+  init_state(st);
+  KVRegs<NT, TK> regs;
+  if (n_tiles > 0) {
+    load_kv<NT, TK>(regs, kb, vb, 0, kvl, tid);
+    store_kv<NT, TK>(regs, sk[0], sv[0], tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_tiles) load_kv<NT, TK>(regs, kb, vb, (it + 1) * TK, kvl, tid);
+    const int key0 = it * TK;
+    if (key0 < key_end_w) {
+      const bool masked = key0 + TK > kmin_w;
+      attend_tile<TK, TK / 8>(st, qf, sk[buf], sv[buf], key0, kend_row, masked, a.scale_log2, l32, hh);
+    }
+    if (it + 1 < n_tiles) store_kv<NT, TK>(regs, sk[buf ^ 1], sv[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+  const float lt = st.l + wave_xor32(st.l);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (!row_valid) return;
+  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * ((size_t)a.Hq * kD) + (size_t)hq * kD;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w.x = pack_bf16x2(st.o[d][4 * j + 0] * inv, st.o[d][4 * j + 1] * inv);
+      w.y = pack_bf16x2(st.o[d][4 * j + 2] * inv, st.o[d][4 * j + 3] * inv);
+      st8(orow + 32 * d + 8 * j + 4 * hh, w);
+    }
+}
+
+constexpr int kDecodeTK = 32;
+constexpr int kDecodeNT = 64;
+
+__global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
+  constexpr int TK = kDecodeTK, NT = kDecodeNT;
+  __shared__ u32x4 sk[2][TK * 16];
+  __shared__ u32x4 sv[2][kD * TK / 8];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int rows = a.G * a.Lq;
+  const bool row_valid = l32 < rows;
+  const int head_local = row_valid ? l32 / a.Lq : 0;
+  const int tq = row_valid ? l32 - head_local * a.Lq : 0;
+  const int hq = kvh * a.G + head_local;
+
+  const int kvl = kv_len_of(a, b);
+  const int off = kvl - a.Lq;
+  int ks = split * a.chunk;
+  int ke = min(ks + a.chunk, kvl);
+  if (a.causal) ke = min(ke, off + a.Lq);
+  const int n_tiles = ke > ks ? (ke - ks + TK - 1) / TK : 0;
+  const int kend_row = row_valid ? min(ke, a.causal ? min(kvl, off + tq + 1) : kvl) : 0;
+  const int kmin = min(ke, a.causal ? min(kvl, off + 1) : kvl);
+
+  u32x4 qf[8];
+  load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + tq) * kD, row_valid, hh);
+
+  const bf16* kb = a.k + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const bf16* vb = a.v + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+
+  RowState st;
+  init_state(st);
+  KVRegs<NT, TK> regs;
+  if (n_tiles > 0) {
+    load_kv<NT, TK>(regs, kb, vb, ks, ke, lane);
+    store_kv<NT, TK>(regs, sk[0], sv[0], lane);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const int key0 = ks + it * TK;
+    if (it + 1 < n_tiles) load_kv<NT, TK>(regs, kb, vb, key0 + TK, ke, lane);
+    const bool masked = key0 + TK > kmin;
+    attend_tile<TK, TK / 8>(st, qf, sk[buf], sv[buf], key0, kend_row, masked, a.scale_log2, l32, hh);
+    if (it + 1 < n_tiles) store_kv<NT, TK>(regs, sk[buf ^ 1], sv[buf ^ 1], lane);
+    __syncthreads();
+  }
+
+  const float lt = st.l + wave_xor32(st.l);
+  if (!row_valid) return;  // only the group's real rows are merged
+  const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * 32 + l32;
+  if (hh == 0) a.part_ml[pidx] = make_float2(st.m, lt);
+  float* po = a.part_o + pidx * kD;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      floatx4 w = {st.o[d][4 * j + 0], st.o[d][4 * j + 1], st.o[d][4 * j + 2], st.o[d][4 * j + 3]};
+      *reinterpret_cast<floatx4*>(po + 32 * d + 8 * j + 4 * hh) = w;
+    }
+}
+
+// Merge the per-split partials of one (sequence, KV head, row) with their
+// log-sum-exp weights.
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int head_local = row / a.Lq;
+  const int tq = row - head_local * a.Lq;
+  const int hq = kvh * a.G + head_local;
+  const size_t base = (((size_t)b * a.Hkv + kvh) * a.n_splits) * 32 + row;
+  float mmax = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
+  const float muse = mmax == -INFINITY ? 0.f : mmax;
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float2 ml = a.part_ml[base + (size_t)s * 32];
+    const float w = fast_exp2(ml.x - muse);
+    lsum += w * ml.y;
+    const float* po = a.part_o + (base + (size_t)s * 32) * kD + 2 * lane;
+    o0 += w * po[0];
+    o1 += w * po[1];
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * ((size_t)a.Hq * kD) + (size_t)hq * kD;
+  *reinterpret_cast<unsigned int*>(orow + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+  dim3 grid(a.Hkv * a.n_hsub, a.B, a.n_qtiles);
+  attn_prefill_kernel<<<grid, kPrefillNT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode_bf16(const AttnArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_splits, a.Hkv, a.B);
+  attn_decode_kernel<<<grid, kDecodeNT, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid2(a.G * a.Lq, a.Hkv, a.B);
+  attn_combine_kernel<<<grid2, 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,176 @@
+// fp32 path of the layer (any even head_dim from 2 to 256).  Plain VALU
+// kernels: a tiled GEMM, a per-(token, head) QK-norm + RoPE + scatter, and a
+// one-wave-per-query attention with an online softmax.  Same steps as the
+// bf16 path (tutorial "Multi-Head and Grouped-Query Attention (Full Layer)",
+// section 4 steps 1-7), in float throughout.
+#include "common.h"
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kT = 64;   // output tile (tokens and features)
+constexpr int kKT = 16;  // K step
+
+// y[m, n] = sum_k x[m, k] w[n, k]; 256 threads, 4 x 4 outputs each.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args a) {
+  __shared__ float sx[kKT][kT + 1];
+  __shared__ float sw[kKT][kT + 1];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < a.K; k0 += kKT) {
+    for (int i = tid; i < kT * kKT; i += 256) {
+      const int r = i / kKT, c = i % kKT;
+      const int gm = m0 + r, gn = n0 + r, gk = k0 + c;
+      sx[c][r] = (gm < a.M && gk < a.K) ? a.x[(size_t)gm * a.K + gk] : 0.f;
+      sw[c][r] = (gn < a.N && gk < a.K) ? a.w[(size_t)gn * a.K + gk] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < kKT; ++c) {
+      float xv[4], wv[4];
+      for (int i = 0; i < 4; ++i) xv[i] = sx[c][ty + 16 * i];
+      for (int j = 0; j < 4; ++j) wv[j] = sw[c][tx + 16 * j];
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty + 16 * i;
+    if (m >= a.M) continue;
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n < a.N) a.y[(size_t)m * a.N + n] = acc[i][j];
+    }
+  }
+}
+
+// One workgroup per (token, head of the fused projection); thread j < d/2
+// owns the RoPE pair (j, j + d/2).
+__global__ __launch_bounds__(128) void normrope_f32_kernel(F32NormRopeArgs a) {
+  __shared__ float red[128];
+  const int m = blockIdx.x;       // token
+  const int head = blockIdx.y;    // 0 .. Hq + 2 Hkv - 1
+  const int j = threadIdx.x;
+  const int d = a.d, half = d >> 1;
+  const int b = m / a.L, tok = m - b * a.L;
+  const int n_qkv = (a.Hq + 2 * a.Hkv) * d;
+  const float* y = a.y + (size_t)m * n_qkv + (size_t)head * d;
+  int kind, h;
+  if (head < a.Hq) { kind = 0; h = head; }
+  else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
+  else { kind = 2; h = head - a.Hq - a.Hkv; }
+  const bool act = j < half;
+  float x1 = act ? y[j] : 0.f;
+  float x2 = act ? y[j + half] : 0.f;
+  const long pos = (long)(a.start_pos ? a.start_pos[b] : 0) + tok;
+  if (kind != 2) {
+    if (a.qk_norm) {
+      red[j] = x1 * x1 + x2 * x2;
+      __syncthreads();
+      for (int s = 64; s > 0; s >>= 1) {
+        if (j < s) red[j] += red[j + s];
+        __syncthreads();
+      }
+      const float inv = 1.0f / sqrtf(red[0] / (float)d + a.eps);
+      const float* w = kind == 0 ? a.q_norm_w : a.k_norm_w;
+      if (act) {
+        x1 = x1 * inv * w[j];
+        x2 = x2 * inv * w[j + half];
+      }
+    }
+    if (act) {
+      const double ang = (double)pos * pow(a.theta, -2.0 * (double)j / (double)d);
+      double sd, cd;
+      sincos(ang, &sd, &cd);
+      const float c = (float)cd, s = (float)sd;
+      const float y1 = x1 * c - x2 * s;
+      const float y2 = x2 * c + x1 * s;
+      x1 = y1;
+      x2 = y2;
+    }
+  }
+  if (!act) return;
+  float* dst;
+  if (kind == 0) {
+    dst = a.q + (((size_t)b * a.Hq + h) * a.L + tok) * d;
+  } else {
+    if (pos < 0 || pos >= a.cap) return;
+    dst = (kind == 1 ? a.k_cache : a.v_cache) + (((size_t)b * a.Hkv + h) * a.cap + pos) * d;
+  }
+  dst[j] = x1;
+  dst[j + half] = x2;
+}
+
+// One wave per (query, head, sequence); lane e owns features e, e+64, ...
+__global__ __launch_bounds__(64) void attn_f32_kernel(F32AttnArgs a) {
+  const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int d = a.d;
+  const int G = a.Hq / a.Hkv;
+  const int kvh = hq / G;
+  int kvl = (a.kv_base ? a.kv_base[b] : 0) + a.kv_add;
+  kvl = kvl < 0 ? 0 : (kvl > a.cap ? a.cap : kvl);
+  const int qpos = kvl - a.Lq + i;
+  const int kend = a.causal ? min(kvl, qpos + 1) : kvl;
+  const float* q = a.q + (((size_t)b * a.Hq + hq) * a.Lq + i) * d;
+  const float* kb = a.k + ((size_t)b * a.Hkv + kvh) * a.cap * d;
+  const float* vb = a.v + ((size_t)b * a.Hkv + kvh) * a.cap * d;
+  float qv[4], ov[4];
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    qv[u] = e < d ? q[e] : 0.f;
+    ov[u] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < kend; ++j) {
+    const float* kr = kb + (size_t)j * d;
+    float part = 0.f;
+    for (int u = 0; u < 4; ++u) {
+      const int e = lane + 64 * u;
+      if (e < d) part = fmaf(qv[u], kr[e], part);
+    }
+    for (int s = 32; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
+    const float x = part * a.scale;
+    const float m_new = fmaxf(m, x);
+    const float alpha = expf(m - m_new);
+    const float p = expf(x - m_new);
+    l = l * alpha + p;
+    const float* vr = vb + (size_t)j * d;
+    for (int u = 0; u < 4; ++u) {
+      const int e = lane + 64 * u;
+      ov[u] = ov[u] * alpha + (e < d ? p * vr[e] : 0.f);
+    }
+    m = m_new;
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  float* o = a.o + ((size_t)b * a.Lq + i) * ((size_t)a.Hq * d) + (size_t)hq * d;
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    if (e < d) o[e] = ov[u] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f32(const F32Args& a, hipStream_t stream) {
+  dim3 grid((a.N + kT - 1) / kT, (a.M + kT - 1) / kT);
+  gemm_f32_kernel<<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_normrope_f32(const F32NormRopeArgs& a, hipStream_t stream) {
+  dim3 grid(a.B * a.L, a.Hq + 2 * a.Hkv);
+  normrope_f32_kernel<<<grid, 128, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const F32AttnArgs& a, hipStream_t stream) {
+  dim3 grid(a.Lq, a.Hq, a.B);
+  attn_f32_kernel<<<grid, 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

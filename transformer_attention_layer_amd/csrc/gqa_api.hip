@@ -1,0 +1,428 @@
+// C ABI of the GQA layer library: host-side resolution and validation of the
+// configuration, workspace sizing, and dispatch to the gfx950 kernels.
+//
+// Configuration rules (GPT-NeoX issue "Support explicit attention head_dim
+// independent of hidden_size / num_attention_heads", sections "Proposed
+// configuration behavior", "Proposed implementation" and "Scaling and
+// RoPE"; "Attention head partitions: keep each head's dependencies intact"
+// for whole GQA groups):
+//   d   = head_dim if set, else hidden / Hq (which must then divide evenly)
+//   Hkv = num_kv_heads if set, else Hq;  Hq % Hkv == 0;  d even.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gqa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gqa_status fail(gqa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gqa_status ok() {
+  g_err[0] = '\0';
+  return GQA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+  int H, Hq, Hkv, d, G, n_qkv;
+  bool bf16;
+  bool out_f32;  // o_proj output in fp32
+};
+
+gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
+  if (!in) return fail(GQA_ERR_INVALID_ARG, "config pointer is null");
+  gqa_config c = *in;
+  if (c.hidden_size <= 0 || c.num_heads <= 0)
+    return fail(GQA_ERR_INVALID_ARG, "hidden_size (%d) and num_heads (%d) must be positive",
+                c.hidden_size, c.num_heads);
+  if (c.num_kv_heads < 0 || c.head_dim < 0)
+    return fail(GQA_ERR_INVALID_ARG, "num_kv_heads and head_dim must be >= 0 (0 = unset)");
+  if (c.head_dim == 0) {
+    if (c.hidden_size % c.num_heads != 0)
+      return fail(GQA_ERR_HEAD_DIM_INDIVISIBLE,
+                  "head_dim unset and hidden_size %d is not divisible by num_heads %d",
+                  c.hidden_size, c.num_heads);
+    c.head_dim = c.hidden_size / c.num_heads;
+  }
+  if (c.num_kv_heads == 0) c.num_kv_heads = c.num_heads;
+  if (c.num_heads % c.num_kv_heads != 0)
+    return fail(GQA_ERR_GROUP_INDIVISIBLE, "num_heads %d is not a multiple of num_kv_heads %d",
+                c.num_heads, c.num_kv_heads);
+  if (c.head_dim % 2 != 0)
+    return fail(GQA_ERR_ODD_HEAD_DIM, "head_dim %d is odd; RoPE needs an even head_dim",
+                c.head_dim);
+  if (c.dtype != GQA_F32 && c.dtype != GQA_BF16)
+    return fail(GQA_ERR_UNSUPPORTED_DTYPE, "dtype %d is not GQA_F32 or GQA_BF16", c.dtype);
+  if (c.dtype == GQA_BF16 && c.head_dim != 128)
+    return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
+                "Unsupported head_dim %d: the bf16 MFMA kernels are built for head_dim 128",
+                c.head_dim);
+  if (c.dtype == GQA_F32 && c.head_dim > 256)
+    return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
+                "Unsupported head_dim %d: the fp32 kernels take even head_dim up to 256", c.head_dim);
+  if (c.dtype == GQA_BF16 && c.hidden_size % 8 != 0)
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "hidden_size %d must be a multiple of 8 for bf16",
+                c.hidden_size);
+  if (!(c.rope_theta > 0.f) || !isfinite(c.rope_theta))
+    return fail(GQA_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+  if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
+    return fail(GQA_ERR_INVALID_ARG, "rms_eps must be >= 0 and finite");
+  if ((c.qk_norm != 0 && c.qk_norm != 1) || (c.causal != 0 && c.causal != 1) ||
+      (c.out_f32 != 0 && c.out_f32 != 1))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm, causal and out_f32 must be 0 or 1");
+  // every kernel indexes heads and widths in 32-bit
+  const long long n_qkv = (long long)(c.num_heads + 2LL * c.num_kv_heads) * c.head_dim;
+  if (n_qkv > (1LL << 30) || (long long)c.num_heads * c.head_dim > (1LL << 30))
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "projection widths exceed 2^30");
+  if (out) *out = c;
+  if (sh) {
+    sh->H = c.hidden_size;
+    sh->Hq = c.num_heads;
+    sh->Hkv = c.num_kv_heads;
+    sh->d = c.head_dim;
+    sh->G = c.num_heads / c.num_kv_heads;
+    sh->n_qkv = (int)n_qkv;
+    sh->bf16 = c.dtype == GQA_BF16;
+    sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
+  }
+  return GQA_OK;
+}
+
+size_t esize(const Shape& s) { return s.bf16 ? 2 : 4; }
+
+// split-KV decode is used when a KV group's query rows fit one wave
+bool use_decode(const Shape& s, int q_len) { return s.bf16 && s.G * q_len <= 32; }
+
+void decode_split(const Shape& s, int batch, int cap, int* n_splits, int* chunk) {
+  const long long streams = (long long)batch * s.Hkv;
+  long long want = (4096 + streams - 1) / (streams > 0 ? streams : 1);
+  long long max_splits = (cap + 255) / 256;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  int ch = (int)((cap + want - 1) / want);
+  ch = (ch + 31) / 32 * 32;
+  if (ch < 32) ch = 32;
+  *chunk = ch;
+  *n_splits = (cap + ch - 1) / ch;
+  if (*n_splits < 1) *n_splits = 1;
+}
+
+size_t ws_qkv(const Shape& s, int batch, int q_len) {
+  const size_t T = (size_t)batch * q_len;
+  if (s.bf16) return align_up(T * (s.d / 2) * sizeof(float) * 2);  // rope table, T rows max
+  return align_up(T * (size_t)s.n_qkv * sizeof(float));             // fp32 projection output
+}
+
+size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
+  if (!use_decode(s, q_len)) return 0;
+  int ns, ch;
+  decode_split(s, batch, cap, &ns, &ch);
+  const size_t parts = (size_t)batch * s.Hkv * ns * 32;
+  return align_up(parts * 128 * sizeof(float)) + align_up(parts * 2 * sizeof(float));
+}
+
+size_t ws_layer(const Shape& s, int batch, int q_len, int cap) {
+  const size_t T = (size_t)batch * q_len;
+  return ws_qkv(s, batch, q_len) + align_up(T * s.Hq * s.d * esize(s)) /* q */ +
+         align_up(T * s.Hq * s.d * esize(s)) /* attention output */ + ws_attn(s, batch, q_len, cap);
+}
+
+gqa_status check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return GQA_OK;
+}
+
+gqa_status check_common(const Shape& s, int batch, int q_len, int cap) {
+  if (batch < 0 || q_len < 0) return fail(GQA_ERR_INVALID_ARG, "batch and q_len must be >= 0");
+  if (cap < q_len)
+    return fail(GQA_ERR_CAPACITY, "kv_capacity %d is smaller than q_len %d", cap, q_len);
+  if ((long long)batch * q_len > 65535LL * 64)
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "batch * q_len exceeds %lld tokens", 65535LL * 64);
+  if (batch > 65535) return fail(GQA_ERR_UNSUPPORTED_SHAPE, "batch exceeds 65535");
+  (void)s;
+  return GQA_OK;
+}
+
+gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, const void* x,
+                   const void* w_qkv, const void* qn, const void* kn, const int32_t* start_pos,
+                   void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st) {
+  const int T = batch * q_len;
+  if (s.bf16) {
+    float2* table = reinterpret_cast<float2*>(ws);
+    const int rows = start_pos ? T : q_len;
+    gqa_status r = check_launch(
+        gqa::launch_rope_table(table, start_pos, rows, q_len, s.d / 2, (double)c.rope_theta, st),
+        "rope table");
+    if (r != GQA_OK) return r;
+    gqa::GemmArgs g{};
+    g.W = static_cast<const __bf16*>(w_qkv);
+    g.X = static_cast<const __bf16*>(x);
+    g.N = s.n_qkv;
+    g.M = T;
+    g.K = s.H;
+    g.q = static_cast<__bf16*>(q);
+    g.k_cache = static_cast<__bf16*>(kc);
+    g.v_cache = static_cast<__bf16*>(vc);
+    g.q_norm_w = static_cast<const __bf16*>(qn);
+    g.k_norm_w = static_cast<const __bf16*>(kn);
+    g.rope = table;
+    g.start_pos = start_pos;
+    g.L = q_len;
+    g.Hq = s.Hq;
+    g.Hkv = s.Hkv;
+    g.cap = cap;
+    g.qk_norm = c.qk_norm;
+    g.eps = c.rms_eps;
+    return check_launch(gqa::launch_gemm_qkv_bf16(g, st), "qkv projection");
+  }
+  float* y = reinterpret_cast<float*>(ws);
+  gqa::F32Args g{static_cast<const float*>(x), static_cast<const float*>(w_qkv), y, T, s.n_qkv, s.H};
+  gqa_status r = check_launch(gqa::launch_gemm_f32(g, st), "qkv projection (f32)");
+  if (r != GQA_OK) return r;
+  gqa::F32NormRopeArgs n{};
+  n.y = y;
+  n.q_norm_w = static_cast<const float*>(qn);
+  n.k_norm_w = static_cast<const float*>(kn);
+  n.start_pos = start_pos;
+  n.q = static_cast<float*>(q);
+  n.k_cache = static_cast<float*>(kc);
+  n.v_cache = static_cast<float*>(vc);
+  n.B = batch;
+  n.L = q_len;
+  n.Hq = s.Hq;
+  n.Hkv = s.Hkv;
+  n.d = s.d;
+  n.cap = cap;
+  n.qk_norm = c.qk_norm;
+  n.eps = c.rms_eps;
+  n.theta = (double)c.rope_theta;
+  return check_launch(gqa::launch_normrope_f32(n, st), "norm + rope (f32)");
+}
+
+gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, const void* q,
+                    const void* kc, const void* vc, const int32_t* kv_base, int kv_add, int cap,
+                    void* o, void* ws, hipStream_t st) {
+  const double scale = 1.0 / sqrt((double)s.d);
+  if (!s.bf16) {
+    gqa::F32AttnArgs a{};
+    a.q = static_cast<const float*>(q);
+    a.k = static_cast<const float*>(kc);
+    a.v = static_cast<const float*>(vc);
+    a.o = static_cast<float*>(o);
+    a.kv_base = kv_base;
+    a.kv_add = kv_add;
+    a.B = batch;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.Lq = q_len;
+    a.cap = cap;
+    a.d = s.d;
+    a.causal = c.causal;
+    a.scale = (float)scale;
+    return check_launch(gqa::launch_attn_f32(a, st), "attention (f32)");
+  }
+  gqa::AttnArgs a{};
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(kc);
+  a.v = static_cast<const __bf16*>(vc);
+  a.o = static_cast<__bf16*>(o);
+  a.kv_base = kv_base;
+  a.kv_add = kv_add;
+  a.B = batch;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.Lq = q_len;
+  a.cap = cap;
+  a.causal = c.causal;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  if (use_decode(s, q_len)) {
+    decode_split(s, batch, cap, &a.n_splits, &a.chunk);
+    const size_t parts = (size_t)batch * s.Hkv * a.n_splits * 32;
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(parts * 128 * sizeof(float)));
+    return check_launch(gqa::launch_attn_decode_bf16(a, st), "decode attention");
+  }
+  int hpw = 1;
+  if (s.G % 4 == 0) hpw = 4;
+  else if (s.G % 2 == 0) hpw = 2;
+  a.hpw = hpw;
+  a.pb = 4 / hpw;
+  a.n_hsub = s.G / hpw;
+  a.n_qtiles = (q_len + a.pb * 32 - 1) / (a.pb * 32);
+  if (a.n_qtiles > 65535)
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "q_len %d needs more than 65535 query tiles", q_len);
+  return check_launch(gqa::launch_attn_prefill_bf16(a, st), "prefill attention");
+}
+
+gqa_status run_oproj(const Shape& s, int tokens, const void* o, const void* w_o, void* out,
+                     hipStream_t st) {
+  if (s.bf16) {
+    gqa::GemmArgs g{};
+    g.W = static_cast<const __bf16*>(w_o);
+    g.X = static_cast<const __bf16*>(o);
+    g.N = s.H;
+    g.M = tokens;
+    g.K = s.Hq * s.d;
+    g.out = out;
+    g.out_f32 = s.out_f32;
+    return check_launch(gqa::launch_gemm_plain_bf16(g, st), "o_proj");
+  }
+  gqa::F32Args g{static_cast<const float*>(o), static_cast<const float*>(w_o),
+                 static_cast<float*>(out), tokens, s.H, s.Hq * s.d};
+  return check_launch(gqa::launch_gemm_f32(g, st), "o_proj (f32)");
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_resolve(const gqa_config* in, gqa_config* out) {
+  gqa_status r = resolve(in, out, nullptr);
+  return r == GQA_OK ? ok() : r;
+}
+
+size_t gqa_workspace_bytes(const gqa_config* cfg, int32_t batch, int32_t q_len,
+                           int32_t kv_capacity, int32_t kind) {
+  Shape s;
+  if (resolve(cfg, nullptr, &s) != GQA_OK || batch < 0 || q_len < 0) return 0;
+  switch (kind) {
+    case GQA_WS_QKV: return ws_qkv(s, batch, q_len);
+    case GQA_WS_ATTN: return ws_attn(s, batch, q_len, kv_capacity);
+    case GQA_WS_LAYER: return ws_layer(s, batch, q_len, kv_capacity);
+    case GQA_WS_OPROJ: return 0;
+    default: return 0;
+  }
+}
+
+gqa_status qkv_proj_normrope(const gqa_config* cfg, int32_t batch, int32_t q_len, const void* x,
+                             const void* w_qkv, const void* q_norm_w, const void* k_norm_w,
+                             const int32_t* start_pos, void* q, void* k_cache, void* v_cache,
+                             int32_t kv_capacity, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  gqa_config c;
+  Shape s;
+  gqa_status r = resolve(cfg, &c, &s);
+  if (r != GQA_OK) return r;
+  if ((r = check_common(s, batch, q_len, kv_capacity)) != GQA_OK) return r;
+  if (batch == 0 || q_len == 0) return ok();
+  if (!x || !w_qkv || !q || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, q, k_cache and v_cache must be non-null");
+  if (c.qk_norm && (!q_norm_w || !k_norm_w))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
+  const size_t need = ws_qkv(s, batch, q_len);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes);
+  r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, start_pos, q, k_cache, v_cache,
+              kv_capacity, workspace, (hipStream_t)stream);
+  return r == GQA_OK ? ok() : r;
+}
+
+gqa_status gqa_attn_core(const gqa_config* cfg, int32_t batch, int32_t q_len, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                         int32_t kv_capacity, void* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  gqa_config c;
+  Shape s;
+  gqa_status r = resolve(cfg, &c, &s);
+  if (r != GQA_OK) return r;
+  if ((r = check_common(s, batch, q_len, kv_capacity)) != GQA_OK) return r;
+  if (batch == 0 || q_len == 0) return ok();
+  if (!q || !k_cache || !v_cache || !o)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-null");
+  const size_t need = ws_attn(s, batch, q_len, kv_capacity);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes);
+  r = run_attn(c, s, batch, q_len, q, k_cache, v_cache, kv_len, kv_len ? 0 : q_len, kv_capacity, o,
+               workspace, (hipStream_t)stream);
+  return r == GQA_OK ? ok() : r;
+}
+
+gqa_status gqa_o_proj(const gqa_config* cfg, int32_t tokens, const void* o, const void* w_o,
+                      void* out, void* stream) {
+  gqa_config c;
+  Shape s;
+  gqa_status r = resolve(cfg, &c, &s);
+  if (r != GQA_OK) return r;
+  if (tokens < 0) return fail(GQA_ERR_INVALID_ARG, "tokens must be >= 0");
+  if (tokens > 65535 * 64) return fail(GQA_ERR_UNSUPPORTED_SHAPE, "too many tokens");
+  if (tokens == 0) return ok();
+  if (!o || !w_o || !out) return fail(GQA_ERR_INVALID_ARG, "o, w_o and out must be non-null");
+  r = run_oproj(s, tokens, o, w_o, out, (hipStream_t)stream);
+  return r == GQA_OK ? ok() : r;
+}
+
+gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len, const void* x,
+                             const void* w_qkv, const void* q_norm_w, const void* k_norm_w,
+                             const void* w_o, void* k_cache, void* v_cache, int32_t kv_capacity,
+                             const int32_t* cache_len, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  gqa_config c;
+  Shape s;
+  gqa_status r = resolve(cfg, &c, &s);
+  if (r != GQA_OK) return r;
+  if ((r = check_common(s, batch, q_len, kv_capacity)) != GQA_OK) return r;
+  if (batch == 0 || q_len == 0) return ok();
+  if (!x || !w_qkv || !w_o || !k_cache || !v_cache || !out)
+    return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, w_o, k_cache, v_cache and out must be non-null");
+  if (c.qk_norm && (!q_norm_w || !k_norm_w))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
+  const size_t need = ws_layer(s, batch, q_len, kv_capacity);
+  if (!workspace || workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes);
+  const size_t T = (size_t)batch * q_len;
+  char* w = static_cast<char*>(workspace);
+  void* ws_q = w;
+  w += ws_qkv(s, batch, q_len);
+  void* qbuf = w;
+  w += align_up(T * s.Hq * s.d * esize(s));
+  void* obuf = w;
+  w += align_up(T * s.Hq * s.d * esize(s));
+  void* ws_a = w;
+  hipStream_t st = (hipStream_t)stream;
+  r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, cache_len, qbuf, k_cache, v_cache,
+              kv_capacity, ws_q, st);
+  if (r != GQA_OK) return r;
+  r = run_attn(c, s, batch, q_len, qbuf, k_cache, v_cache, cache_len, q_len, kv_capacity, obuf,
+               ws_a, st);
+  if (r != GQA_OK) return r;
+  r = run_oproj(s, (int)T, obuf, w_o, out, st);
+  return r == GQA_OK ? ok() : r;
+}
+
+const char* gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG";
+    case GQA_ERR_HEAD_DIM_INDIVISIBLE: return "GQA_ERR_HEAD_DIM_INDIVISIBLE";
+    case GQA_ERR_GROUP_INDIVISIBLE: return "GQA_ERR_GROUP_INDIVISIBLE";
+    case GQA_ERR_ODD_HEAD_DIM: return "GQA_ERR_ODD_HEAD_DIM";
+    case GQA_ERR_UNSUPPORTED_HEAD_DIM: return "GQA_ERR_UNSUPPORTED_HEAD_DIM";
+    case GQA_ERR_UNSUPPORTED_DTYPE: return "GQA_ERR_UNSUPPORTED_DTYPE";
+    case GQA_ERR_UNSUPPORTED_SHAPE: return "GQA_ERR_UNSUPPORTED_SHAPE";
+    case GQA_ERR_WORKSPACE_TOO_SMALL: return "GQA_ERR_WORKSPACE_TOO_SMALL";
+    case GQA_ERR_CAPACITY: return "GQA_ERR_CAPACITY";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP";
+  }
+  return "GQA_ERR_UNKNOWN";
+}
+
+const char* gqa_last_error(void) { return g_err; }
+
+}  // extern "C"

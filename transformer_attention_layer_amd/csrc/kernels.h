@@ -1,0 +1,83 @@
+// Internal launch interface between the C-ABI host code and the gfx950
+// kernels.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+enum { kEpiPlain = 0, kEpiQKV = 1 };
+
+// C^T[n, m] = sum_k W[n, k] X[m, k]  (bf16 in, fp32 accumulate)
+struct GemmArgs {
+  const __bf16* W;  // [N, K]
+  const __bf16* X;  // [M, K]
+  int N, M, K;
+  // plain epilogue: out[m, n], bf16 or (out_f32) fp32
+  void* out;
+  int out_f32;
+  // QKV epilogue (head_dim 128)
+  __bf16* q;        // [B, Hq, L, 128]
+  __bf16* k_cache;  // [B, Hkv, cap, 128]
+  __bf16* v_cache;
+  const __bf16* q_norm_w;
+  const __bf16* k_norm_w;
+  const float2* rope;     // [rows, 64] (cos, sin); rows = T if start_pos else L
+  const int* start_pos;   // [B] or null
+  int L, Hq, Hkv, cap, qk_norm;
+  float eps;
+};
+
+struct AttnArgs {
+  const __bf16* q;  // [B, Hq, Lq, 128]
+  const __bf16* k;  // [B, Hkv, cap, 128]
+  const __bf16* v;
+  __bf16* o;        // [B, Lq, Hq * 128]
+  const int* kv_base;  // kv_len[b] = (kv_base ? kv_base[b] : 0) + kv_add, clamped to [0, cap]
+  int kv_add;
+  int B, Hq, Hkv, G, Lq, cap, causal;
+  float scale_log2;    // d^-0.5 * log2(e)
+  // prefill work split
+  int hpw, pb, n_qtiles, n_hsub;
+  // split-KV decode
+  float* part_o;       // [B, Hkv, n_splits, 32, 128]
+  float2* part_ml;     // [B, Hkv, n_splits, 32] (running max in log2 units, sum)
+  int n_splits, chunk;
+};
+
+hipError_t launch_rope_table(float2* table, const int* start_pos, int rows, int L, int half,
+                             double theta, hipStream_t stream);
+hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream);
+hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream);
+
+hipError_t launch_attn_prefill_bf16(const AttnArgs& args, hipStream_t stream);
+hipError_t launch_attn_decode_bf16(const AttnArgs& args, hipStream_t stream);
+
+// fp32 path (any even head_dim up to 256)
+struct F32Args {
+  const float* x; const float* w; float* y;  // y[M, N] = x[M, K] w[N, K]^T
+  int M, N, K;
+};
+hipError_t launch_gemm_f32(const F32Args& args, hipStream_t stream);
+
+struct F32NormRopeArgs {
+  const float* y;     // [T, (Hq + 2 Hkv) d] projection output
+  const float* q_norm_w; const float* k_norm_w;
+  const int* start_pos;
+  float* q; float* k_cache; float* v_cache;
+  int B, L, Hq, Hkv, d, cap, qk_norm;
+  float eps; double theta;
+};
+hipError_t launch_normrope_f32(const F32NormRopeArgs& args, hipStream_t stream);
+
+struct F32AttnArgs {
+  const float* q; const float* k; const float* v; float* o;
+  const int* kv_base; int kv_add;
+  int B, Hq, Hkv, Lq, cap, d, causal;
+  float scale;
+};
+hipError_t launch_attn_f32(const F32AttnArgs& args, hipStream_t stream);
+
+}  // namespace gqa
