@@ -73,7 +73,8 @@ def _time_loop(fn, iters, torch):
 def bench_prefill(w, steps, warmup, torch, T, GI):
     cfg = T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
                       head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
-                      qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True)
+                      qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True,
+                      o_split=w.o_split)
     h = GI.device_layer_inputs(w)
     d = w.d
     dt = GI.torch_dtype(w)
@@ -112,7 +113,8 @@ def bench_prefill(w, steps, warmup, torch, T, GI):
 def bench_decode(w, steps, warmup, torch, T, GI):
     cfg = T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
                       head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
-                      qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True)
+                      qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True,
+                      o_split=w.o_split)
     h = GI.device_layer_inputs(w)
     c = GI.device_cache(w)
     cl = torch.full((w.batch,), w.cache_len, dtype=torch.int32, device="cuda")
@@ -207,7 +209,7 @@ def main():
             "num_heads": w.hq, "num_kv_heads": w.hkv, "head_dim": w.d,
             "head_dim_explicit": w.head_dim is not None, "qk_norm": w.qk_norm,
             "rope_theta": w.rope_theta, "causal": w.causal, "cache_len": w.cache_len,
-            "out_dtype": "f32"}
+            "out_dtype": "f32", "o_split": w.o_split}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     if w.cache_len == 0:
         ms, part_ms = bench_prefill(w, args.steps, args.warmup, torch, T, GI)

@@ -79,6 +79,12 @@ typedef struct {
   int32_t out_f32;       /* 1: the o_proj output (gqa_o_proj, gqa_layer_forward)
                             is written as fp32, straight from the fp32
                             accumulator; 0: in `dtype` */
+  int32_t o_split;       /* bf16 only, gqa_layer_forward only.  1: the attention
+                            output reaches o_proj as a bf16 pair hi + lo
+                            (lo = bf16(o - hi)), about 16 significant bits, so
+                            its rounding stays out of the output; costs one more
+                            o_proj pass.  0: one bf16 value, the tutorial's cast
+                            of the attention result to the input dtype. */
 } gqa_config;
 
 /* Host only (no device needed): copy *in to *out with num_kv_heads and

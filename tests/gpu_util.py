@@ -39,14 +39,16 @@ def announce(msg: str):
     sys.stdout.flush()
 
 
-def cfg_of(w: GI.Workload, out_f32: bool = True):
-    """The binding's config for a workload.  Parity runs take the o_proj
-    output in fp32 (the accumulator): a bf16 output is that value rounded
-    once more, checked bit-exactly in its own test."""
+def cfg_of(w: GI.Workload, out_f32: bool = True, o_split=None):
+    """The binding's config for a workload, with the workload's own launch
+    options.  Parity runs take the o_proj output in fp32 (the accumulator):
+    a bf16 output is that value rounded once more, checked bit-exactly in
+    its own test."""
     import transformer_attention_layer_amd as T
     return T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
                        head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
-                       qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=out_f32)
+                       qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=out_f32,
+                       o_split=w.o_split if o_split is None else o_split)
 
 
 def resolved(w: GI.Workload):

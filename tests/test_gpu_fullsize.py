@@ -1,0 +1,91 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times, on sampled output rows the oracle computes one by one.
+
+Prefill rows come from the oracle's row mode (row t needs only x[b, :t+1]);
+decode rows from the oracle's layer forward on a few sequences of the
+cache.  The oracle runs in float32 here, the precision the tutorial's
+attention step names, to keep the host work to seconds."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gqa_inputs as GI  # noqa: E402
+from gpu_util import announce, assert_close, cfg_of, resolved, to_np  # noqa: E402
+from oracle import gqa_oracle as O  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_attention_layer_amd as T
+    T.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+PREFILL_ROWS = {
+    "prefill_h1024": [(0, 0), (0, 1), (0, 63), (0, 64), (3, 1000), (5, 2046), (7, 2047)],
+    "quotient_h4096": [(0, 0), (0, 129), (1, 4095), (2, 77), (3, 8191)],
+    "wide_h5120": [(0, 0), (0, 5000), (1, 1), (1, 16383)],
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_ROWS))
+def test_prefill_full_size(name):
+    import transformer_attention_layer_amd as T
+    w = GI.WORKLOADS[name]
+    rows = PREFILL_ROWS[name]
+    announce(f"[full size] {name} B={w.batch} L={w.seq} o_split={w.o_split} rows={rows}")
+    h = GI.host_layer_inputs(w)
+    d = GI.to_device(h, w)
+    out, _, _ = T.gqa_layer_forward(cfg_of(w), d["x"], d["w_qkv"], d["q_norm_w"],
+                                    d["k_norm_w"], d["w_o"])
+    torch.cuda.synchronize()
+    del d
+    idx_b = torch.tensor([b for b, _ in rows], device="cuda")
+    idx_t = torch.tensor([t for _, t in rows], device="cuda")
+    got = to_np(out[idx_b, idx_t])
+    del out
+    ref = O.layer_forward_rows(resolved(w), h["x"], h["w_qkv"], h["q_norm_w"], h["k_norm_w"],
+                               h["w_o"], rows, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+                               qk_norm=w.qk_norm, dtype=np.float32)
+    assert_close(got, ref, w.dtype, "sampled rows")
+
+
+@pytest.mark.parametrize("name", ["decode_h2560_gqa", "decode_h2560_mqa"])
+def test_decode_full_size(name):
+    import transformer_attention_layer_amd as T
+    w = GI.WORKLOADS[name]
+    seqs = [0, 37, 63]
+    announce(f"[full size] {name} B={w.batch} cache={w.cache_len} sequences={seqs}")
+    h = GI.host_layer_inputs(w)
+    d = GI.to_device(h, w)
+    cache = GI.device_cache(w)
+    # host copies of the sampled sequences' caches, taken before the call
+    kc_h = cache["k_cache"][seqs].float().cpu().numpy()
+    vc_h = cache["v_cache"][seqs].float().cpu().numpy()
+    cl = torch.full((w.batch,), w.cache_len, dtype=torch.int32, device="cuda")
+    out, kc, vc = T.gqa_layer_forward(cfg_of(w), d["x"], d["w_qkv"], d["q_norm_w"],
+                                      d["k_norm_w"], d["w_o"], k_cache=cache["k_cache"],
+                                      v_cache=cache["v_cache"], cache_len=cl)
+    torch.cuda.synchronize()
+    got = to_np(out[seqs])
+    new_k = to_np(kc[seqs][:, :, w.cache_len])
+    del cache, kc, vc, out
+    torch.cuda.empty_cache()
+    sub = {k: v[seqs] for k, v in h.items() if k == "x"}
+    ref, rk, _ = O.layer_forward(resolved(w), sub["x"], h["w_qkv"], h["q_norm_w"],
+                                 h["k_norm_w"], h["w_o"], rope_theta=w.rope_theta,
+                                 rms_eps=w.rms_eps, qk_norm=w.qk_norm, k_cache=kc_h,
+                                 v_cache=vc_h, cache_len=np.full(len(seqs), w.cache_len),
+                                 dtype=np.float32)
+    assert_close(new_k, rk[:, :, w.cache_len], w.dtype, "appended k")
+    assert_close(got, ref, w.dtype, "sampled sequences")

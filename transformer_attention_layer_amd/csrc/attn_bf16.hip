@@ -209,6 +209,21 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[8], const bf16* qrow, bool va
   }
 }
 
+// Four consecutive output features as bf16; with `split` also the rounding
+// residual (value - bf16(value)) as bf16, `width` elements further on.
+__device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)[4], int split) {
+  u32x2 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  st8(p, w);
+  if (split) {
+    u32x2 r;
+    r.x = pack_bf16x2(v[0] - lo_bf16(w.x), v[1] - hi_bf16(w.x));
+    r.y = pack_bf16x2(v[2] - lo_bf16(w.y), v[3] - hi_bf16(w.y));
+    st8(p + width, r);
+  }
+}
+
 constexpr int kPrefillTK = 64;
 constexpr int kPrefillNT = 256;
 
@@ -272,15 +287,16 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   const float lt = st.l + wave_xor32(st.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (!row_valid) return;
-  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * ((size_t)a.Hq * kD) + (size_t)hq * kD;
+  const size_t width = (size_t)a.Hq * kD;
+  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * kD;
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 w;
-      w.x = pack_bf16x2(st.o[d][4 * j + 0] * inv, st.o[d][4 * j + 1] * inv);
-      w.y = pack_bf16x2(st.o[d][4 * j + 2] * inv, st.o[d][4 * j + 3] * inv);
-      st8(orow + 32 * d + 8 * j + 4 * hh, w);
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = st.o[d][4 * j + i] * inv;
+      store_o4(orow + 32 * d + 8 * j + 4 * hh, width, v, a.o_split);
     }
 }
 
@@ -370,8 +386,15 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
     o1 += w * po[1];
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * ((size_t)a.Hq * kD) + (size_t)hq * kD;
-  *reinterpret_cast<unsigned int*>(orow + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+  const size_t width = (size_t)a.Hq * kD;
+  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * kD;
+  const float h0 = o0 * inv, h1 = o1 * inv;
+  *reinterpret_cast<unsigned int*>(orow + 2 * lane) = pack_bf16x2(h0, h1);
+  if (a.o_split) {
+    const unsigned int hi = pack_bf16x2(h0, h1);
+    *reinterpret_cast<unsigned int*>(orow + width + 2 * lane) =
+        pack_bf16x2(h0 - lo_bf16(hi), h1 - hi_bf16(hi));
+  }
 }
 
 }  // namespace

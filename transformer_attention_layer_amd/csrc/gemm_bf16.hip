@@ -88,7 +88,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   TileRegs<BN> ra;
   TileRegs<BM> rb;
   const int nk = (K + kBK - 1) / kBK;
-  load_tile<BN>(ra, a.W, n0, N, 0, K, tid);
+  // W may be narrower than X along K (w_kmod): X = [hi | lo] reads W twice
+  const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
+  load_tile<BN>(ra, a.W, n0, N, 0, Kw, tid);
   load_tile<BM>(rb, a.X, m0, M, 0, K, tid);
   store_tile<BN>(ra, &lds[0][0], tid);
   store_tile<BM>(rb, &lds[0][BN * 8], tid);
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
-      load_tile<BN>(ra, a.W, n0, N, (kt + 1) * kBK, K, tid);
+      load_tile<BN>(ra, a.W, n0, N, ((kt + 1) * kBK) % Kw, Kw, tid);
       load_tile<BM>(rb, a.X, m0, M, (kt + 1) * kBK, K, tid);
     }
     const u32x4* sa = &lds[buf][0];

@@ -40,6 +40,7 @@ struct Shape {
   int H, Hq, Hkv, d, G, n_qkv;
   bool bf16;
   bool out_f32;  // o_proj output in fp32
+  bool o_split;  // layer forward: attention output as a bf16 hi + lo pair
 };
 
 gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
@@ -81,8 +82,8 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
   if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
     return fail(GQA_ERR_INVALID_ARG, "rms_eps must be >= 0 and finite");
   if ((c.qk_norm != 0 && c.qk_norm != 1) || (c.causal != 0 && c.causal != 1) ||
-      (c.out_f32 != 0 && c.out_f32 != 1))
-    return fail(GQA_ERR_INVALID_ARG, "qk_norm, causal and out_f32 must be 0 or 1");
+      (c.out_f32 != 0 && c.out_f32 != 1) || (c.o_split != 0 && c.o_split != 1))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm, causal, out_f32 and o_split must be 0 or 1");
   // every kernel indexes heads and widths in 32-bit
   const long long n_qkv = (long long)(c.num_heads + 2LL * c.num_kv_heads) * c.head_dim;
   if (n_qkv > (1LL << 30) || (long long)c.num_heads * c.head_dim > (1LL << 30))
@@ -97,6 +98,7 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->n_qkv = (int)n_qkv;
     sh->bf16 = c.dtype == GQA_BF16;
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
+    sh->o_split = c.o_split && c.dtype == GQA_BF16;
   }
   return GQA_OK;
 }
@@ -137,7 +139,8 @@ size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
 size_t ws_layer(const Shape& s, int batch, int q_len, int cap) {
   const size_t T = (size_t)batch * q_len;
   return ws_qkv(s, batch, q_len) + align_up(T * s.Hq * s.d * esize(s)) /* q */ +
-         align_up(T * s.Hq * s.d * esize(s)) /* attention output */ + ws_attn(s, batch, q_len, cap);
+         align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1)) /* attention output */ +
+         ws_attn(s, batch, q_len, cap);
 }
 
 gqa_status check_launch(hipError_t e, const char* what) {
@@ -214,7 +217,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
 
 gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, const void* q,
                     const void* kc, const void* vc, const int32_t* kv_base, int kv_add, int cap,
-                    void* o, void* ws, hipStream_t st) {
+                    void* o, bool o_split, void* ws, hipStream_t st) {
   const double scale = 1.0 / sqrt((double)s.d);
   if (!s.bf16) {
     gqa::F32AttnArgs a{};
@@ -239,6 +242,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   a.k = static_cast<const __bf16*>(kc);
   a.v = static_cast<const __bf16*>(vc);
   a.o = static_cast<__bf16*>(o);
+  a.o_split = o_split;
   a.kv_base = kv_base;
   a.kv_add = kv_add;
   a.B = batch;
@@ -268,15 +272,16 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   return check_launch(gqa::launch_attn_prefill_bf16(a, st), "prefill attention");
 }
 
-gqa_status run_oproj(const Shape& s, int tokens, const void* o, const void* w_o, void* out,
-                     hipStream_t st) {
+gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, const void* w_o,
+                     void* out, hipStream_t st) {
   if (s.bf16) {
     gqa::GemmArgs g{};
     g.W = static_cast<const __bf16*>(w_o);
     g.X = static_cast<const __bf16*>(o);
     g.N = s.H;
     g.M = tokens;
-    g.K = s.Hq * s.d;
+    g.K = s.Hq * s.d * (o_split ? 2 : 1);
+    g.w_kmod = o_split ? s.Hq * s.d : 0;
     g.out = out;
     g.out_f32 = s.out_f32;
     return check_launch(gqa::launch_gemm_plain_bf16(g, st), "o_proj");
@@ -349,7 +354,7 @@ gqa_status gqa_attn_core(const gqa_config* cfg, int32_t batch, int32_t q_len, co
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace_bytes);
   r = run_attn(c, s, batch, q_len, q, k_cache, v_cache, kv_len, kv_len ? 0 : q_len, kv_capacity, o,
-               workspace, (hipStream_t)stream);
+               false, workspace, (hipStream_t)stream);
   return r == GQA_OK ? ok() : r;
 }
 
@@ -363,7 +368,7 @@ gqa_status gqa_o_proj(const gqa_config* cfg, int32_t tokens, const void* o, cons
   if (tokens > 65535 * 64) return fail(GQA_ERR_UNSUPPORTED_SHAPE, "too many tokens");
   if (tokens == 0) return ok();
   if (!o || !w_o || !out) return fail(GQA_ERR_INVALID_ARG, "o, w_o and out must be non-null");
-  r = run_oproj(s, tokens, o, w_o, out, (hipStream_t)stream);
+  r = run_oproj(s, tokens, o, false, w_o, out, (hipStream_t)stream);
   return r == GQA_OK ? ok() : r;
 }
 
@@ -393,16 +398,16 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
   void* qbuf = w;
   w += align_up(T * s.Hq * s.d * esize(s));
   void* obuf = w;
-  w += align_up(T * s.Hq * s.d * esize(s));
+  w += align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1));
   void* ws_a = w;
   hipStream_t st = (hipStream_t)stream;
   r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, cache_len, qbuf, k_cache, v_cache,
               kv_capacity, ws_q, st);
   if (r != GQA_OK) return r;
   r = run_attn(c, s, batch, q_len, qbuf, k_cache, v_cache, cache_len, q_len, kv_capacity, obuf,
-               ws_a, st);
+               s.o_split, ws_a, st);
   if (r != GQA_OK) return r;
-  r = run_oproj(s, (int)T, obuf, w_o, out, st);
+  r = run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st);
   return r == GQA_OK ? ok() : r;
 }
 

@@ -18,6 +18,7 @@ struct GemmArgs {
   // plain epilogue: out[m, n], bf16 or (out_f32) fp32
   void* out;
   int out_f32;
+  int w_kmod;       // > 0: W column k % w_kmod (W read twice along K for a hi | lo X)
   // QKV epilogue (head_dim 128)
   __bf16* q;        // [B, Hq, L, 128]
   __bf16* k_cache;  // [B, Hkv, cap, 128]
@@ -34,7 +35,8 @@ struct AttnArgs {
   const __bf16* q;  // [B, Hq, Lq, 128]
   const __bf16* k;  // [B, Hkv, cap, 128]
   const __bf16* v;
-  __bf16* o;        // [B, Lq, Hq * 128]
+  __bf16* o;        // [B, Lq, Hq * 128], or [B, Lq, 2, Hq * 128] (hi | lo) when o_split
+  int o_split;
   const int* kv_base;  // kv_len[b] = (kv_base ? kv_base[b] : 0) + kv_add, clamped to [0, cap]
   int kv_add;
   int B, Hq, Hkv, G, Lq, cap, causal;
