@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--workload", default="prefill_h1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -244,6 +246,16 @@ def main():
                          "attn_ms": round(attn_ms, 4), "layer_ms": round(dms, 4),
                          "kv_bytes": kv_bytes_of(wd)}
         result["decode"] = dec
+
+    if args.copy_probe_mb:
+        # a plain device-to-device copy of known size, outside the timed
+        # region, so that HBM byte counters can be calibrated against it
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w) if w.cache_len == 0 else None

@@ -18,7 +18,9 @@ from dataclasses import dataclass
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgqa.so")
+# GQA_LIB may point at another build of the same library (A/B timing); the
+# binding never falls back to anything else when the file is missing.
+LIB_PATH = os.environ.get("GQA_LIB", os.path.join(_HERE, "libgqa.so"))
 
 GQA_F32 = 0
 GQA_BF16 = 1

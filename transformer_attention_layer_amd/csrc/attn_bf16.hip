@@ -17,6 +17,13 @@
 // registers; V^T is built in LDS while the tile is stored, with the keys of
 // each 16-key group in the order the score registers hold them.
 //
+// Softmax bookkeeping per key tile: the tile's row max is taken on the raw
+// scores (the scale is positive), exp2(s * scale*log2(e) - m) is one FMA and
+// one v_exp, and the running max m is moved (and the output rescaled) only
+// when some row's max grew by more than 2^8; until then p may exceed 1 by up
+// to that factor, which bf16 P and the fp32 sums carry as well.  The row
+// sums add the bf16-rounded P that the PV product uses (v_dot2).
+//
 // Two kernels:
 //   prefill: a workgroup of 4 waves covers up to 4 query heads of one KV
 //            group at the same 32 positions (or 2 heads x 64 positions, or
@@ -25,6 +32,8 @@
 //   decode : one wave per (sequence, KV head, key split); its 32 rows are the
 //            group's query heads (x the few new tokens).  Partial (max, sum,
 //            unnormalised output) per split are merged by a second kernel.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,6 +41,7 @@ namespace gqa {
 namespace {
 
 constexpr int kD = 128;
+constexpr float kLazyRescale = 8.0f;  // log2 of the growth allowed before rescaling
 
 // K tile: rows = keys, 256 B = 16 chunks each; chunk c of row r at slot
 // c ^ (r & 15).
@@ -47,57 +57,58 @@ __device__ __forceinline__ int vslot(int row, int chunk) {
   return row * NCH + (chunk ^ ((row ^ (row >> 2)) & (NCH - 1)));
 }
 
+// K tile straight into LDS (buffer_load ... lds): one instruction fills 64
+// consecutive slots = 4 key rows; lane i writes slot i, so it loads the
+// chunk the swizzle puts there.  Keys past the descriptor's range read as 0.
 template <int NT, int TK>
-struct KVRegs {
-  static constexpr int kK = TK * 16 / NT;  // 16-byte chunks of K per thread
-  static constexpr int kV = TK * 8 / NT;   // 4-key x 4-feature groups of V per thread
-  u32x4 k[kK];
-  u32x2 v[kV][4];
+__device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, u32x4* sk, int key0, int wave,
+                                      int lane) {
+  constexpr int JW = TK / 4 / (NT / 64);  // instructions per wave
+  const int r_in = lane >> 4;
+  const int slot = lane & 15;
+#pragma unroll
+  for (int j = 0; j < JW; ++j) {
+    const int r0 = (wave * JW + j) * 4;
+    const int row = r0 + r_in;
+    const int c = slot ^ (row & 15);
+    dma16(rk, sk + r0 * 16, (unsigned)((key0 + row) * (kD * 2) + c * 16));
+  }
+}
+
+// V tile through registers: a thread loads 4 keys x 4 features (8-byte
+// loads, zero past the range) ...
+template <int NT, int TK>
+struct VRegs {
+  static constexpr int kG = TK * 8 / NT;  // 4-key x 4-feature groups per thread
+  u32x2 v[kG][4];
 };
 
 template <int NT, int TK>
-__device__ __forceinline__ void load_kv(KVRegs<NT, TK>& r, const bf16* __restrict__ kb,
-                                        const bf16* __restrict__ vb, int key0, int kend, int tid) {
+__device__ __forceinline__ void load_v(VRegs<NT, TK>& r, __amdgpu_buffer_rsrc_t rv, int key0,
+                                       int tid) {
 #pragma unroll
-  for (int i = 0; i < KVRegs<NT, TK>::kK; ++i) {
-    const int idx = tid + i * NT;
-    const int key = key0 + (idx >> 4);
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < kend) val = ld16(kb + (size_t)key * kD + (idx & 15) * 8);
-    r.k[i] = val;
-  }
-#pragma unroll
-  for (int i = 0; i < KVRegs<NT, TK>::kV; ++i) {
+  for (int i = 0; i < VRegs<NT, TK>::kG; ++i) {
     const int idx = tid + i * NT;
     const int g4 = idx & 31;
     const int kq = idx >> 5;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = key0 + 4 * kq + e;
-      u32x2 val = {0u, 0u};
-      if (key < kend) val = ld8(vb + (size_t)key * kD + 4 * g4);
-      r.v[i][e] = val;
-    }
+    for (int e = 0; e < 4; ++e)
+      r.v[i][e] = buf_ld8(rv, (unsigned)((key0 + 4 * kq + e) * (kD * 2) + 8 * g4));
   }
 }
 
+// ... and stores them transposed: 4 features x 4 keys, each 8 bytes.
 template <int NT, int TK>
-__device__ __forceinline__ void store_kv(const KVRegs<NT, TK>& r, u32x4* sk, u32x4* sv, int tid) {
-#pragma unroll
-  for (int i = 0; i < KVRegs<NT, TK>::kK; ++i) {
-    const int idx = tid + i * NT;
-    sk[kslot(idx >> 4, idx & 15)] = r.k[i];
-  }
+__device__ __forceinline__ void store_vt(const VRegs<NT, TK>& r, u32x4* sv, int tid) {
   u32x2* sv2 = reinterpret_cast<u32x2*>(sv);
 #pragma unroll
-  for (int i = 0; i < KVRegs<NT, TK>::kV; ++i) {
+  for (int i = 0; i < VRegs<NT, TK>::kG; ++i) {
     const int idx = tid + i * NT;
     const int g4 = idx & 31;
     const int kq = idx >> 5;                 // keys 4kq .. 4kq+3 of the tile
     const int chunk = 2 * (kq >> 2) + (kq & 1);
     const int half = (kq >> 1) & 1;
     const u32x2* v = r.v[i];
-    // 4 keys x 4 features -> 4 features x 4 keys
     u32x2 t0, t1, t2, t3;
     t0.x = (v[0].x & 0xffffu) | (v[1].x << 16);
     t0.y = (v[2].x & 0xffffu) | (v[3].x << 16);
@@ -115,10 +126,26 @@ __device__ __forceinline__ void store_kv(const KVRegs<NT, TK>& r, u32x4* sk, u32
   }
 }
 
+// Per-lane LDS offsets (u32x4 units) of the MFMA fragments; the same for
+// every tile and buffer.
+template <int TK>
+struct LaneOffsets {
+  int k[8];            // K fragment of d-chunk c: key row l32 (+32 kb)
+  int v[TK / 16];      // V^T fragment of key group g: feature row l32 (+32 d)
+};
+
+template <int TK>
+__device__ __forceinline__ void lane_offsets(LaneOffsets<TK>& o, int l32, int hh) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o.k[c] = kslot(l32, 2 * c + hh);
+#pragma unroll
+  for (int g = 0; g < TK / 16; ++g) o.v[g] = vslot<TK>(l32, 2 * g + hh);
+}
+
 // Running state of one wave: 32 query rows, lane = row (l % 32).
 struct RowState {
   floatx16 o[4];   // O^T: value feature 32*db + 8*(r/4) + 4*(l/32) + r%4
-  float m;         // running max (log2 units)
+  float m;         // running max (log2 units, scaled scores)
   float l;         // running sum, this lane-half's keys only
 };
 
@@ -132,66 +159,67 @@ __device__ __forceinline__ void init_state(RowState& st) {
 }
 
 // One key tile: scores, online softmax, PV.  `kend_row` = one past the last
-// key this lane's query may see; `masked` = some key of the tile may be past
-// it for some row of the wave.
-template <int TK, int NCH_V>
+// key this lane's query may see; `masked` (wave-uniform) = some key of the
+// tile may be past it for some row of the wave.
+template <int TK>
 __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], const u32x4* sk,
-                                            const u32x4* sv, int key0, int kend_row, bool masked,
-                                            float scale_log2, int l32, int hh) {
+                                            const u32x4* sv, const LaneOffsets<TK>& lo, int key0,
+                                            int kend_row, bool masked, float c_log2, int hh) {
   constexpr int KB = TK / 32;
+  constexpr int NCH = TK / 8;
   floatx16 s[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
+    const floatx16 z = {};
+    s[kb] = mfma32x32x16(sk[kb * 512 + lo.k[0]], qf[0], z);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    for (int c = 1; c < 8; ++c) s[kb] = mfma32x32x16(sk[kb * 512 + lo.k[c]], qf[c], s[kb]);
+  }
+  if (masked) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[kb] = mfma32x32x16(sk[kslot(32 * kb + l32, 2 * c + hh)], qf[c], s[kb]);
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= kend_row) s[kb][r] = -INFINITY;
+      }
   }
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[kb][r] * scale_log2;
-      if (masked) {
-        const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        x = key < kend_row ? x : -INFINITY;
-      }
-      s[kb][r] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
   mx = fmaxf(mx, wave_xor32(mx));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_use);
-  float rs = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(s[kb][r] - m_use);
-      s[kb][r] = p;
-      rs += p;
-    }
-  st.l = st.l * alpha + rs;
-  st.m = m_new;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+  const float mt = mx * c_log2;  // -inf stays -inf (c_log2 > 0)
+  if (__builtin_amdgcn_ballot_w64(mt > st.m + kLazyRescale)) {
+    const float mn = fmaxf(st.m, mt);
+    const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(st.m - mn);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[d][r] *= alpha;
+    st.l *= alpha;
+    st.m = mn;
   }
+  const float mb = st.m == -INFINITY ? 0.f : st.m;
 #pragma unroll
   for (int g = 0; g < TK / 16; ++g) {
     const int kb = g >> 1;
     const int rb = 8 * (g & 1);
-    u32x4 pf;
-    pf.x = pack_bf16x2(s[kb][rb + 0], s[kb][rb + 1]);
-    pf.y = pack_bf16x2(s[kb][rb + 2], s[kb][rb + 3]);
-    pf.z = pack_bf16x2(s[kb][rb + 4], s[kb][rb + 5]);
-    pf.w = pack_bf16x2(s[kb][rb + 6], s[kb][rb + 7]);
+    float p[8];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st.o[d] = mfma32x32x16(sv[vslot<TK>(32 * d + l32, 2 * g + hh)], pf, st.o[d]);
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kb][rb + e], c_log2, -mb));
+    u32x4 pf;
+    pf.x = pack_bf16x2(p[0], p[1]);
+    pf.y = pack_bf16x2(p[2], p[3]);
+    pf.z = pack_bf16x2(p[4], p[5]);
+    pf.w = pack_bf16x2(p[6], p[7]);
+    st.l = sum_bf16x2(pf.x, st.l);
+    st.l = sum_bf16x2(pf.y, st.l);
+    st.l = sum_bf16x2(pf.z, st.l);
+    st.l = sum_bf16x2(pf.w, st.l);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) st.o[d] = mfma32x32x16(sv[d * 32 * NCH + lo.v[g]], pf, st.o[d]);
   }
 }
 
@@ -232,7 +260,8 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   __shared__ u32x4 sk[2][TK * 16];
   __shared__ u32x4 sv[2][kD * TK / 8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int qt = a.n_qtiles - 1 - (int)blockIdx.z;  // heaviest query tiles first
   const int b = blockIdx.y;
@@ -261,27 +290,40 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   u32x4 qf[8];
   load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + (row_valid ? tq : 0)) * kD, row_valid, hh);
 
-  const bf16* kb = a.k + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
-  const bf16* vb = a.v + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base, (long long)kvl * kD * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base, (long long)kvl * kD * 2);
+  LaneOffsets<TK> lo;
+  lane_offsets<TK>(lo, l32, hh);
 
   RowState st;
   init_state(st);
-  KVRegs<NT, TK> regs;
+  VRegs<NT, TK> vr;
   if (n_tiles > 0) {
-    load_kv<NT, TK>(regs, kb, vb, 0, kvl, tid);
-    store_kv<NT, TK>(regs, sk[0], sv[0], tid);
+    dma_k<NT, TK>(rk, sk[0], 0, wave, lane);
+    load_v<NT, TK>(vr, rv, 0, tid);
+    store_vt<NT, TK>(vr, sv[0], tid);
   }
   __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_tiles) load_kv<NT, TK>(regs, kb, vb, (it + 1) * TK, kvl, tid);
+  // two tiles per trip, so each buffer's LDS addresses are constants
+  auto step = [&](auto bufc, int it) {
+    constexpr int B = decltype(bufc)::value;
+    const bool more = it + 1 < n_tiles;
+    if (more) {
+      dma_k<NT, TK>(rk, sk[B ^ 1], (it + 1) * TK, wave, lane);
+      load_v<NT, TK>(vr, rv, (it + 1) * TK, tid);
+    }
     const int key0 = it * TK;
     if (key0 < key_end_w) {
       const bool masked = key0 + TK > kmin_w;
-      attend_tile<TK, TK / 8>(st, qf, sk[buf], sv[buf], key0, kend_row, masked, a.scale_log2, l32, hh);
+      attend_tile<TK>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2, hh);
     }
-    if (it + 1 < n_tiles) store_kv<NT, TK>(regs, sk[buf ^ 1], sv[buf ^ 1], tid);
+    if (more) store_vt<NT, TK>(vr, sv[B ^ 1], tid);
     __syncthreads();
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   const float lt = st.l + wave_xor32(st.l);
@@ -319,7 +361,7 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
 
   const int kvl = kv_len_of(a, b);
   const int off = kvl - a.Lq;
-  int ks = split * a.chunk;
+  const int ks = split * a.chunk;
   int ke = min(ks + a.chunk, kvl);
   if (a.causal) ke = min(ke, off + a.Lq);
   const int n_tiles = ke > ks ? (ke - ks + TK - 1) / TK : 0;
@@ -329,25 +371,38 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   u32x4 qf[8];
   load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + tq) * kD, row_valid, hh);
 
-  const bf16* kb = a.k + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
-  const bf16* vb = a.v + ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const long long bytes = (long long)(ke > 0 ? ke : 0) * kD * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base, bytes);
+  LaneOffsets<TK> lo;
+  lane_offsets<TK>(lo, l32, hh);
 
   RowState st;
   init_state(st);
-  KVRegs<NT, TK> regs;
+  VRegs<NT, TK> vr;
   if (n_tiles > 0) {
-    load_kv<NT, TK>(regs, kb, vb, ks, ke, lane);
-    store_kv<NT, TK>(regs, sk[0], sv[0], lane);
+    dma_k<NT, TK>(rk, sk[0], ks, 0, lane);
+    load_v<NT, TK>(vr, rv, ks, lane);
+    store_vt<NT, TK>(vr, sv[0], lane);
   }
   __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
+  auto step = [&](auto bufc, int it) {
+    constexpr int B = decltype(bufc)::value;
     const int key0 = ks + it * TK;
-    if (it + 1 < n_tiles) load_kv<NT, TK>(regs, kb, vb, key0 + TK, ke, lane);
+    const bool more = it + 1 < n_tiles;
+    if (more) {
+      dma_k<NT, TK>(rk, sk[B ^ 1], key0 + TK, 0, lane);
+      load_v<NT, TK>(vr, rv, key0 + TK, lane);
+    }
     const bool masked = key0 + TK > kmin;
-    attend_tile<TK, TK / 8>(st, qf, sk[buf], sv[buf], key0, kend_row, masked, a.scale_log2, l32, hh);
-    if (it + 1 < n_tiles) store_kv<NT, TK>(regs, sk[buf ^ 1], sv[buf ^ 1], lane);
+    attend_tile<TK>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2, hh);
+    if (more) store_vt<NT, TK>(vr, sv[B ^ 1], lane);
     __syncthreads();
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   const float lt = st.l + wave_xor32(st.l);
@@ -389,12 +444,11 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const size_t width = (size_t)a.Hq * kD;
   bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * kD;
   const float h0 = o0 * inv, h1 = o1 * inv;
-  *reinterpret_cast<unsigned int*>(orow + 2 * lane) = pack_bf16x2(h0, h1);
-  if (a.o_split) {
-    const unsigned int hi = pack_bf16x2(h0, h1);
+  const unsigned int hi = pack_bf16x2(h0, h1);
+  *reinterpret_cast<unsigned int*>(orow + 2 * lane) = hi;
+  if (a.o_split)
     *reinterpret_cast<unsigned int*>(orow + width + 2 * lane) =
         pack_bf16x2(h0 - lo_bf16(hi), h1 - hi_bf16(hi));
-  }
 }
 
 }  // namespace

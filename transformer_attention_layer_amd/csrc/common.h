@@ -25,12 +25,48 @@ GQA_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 GQA_DEV float bf16_to_f32(bf16 v) { return (float)v; }
 
-// Round-to-nearest-even float -> bf16 bits (two values packed, low first).
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> bf16 bits (two values packed, low first);
+// one v_cvt_pk_bf16_f32.
 GQA_DEV unsigned int pack_bf16x2(float lo, float hi) {
-  bf16 a = (bf16)lo;
-  bf16 b = (bf16)hi;
-  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+  const floatx2 f = {lo, hi};
+  const bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(unsigned int, b);
+}
+
+// lo + hi of a packed bf16 pair, accumulated into `acc` in fp32 (v_dot2 with
+// ones).
+GQA_DEV float sum_bf16x2(unsigned int packed, float acc) {
+  const bf16x2 v = __builtin_bit_cast(bf16x2, packed);
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(v, ones, acc, false);
+}
+
+// Wave-uniform copy of a value (lets the compiler keep it in an SGPR and
+// branch on it with scalar branches).
+GQA_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Raw buffer descriptor over `bytes` bytes from `base`; loads at or past the
+// end return zero (hardware bounds check).
+GQA_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+
+GQA_DEV void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, voff, 0, 0, 0);
+}
+
+GQA_DEV u32x2 buf_ld8(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+  u32x2 out;
+  out.x = v[0];
+  out.y = v[1];
+  return out;
 }
 
 GQA_DEV float lo_bf16(unsigned int w) { return __builtin_bit_cast(float, w << 16); }

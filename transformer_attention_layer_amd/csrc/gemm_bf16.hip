@@ -27,35 +27,66 @@ constexpr int kThreads = 256;    // 4 waves, 2 x 2 over the C^T tile
 // hit eight distinct 16-byte bank groups.
 __device__ __forceinline__ int swz8(int row, int chunk) { return (row << 3) + (chunk ^ (row & 7)); }
 
-template <int ROWS>
-struct TileRegs {
-  static constexpr int kPer = ROWS * 8 / kThreads;  // 16-byte chunks per thread
-  u32x4 v[kPer];
-};
+// Raw buffer descriptor over rows [row0, nrows) of a row-major bf16 matrix
+// with `ld` elements per row.  Loads past the end of the range return zero
+// (hardware bounds check), which zero-fills ragged row and K tails.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int row0, int nrows,
+                                                            int ld) {
+  long long bytes = (long long)(nrows - row0) * ld * 2;
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * ld), 0, (int)bytes,
+                                           0x00020000);
+}
 
+// Stage one kBK-wide tile of ROWS rows straight from global memory into LDS
+// (buffer_load ... lds, no register staging).  One instruction fills 64
+// consecutive 16-byte LDS slots = 8 rows; lane i writes slot i, so it loads
+// the global chunk that the XOR swizzle places there: chunk (i & 7) ^ (i >> 3)
+// of row i >> 3.  Chunks at or past column `kcols` read as zero.
 template <int ROWS>
-__device__ __forceinline__ void load_tile(TileRegs<ROWS>& r, const bf16* __restrict__ base,
-                                          int row0, int nrows, int k0, int K, int tid) {
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, u32x4* lds, int ld, int k0,
+                                         int kcols, int wave, int lane) {
+  constexpr int kInstr = ROWS / 8 / 4;  // per wave
+  const int r_in = lane >> 3;
+  const int c = (lane & 7) ^ r_in;
+  const int k = k0 + c * 8;
 #pragma unroll
-  for (int i = 0; i < TileRegs<ROWS>::kPer; ++i) {
-    const int idx = tid + i * kThreads;
-    const int row = idx >> 3;
-    const int ch = idx & 7;
-    const int gr = row0 + row;
-    const int gk = k0 + ch * 8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (gr < nrows && gk < K) val = ld16(base + (size_t)gr * K + gk);
-    r.v[i] = val;
+  for (int j = 0; j < kInstr; ++j) {
+    const int r0 = (wave * kInstr + j) * 8;
+    const unsigned voff = k < kcols ? (unsigned)(((r0 + r_in) * ld + k) * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds + r0 * 8), 16, voff, 0, 0, 0);
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void store_tile(const TileRegs<ROWS>& r, u32x4* lds, int tid) {
-#pragma unroll
-  for (int i = 0; i < TileRegs<ROWS>::kPer; ++i) {
-    const int idx = tid + i * kThreads;
-    lds[swz8(idx >> 3, idx & 7)] = r.v[i];
-  }
+// Workgroup -> output tile.  The grid is 1-D and padded to a multiple of the
+// 8 XCDs; workgroup i runs on XCD i % 8, so each XCD is handed one
+// contiguous run of the tile order below.  That order walks groups of
+// kGroupM token tiles and, inside a group, the feature tiles token tile by
+// token tile, so the tiles an XCD works on at one time share activations
+// and weights through its L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ bool tile_of(const GemmArgs& a, int BN, int BM, int& tn, int& tm) {
+  const int ntn = (a.N + BN - 1) / BN;
+  const int ntm = (a.M + BM - 1) / BM;
+  const int total = ntn * ntm;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int id = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (id >= total) return false;
+  const int group = id / (kGroupM * ntn);
+  const int first_m = group * kGroupM;
+  const int gm = min(ntm - first_m, kGroupM);
+  const int in = id - group * kGroupM * ntn;
+  tm = first_m + in % gm;
+  tn = in / gm;
+  return true;
+}
+
+__host__ __device__ constexpr int gemm_grid(int N, int M, int BN, int BM) {
+  return ((((N + BN - 1) / BN) * ((M + BM - 1) / BM) + kXcds - 1) / kXcds) * kXcds;
 }
 
 template <int BN, int BM, int EPI>
@@ -71,11 +102,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Tiles along N are the fast grid dimension so that the activation tile
-  // (tokens) of neighbouring workgroups is shared through L2.
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
   const int N = a.N, M = a.M, K = a.K;
+  int tn, tm;
+  if (!tile_of(a, BN, BM, tn, tm)) return;  // padding workgroup
+  const int n0 = tn * BN;
+  const int m0 = tm * BM;
 
   floatx16 acc[FB][TB];
 #pragma unroll
@@ -85,43 +116,50 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[f][t][r] = 0.f;
 
-  TileRegs<BN> ra;
-  TileRegs<BM> rb;
   const int nk = (K + kBK - 1) / kBK;
   // W may be narrower than X along K (w_kmod): X = [hi | lo] reads W twice
   const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
-  load_tile<BN>(ra, a.W, n0, N, 0, Kw, tid);
-  load_tile<BM>(rb, a.X, m0, M, 0, K, tid);
-  store_tile<BN>(ra, &lds[0][0], tid);
-  store_tile<BM>(rb, &lds[0][BN * 8], tid);
+  const __amdgpu_buffer_rsrc_t rw = rows_rsrc(a.W, n0, N, Kw);
+  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(a.X, m0, M, K);
+  dma_tile<BN>(rw, &lds[0][0], Kw, 0, Kw, wave, lane);
+  dma_tile<BM>(rx, &lds[0][BN * 8], K, 0, K, wave, lane);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
-      load_tile<BN>(ra, a.W, n0, N, ((kt + 1) * kBK) % Kw, Kw, tid);
-      load_tile<BM>(rb, a.X, m0, M, (kt + 1) * kBK, K, tid);
+      // the other buffer was last read before the barrier that ended the
+      // previous iteration
+      dma_tile<BN>(rw, &lds[buf ^ 1][0], Kw, ((kt + 1) * kBK) % Kw, Kw, wave, lane);
+      dma_tile<BM>(rx, &lds[buf ^ 1][BN * 8], K, (kt + 1) * kBK, K, wave, lane);
     }
     const u32x4* sa = &lds[buf][0];
     const u32x4* sb = &lds[buf][BN * 8];
+    // fragments of k-substep s+1 are read from LDS while the MFMAs of
+    // substep s run
+    u32x4 fa[2][FB], fb[2][TB];
+#pragma unroll
+    for (int f = 0; f < FB; ++f) fa[0][f] = sa[swz8(wn * WN + 32 * f + l32, hh)];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) fb[0][t] = sb[swz8(wm * WM + 32 * t + l32, hh)];
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const int ch = 2 * s + hh;
-      u32x4 fa[FB], fb[TB];
+      const int cur = s & 1;
+      if (s + 1 < kBK / 16) {
+        const int ch = 2 * (s + 1) + hh;
 #pragma unroll
-      for (int f = 0; f < FB; ++f) fa[f] = sa[swz8(wn * WN + 32 * f + l32, ch)];
+        for (int f = 0; f < FB; ++f) fa[cur ^ 1][f] = sa[swz8(wn * WN + 32 * f + l32, ch)];
 #pragma unroll
-      for (int t = 0; t < TB; ++t) fb[t] = sb[swz8(wm * WM + 32 * t + l32, ch)];
+        for (int t = 0; t < TB; ++t) fb[cur ^ 1][t] = sb[swz8(wm * WM + 32 * t + l32, ch)];
+      }
 #pragma unroll
       for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int t = 0; t < TB; ++t) acc[f][t] = mfma32x32x16(fa[f], fb[t], acc[f][t]);
+        for (int t = 0; t < TB; ++t) acc[f][t] = mfma32x32x16(fa[cur][f], fb[cur][t], acc[f][t]);
     }
-    if (kt + 1 < nk) {
-      store_tile<BN>(ra, &lds[buf ^ 1][0], tid);
-      store_tile<BM>(rb, &lds[buf ^ 1][BN * 8], tid);
-    }
-    __syncthreads();
+    // let the scheduler interleave the LDS fragment reads with the MFMAs
+    __builtin_amdgcn_iglp_opt(0);
+    __syncthreads();  // the next tile's loads are complete and visible
   }
 
   const int nw = n0 + wn * WN;  // first feature of this wave
@@ -163,7 +201,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 
   const bool do_norm = (kind != 2) && a.qk_norm;
   const bf16* wsrc = kind == 0 ? a.q_norm_w : a.k_norm_w;
+  // norm weights of this lane's features 32f + 8j + 4hh + (0..3), kept packed
+  u32x2 wpk[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 z = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+      wpk[f][j] = do_norm ? ld8(wsrc + 32 * f + 8 * j + 4 * hh) : z;
+    }
 
+  // One token block (32 tokens) at a time; within it, a lane handles four
+  // consecutive features i..i+3 of the first half together with their RoPE
+  // partners i+64..i+67, so only a few values are live at once.
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int m = m0 + wm * WM + 32 * t + l32;
@@ -171,42 +221,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     const int mm = valid ? m : 0;
     const int b = mm / a.L;
     const int tok = mm - b * a.L;
-    float v[4][16];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[f][r] = acc[f][t][r];
-
+    float inv = 1.0f;
     if (do_norm) {
       float ss = 0.f;
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ss += v[f][r] * v[f][r];
+        for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
       ss += wave_xor32(ss);
-      const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          v[f][r] = v[f][r] * inv * (float)wsrc[32 * f + 8 * (r >> 2) + 4 * hh + (r & 3)];
-    }
-    const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
-    if (kind != 2) {
-      // rotate-half RoPE: feature i (< 64) pairs with i + 64, same lane, f+2
-      const float2* cs = a.rope + (size_t)(a.start_pos ? mm : tok) * 64;
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * f + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const float2 c = valid ? cs[i] : make_float2(1.f, 0.f);
-          const float x1 = v[f][r], x2 = v[f + 2][r];
-          v[f][r] = x1 * c.x - x2 * c.y;
-          v[f + 2][r] = x2 * c.x + x1 * c.y;
-        }
+      inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
     }
     if (!valid) continue;
+    const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
     bf16* dst;
     if (kind == 0) {
       dst = a.q + (((size_t)b * Hq + h) * a.L + tok) * 128;
@@ -215,14 +241,48 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
       dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
     }
+    if (kind == 2) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 w;
+          w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
+          w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
+          st8(dst + 32 * f + 8 * j + 4 * hh, w);
+        }
+      continue;
+    }
+    // rotate-half RoPE: feature i (< 64) pairs with i + 64 (block f + 2)
+    const float2* cs = a.rope + (size_t)(a.start_pos ? mm : tok) * 64;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w.x = pack_bf16x2(v[f][4 * j + 0], v[f][4 * j + 1]);
-        w.y = pack_bf16x2(v[f][4 * j + 2], v[f][4 * j + 3]);
-        st8(dst + 32 * f + 8 * j + 4 * hh, w);
+        const int i0 = 32 * f + 8 * j + 4 * hh;
+        // (cos, sin) of features i0 .. i0+3: two 16-byte loads
+        const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
+        const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
+        const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
+        const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+        const u32x2 w1 = wpk[f][j], w2 = wpk[f + 2][j];
+        const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
+        const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
+        float y1[4], y2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x1 = acc[f][t][4 * j + e] * inv * g1[e];
+          const float x2 = acc[f + 2][t][4 * j + e] * inv * g2[e];
+          y1[e] = x1 * cc[e] - x2 * sn[e];
+          y2[e] = x2 * cc[e] + x1 * sn[e];
+        }
+        u32x2 o1, o2;
+        o1.x = pack_bf16x2(y1[0], y1[1]);
+        o1.y = pack_bf16x2(y1[2], y1[3]);
+        o2.x = pack_bf16x2(y2[0], y2[1]);
+        o2.y = pack_bf16x2(y2[2], y2[3]);
+        st8(dst + i0, o1);
+        st8(dst + i0 + 64, o2);
       }
   }
 }
@@ -259,16 +319,14 @@ hipError_t launch_rope_table(float2* table, const int* start_pos, int rows, int 
 }
 
 hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
-  constexpr int BN = 256, BM = 128;
-  dim3 grid((args.N + BN - 1) / BN, (args.M + BM - 1) / BM);
-  gemm_bf16_kernel<BN, BM, kEpiQKV><<<grid, kThreads, 0, stream>>>(args);
+  constexpr int BN = 256, BM = 256;
+  gemm_bf16_kernel<BN, BM, kEpiQKV><<<gemm_grid(args.N, args.M, BN, BM), kThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream) {
-  constexpr int BN = 256, BM = 128;
-  dim3 grid((args.N + BN - 1) / BN, (args.M + BM - 1) / BM);
-  gemm_bf16_kernel<BN, BM, kEpiPlain><<<grid, kThreads, 0, stream>>>(args);
+  constexpr int BN = 256, BM = 256;
+  gemm_bf16_kernel<BN, BM, kEpiPlain><<<gemm_grid(args.N, args.M, BN, BM), kThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 
