@@ -58,6 +58,39 @@ def kv_bytes_of(w):
     return 2.0 * w.batch * w.hkv * (w.cache_len + w.seq) * w.d * el
 
 
+KERNEL_OF_PART = {"qkv": "qkv_gemm", "attn": "attn_prefill", "oproj": "oproj_gemm",
+                  "attn_decode": "attn_decode"}
+SOURCES_OF_KERNEL = {"qkv_gemm": "gemm_bf16.hip", "oproj_gemm": "gemm_bf16.hip",
+                     "attn_prefill": "attn_bf16.hip", "attn_decode": "attn_bf16.hip"}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    """Hash of the sources a kernel is built from (its file plus the shared
+    headers), to tell whether stored counter readings still describe it."""
+    import hashlib
+    csrc = os.path.join(ROOT, "transformer_attention_layer_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("common.h", "kernels.h", SOURCES_OF_KERNEL[kernel]):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from the
+    committed counter summary, or None when it is missing or was taken on a
+    different version of the kernel's source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha(kernel):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def _time_loop(fn, iters, torch):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -223,18 +256,22 @@ def main():
                        "ms_per_step": round(ms, 4), "frac_of_peak": round(value / peak, 4)})
         result["config"] = cfgd
         result["kernels_ms"] = {k: round(v, 4) for k, v in part_ms.items()}
-        result["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
+        kern = KERNEL_OF_PART[dom]
+        result["roofline"] = {"bound": "mfma", "kernel": kern, "achieved": round(ach, 2),
                               "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                              "traffic": None}
+                              "traffic": stored_traffic(w.name, kern),
+                              "algorithmic_flop": fl[dom], "avg_launch_ms": round(part_ms[dom], 5)}
     else:
         ms, attn_ms = bench_decode(w, args.steps, args.warmup, torch, T, GI)
         kvb = kv_bytes_of(w)
         gbs = kvb / (attn_ms * 1e-3) / 1e9
         result.update({"value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 4)})
         result["config"] = cfgd
-        result["roofline"] = {"bound": "hbm", "kernel": "attn", "achieved": round(gbs, 1),
+        result["roofline"] = {"bound": "hbm", "kernel": "attn_decode", "achieved": round(gbs, 1),
                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                              "frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "traffic": stored_traffic(w.name, "attn_decode"),
+                              "algorithmic_bytes": kvb, "avg_launch_ms": round(attn_ms, 5)}
 
     if w.cache_len == 0 and not args.no_decode:
         dec = {}

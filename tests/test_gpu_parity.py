@@ -37,7 +37,7 @@ SMALL = {
     "tiny_f32": GI.WORKLOADS["tiny_f32"],
     "prefill_h1024": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=200),
     "quotient_h4096": GI.WORKLOADS["quotient_h4096"].with_(batch=1, seq=300),
-    "wide_h5120": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=130),
+    "wide_h5120": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=260),
     "decode_h2560_gqa": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000),
     "decode_h2560_mqa": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777),
 }
@@ -130,6 +130,21 @@ def test_prefill_variants(variant):
     out, _, _ = run_layer(w, h)
     ref, _, _ = oracle_layer(w, h)
     assert_close(to_np(out), ref, w.dtype, "out")
+
+
+@pytest.mark.parametrize("tokens", [1, 17, 64, 65, 200, 256])
+def test_few_token_projection_path(tokens):
+    """Up to 256 tokens take the weight-streaming projections (32-feature
+    tiles, K split over 8 waves) and a separate norm + RoPE pass; ragged
+    token and feature counts, with and without QK-norm and the hi+lo split."""
+    for base, kw in (("prefill_h1024", {}), ("wide_h5120", {"hq": 40, "hkv": 8}),
+                     ("quotient_h4096", {})):
+        w = GI.WORKLOADS[base].with_(batch=1, seq=tokens, **kw)
+        announce(f"[few tokens] {base} {kw} T={tokens} o_split={w.o_split}")
+        h = GI.host_layer_inputs(w)
+        out, _, _ = run_layer(w, h)
+        ref, _, _ = oracle_layer(w, h)
+        assert_close(to_np(out), ref, w.dtype, "out")
 
 
 def test_chunked_prefill_with_ragged_cache():

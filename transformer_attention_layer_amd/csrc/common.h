@@ -61,6 +61,16 @@ GQA_DEV void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, unsigned voff) {
                                            16, voff, 0, 0, 0);
 }
 
+GQA_DEV u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  u32x4 out;
+  out.x = v[0];
+  out.y = v[1];
+  out.z = v[2];
+  out.w = v[3];
+  return out;
+}
+
 GQA_DEV u32x2 buf_ld8(__amdgpu_buffer_rsrc_t r, unsigned voff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
   u32x2 out;

@@ -48,8 +48,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args a) {
 }
 
 // One workgroup per (token, head of the fused projection); thread j < d/2
-// owns the RoPE pair (j, j + d/2).
-__global__ __launch_bounds__(128) void normrope_f32_kernel(F32NormRopeArgs a) {
+// owns the RoPE pair (j, j + d/2).  T is the element type of the norm
+// weights and of q / the caches (float, or bf16 for the few-token bf16 path).
+template <typename T>
+__global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
   __shared__ float red[128];
   const int m = blockIdx.x;       // token
   const int head = blockIdx.y;    // 0 .. Hq + 2 Hkv - 1
@@ -75,10 +77,10 @@ __global__ __launch_bounds__(128) void normrope_f32_kernel(F32NormRopeArgs a) {
         __syncthreads();
       }
       const float inv = 1.0f / sqrtf(red[0] / (float)d + a.eps);
-      const float* w = kind == 0 ? a.q_norm_w : a.k_norm_w;
+      const T* w = static_cast<const T*>(kind == 0 ? a.q_norm_w : a.k_norm_w);
       if (act) {
-        x1 = x1 * inv * w[j];
-        x2 = x2 * inv * w[j + half];
+        x1 = x1 * inv * (float)w[j];
+        x2 = x2 * inv * (float)w[j + half];
       }
     }
     if (act) {
@@ -93,15 +95,16 @@ __global__ __launch_bounds__(128) void normrope_f32_kernel(F32NormRopeArgs a) {
     }
   }
   if (!act) return;
-  float* dst;
+  T* dst;
   if (kind == 0) {
-    dst = a.q + (((size_t)b * a.Hq + h) * a.L + tok) * d;
+    dst = static_cast<T*>(a.q) + (((size_t)b * a.Hq + h) * a.L + tok) * d;
   } else {
     if (pos < 0 || pos >= a.cap) return;
-    dst = (kind == 1 ? a.k_cache : a.v_cache) + (((size_t)b * a.Hkv + h) * a.cap + pos) * d;
+    dst = static_cast<T*>(kind == 1 ? a.k_cache : a.v_cache) +
+          (((size_t)b * a.Hkv + h) * a.cap + pos) * d;
   }
-  dst[j] = x1;
-  dst[j + half] = x2;
+  dst[j] = (T)x1;
+  dst[j + half] = (T)x2;
 }
 
 // One wave per (query, head, sequence); lane e owns features e, e+64, ...
@@ -161,9 +164,12 @@ hipError_t launch_gemm_f32(const F32Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_normrope_f32(const F32NormRopeArgs& a, hipStream_t stream) {
+hipError_t launch_normrope(const NormRopeArgs& a, hipStream_t stream) {
   dim3 grid(a.B * a.L, a.Hq + 2 * a.Hkv);
-  normrope_f32_kernel<<<grid, 128, 0, stream>>>(a);
+  if (a.bf16)
+    normrope_kernel<bf16><<<grid, 128, 0, stream>>>(a);
+  else
+    normrope_kernel<float><<<grid, 128, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -308,7 +308,88 @@ __global__ void rope_table_kernel(float2* __restrict__ table, const int* __restr
   table[idx] = make_float2((float)c, (float)s);
 }
 
+// Few-token projection (decode): weight streaming.  A workgroup computes a
+// C^T tile of 32 features x 64 tokens; its 8 waves each take one eighth of
+// K, reading the MFMA fragments straight from global memory (the weights
+// are read once; the activations stay in L2), and the partial tiles are
+// summed through LDS.  Out-of-range rows and K tails read as zero.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyUnroll = 4;
+
+__global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs a) {
+  __shared__ floatx16 red[kSkinnyWaves - 1][2][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int N = a.N, M = a.M, K = a.K;
+  const int f0 = blockIdx.x * 32;
+  const int m0 = blockIdx.y * 64;
+  const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W + (size_t)f0 * Kw, (long long)(N - f0) * Kw * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + (size_t)m0 * K, (long long)(M - m0) * K * 2);
+  const int ksteps = (K + 15) / 16;
+  const int per = (ksteps + kSkinnyWaves - 1) / kSkinnyWaves;
+  const int kb = wave * per * 16;
+  const int ke = min(K, kb + per * 16);
+  constexpr unsigned kOob = 0x80000000u;
+
+  floatx16 acc0 = {}, acc1 = {};
+  auto step = [&](int k) {
+    const int kwc = k % Kw + 8 * hh;
+    const int kxc = k + 8 * hh;
+    const u32x4 fa = buf_ld16(rw, kwc < Kw ? (unsigned)((l32 * Kw + kwc) * 2) : kOob);
+    const u32x4 fb0 = buf_ld16(rx, kxc < K ? (unsigned)((l32 * K + kxc) * 2) : kOob);
+    const u32x4 fb1 = buf_ld16(rx, kxc < K ? (unsigned)(((32 + l32) * K + kxc) * 2) : kOob);
+    acc0 = mfma32x32x16(fa, fb0, acc0);
+    acc1 = mfma32x32x16(fa, fb1, acc1);
+  };
+  int k = kb;
+  for (; k + 16 * kSkinnyUnroll <= ke; k += 16 * kSkinnyUnroll) {
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) step(k + 16 * u);
+  }
+  for (; k < ke; k += 16) step(k);
+
+  if (wave > 0) {
+    red[wave - 1][0][lane] = acc0;
+    red[wave - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kSkinnyWaves - 1; ++w) {
+    acc0 += red[w][0][lane];
+    acc1 += red[w][1][lane];
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const floatx16& c = t == 0 ? acc0 : acc1;
+    const int m = m0 + 32 * t + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = f0 + 8 * j + 4 * hh;
+      if (n >= N) continue;
+      if (a.out_f32) {
+        floatx4 w = {c[4 * j + 0], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]};
+        *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + (size_t)m * N + n) = w;
+      } else {
+        u32x2 w;
+        w.x = pack_bf16x2(c[4 * j + 0], c[4 * j + 1]);
+        w.y = pack_bf16x2(c[4 * j + 2], c[4 * j + 3]);
+        st8(static_cast<bf16*>(a.out) + (size_t)m * N + n, w);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
+  dim3 grid((args.N + 31) / 32, (args.M + 63) / 64);
+  gemm_skinny_kernel<<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_table(float2* table, const int* start_pos, int rows, int L, int half,
                              double theta, hipStream_t stream) {

@@ -122,10 +122,15 @@ void decode_split(const Shape& s, int batch, int cap, int* n_splits, int* chunk)
   if (*n_splits < 1) *n_splits = 1;
 }
 
+// Few tokens (decode): weight-streaming projections instead of 256x256 tiles.
+constexpr long long kSkinnyMaxTokens = 256;
+bool use_skinny(const Shape& s, long long tokens) { return s.bf16 && tokens <= kSkinnyMaxTokens; }
+
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
-  if (s.bf16) return align_up(T * (s.d / 2) * sizeof(float) * 2);  // rope table, T rows max
-  return align_up(T * (size_t)s.n_qkv * sizeof(float));             // fp32 projection output
+  if (s.bf16 && !use_skinny(s, (long long)T))
+    return align_up(T * (s.d / 2) * sizeof(float) * 2);  // rope table, T rows max
+  return align_up(T * (size_t)s.n_qkv * sizeof(float));   // fp32 projection output
 }
 
 size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
@@ -163,7 +168,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
                    const void* w_qkv, const void* qn, const void* kn, const int32_t* start_pos,
                    void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st) {
   const int T = batch * q_len;
-  if (s.bf16) {
+  if (s.bf16 && !use_skinny(s, T)) {
     float2* table = reinterpret_cast<float2*>(ws);
     const int rows = start_pos ? T : q_len;
     gqa_status r = check_launch(
@@ -192,17 +197,31 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     return check_launch(gqa::launch_gemm_qkv_bf16(g, st), "qkv projection");
   }
   float* y = reinterpret_cast<float*>(ws);
-  gqa::F32Args g{static_cast<const float*>(x), static_cast<const float*>(w_qkv), y, T, s.n_qkv, s.H};
-  gqa_status r = check_launch(gqa::launch_gemm_f32(g, st), "qkv projection (f32)");
+  gqa_status r;
+  if (s.bf16) {  // few tokens: fp32 projection, then norm + rope + scatter
+    gqa::GemmArgs g{};
+    g.W = static_cast<const __bf16*>(w_qkv);
+    g.X = static_cast<const __bf16*>(x);
+    g.N = s.n_qkv;
+    g.M = T;
+    g.K = s.H;
+    g.out = y;
+    g.out_f32 = 1;
+    r = check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection (few tokens)");
+  } else {
+    gqa::F32Args g{static_cast<const float*>(x), static_cast<const float*>(w_qkv), y, T, s.n_qkv,
+                   s.H};
+    r = check_launch(gqa::launch_gemm_f32(g, st), "qkv projection (f32)");
+  }
   if (r != GQA_OK) return r;
-  gqa::F32NormRopeArgs n{};
+  gqa::NormRopeArgs n{};
   n.y = y;
-  n.q_norm_w = static_cast<const float*>(qn);
-  n.k_norm_w = static_cast<const float*>(kn);
+  n.q_norm_w = qn;
+  n.k_norm_w = kn;
   n.start_pos = start_pos;
-  n.q = static_cast<float*>(q);
-  n.k_cache = static_cast<float*>(kc);
-  n.v_cache = static_cast<float*>(vc);
+  n.q = q;
+  n.k_cache = kc;
+  n.v_cache = vc;
   n.B = batch;
   n.L = q_len;
   n.Hq = s.Hq;
@@ -210,9 +229,10 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   n.d = s.d;
   n.cap = cap;
   n.qk_norm = c.qk_norm;
+  n.bf16 = s.bf16;
   n.eps = c.rms_eps;
   n.theta = (double)c.rope_theta;
-  return check_launch(gqa::launch_normrope_f32(n, st), "norm + rope (f32)");
+  return check_launch(gqa::launch_normrope(n, st), "norm + rope");
 }
 
 gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, const void* q,
@@ -284,6 +304,8 @@ gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, co
     g.w_kmod = o_split ? s.Hq * s.d : 0;
     g.out = out;
     g.out_f32 = s.out_f32;
+    if (use_skinny(s, tokens))
+      return check_launch(gqa::launch_gemm_skinny_bf16(g, st), "o_proj (few tokens)");
     return check_launch(gqa::launch_gemm_plain_bf16(g, st), "o_proj");
   }
   gqa::F32Args g{static_cast<const float*>(o), static_cast<const float*>(w_o),

@@ -64,15 +64,20 @@ struct F32Args {
 };
 hipError_t launch_gemm_f32(const F32Args& args, hipStream_t stream);
 
-struct F32NormRopeArgs {
+// Per-(token, head) QK-norm + RoPE + scatter of an fp32 projection output;
+// weights and outputs are fp32 or (bf16 != 0) bf16.
+struct NormRopeArgs {
   const float* y;     // [T, (Hq + 2 Hkv) d] projection output
-  const float* q_norm_w; const float* k_norm_w;
+  const void* q_norm_w; const void* k_norm_w;
   const int* start_pos;
-  float* q; float* k_cache; float* v_cache;
-  int B, L, Hq, Hkv, d, cap, qk_norm;
+  void* q; void* k_cache; void* v_cache;
+  int B, L, Hq, Hkv, d, cap, qk_norm, bf16;
   float eps; double theta;
 };
-hipError_t launch_normrope_f32(const F32NormRopeArgs& args, hipStream_t stream);
+hipError_t launch_normrope(const NormRopeArgs& args, hipStream_t stream);
+
+// few-token (decode) projections: out[m, n] = sum_k X[m, k] W[n, k], fp32 or bf16 out
+hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream);
 
 struct F32AttnArgs {
   const float* q; const float* k; const float* v; float* o;
