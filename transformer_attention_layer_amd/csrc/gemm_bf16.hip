@@ -20,6 +20,10 @@ namespace gqa {
 namespace {
 
 constexpr int kBK = 64;          // K elements per LDS stage (8 chunks of 16 B)
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
 constexpr int kThreads = 256;    // 4 waves, 2 x 2 over the C^T tile
 
 // LDS row of one tile: kBK bf16 = 128 B = 8 chunks of 16 B.  Chunk c of row r
@@ -152,13 +156,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) fb[cur ^ 1][t] = sb[swz8(wm * WM + 32 * t + l32, ch)];
       }
+      // Fence the scheduler: substep s+1's reads stay ahead of substep s's
+      // MFMAs, so the wait before each substep only covers reads issued a
+      // whole substep (16 MFMAs) earlier.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < FB; ++f)
 #pragma unroll
         for (int t = 0; t < TB; ++t) acc[f][t] = mfma32x32x16(fa[cur][f], fb[cur][t], acc[f][t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // let the scheduler interleave the LDS fragment reads with the MFMAs
-    __builtin_amdgcn_iglp_opt(0);
     __syncthreads();  // the next tile's loads are complete and visible
   }
 
