@@ -12,6 +12,8 @@
 // accumulator holds, for one token, 64 of the 128 features of a head and the
 // other 64 sit in lane l^32: the per-head RMS needs one cross-lane exchange,
 // and the RoPE partners (feature i and i + 64) sit in the same lane.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -19,17 +21,22 @@ namespace gqa {
 
 namespace {
 
-constexpr int kBK = 64;          // K elements per LDS stage (8 chunks of 16 B)
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
-constexpr int kSchedDsRead = 0x100;
+constexpr int kBK = 32;          // K elements per LDS stage
+constexpr int kStages = 4;       // LDS ring: loads run kStages - 1 stages ahead
+constexpr int kCPR = kBK / 8;    // 16-byte chunks per LDS row
 constexpr int kThreads = 256;    // 4 waves, 2 x 2 over the C^T tile
 
-// LDS row of one tile: kBK bf16 = 128 B = 8 chunks of 16 B.  Chunk c of row r
-// lives at slot c ^ (r & 7): eight consecutive rows read at one chunk index
-// hit eight distinct 16-byte bank groups.
-__device__ __forceinline__ int swz8(int row, int chunk) { return (row << 3) + (chunk ^ (row & 7)); }
+// LDS row of one tile: kBK bf16 = kCPR chunks of 16 B.  gfx950's LDS serves a
+// 16-byte read 16 lanes at a time over 64 banks (256 B), and a fragment read
+// has 16 lanes on 16 consecutive rows at one chunk index.  kRPW rows share
+// one 256-byte bank window, so chunk c of row r lives at slot
+// c ^ ((r / kRPW) % kCPR): the rows of a 16-row run that fall on the same
+// window offset take kCPR distinct slots.
+constexpr int kRPW = 256 / (kBK * 2);
+static_assert(kRPW * kCPR == 16, "16 rows must cover every bank once");
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kCPR + (chunk ^ ((row / kRPW) & (kCPR - 1)));
+}
 
 // Raw buffer descriptor over rows [row0, nrows) of a row-major bf16 matrix
 // with `ld` elements per row.  Loads past the end of the range return zero
@@ -43,25 +50,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, in
                                            0x00020000);
 }
 
-// Stage one kBK-wide tile of ROWS rows straight from global memory into LDS
-// (buffer_load ... lds, no register staging).  One instruction fills 64
-// consecutive 16-byte LDS slots = 8 rows; lane i writes slot i, so it loads
-// the global chunk that the XOR swizzle places there: chunk (i & 7) ^ (i >> 3)
-// of row i >> 3.  Chunks at or past column `kcols` read as zero.
+// One operand's share of a K stage, staged straight from global memory into
+// LDS (buffer_load ... lds, no register staging).  One instruction fills 64
+// consecutive 16-byte LDS slots = kRowsPerDma rows; lane i writes slot i, so
+// it loads the global chunk that the swizzle places there.  A wave issues
+// kInstr of them per stage; the per-lane byte offsets at K = 0 are computed
+// once, and chunks at or past column `kcols` read as zero.
+constexpr int kRowsPerDma = 64 / kCPR;
+static_assert(kRowsPerDma % (kRPW * kCPR) == 0, "one swizzle term per lane for all instructions");
+
 template <int ROWS>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, u32x4* lds, int ld, int k0,
-                                         int kcols, int wave, int lane) {
-  constexpr int kInstr = ROWS / 8 / 4;  // per wave
-  const int r_in = lane >> 3;
-  const int c = (lane & 7) ^ r_in;
-  const int k = k0 + c * 8;
+struct DmaPlan {
+  static constexpr int kInstr = ROWS / kRowsPerDma / (kThreads / 64);
+  unsigned voff[kInstr];  // byte offset of this lane's chunk at K = 0
+  int kc;                 // K offset (elements) of this lane's chunk
+  int slot0;              // first LDS slot of this wave's rows
+
+  __device__ __forceinline__ void init(int ld, int wave, int lane) {
+    const int r_in = lane / kCPR;
+    // the swizzle term depends on row / kRPW, which is the same for every
+    // instruction of the wave (rows advance in multiples of kRowsPerDma,
+    // a multiple of kRPW * kCPR)
+    const int c = (lane % kCPR) ^ ((r_in / kRPW) & (kCPR - 1));
 #pragma unroll
-  for (int j = 0; j < kInstr; ++j) {
-    const int r0 = (wave * kInstr + j) * 8;
-    const unsigned voff = k < kcols ? (unsigned)(((r0 + r_in) * ld + k) * 2) : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(lds + r0 * 8), 16, voff, 0, 0, 0);
+    for (int j = 0; j < kInstr; ++j) {
+      const int row = (wave * kInstr + j) * kRowsPerDma + r_in;
+      voff[j] = (unsigned)((row * ld + c * 8) * 2);
+    }
+    kc = c * 8;
+    slot0 = wave * kInstr * kRowsPerDma * kCPR;
   }
+
+  // instruction j of the stage whose K offset is k0, into `stage` (the
+  // operand's first slot in that LDS stage)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, u32x4* stage, int j, int k0,
+                                        int kcols) const {
+    const unsigned v = k0 + kc < kcols ? voff[j] + (unsigned)(k0 * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(stage + slot0 + j * kRowsPerDma * kCPR), 16,
+        v, 0, 0, 0);
+  }
+};
+
+// s_waitcnt with the vector-memory counter limited to N (0..63): the oldest
+// loads of this wave, all but its N most recent, have completed.  LDS: also
+// wait for all of this wave's LDS reads.
+template <int N, bool LDS = false>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LDS ? 0 : 15) << 8));
 }
 
 // Workgroup -> output tile.  The grid is 1-D and padded to a multiple of the
@@ -98,11 +135,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FB = WN / 32, TB = WM / 32;
   static_assert(EPI != kEpiQKV || WN == 128, "QKV epilogue needs one head (128 features) per wave");
-  __shared__ u32x4 lds[2][(BN + BM) * 8];
+  static_assert(kBK == 32 && kStages == 4, "the pipeline below is written for 2 substeps x 4 stages");
+  static_assert(FB == 4 && TB == 4, "16 MFMAs per substep");
+  __shared__ u32x4 lds[kStages][(BN + BM) * kCPR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -125,49 +164,112 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
   const __amdgpu_buffer_rsrc_t rw = rows_rsrc(a.W, n0, N, Kw);
   const __amdgpu_buffer_rsrc_t rx = rows_rsrc(a.X, m0, M, K);
-  dma_tile<BN>(rw, &lds[0][0], Kw, 0, Kw, wave, lane);
-  dma_tile<BM>(rx, &lds[0][BN * 8], K, 0, K, wave, lane);
-  __syncthreads();
+  DmaPlan<BN> pw;
+  DmaPlan<BM> px;
+  pw.init(Kw, wave, lane);
+  px.init(K, wave, lane);
+  constexpr int kLw = DmaPlan<BN>::kInstr, kLx = DmaPlan<BM>::kInstr;
+  static_assert(kLw == 4 && kLx == 4, "one load per two MFMAs in each substep's second half");
+  // K offset into W of stage kt (K <= 2 Kw: X = [hi | lo] reads W at most twice)
+  auto w_k0 = [&](int kt) { const int k0 = kt * kBK; return k0 >= Kw ? k0 - Kw : k0; };
+  auto stage_w = [&](int kt) { return &lds[kt % kStages][0]; };
+  auto stage_x = [&](int kt) { return &lds[kt % kStages][BN * kCPR]; };
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      // the other buffer was last read before the barrier that ended the
-      // previous iteration
-      dma_tile<BN>(rw, &lds[buf ^ 1][0], Kw, ((kt + 1) * kBK) % Kw, Kw, wave, lane);
-      dma_tile<BM>(rx, &lds[buf ^ 1][BN * 8], K, (kt + 1) * kBK, K, wave, lane);
-    }
-    const u32x4* sa = &lds[buf][0];
-    const u32x4* sb = &lds[buf][BN * 8];
-    // fragments of k-substep s+1 are read from LDS while the MFMAs of
-    // substep s run
-    u32x4 fa[2][FB], fb[2][TB];
+  // LDS offsets (16-byte slots) of this lane's fragments: row-major
+  // fragments of W (features) and X (tokens), chunk = 2 * substep + hh
+  int oa[2][FB], ob[2][TB];
 #pragma unroll
-    for (int f = 0; f < FB; ++f) fa[0][f] = sa[swz8(wn * WN + 32 * f + l32, hh)];
+  for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-    for (int t = 0; t < TB; ++t) fb[0][t] = sb[swz8(wm * WM + 32 * t + l32, hh)];
+    for (int f = 0; f < FB; ++f) oa[sub][f] = swz(wn * WN + 32 * f + l32, 2 * sub + hh);
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < kBK / 16) {
-        const int ch = 2 * (s + 1) + hh;
-#pragma unroll
-        for (int f = 0; f < FB; ++f) fa[cur ^ 1][f] = sa[swz8(wn * WN + 32 * f + l32, ch)];
-#pragma unroll
-        for (int t = 0; t < TB; ++t) fb[cur ^ 1][t] = sb[swz8(wm * WM + 32 * t + l32, ch)];
-      }
-      // Fence the scheduler: substep s+1's reads stay ahead of substep s's
-      // MFMAs, so the wait before each substep only covers reads issued a
-      // whole substep (16 MFMAs) earlier.
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int f = 0; f < FB; ++f)
-#pragma unroll
-        for (int t = 0; t < TB; ++t) acc[f][t] = mfma32x32x16(fa[cur][f], fb[cur][t], acc[f][t]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();  // the next tile's loads are complete and visible
+    for (int t = 0; t < TB; ++t) ob[sub][t] = BN * kCPR + swz(wm * WM + 32 * t + l32, 2 * sub + hh);
   }
+
+  // Prologue: stages 0 .. kStages - 2 in flight, stage 0 landed and visible.
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p) {
+    if (p < nk) {
+#pragma unroll
+      for (int j = 0; j < kLw; ++j) pw.issue(rw, stage_w(p), j, w_k0(p), Kw);
+#pragma unroll
+      for (int j = 0; j < kLx; ++j) px.issue(rx, stage_x(p), j, p * kBK, K);
+    }
+  }
+  if (nk >= 3) wait_vmem<2 * (kLw + kLx)>();
+  else if (nk == 2) wait_vmem<kLw + kLx>();
+  else wait_vmem<0>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  u32x4 fa[2][FB], fb[2][TB];
+  {
+    const u32x4* st = &lds[0][0];
+#pragma unroll
+    for (int f = 0; f < FB; ++f) fa[0][f] = st[oa[0][f]];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) fb[0][t] = st[ob[0][t]];
+  }
+
+  // Main loop, one K stage (two 16-wide substeps) per trip.  Each substep
+  // issues its 16 MFMAs interleaved with the 8 LDS reads of the next
+  // substep's fragments (first half) and 4 of the loads of stage kt + 3
+  // (second half), so that no wave stalls for long on a queue of loads.
+  // Stage kt + 3 goes to the LDS stage of kt - 1.  Every wave's reads of
+  // that stage had completed (s_waitcnt lgkmcnt(0)) before it reached the
+  // barrier in the middle of trip kt - 1, which in turn makes stage kt
+  // visible.  LOAD: stage kt + 3 exists; NEXT: stage kt + 1 exists.
+  auto trip = [&](int kt, auto LOAD, auto NEXT) {
+    const int kn = kt + kStages - 1;
+    const int kwn = w_k0(kn);
+    const u32x4* st = &lds[kt % kStages][0];
+    const u32x4* st1 = &lds[(kt + 1) % kStages][0];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      if (sub == 1) {
+        if constexpr (NEXT) {
+          // stage kt + 1 landed: at most stage kt + 2 (8 loads) and the
+          // first half of stage kt + 3 (4 loads) may still be in flight;
+          // this wave's reads of stage kt are done
+          if constexpr (LOAD) wait_vmem<kLw + kLx + kLw, true>();
+          else if (kt + 2 < nk) wait_vmem<kLw + kLx, true>();
+          else wait_vmem<0, true>();
+          __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool reads = sub == 0 || NEXT;
+      const u32x4* rs = sub == 0 ? st : st1;
+      const int(&ra)[FB] = oa[sub ^ 1];
+      const int(&rb)[TB] = ob[sub ^ 1];
+#pragma unroll
+      for (int i = 0; i < FB * TB; ++i) {
+        const int f = i / TB, t = i % TB;
+        acc[f][t] = mfma32x32x16(fa[sub][f], fb[sub][t], acc[f][t]);
+        if (i < 8) {
+          // next substep's fragments in the order its MFMAs use them
+          if (reads) {
+            if (i == 0) fa[sub ^ 1][0] = rs[ra[0]];
+            else if (i <= 4) fb[sub ^ 1][i - 1] = rs[rb[i - 1]];
+            else fa[sub ^ 1][i - 4] = rs[ra[i - 4]];
+          }
+        } else if ((i & 1) == 0) {
+          if constexpr (LOAD) {
+            const int j = (i - 8) / 2;
+            if (sub == 0) pw.issue(rw, stage_w(kn), j, kwn, Kw);
+            else px.issue(rx, stage_x(kn), j, kn * kBK, K);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+  int kt = 0;
+  for (; kt < nk - (kStages - 1); ++kt) trip(kt, True(), True());
+  for (; kt < nk - 1; ++kt) trip(kt, False(), True());
+  trip(kt, False(), False());
 
   const int nw = n0 + wn * WN;  // first feature of this wave
   if (EPI == kEpiPlain) {
