@@ -47,22 +47,21 @@ constexpr float kLazyRescale = 8.0f;  // log2 of the growth allowed before resca
 // c ^ (r & 15).
 __device__ __forceinline__ int kslot(int row, int chunk) { return (row << 4) + (chunk ^ (row & 15)); }
 
-// V^T tile: rows = the 128 value features, TK keys each (TK/8 chunks).  Key
-// 16g + 8a + 4h + i is stored at position 16g + 8h + 4a + i, so chunk 2g + h
-// holds exactly the eight keys lane-half h feeds to the PV product of key
-// group g.  Chunks are XOR-swizzled with (r ^ r>>2) to spread rows over banks.
-template <int TK>
+// V tile: rows = keys, 256 B = 16 chunks each, as in memory.  The PV
+// product reads it transposed with ds_read_b64_tr_b16 (below); one such read
+// by 32 lanes touches 4 consecutive rows x 64 bytes, so chunk c of row r
+// sits at slot c ^ (4 (r & 3)): the 4 rows land on disjoint bank ranges.
 __device__ __forceinline__ int vslot(int row, int chunk) {
-  constexpr int NCH = TK / 8;
-  return row * NCH + (chunk ^ ((row ^ (row >> 2)) & (NCH - 1)));
+  return (row << 4) + (chunk ^ ((row & 3) << 2));
 }
 
-// K tile straight into LDS (buffer_load ... lds): one instruction fills 64
-// consecutive slots = 4 key rows; lane i writes slot i, so it loads the
-// chunk the swizzle puts there.  Keys past the descriptor's range read as 0.
-template <int NT, int TK>
-__device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, u32x4* sk, int key0, int wave,
-                                      int lane) {
+// K or V tile straight into LDS (buffer_load ... lds): one instruction fills
+// 64 consecutive slots = 4 key rows; lane i writes slot i, so it loads the
+// chunk that the tile's swizzle puts there.  Keys past the descriptor's
+// range read as 0.  swz(row) is the XOR applied to chunk indices of a row.
+template <int NT, int TK, typename Swz>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, u32x4* lds, int key0, int wave,
+                                         int lane, Swz swz) {
   constexpr int JW = TK / 4 / (NT / 64);  // instructions per wave
   const int r_in = lane >> 4;
   const int slot = lane & 15;
@@ -70,76 +69,62 @@ __device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, u32x4* sk, int 
   for (int j = 0; j < JW; ++j) {
     const int r0 = (wave * JW + j) * 4;
     const int row = r0 + r_in;
-    const int c = slot ^ (row & 15);
-    dma16(rk, sk + r0 * 16, (unsigned)((key0 + row) * (kD * 2) + c * 16));
+    const int c = slot ^ swz(row);
+    dma16(r, lds + r0 * 16, (unsigned)((key0 + row) * (kD * 2) + c * 16));
   }
 }
 
-// V tile through registers: a thread loads 4 keys x 4 features (8-byte
-// loads, zero past the range) ...
 template <int NT, int TK>
-struct VRegs {
-  static constexpr int kG = TK * 8 / NT;  // 4-key x 4-feature groups per thread
-  u32x2 v[kG][4];
-};
-
-template <int NT, int TK>
-__device__ __forceinline__ void load_v(VRegs<NT, TK>& r, __amdgpu_buffer_rsrc_t rv, int key0,
-                                       int tid) {
-#pragma unroll
-  for (int i = 0; i < VRegs<NT, TK>::kG; ++i) {
-    const int idx = tid + i * NT;
-    const int g4 = idx & 31;
-    const int kq = idx >> 5;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.v[i][e] = buf_ld8(rv, (unsigned)((key0 + 4 * kq + e) * (kD * 2) + 8 * g4));
-  }
+__device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, u32x4* sk, int key0, int wave,
+                                      int lane) {
+  dma_rows<NT, TK>(rk, sk, key0, wave, lane, [](int row) { return row & 15; });
 }
 
-// ... and stores them transposed: 4 features x 4 keys, each 8 bytes.
 template <int NT, int TK>
-__device__ __forceinline__ void store_vt(const VRegs<NT, TK>& r, u32x4* sv, int tid) {
-  u32x2* sv2 = reinterpret_cast<u32x2*>(sv);
-#pragma unroll
-  for (int i = 0; i < VRegs<NT, TK>::kG; ++i) {
-    const int idx = tid + i * NT;
-    const int g4 = idx & 31;
-    const int kq = idx >> 5;                 // keys 4kq .. 4kq+3 of the tile
-    const int chunk = 2 * (kq >> 2) + (kq & 1);
-    const int half = (kq >> 1) & 1;
-    const u32x2* v = r.v[i];
-    u32x2 t0, t1, t2, t3;
-    t0.x = (v[0].x & 0xffffu) | (v[1].x << 16);
-    t0.y = (v[2].x & 0xffffu) | (v[3].x << 16);
-    t1.x = (v[0].x >> 16) | (v[1].x & 0xffff0000u);
-    t1.y = (v[2].x >> 16) | (v[3].x & 0xffff0000u);
-    t2.x = (v[0].y & 0xffffu) | (v[1].y << 16);
-    t2.y = (v[2].y & 0xffffu) | (v[3].y << 16);
-    t3.x = (v[0].y >> 16) | (v[1].y & 0xffff0000u);
-    t3.y = (v[2].y >> 16) | (v[3].y & 0xffff0000u);
-    const int row = 4 * g4;
-    sv2[vslot<TK>(row + 0, chunk) * 2 + half] = t0;
-    sv2[vslot<TK>(row + 1, chunk) * 2 + half] = t1;
-    sv2[vslot<TK>(row + 2, chunk) * 2 + half] = t2;
-    sv2[vslot<TK>(row + 3, chunk) * 2 + half] = t3;
-  }
+__device__ __forceinline__ void dma_v(__amdgpu_buffer_rsrc_t rv, u32x4* sv, int key0, int wave,
+                                      int lane) {
+  dma_rows<NT, TK>(rv, sv, key0, wave, lane, [](int row) { return (row & 3) << 2; });
 }
 
-// Per-lane LDS offsets (u32x4 units) of the MFMA fragments; the same for
-// every tile and buffer.
-template <int TK>
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at a byte address of LDS.  Within each 16-lane group,
+// lane i receives element i % 4 of the 8 bytes that lane 4e + i / 4 of the
+// group points at, as its element e (a 16 x 4 block of 16-bit values comes
+// back transposed).
+GQA_DEV u32x2 lds_read_tr16(const void* p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Per-lane LDS offsets of the MFMA fragments; the same for every tile and
+// buffer.
 struct LaneOffsets {
-  int k[8];            // K fragment of d-chunk c: key row l32 (+32 kb)
-  int v[TK / 16];      // V^T fragment of key group g: feature row l32 (+32 d)
+  int k[8];  // K fragment of d-chunk c (16-byte slots): key row l32
+  int v[4];  // V^T fragment of feature block d (bytes), first read of key group 0
 };
 
-template <int TK>
-__device__ __forceinline__ void lane_offsets(LaneOffsets<TK>& o, int l32, int hh) {
+// V^T fragment (A operand of O^T = V^T P^T) for 32 features x 16 keys: lane
+// l = 16 G + i must hold feature l % 32 and, in MFMA K order, the keys its
+// P^T half holds: 4 hh + 0..3 and 8 + 4 hh + 0..3 of the 16-key group
+// (hh = l / 32 = G / 2).  A transposing read in which lane j of group G
+// points at row (key) 4 (G / 2) + j / 4, features 16 (G % 2) + 4 (j % 4)
+// + 0..3, hands lane i features 16 (G % 2) + i of the 4 keys 4 (G / 2) + e;
+// the second read is the same, 8 keys (rows) further on.  The swizzle term
+// of those rows is 4 (j / 4) for every key group, so only the feature block
+// changes the lane offset.
+__device__ __forceinline__ void lane_offsets(LaneOffsets& o, int lane) {
+  const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int c = 0; c < 8; ++c) o.k[c] = kslot(l32, 2 * c + hh);
+  const int G = lane >> 4, j = lane & 15;
+  const int row = 4 * (G >> 1) + (j >> 2);
 #pragma unroll
-  for (int g = 0; g < TK / 16; ++g) o.v[g] = vslot<TK>(l32, 2 * g + hh);
+  for (int d = 0; d < 4; ++d) {
+    const int feat = 32 * d + 16 * (G & 1) + 4 * (j & 3);
+    o.v[d] = vslot(row, feat >> 3) * 16 + (feat & 7) * 2;
+  }
 }
 
 // Running state of one wave: 32 query rows, lane = row (l % 32).
@@ -163,7 +148,7 @@ __device__ __forceinline__ void init_state(RowState& st) {
 // tile may be past it for some row of the wave.
 template <int TK>
 __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], const u32x4* sk,
-                                            const u32x4* sv, const LaneOffsets<TK>& lo, int key0,
+                                            const u32x4* sv, const LaneOffsets& lo, int key0,
                                             int kend_row, bool masked, float c_log2, int hh) {
   constexpr int KB = TK / 32;
   constexpr int NCH = TK / 8;
@@ -218,8 +203,14 @@ __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], 
     st.l = sum_bf16x2(pf.y, st.l);
     st.l = sum_bf16x2(pf.z, st.l);
     st.l = sum_bf16x2(pf.w, st.l);
+    const char* vg = reinterpret_cast<const char*>(sv) + g * 16 * (kD * 2);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st.o[d] = mfma32x32x16(sv[d * 32 * NCH + lo.v[g]], pf, st.o[d]);
+    for (int d = 0; d < 4; ++d) {
+      const u32x2 k0 = lds_read_tr16(vg + lo.v[d]);
+      const u32x2 k1 = lds_read_tr16(vg + lo.v[d] + 8 * (kD * 2));
+      const u32x4 vf = {k0.x, k0.y, k1.x, k1.y};
+      st.o[d] = mfma32x32x16(vf, pf, st.o[d]);
+    }
   }
 }
 
@@ -293,16 +284,14 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base, (long long)kvl * kD * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base, (long long)kvl * kD * 2);
-  LaneOffsets<TK> lo;
-  lane_offsets<TK>(lo, l32, hh);
+  LaneOffsets lo;
+  lane_offsets(lo, lane);
 
   RowState st;
   init_state(st);
-  VRegs<NT, TK> vr;
   if (n_tiles > 0) {
     dma_k<NT, TK>(rk, sk[0], 0, wave, lane);
-    load_v<NT, TK>(vr, rv, 0, tid);
-    store_vt<NT, TK>(vr, sv[0], tid);
+    dma_v<NT, TK>(rv, sv[0], 0, wave, lane);
   }
   __syncthreads();
   // two tiles per trip, so each buffer's LDS addresses are constants
@@ -311,14 +300,13 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
     const bool more = it + 1 < n_tiles;
     if (more) {
       dma_k<NT, TK>(rk, sk[B ^ 1], (it + 1) * TK, wave, lane);
-      load_v<NT, TK>(vr, rv, (it + 1) * TK, tid);
+      dma_v<NT, TK>(rv, sv[B ^ 1], (it + 1) * TK, wave, lane);
     }
     const int key0 = it * TK;
     if (key0 < key_end_w) {
       const bool masked = key0 + TK > kmin_w;
       attend_tile<TK>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2, hh);
     }
-    if (more) store_vt<NT, TK>(vr, sv[B ^ 1], tid);
     __syncthreads();
   };
   for (int it = 0; it < n_tiles; it += 2) {
@@ -375,16 +363,14 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   const long long bytes = (long long)(ke > 0 ? ke : 0) * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base, bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base, bytes);
-  LaneOffsets<TK> lo;
-  lane_offsets<TK>(lo, l32, hh);
+  LaneOffsets lo;
+  lane_offsets(lo, lane);
 
   RowState st;
   init_state(st);
-  VRegs<NT, TK> vr;
   if (n_tiles > 0) {
     dma_k<NT, TK>(rk, sk[0], ks, 0, lane);
-    load_v<NT, TK>(vr, rv, ks, lane);
-    store_vt<NT, TK>(vr, sv[0], lane);
+    dma_v<NT, TK>(rv, sv[0], ks, 0, lane);
   }
   __syncthreads();
   auto step = [&](auto bufc, int it) {
@@ -393,11 +379,10 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
     const bool more = it + 1 < n_tiles;
     if (more) {
       dma_k<NT, TK>(rk, sk[B ^ 1], key0 + TK, 0, lane);
-      load_v<NT, TK>(vr, rv, key0 + TK, lane);
+      dma_v<NT, TK>(rv, sv[B ^ 1], key0 + TK, 0, lane);
     }
     const bool masked = key0 + TK > kmin;
     attend_tile<TK>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2, hh);
-    if (more) store_vt<NT, TK>(vr, sv[B ^ 1], lane);
     __syncthreads();
   };
   for (int it = 0; it < n_tiles; it += 2) {
