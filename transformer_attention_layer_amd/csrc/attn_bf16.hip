@@ -58,33 +58,59 @@ __device__ __forceinline__ int vslot(int row, int chunk) {
 // K or V tile straight into LDS (buffer_load ... lds): one instruction fills
 // 64 consecutive slots = 4 key rows; lane i writes slot i, so it loads the
 // chunk that the tile's swizzle puts there.  Keys past the descriptor's
-// range read as 0.  swz(row) is the XOR applied to chunk indices of a row.
-template <int NT, int TK, typename Swz>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, u32x4* lds, int key0, int wave,
-                                         int lane, Swz swz) {
-  constexpr int JW = TK / 4 / (NT / 64);  // instructions per wave
-  const int r_in = lane >> 4;
-  const int slot = lane & 15;
+// range read as 0.  A wave issues JW = TK / 4 / (NT / 64) instructions per
+// tile and per operand; the per-lane byte offsets within a tile are fixed.
+// Each tile gets descriptors based at its first key, so that the hardware
+// range check (which covers the per-lane offset only, not a scalar offset)
+// still zero-fills the keys past the end.
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+__device__ __forceinline__ int vswz(int row) { return (row & 3) << 2; }
+
+template <int NT, int TK>
+struct TileLoads {
+  static constexpr int JW = TK / 4 / (NT / 64);
+  unsigned ko[JW], vo[JW];  // per-lane byte offsets of instruction j
+  int slot0;                // first LDS slot of this wave's rows
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int j = 0; j < JW; ++j) {
-    const int r0 = (wave * JW + j) * 4;
-    const int row = r0 + r_in;
-    const int c = slot ^ swz(row);
-    dma16(r, lds + r0 * 16, (unsigned)((key0 + row) * (kD * 2) + c * 16));
+    for (int j = 0; j < JW; ++j) {
+      const int row = (wave * JW + j) * 4 + (lane >> 4);
+      ko[j] = (unsigned)(row * (kD * 2) + (((lane & 15) ^ kswz(row)) << 4));
+      vo[j] = (unsigned)(row * (kD * 2) + (((lane & 15) ^ vswz(row)) << 4));
+    }
+    slot0 = wave * JW * 64;
   }
-}
+};
 
+// The loads of one tile into one buffer; rk / rv start at the tile's first
+// key and end at the last valid key.
 template <int NT, int TK>
-__device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, u32x4* sk, int key0, int wave,
-                                      int lane) {
-  dma_rows<NT, TK>(rk, sk, key0, wave, lane, [](int row) { return row & 15; });
-}
-
-template <int NT, int TK>
-__device__ __forceinline__ void dma_v(__amdgpu_buffer_rsrc_t rv, u32x4* sv, int key0, int wave,
-                                      int lane) {
-  dma_rows<NT, TK>(rv, sv, key0, wave, lane, [](int row) { return (row & 3) << 2; });
-}
+struct TileDst {
+  const TileLoads<NT, TK>* plan;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  u32x4* sk;
+  u32x4* sv;
+  bool live;  // the tile exists
+  __device__ __forceinline__ void k(int j) const {
+    if (live)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(sk + plan->slot0 + 64 * j), 16, plan->ko[j],
+          0, 0, 0);
+  }
+  __device__ __forceinline__ void v(int j) const {
+    if (live)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(sv + plan->slot0 + 64 * j), 16, plan->vo[j],
+          0, 0, 0);
+  }
+  __device__ __forceinline__ void all() const {
+#pragma unroll
+    for (int j = 0; j < TileLoads<NT, TK>::JW; ++j) k(j);
+#pragma unroll
+    for (int j = 0; j < TileLoads<NT, TK>::JW; ++j) v(j);
+  }
+};
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -145,20 +171,37 @@ __device__ __forceinline__ void init_state(RowState& st) {
 
 // One key tile: scores, online softmax, PV.  `kend_row` = one past the last
 // key this lane's query may see; `masked` (wave-uniform) = some key of the
-// tile may be past it for some row of the wave.
-template <int TK>
+// tile may be past it for some row of the wave.  `loads` issues the JW K
+// (loads.k(j)) and JW V (loads.v(j)) loads of the next tile, kPer after each
+// of the first QK MFMAs.
+template <int TK, int JW, typename Loads>
 __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], const u32x4* sk,
                                             const u32x4* sv, const LaneOffsets& lo, int key0,
-                                            int kend_row, bool masked, float c_log2, int hh) {
+                                            int kend_row, bool masked, float c_log2, int hh,
+                                            const Loads& loads) {
   constexpr int KB = TK / 32;
-  constexpr int NCH = TK / 8;
+  constexpr int kPer = (2 * JW + KB * 8 - 1) / (KB * 8);  // loads per leading QK MFMA
   floatx16 s[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const floatx16 z = {};
-    s[kb] = mfma32x32x16(sk[kb * 512 + lo.k[0]], qf[0], z);
 #pragma unroll
-    for (int c = 1; c < 8; ++c) s[kb] = mfma32x32x16(sk[kb * 512 + lo.k[c]], qf[c], s[kb]);
+    for (int c = 0; c < 8; ++c) {
+      const floatx16 z = {};
+      s[kb] = mfma32x32x16(sk[kb * 512 + lo.k[c]], qf[c], c == 0 ? z : s[kb]);
+      const int m = kb * 8 + c;
+      if (m * kPer < 2 * JW) {
+        // all of the next tile's loads go out during the first MFMAs, so
+        // they have the whole tile to land before the closing barrier
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int idx = m * kPer + q;
+          if (idx < JW) loads.k(idx);
+          else if (idx < 2 * JW) loads.v(idx - JW);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
   if (masked) {
 #pragma unroll
@@ -248,8 +291,13 @@ constexpr int kPrefillNT = 256;
 
 __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a) {
   constexpr int TK = kPrefillTK, NT = kPrefillNT;
-  __shared__ u32x4 sk[2][TK * 16];
-  __shared__ u32x4 sv[2][kD * TK / 8];
+  // Separate arrays per buffer: the compiler then knows that the loads into
+  // one buffer cannot touch the other, and does not make reads of the
+  // current tile wait for the loads of the next.
+  __shared__ u32x4 sk0[TK * 16], sk1[TK * 16];
+  __shared__ u32x4 sv0[kD * TK / 8], sv1[kD * TK / 8];
+  u32x4* const sk[2] = {sk0, sk1};
+  u32x4* const sv[2] = {sv0, sv1};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -282,30 +330,35 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + (row_valid ? tq : 0)) * kD, row_valid, hh);
 
   const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base, (long long)kvl * kD * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base, (long long)kvl * kD * 2);
+  const bf16* kb = a.k + kv_base;
+  const bf16* vb = a.v + kv_base;
+  // descriptors of the tile starting at key k0 (keys k0 .. kvl - 1 valid)
+  auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * kD, (long long)(kvl - k0) * kD * 2); };
+  auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * kD, (long long)(kvl - k0) * kD * 2); };
   LaneOffsets lo;
   lane_offsets(lo, lane);
 
   RowState st;
   init_state(st);
-  if (n_tiles > 0) {
-    dma_k<NT, TK>(rk, sk[0], 0, wave, lane);
-    dma_v<NT, TK>(rv, sv[0], 0, wave, lane);
-  }
+  TileLoads<NT, TK> plan;
+  plan.init(wave, lane);
+  const TileDst<NT, TK> first{&plan, rk_at(0), rv_at(0), sk[0], sv[0], n_tiles > 0};
+  first.all();
   __syncthreads();
   // two tiles per trip, so each buffer's LDS addresses are constants
   auto step = [&](auto bufc, int it) {
     constexpr int B = decltype(bufc)::value;
-    const bool more = it + 1 < n_tiles;
-    if (more) {
-      dma_k<NT, TK>(rk, sk[B ^ 1], (it + 1) * TK, wave, lane);
-      dma_v<NT, TK>(rv, sv[B ^ 1], (it + 1) * TK, wave, lane);
-    }
+    // the next tile goes to the other buffer, last read before the barrier
+    // that ended the previous trip
+    const TileDst<NT, TK> next{&plan, rk_at((it + 1) * TK), rv_at((it + 1) * TK), sk[B ^ 1],
+                               sv[B ^ 1], it + 1 < n_tiles};
     const int key0 = it * TK;
     if (key0 < key_end_w) {
       const bool masked = key0 + TK > kmin_w;
-      attend_tile<TK>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2, hh);
+      attend_tile<TK, TileLoads<NT, TK>::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked,
+                                             a.scale_log2, hh, next);
+    } else {
+      next.all();  // the other waves still need this wave's share
     }
     __syncthreads();
   };
@@ -335,8 +388,13 @@ constexpr int kDecodeNT = 64;
 
 __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   constexpr int TK = kDecodeTK, NT = kDecodeNT;
-  __shared__ u32x4 sk[2][TK * 16];
-  __shared__ u32x4 sv[2][kD * TK / 8];
+  // Separate arrays per buffer: the compiler then knows that the loads into
+  // one buffer cannot touch the other, and does not make reads of the
+  // current tile wait for the loads of the next.
+  __shared__ u32x4 sk0[TK * 16], sk1[TK * 16];
+  __shared__ u32x4 sv0[kD * TK / 8], sv1[kD * TK / 8];
+  u32x4* const sk[2] = {sk0, sk1};
+  u32x4* const sv[2] = {sv0, sv1};
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -360,29 +418,29 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + tq) * kD, row_valid, hh);
 
   const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
-  const long long bytes = (long long)(ke > 0 ? ke : 0) * kD * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base, bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base, bytes);
+  const bf16* kb = a.k + kv_base;
+  const bf16* vb = a.v + kv_base;
+  // descriptors of the tile starting at key k0 (keys k0 .. ke - 1 valid)
+  auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * kD, (long long)(ke - k0) * kD * 2); };
+  auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * kD, (long long)(ke - k0) * kD * 2); };
   LaneOffsets lo;
   lane_offsets(lo, lane);
 
   RowState st;
   init_state(st);
-  if (n_tiles > 0) {
-    dma_k<NT, TK>(rk, sk[0], ks, 0, lane);
-    dma_v<NT, TK>(rv, sv[0], ks, 0, lane);
-  }
+  TileLoads<NT, TK> plan;
+  plan.init(0, lane);
+  const TileDst<NT, TK> first{&plan, rk_at(ks), rv_at(ks), sk[0], sv[0], n_tiles > 0};
+  first.all();
   __syncthreads();
   auto step = [&](auto bufc, int it) {
     constexpr int B = decltype(bufc)::value;
     const int key0 = ks + it * TK;
-    const bool more = it + 1 < n_tiles;
-    if (more) {
-      dma_k<NT, TK>(rk, sk[B ^ 1], key0 + TK, 0, lane);
-      dma_v<NT, TK>(rv, sv[B ^ 1], key0 + TK, 0, lane);
-    }
+    const TileDst<NT, TK> next{&plan, rk_at(key0 + TK), rv_at(key0 + TK), sk[B ^ 1], sv[B ^ 1],
+                               it + 1 < n_tiles};
     const bool masked = key0 + TK > kmin;
-    attend_tile<TK>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2, hh);
+    attend_tile<TK, TileLoads<NT, TK>::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked,
+                                           a.scale_log2, hh, next);
     __syncthreads();
   };
   for (int it = 0; it < n_tiles; it += 2) {
