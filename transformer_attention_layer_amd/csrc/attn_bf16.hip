@@ -174,35 +174,55 @@ __device__ __forceinline__ void init_state(RowState& st) {
 // tile may be past it for some row of the wave.  `loads` issues the JW K
 // (loads.k(j)) and JW V (loads.v(j)) loads of the next tile, kPer after each
 // of the first QK MFMAs.
+//
+// LDS reads are issued a whole phase ahead of their MFMAs: all K fragments of
+// the tile before the QK product, all V^T fragments (into the same registers)
+// while the QK MFMAs drain and the softmax runs.
 template <int TK, int JW, typename Loads>
 __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], const u32x4* sk,
                                             const u32x4* sv, const LaneOffsets& lo, int key0,
                                             int kend_row, bool masked, float c_log2, int hh,
                                             const Loads& loads) {
   constexpr int KB = TK / 32;
-  constexpr int kPer = (2 * JW + KB * 8 - 1) / (KB * 8);  // loads per leading QK MFMA
+  constexpr int NF = KB * 8;  // K fragments per tile = V^T fragments per tile
+  static_assert(NF == TK / 16 * 4, "as many V^T as K fragments");
+  constexpr int kPer = (2 * JW + NF - 1) / NF;  // loads per leading QK MFMA
+  u32x4 fr[NF];
+#pragma unroll
+  for (int m = 0; m < NF; ++m) fr[m] = sk[(m >> 3) * 512 + lo.k[m & 7]];
+  __builtin_amdgcn_sched_barrier(0);
   floatx16 s[KB];
+  // the KB accumulation chains are interleaved
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
+  for (int i = 0; i < NF; ++i) {
+    const int kb = i % KB, c = i / KB, m = kb * 8 + c;
+    const floatx16 z = {};
+    s[kb] = mfma32x32x16(fr[m], qf[c], c == 0 ? z : s[kb]);
+    if (i * kPer < 2 * JW) {
+      // all of the next tile's loads go out during the first MFMAs, so
+      // they have the whole tile to land before the closing barrier
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const floatx16 z = {};
-      s[kb] = mfma32x32x16(sk[kb * 512 + lo.k[c]], qf[c], c == 0 ? z : s[kb]);
-      const int m = kb * 8 + c;
-      if (m * kPer < 2 * JW) {
-        // all of the next tile's loads go out during the first MFMAs, so
-        // they have the whole tile to land before the closing barrier
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          const int idx = m * kPer + q;
-          if (idx < JW) loads.k(idx);
-          else if (idx < 2 * JW) loads.v(idx - JW);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < kPer; ++q) {
+        const int idx = i * kPer + q;
+        if (idx < JW) loads.k(idx);
+        else if (idx < 2 * JW) loads.v(idx - JW);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < TK / 16; ++g) {
+    const char* vg = reinterpret_cast<const char*>(sv) + g * 16 * (kD * 2);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x2 k0 = lds_read_tr16(vg + lo.v[d]);
+      const u32x2 k1 = lds_read_tr16(vg + lo.v[d] + 8 * (kD * 2));
+      fr[g * 4 + d] = u32x4{k0.x, k0.y, k1.x, k1.y};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   if (masked) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -246,14 +266,8 @@ __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], 
     st.l = sum_bf16x2(pf.y, st.l);
     st.l = sum_bf16x2(pf.z, st.l);
     st.l = sum_bf16x2(pf.w, st.l);
-    const char* vg = reinterpret_cast<const char*>(sv) + g * 16 * (kD * 2);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const u32x2 k0 = lds_read_tr16(vg + lo.v[d]);
-      const u32x2 k1 = lds_read_tr16(vg + lo.v[d] + 8 * (kD * 2));
-      const u32x4 vf = {k0.x, k0.y, k1.x, k1.y};
-      st.o[d] = mfma32x32x16(vf, pf, st.o[d]);
-    }
+    for (int d = 0; d < 4; ++d) st.o[d] = mfma32x32x16(fr[g * 4 + d], pf, st.o[d]);
   }
 }
 
