@@ -479,24 +479,54 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
 // Merge the per-split partials of one (sequence, KV head, row) with their
 // log-sum-exp weights.
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wsh[64];
   const int lane = threadIdx.x;
   const int row = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int head_local = row / a.Lq;
   const int tq = row - head_local * a.Lq;
   const int hq = kvh * a.G + head_local;
   const size_t base = (((size_t)b * a.Hkv + kvh) * a.n_splits) * 32 + row;
+  // split maxima and sums: lane s holds split s (then s + 64, ...)
   float mmax = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
+  for (int s = lane; s < a.n_splits; s += 64) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x, 64));
   const float muse = mmax == -INFINITY ? 0.f : mmax;
   float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float2 ml = a.part_ml[base + (size_t)s * 32];
-    const float w = fast_exp2(ml.x - muse);
-    lsum += w * ml.y;
-    const float* po = a.part_o + (base + (size_t)s * 32) * kD + 2 * lane;
-    o0 += w * po[0];
-    o1 += w * po[1];
+  const float* po = a.part_o + base * kD + 2 * lane;
+  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < a.n_splits) {
+      const float2 ml = a.part_ml[base + (size_t)s * 32];
+      w = fast_exp2(ml.x - muse);
+      lsum += w * ml.y;
+    }
+    __syncthreads();  // previous chunk's weights are consumed
+    wsh[lane] = w;
+    __syncthreads();
+    const int n = min(64, a.n_splits - s0);
+    // lane holds features 2 lane, 2 lane + 1 of every split row
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = *reinterpret_cast<const float2*>(po + (size_t)(s0 + i + u) * 32 * kD);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o0 += wsh[i + u] * v[u].x;
+        o1 += wsh[i + u] * v[u].y;
+      }
+    }
+    for (; i < n; ++i) {
+      const float2 v = *reinterpret_cast<const float2*>(po + (size_t)(s0 + i) * 32 * kD);
+      o0 += wsh[i] * v.x;
+      o1 += wsh[i] * v.y;
+    }
   }
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) lsum += __shfl_xor(lsum, x, 64);
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   const size_t width = (size_t)a.Hq * kD;
   bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * kD;

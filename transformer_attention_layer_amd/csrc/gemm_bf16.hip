@@ -299,6 +299,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   }
 
   // ---- QKV epilogue: one head of 128 features per wave ----
+  // Per 32-token block the lane's values are normalised and rotated in
+  // registers and written to this wave's 32 KB of LDS as rows of 128 bf16
+  // per token; the rows are then stored 16 bytes per lane, 4 whole rows per
+  // instruction (a head's rows are contiguous in q and in the caches).
+  // Row r's 16-byte chunk c sits at slot c ^ (r & 15).
+  __syncthreads();  // every wave is done reading the last K stages
   if (nw >= N) return;  // wave-uniform
   const int head = nw >> 7;
   const int Hq = a.Hq, Hkv = a.Hkv;
@@ -307,6 +313,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   if (head < Hq) { kind = 0; h = head; }
   else if (head < Hq + Hkv) { kind = 1; h = head - Hq; }
   else { kind = 2; h = head - Hq - Hkv; }
+  u32x4* const stage = &lds[wave][0];   // 128 rows x 16 chunks
+  u32x2* const stage8 = reinterpret_cast<u32x2*>(stage);
+  auto put8 = [&](int row, int feat, u32x2 v) {  // 4 features at feat (multiple of 4)
+    stage8[(row * 16 + ((feat >> 3) ^ (row & 15))) * 2 + ((feat >> 2) & 1)] = v;
+  };
 
   const bool do_norm = (kind != 2) && a.qk_norm;
   const bf16* wsrc = kind == 0 ? a.q_norm_w : a.k_norm_w;
@@ -325,11 +336,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // partners i+64..i+67, so only a few values are live at once.
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
-    const int m = m0 + wm * WM + 32 * t + l32;
-    const bool valid = m < M;
-    const int mm = valid ? m : 0;
-    const int b = mm / a.L;
-    const int tok = mm - b * a.L;
+    const int row = 32 * t + l32;
+    const int m = m0 + wm * WM + row;
+    const int mm = m < M ? m : 0;
+    const int tok = mm % a.L;
     float inv = 1.0f;
     if (do_norm) {
       float ss = 0.f;
@@ -340,16 +350,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       ss += wave_xor32(ss);
       inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
     }
-    if (!valid) continue;
-    const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
-    bf16* dst;
-    if (kind == 0) {
-      dst = a.q + (((size_t)b * Hq + h) * a.L + tok) * 128;
-    } else {
-      if (pos < 0 || pos >= a.cap) continue;
-      bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
-      dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
-    }
     if (kind == 2) {
 #pragma unroll
       for (int f = 0; f < 4; ++f)
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           u32x2 w;
           w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
           w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
-          st8(dst + 32 * f + 8 * j + 4 * hh, w);
+          put8(row, 32 * f + 8 * j + 4 * hh, w);
         }
       continue;
     }
@@ -390,9 +390,30 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         o1.y = pack_bf16x2(y1[2], y1[3]);
         o2.x = pack_bf16x2(y2[0], y2[1]);
         o2.y = pack_bf16x2(y2[2], y2[3]);
-        st8(dst + i0, o1);
-        st8(dst + i0 + 64, o2);
+        put8(row, i0, o1);
+        put8(row, i0 + 64, o2);
       }
+  }
+
+  // Store: lane l moves chunk l % 16 of row 4 i + l / 16.
+  const int c = lane & 15;
+#pragma unroll 4
+  for (int i = 0; i < WM / 4; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    const int m = m0 + wm * WM + row;
+    if (m >= M) continue;
+    const int b = m / a.L;
+    const int tok = m - b * a.L;
+    bf16* dst;
+    if (kind == 0) {
+      dst = a.q + (((size_t)b * Hq + h) * a.L + tok) * 128;
+    } else {
+      const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
+      if (pos < 0 || pos >= a.cap) continue;
+      bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
+      dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
+    }
+    st16(dst + 8 * c, stage[row * 16 + (c ^ (row & 15))]);
   }
 }
 

@@ -108,10 +108,13 @@ size_t esize(const Shape& s) { return s.bf16 ? 2 : 4; }
 // split-KV decode is used when a KV group's query rows fit one wave
 bool use_decode(const Shape& s, int q_len) { return s.bf16 && s.G * q_len <= 32; }
 
+// Splits of at least kDecodeMinChunk keys: shorter ones make the partial
+// results (32 rows x 128 floats per split) a sizeable share of the traffic.
+constexpr int kDecodeMinChunk = 1024;
 void decode_split(const Shape& s, int batch, int cap, int* n_splits, int* chunk) {
   const long long streams = (long long)batch * s.Hkv;
   long long want = (4096 + streams - 1) / (streams > 0 ? streams : 1);
-  long long max_splits = (cap + 255) / 256;
+  long long max_splits = (cap + kDecodeMinChunk - 1) / kDecodeMinChunk;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
   int ch = (int)((cap + want - 1) / want);
