@@ -180,6 +180,29 @@ def bench_decode(w, steps, warmup, torch, T, GI):
     return ms, attn_ms
 
 
+def measured_peaks(torch):
+    """What this machine delivers to a library GEMM and to a plain streaming read,
+    as references beside the vendor peaks: a bf16 8192^3 torch.matmul
+    (hipBLASLt) and a torch.sum over 2 GiB of fp32."""
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(3):  # library setup and clocks
+        torch.matmul(a, b)
+    gemm_ms = _time_loop(lambda: torch.matmul(a, b), 10, torch)
+    del a, b
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum()
+    read_ms = _time_loop(lambda: x.sum(), 10, torch)
+    del x
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm": "torch.matmul bf16 8192x8192x8192 (hipBLASLt)",
+            "hbm_read_gbs": round((1 << 31) / (read_ms * 1e-3) / 1e9, 1),
+            "read": "torch.sum over 2 GiB fp32"}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it is, on a bounded sample: whole sequences of the
     same workload (float64), as many as fit the time budget (at least one).
@@ -205,8 +228,12 @@ def cpu_baseline(w, budget_s=12.0):
         elapsed += time.perf_counter() - t0
         done += 1
     fl = flops_of(one)["total"] * done
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
+    except Exception:  # pragma: no cover
+        blas = "unknown"
     return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": os.cpu_count(), "blas": blas,
             "sample": f"{done} of {w.batch} sequences ({one.seq} tokens each), float64 numpy, "
                       f"{elapsed:.1f} s"}
 
@@ -219,6 +246,8 @@ def main():
     ap.add_argument("--workload", default="prefill_h1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured GEMM / read references")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -283,6 +312,15 @@ def main():
                          "attn_ms": round(attn_ms, 4), "layer_ms": round(dms, 4),
                          "kv_bytes": kv_bytes_of(wd)}
         result["decode"] = dec
+
+    if not args.no_peaks:
+        mp = measured_peaks(torch)
+        result["measured_peaks"] = mp
+        rl = result["roofline"]
+        ref = mp["gemm_bf16_tflops"] if rl["bound"] == "mfma" else mp["hbm_read_gbs"]
+        rl["frac_of_measured"] = round(rl["achieved"] / ref, 4)
+        for d in result.get("decode", {}).values():
+            d["frac_of_measured_read"] = round(d["kv_gb_per_s"] / mp["hbm_read_gbs"], 4)
 
     if args.copy_probe_mb:
         # a plain device-to-device copy of known size, outside the timed
