@@ -237,7 +237,7 @@ __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], 
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, wave_xor32(mx));
+  mx = max_xor32(mx);
   const float mt = mx * c_log2;  // -inf stays -inf (c_log2 > 0)
   if (__builtin_amdgcn_ballot_w64(mt > st.m + kLazyRescale)) {
     const float mn = fmaxf(st.m, mt);
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
     if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  const float lt = st.l + wave_xor32(st.l);
+  const float lt = sum_xor32(st.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (!row_valid) return;
   const size_t width = (size_t)a.Hq * kD;
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
     if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  const float lt = st.l + wave_xor32(st.l);
+  const float lt = sum_xor32(st.l);
   if (!row_valid) return;  // only the group's real rows are merged
   const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * 32 + l32;
   if (hh == 0) a.part_ml[pidx] = make_float2(st.m, lt);

@@ -91,4 +91,19 @@ GQA_DEV floatx16 mfma32x32x16(u32x4 a, u32x4 b, floatx16 c) {
 
 GQA_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Combine v across lanes l and l ^ 32 with v_permlane32_swap (a VALU
+// instruction, unlike ds_bpermute it does not wait behind this wave's LDS
+// reads): swap(v, v) returns v of lanes 0..31 in both halves of its first
+// result and v of lanes 32..63 in both halves of its second.
+GQA_DEV float max_xor32(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
+}
+GQA_DEV float sum_xor32(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_bit_cast(float, (unsigned)q[0]) + __builtin_bit_cast(float, (unsigned)q[1]);
+}
+
 GQA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

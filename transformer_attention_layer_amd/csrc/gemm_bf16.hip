@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
-      ss += wave_xor32(ss);
+      ss = sum_xor32(ss);
       inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
     }
     if (kind == 2) {
