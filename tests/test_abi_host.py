@@ -58,15 +58,22 @@ def test_resolve_explicit_and_quotient():
     assert T.gqa_resolve(cfg(num_kv_heads=None))["num_kv_heads"] == 16
     # explicit head_dim needs no divisibility (1000 % 16 != 0)
     assert T.gqa_resolve(cfg(hidden_size=1000, dtype="f32"))["head_dim"] == 128
+    # bf16 takes any even head_dim up to 256 (128 on the matrix-core path)
+    for d in (64, 80, 256):
+        assert T.gqa_resolve(cfg(head_dim=d))["head_dim"] == d
 
 
 @pytest.mark.parametrize("kw,name", [
     (dict(hidden_size=1000, head_dim=None), "GQA_ERR_HEAD_DIM_INDIVISIBLE"),
     (dict(num_kv_heads=5), "GQA_ERR_GROUP_INDIVISIBLE"),
     (dict(head_dim=127, dtype="f32"), "GQA_ERR_ODD_HEAD_DIM"),
-    (dict(head_dim=64), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(head_dim=258), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
     (dict(head_dim=258, dtype="f32"), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
     (dict(hidden_size=1004), "GQA_ERR_UNSUPPORTED_SHAPE"),
+    # bf16 rows move in 16-byte pieces: Hq*d = 3*6 = 18 is not a multiple of 8
+    (dict(num_heads=3, num_kv_heads=3, head_dim=6), "GQA_ERR_UNSUPPORTED_SHAPE"),
+    # the hi | lo split reads W_o twice in 32-wide K stages: 3*88 % 32 != 0
+    (dict(num_heads=3, num_kv_heads=3, head_dim=88, o_split=True), "GQA_ERR_UNSUPPORTED_SHAPE"),
     (dict(hidden_size=0), "GQA_ERR_INVALID_ARG"),
     (dict(rope_theta=0.0), "GQA_ERR_INVALID_ARG"),
     (dict(rms_eps=-1.0), "GQA_ERR_INVALID_ARG"),
@@ -81,9 +88,11 @@ def test_resolve_rejects(kw, name):
 
 def test_unsupported_head_dim_message_names_the_dimension():
     _lib_or_skip()
+    # the quotient 2560 / 32 = 80 is supported in bf16; 8192 / 16 = 512 is not
+    assert T.gqa_resolve(cfg(hidden_size=2560, num_heads=32, head_dim=None))["head_dim"] == 80
     with pytest.raises(T.GQAError) as e:
-        T.gqa_resolve(cfg(hidden_size=2560, num_heads=32, head_dim=None))  # quotient 80
-    assert "80" in str(e.value)
+        T.gqa_resolve(cfg(hidden_size=8192, num_heads=16, num_kv_heads=16, head_dim=None))
+    assert "512" in str(e.value)
 
 
 def test_workspace_sizes():

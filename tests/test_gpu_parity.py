@@ -40,6 +40,13 @@ SMALL = {
     "wide_h5120": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=260),
     "decode_h2560_gqa": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000),
     "decode_h2560_mqa": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777),
+    # bf16 head sizes other than 128 (separate norm/RoPE pass, vector-unit attention)
+    "bf16_d64": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=150, hq=8, hkv=2, head_dim=64),
+    "bf16_d256": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=130, hq=4, hkv=2, head_dim=256),
+    "bf16_d80_quotient": GI.WORKLOADS["quotient_h4096"].with_(batch=1, seq=90, hidden=640, hq=8,
+                                                             hkv=4),
+    "bf16_d64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=300, hq=8, hkv=4,
+                                                              head_dim=64),
 }
 
 

@@ -1,5 +1,6 @@
-// fp32 path of the layer (any even head_dim from 2 to 256).  Plain VALU
-// kernels: a tiled GEMM, a per-(token, head) QK-norm + RoPE + scatter, and a
+// fp32 path of the layer (any even head_dim from 2 to 256), and the pieces
+// the bf16 path uses for head sizes other than 128.  Plain VALU kernels: a
+// tiled GEMM, a per-(token, head) QK-norm + RoPE + scatter, and a
 // one-wave-per-query attention with an online softmax.  Same steps as the
 // bf16 path (tutorial "Multi-Head and Grouped-Query Attention (Full Layer)",
 // section 4 steps 1-7), in float throughout.
@@ -108,7 +109,12 @@ __global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
 }
 
 // One wave per (query, head, sequence); lane e owns features e, e+64, ...
-__global__ __launch_bounds__(64) void attn_f32_kernel(F32AttnArgs a) {
+// T is the element type of q, the caches and o (float, or bf16 for head
+// sizes the bf16 matrix-core kernels do not cover); with bf16 and o_split
+// the output is the bf16 value followed, Hq * d further on, by its rounding
+// residual.
+template <typename T>
+__global__ __launch_bounds__(64) void attn_vec_kernel(F32AttnArgs a) {
   const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int d = a.d;
@@ -118,22 +124,22 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32AttnArgs a) {
   kvl = kvl < 0 ? 0 : (kvl > a.cap ? a.cap : kvl);
   const int qpos = kvl - a.Lq + i;
   const int kend = a.causal ? min(kvl, qpos + 1) : kvl;
-  const float* q = a.q + (((size_t)b * a.Hq + hq) * a.Lq + i) * d;
-  const float* kb = a.k + ((size_t)b * a.Hkv + kvh) * a.cap * d;
-  const float* vb = a.v + ((size_t)b * a.Hkv + kvh) * a.cap * d;
+  const T* q = static_cast<const T*>(a.q) + (((size_t)b * a.Hq + hq) * a.Lq + i) * d;
+  const T* kb = static_cast<const T*>(a.k) + ((size_t)b * a.Hkv + kvh) * a.cap * d;
+  const T* vb = static_cast<const T*>(a.v) + ((size_t)b * a.Hkv + kvh) * a.cap * d;
   float qv[4], ov[4];
   for (int u = 0; u < 4; ++u) {
     const int e = lane + 64 * u;
-    qv[u] = e < d ? q[e] : 0.f;
+    qv[u] = e < d ? (float)q[e] : 0.f;
     ov[u] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   for (int j = 0; j < kend; ++j) {
-    const float* kr = kb + (size_t)j * d;
+    const T* kr = kb + (size_t)j * d;
     float part = 0.f;
     for (int u = 0; u < 4; ++u) {
       const int e = lane + 64 * u;
-      if (e < d) part = fmaf(qv[u], kr[e], part);
+      if (e < d) part = fmaf(qv[u], (float)kr[e], part);
     }
     for (int s = 32; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
     const float x = part * a.scale;
@@ -141,18 +147,24 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32AttnArgs a) {
     const float alpha = expf(m - m_new);
     const float p = expf(x - m_new);
     l = l * alpha + p;
-    const float* vr = vb + (size_t)j * d;
+    const T* vr = vb + (size_t)j * d;
     for (int u = 0; u < 4; ++u) {
       const int e = lane + 64 * u;
-      ov[u] = ov[u] * alpha + (e < d ? p * vr[e] : 0.f);
+      ov[u] = ov[u] * alpha + (e < d ? p * (float)vr[e] : 0.f);
     }
     m = m_new;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  float* o = a.o + ((size_t)b * a.Lq + i) * ((size_t)a.Hq * d) + (size_t)hq * d;
+  const size_t width = (size_t)a.Hq * d;
+  T* o = static_cast<T*>(a.o) + ((size_t)b * a.Lq + i) * width * (a.o_split ? 2 : 1) +
+         (size_t)hq * d;
   for (int u = 0; u < 4; ++u) {
     const int e = lane + 64 * u;
-    if (e < d) o[e] = ov[u] * inv;
+    if (e >= d) continue;
+    const float val = ov[u] * inv;
+    const T hi = (T)val;
+    o[e] = hi;
+    if (a.o_split) o[width + e] = (T)(val - (float)hi);
   }
 }
 
@@ -173,9 +185,12 @@ hipError_t launch_normrope(const NormRopeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(const F32AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_vec(const F32AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.Lq, a.Hq, a.B);
-  attn_f32_kernel<<<grid, 64, 0, stream>>>(a);
+  if (a.bf16)
+    attn_vec_kernel<bf16><<<grid, 64, 0, stream>>>(a);
+  else
+    attn_vec_kernel<float><<<grid, 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Shape {
   int H, Hq, Hkv, d, G, n_qkv;
   bool bf16;
+  bool mfma;     // bf16 with head_dim 128: the matrix-core attention and fused QKV epilogue
   bool out_f32;  // o_proj output in fp32
   bool o_split;  // layer forward: attention output as a bf16 hi + lo pair
 };
@@ -67,16 +68,23 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
                 c.head_dim);
   if (c.dtype != GQA_F32 && c.dtype != GQA_BF16)
     return fail(GQA_ERR_UNSUPPORTED_DTYPE, "dtype %d is not GQA_F32 or GQA_BF16", c.dtype);
-  if (c.dtype == GQA_BF16 && c.head_dim != 128)
+  if (c.head_dim > 256)
     return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
-                "Unsupported head_dim %d: the bf16 MFMA kernels are built for head_dim 128",
-                c.head_dim);
-  if (c.dtype == GQA_F32 && c.head_dim > 256)
-    return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
-                "Unsupported head_dim %d: the fp32 kernels take even head_dim up to 256", c.head_dim);
-  if (c.dtype == GQA_BF16 && c.hidden_size % 8 != 0)
-    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "hidden_size %d must be a multiple of 8 for bf16",
-                c.hidden_size);
+                "Unsupported head_dim %d: the kernels take even head_dim up to 256", c.head_dim);
+  if (c.dtype == GQA_BF16) {
+    // bf16 rows are moved in 16-byte pieces and stored 4 features at a time
+    if (c.hidden_size % 8 != 0)
+      return fail(GQA_ERR_UNSUPPORTED_SHAPE, "hidden_size %d must be a multiple of 8 for bf16",
+                  c.hidden_size);
+    if (((long long)c.num_heads * c.head_dim) % 8 != 0 ||
+        ((long long)(c.num_heads + 2LL * c.num_kv_heads) * c.head_dim) % 8 != 0)
+      return fail(GQA_ERR_UNSUPPORTED_SHAPE,
+                  "bf16 needs num_heads*head_dim and (num_heads+2*num_kv_heads)*head_dim to be "
+                  "multiples of 8");
+    if (c.o_split && ((long long)c.num_heads * c.head_dim) % 32 != 0)
+      return fail(GQA_ERR_UNSUPPORTED_SHAPE,
+                  "o_split needs num_heads*head_dim to be a multiple of 32");
+  }
   if (!(c.rope_theta > 0.f) || !isfinite(c.rope_theta))
     return fail(GQA_ERR_INVALID_ARG, "rope_theta must be positive and finite");
   if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
@@ -97,6 +105,7 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->G = c.num_heads / c.num_kv_heads;
     sh->n_qkv = (int)n_qkv;
     sh->bf16 = c.dtype == GQA_BF16;
+    sh->mfma = sh->bf16 && c.head_dim == 128;
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
     sh->o_split = c.o_split && c.dtype == GQA_BF16;
   }
@@ -106,7 +115,7 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
 size_t esize(const Shape& s) { return s.bf16 ? 2 : 4; }
 
 // split-KV decode is used when a KV group's query rows fit one wave
-bool use_decode(const Shape& s, int q_len) { return s.bf16 && s.G * q_len <= 32; }
+bool use_decode(const Shape& s, int q_len) { return s.mfma && s.G * q_len <= 32; }
 
 // Splits of at least kDecodeMinChunk keys: shorter ones make the partial
 // results (32 rows x 128 floats per split) a sizeable share of the traffic.
@@ -131,7 +140,7 @@ bool use_skinny(const Shape& s, long long tokens) { return s.bf16 && tokens <= k
 
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
-  if (s.bf16 && !use_skinny(s, (long long)T))
+  if (s.mfma && !use_skinny(s, (long long)T))
     return align_up(T * (s.d / 2) * sizeof(float) * 2);  // rope table, T rows max
   return align_up(T * (size_t)s.n_qkv * sizeof(float));   // fp32 projection output
 }
@@ -171,7 +180,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
                    const void* w_qkv, const void* qn, const void* kn, const int32_t* start_pos,
                    void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st) {
   const int T = batch * q_len;
-  if (s.bf16 && !use_skinny(s, T)) {
+  if (s.mfma && !use_skinny(s, T)) {
     float2* table = reinterpret_cast<float2*>(ws);
     const int rows = start_pos ? T : q_len;
     gqa_status r = check_launch(
@@ -201,7 +210,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   }
   float* y = reinterpret_cast<float*>(ws);
   gqa_status r;
-  if (s.bf16) {  // few tokens: fp32 projection, then norm + rope + scatter
+  if (s.bf16) {  // fp32 projection, then norm + rope + scatter
     gqa::GemmArgs g{};
     g.W = static_cast<const __bf16*>(w_qkv);
     g.X = static_cast<const __bf16*>(x);
@@ -210,7 +219,9 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     g.K = s.H;
     g.out = y;
     g.out_f32 = 1;
-    r = check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection (few tokens)");
+    r = use_skinny(s, T)
+            ? check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection (few tokens)")
+            : check_launch(gqa::launch_gemm_plain_bf16(g, st), "qkv projection");
   } else {
     gqa::F32Args g{static_cast<const float*>(x), static_cast<const float*>(w_qkv), y, T, s.n_qkv,
                    s.H};
@@ -242,12 +253,14 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
                     const void* kc, const void* vc, const int32_t* kv_base, int kv_add, int cap,
                     void* o, bool o_split, void* ws, hipStream_t st) {
   const double scale = 1.0 / sqrt((double)s.d);
-  if (!s.bf16) {
+  if (!s.mfma) {  // fp32, or bf16 with a head_dim other than 128
     gqa::F32AttnArgs a{};
-    a.q = static_cast<const float*>(q);
-    a.k = static_cast<const float*>(kc);
-    a.v = static_cast<const float*>(vc);
-    a.o = static_cast<float*>(o);
+    a.q = q;
+    a.k = kc;
+    a.v = vc;
+    a.o = o;
+    a.bf16 = s.bf16;
+    a.o_split = o_split && s.bf16;
     a.kv_base = kv_base;
     a.kv_add = kv_add;
     a.B = batch;
@@ -258,7 +271,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
     a.d = s.d;
     a.causal = c.causal;
     a.scale = (float)scale;
-    return check_launch(gqa::launch_attn_f32(a, st), "attention (f32)");
+    return check_launch(gqa::launch_attn_vec(a, st), "attention (vector path)");
   }
   gqa::AttnArgs a{};
   a.q = static_cast<const __bf16*>(q);

@@ -79,12 +79,14 @@ hipError_t launch_normrope(const NormRopeArgs& args, hipStream_t stream);
 // few-token (decode) projections: out[m, n] = sum_k X[m, k] W[n, k], fp32 or bf16 out
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream);
 
+// One-wave-per-query attention over fp32 or (bf16 != 0) bf16 q / caches / o,
+// any even head_dim up to 256; o_split as in AttnArgs (bf16 only).
 struct F32AttnArgs {
-  const float* q; const float* k; const float* v; float* o;
+  const void* q; const void* k; const void* v; void* o;
   const int* kv_base; int kv_add;
-  int B, Hq, Hkv, Lq, cap, d, causal;
+  int B, Hq, Hkv, Lq, cap, d, causal, bf16, o_split;
   float scale;
 };
-hipError_t launch_attn_f32(const F32AttnArgs& args, hipStream_t stream);
+hipError_t launch_attn_vec(const F32AttnArgs& args, hipStream_t stream);
 
 }  // namespace gqa
