@@ -40,9 +40,15 @@ Readings where the pages are silent (each also listed in the design doc):
    sees keys at positions <= its own (bottom-right causal alignment); new
    k and v are appended before attending.
 8. The layer returns the o_proj output; the residual add is the caller's.
+9. Partial rotary (the NeoX issue's "existing rotary_pct behavior", not
+   defined on the pages): with rotary_dim r < d, only the first r entries of
+   each head rotate, as a rotate-half RoPE of width r (entry i < r/2 pairs
+   with i + r/2 and turns by ``p * theta**(-2i/r)``); entries r .. d-1 pass
+   through.  r = d is reading 3.
 
-parity unpinned: reading 1 (the exact RMSNorm formula: eps placement) and
-reading 3 (the RoPE pairing convention) are not fixed by the pages.  The
+parity unpinned: reading 1 (the exact RMSNorm formula: eps placement),
+reading 3 (the RoPE pairing convention) and reading 9 (which entries a
+partial rotary turns) are not fixed by the pages.  The
 tests pin them to library routines and mathematical invariants (norm
 preservation, relative-position property, identity at p = 0), not to page
 values.
@@ -185,18 +191,22 @@ def rope_inv_freq(d: int, theta: float) -> np.ndarray:
     return np.power(np.float64(theta), -2.0 * i / d)
 
 
-def apply_rope(v: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+def apply_rope(v: np.ndarray, positions: np.ndarray, theta: float,
+               rotary_dim: Optional[int] = None) -> np.ndarray:
     """Rotate-half RoPE of v [B, L, heads, d] at integer positions [B, L]
     (tutorial section 4, step 3; GPT-NeoX issue "Scaling and RoPE": built at
-    the effective head_dim)."""
+    the effective head_dim, subject to rotary_pct).  ``rotary_dim`` r (None =
+    d) rotates the first r entries as a width-r RoPE and passes the rest
+    (reading 9)."""
     d = v.shape[-1]
-    half = d // 2
-    ang = positions.astype(np.float64)[..., None] * rope_inv_freq(d, theta)
+    r = d if rotary_dim is None else int(rotary_dim)
+    half = r // 2
+    ang = positions.astype(np.float64)[..., None] * rope_inv_freq(r, theta)
     cos = np.cos(ang).astype(v.dtype)[:, :, None, :]
     sin = np.sin(ang).astype(v.dtype)[:, :, None, :]
     x1 = v[..., :half]
-    x2 = v[..., half:]
-    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+    x2 = v[..., half:r]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin, v[..., r:]], axis=-1)
 
 
 def grouped_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -244,7 +254,7 @@ def merge_heads(o: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def qkv_normrope(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, positions,
-                 rope_theta, rms_eps, qk_norm=True, rope=True):
+                 rope_theta, rms_eps, qk_norm=True, rope=True, rotary_dim=None):
     """Steps 1 to 4 of the tutorial's ``Attention.__call__``: project, QK-norm,
     RoPE, transpose to head-major.  Returns q [B, Hq, L, d] and k, v
     [B, Hkv, L, d] (k after norm and RoPE, v raw)."""
@@ -254,8 +264,9 @@ def qkv_normrope(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, positions,
         q = rms_norm_heads(q, q_norm_w, rms_eps)
         k = rms_norm_heads(k, k_norm_w, rms_eps)
     if rope:
-        q = apply_rope(q, positions, rope_theta)
-        k = apply_rope(k, positions, rope_theta)
+        kw = {} if rotary_dim is None else {"rotary_dim": rotary_dim}
+        q = apply_rope(q, positions, rope_theta, **kw)
+        k = apply_rope(k, positions, rope_theta, **kw)
     return (q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3),
             v.transpose(0, 2, 1, 3))
 
@@ -264,7 +275,7 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
                   rope_theta: float, rms_eps: float, qk_norm: bool = True,
                   causal: bool = True, rope: bool = True,
                   k_cache=None, v_cache=None, cache_len=None,
-                  dtype=np.float64):
+                  rotary_dim: Optional[int] = None, dtype=np.float64):
     """The layer forward (tutorial section 4, steps 1 to 7).
 
     x [B, L, hidden]; w_qkv [(Hq+2Hkv)d, hidden]; w_o [hidden, Hq*d].
@@ -277,7 +288,7 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
     Returns (out [B, L, hidden], k_cache', v_cache') where the caches are the
     updated copies (None without a cache).  ``rope=False`` drops step 3 and
     exists only to reduce the layer to textbook multi-head attention in the
-    tests.
+    tests; ``rotary_dim`` is reading 9.
     """
     x = np.asarray(x, dtype=dtype)
     w_qkv = np.asarray(w_qkv, dtype=dtype)
@@ -290,8 +301,9 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
     else:
         start = np.asarray(cache_len, dtype=np.int64)
     positions = start[:, None] + np.arange(seq, dtype=np.int64)[None, :]
+    kw = {} if rotary_dim is None else {"rotary_dim": rotary_dim}
     q, k, v = qkv_normrope(res, x, w_qkv, qn, kn, positions, rope_theta,
-                           rms_eps, qk_norm=qk_norm, rope=rope)
+                           rms_eps, qk_norm=qk_norm, rope=rope, **kw)
     if k_cache is None:
         kk, vv = k, v
         kv_len = np.full(bsz, seq, dtype=np.int64)
@@ -312,7 +324,8 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
 
 def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
                        *, rope_theta: float, rms_eps: float,
-                       qk_norm: bool = True, dtype=np.float64):
+                       qk_norm: bool = True, rotary_dim: Optional[int] = None,
+                       dtype=np.float64):
     """Exact causal prefill output (no cache, positions 0..L-1) for chosen
     (b, t) rows only.
 
@@ -336,7 +349,8 @@ def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
         pos_all = np.arange(tmax + 1, dtype=np.int64)[None, :]
         if qk_norm:
             k = rms_norm_heads(k, np.asarray(k_norm_w, dtype=dtype), rms_eps)
-        k = apply_rope(k, pos_all, rope_theta)
+        kw = {} if rotary_dim is None else {"rotary_dim": rotary_dim}
+        k = apply_rope(k, pos_all, rope_theta, **kw)
         k = k.transpose(0, 2, 1, 3)
         v = v.transpose(0, 2, 1, 3)
         ts = np.array([t for _, t in items], dtype=np.int64)
@@ -345,7 +359,7 @@ def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
         q = q.reshape(1, len(ts), res.hq, res.d)
         if qk_norm:
             q = rms_norm_heads(q, np.asarray(q_norm_w, dtype=dtype), rms_eps)
-        q = apply_rope(q, ts[None, :], rope_theta).transpose(0, 2, 1, 3)
+        q = apply_rope(q, ts[None, :], rope_theta, **kw).transpose(0, 2, 1, 3)
         o = grouped_attention(q, k, v, ts[None, :],
                               np.array([tmax + 1]), res.scale, True)
         o_rows = project(merge_heads(o), np.asarray(w_o, dtype=dtype))[0]

@@ -339,6 +339,27 @@ def check_rope():
     assert max(dots) - min(dots) < 1e-10
 
 
+def check_partial_rope():
+    """Partial rotary (reading 9) against closed forms: with rotary_dim 2 the
+    single pair (0, 1) turns by angle p (theta**0); with rotary_dim 4 the
+    pairs (0, 2) and (1, 3) turn by p and p * theta**(-1/2); the entries past
+    rotary_dim are untouched, and rotary_dim = d is the full RoPE."""
+    rng = np.random.default_rng(11)
+    theta = 1e4
+    pos = np.array([[0, 1, 3, 1000]])
+    v = _rand(rng, 1, 4, 2, 8)
+    for r, pairs in ((2, [(0, 1, 1.0)]), (4, [(0, 2, 1.0), (1, 3, theta ** -0.5)])):
+        got = O.apply_rope(v, pos, theta, rotary_dim=r)
+        assert np.array_equal(got[..., r:], v[..., r:])
+        for i, j, f in pairs:
+            a = pos[0][:, None] * f  # [L, 1], one angle per position
+            c, s_ = np.cos(a), np.sin(a)
+            x1, x2 = v[0, :, :, i], v[0, :, :, j]
+            assert np.max(np.abs(got[0, :, :, i] - (x1 * c - x2 * s_))) < 1e-12
+            assert np.max(np.abs(got[0, :, :, j] - (x2 * c + x1 * s_))) < 1e-12
+    assert np.array_equal(O.apply_rope(v, pos, theta, rotary_dim=8), O.apply_rope(v, pos, theta))
+
+
 def check_position_shift_invariance():
     """Shifting every position by the same offset leaves scores, and so the
     attention output, unchanged (RoPE's relative-position property)."""
@@ -487,7 +508,7 @@ ALL_CHECKS = [
     check_geometries, check_resolve_errors, check_param_counts, check_macs,
     check_projection_bruteforce, check_attention_bruteforce,
     check_attention_vs_torch_sdpa, check_layer_mha_reduces_to_torch_mha,
-    check_layer_vs_torch_composition, check_rmsnorm, check_rope,
+    check_layer_vs_torch_composition, check_rmsnorm, check_rope, check_partial_rope,
     check_position_shift_invariance, check_causality,
     check_gqa_equals_repeated_kv, check_rank_ceiling, check_one_dim_head,
     check_sum_over_heads, check_prefill_equals_decode,

@@ -18,9 +18,9 @@ _orig = {name: getattr(O, name) for name in (
 
 
 def _k_norm_uses_q_weight(res, x, w_qkv, qn, kn, positions, theta, eps,
-                          qk_norm=True, rope=True):
+                          qk_norm=True, rope=True, rotary_dim=None):
     return _orig["qkv_normrope"](res, x, w_qkv, qn, qn, positions, theta, eps,
-                                 qk_norm=qk_norm, rope=rope)
+                                 qk_norm=qk_norm, rope=rope, rotary_dim=rotary_dim)
 
 
 def _attention_with(group_map=None, scale_fn=None, causal_shift=0,
@@ -50,23 +50,24 @@ def _attention_with(group_map=None, scale_fn=None, causal_shift=0,
     return attn
 
 
-def _rope_with(sign=1.0, interleaved=False, freq_factor=2.0):
-    def rope(v, positions, theta):
+def _rope_with(sign=1.0, interleaved=False, freq_factor=2.0, freq_over_head_dim=False):
+    def rope(v, positions, theta, rotary_dim=None):
         d = v.shape[-1]
-        half = d // 2
+        r = d if rotary_dim is None else rotary_dim
+        half = r // 2
         i = np.arange(half, dtype=np.float64)
         ang = positions.astype(np.float64)[..., None] * \
-            np.power(np.float64(theta), -freq_factor * i / d) * sign
+            np.power(np.float64(theta), -freq_factor * i / (d if freq_over_head_dim else r)) * sign
         cos = np.cos(ang)[:, :, None, :]
         sin = np.sin(ang)[:, :, None, :]
         if interleaved:
-            x1, x2 = v[..., 0::2], v[..., 1::2]
-            y = np.empty_like(v)
-            y[..., 0::2] = x1 * cos - x2 * sin
-            y[..., 1::2] = x2 * cos + x1 * sin
+            x1, x2 = v[..., 0:r:2], v[..., 1:r:2]
+            y = v.copy()
+            y[..., 0:r:2] = x1 * cos - x2 * sin
+            y[..., 1:r:2] = x2 * cos + x1 * sin
             return y
-        x1, x2 = v[..., :half], v[..., half:]
-        return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], -1)
+        x1, x2 = v[..., :half], v[..., half:r]
+        return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin, v[..., r:]], -1)
     return rope
 
 
@@ -110,6 +111,7 @@ MUTATIONS = {
     "rope_sign_flipped": ("apply_rope", _rope_with(sign=-1.0)),
     "rope_interleaved_pairs": ("apply_rope", _rope_with(interleaved=True)),
     "rope_freq_dropped_factor_2": ("apply_rope", _rope_with(freq_factor=1.0)),
+    "partial_rope_freq_over_head_dim": ("apply_rope", _rope_with(freq_over_head_dim=True)),
     "rmsnorm_eps_outside_sqrt": (
         "rms_norm_heads",
         lambda v, w, eps: v / (np.sqrt(np.mean(v * v, -1, keepdims=True)) + eps) * w),
