@@ -42,6 +42,7 @@ class Workload:
     # o_proj reduces over Hq*d >= 4096 values, where the bf16 rounding of
     # the attention output alone moves outputs by ~1e-2.
     o_split: bool = False
+    rotary_dim: Optional[int] = None  # partial rotary width; None = head_dim
 
     @property
     def d(self) -> int:

@@ -48,7 +48,8 @@ def cfg_of(w: GI.Workload, out_f32: bool = True, o_split=None):
     return T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
                        head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
                        qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=out_f32,
-                       o_split=w.o_split if o_split is None else o_split)
+                       o_split=w.o_split if o_split is None else o_split,
+                       rotary_dim=w.rotary_dim)
 
 
 def resolved(w: GI.Workload):
@@ -66,4 +67,4 @@ def oracle_layer(w: GI.Workload, h: dict, cache=None, cache_len=None, dtype=np.f
                            qk_norm=w.qk_norm, causal=w.causal,
                            k_cache=None if cache is None else cache["k_cache"],
                            v_cache=None if cache is None else cache["v_cache"],
-                           cache_len=cache_len, dtype=dtype)
+                           cache_len=cache_len, rotary_dim=w.rotary_dim, dtype=dtype)

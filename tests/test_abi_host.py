@@ -61,6 +61,9 @@ def test_resolve_explicit_and_quotient():
     # bf16 takes any even head_dim up to 256 (128 on the matrix-core path)
     for d in (64, 80, 256):
         assert T.gqa_resolve(cfg(head_dim=d))["head_dim"] == d
+    # rotary_dim 0 / None means the whole head
+    assert T.gqa_resolve(cfg())["rotary_dim"] == 128
+    assert T.gqa_resolve(cfg(rotary_dim=32))["rotary_dim"] == 32
 
 
 @pytest.mark.parametrize("kw,name", [
@@ -75,6 +78,8 @@ def test_resolve_explicit_and_quotient():
     # the hi | lo split reads W_o twice in 32-wide K stages: 3*88 % 32 != 0
     (dict(num_heads=3, num_kv_heads=3, head_dim=88, o_split=True), "GQA_ERR_UNSUPPORTED_SHAPE"),
     (dict(hidden_size=0), "GQA_ERR_INVALID_ARG"),
+    (dict(rotary_dim=63), "GQA_ERR_INVALID_ARG"),
+    (dict(rotary_dim=130), "GQA_ERR_INVALID_ARG"),
     (dict(rope_theta=0.0), "GQA_ERR_INVALID_ARG"),
     (dict(rms_eps=-1.0), "GQA_ERR_INVALID_ARG"),
 ])

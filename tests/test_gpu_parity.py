@@ -47,6 +47,13 @@ SMALL = {
                                                              hkv=4),
     "bf16_d64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=300, hq=8, hkv=4,
                                                               head_dim=64),
+    # partial rotary: 64 of 128 in the fused epilogue, 48 of 128 through the
+    # separate norm/RoPE pass, 32 of 64 on the fallback path, 64 of 128 decode
+    "rot64_of_128": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=170, rotary_dim=64),
+    "rot48_of_128": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=140, rotary_dim=48),
+    "rot32_of_64": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=90, hq=8, hkv=2, head_dim=64,
+                                                       rotary_dim=32),
+    "rot64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=500, rotary_dim=64),
 }
 
 

@@ -48,7 +48,7 @@ class _CConfig(ctypes.Structure):
                 ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("qk_norm", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_f32", ctypes.c_int32),
-                ("o_split", ctypes.c_int32)]
+                ("o_split", ctypes.c_int32), ("rotary_dim", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -66,13 +66,14 @@ class GQAConfig:
     dtype: str = "bf16"
     out_f32: bool = False   # o_proj output in fp32 (the accumulator) instead of dtype
     o_split: bool = False   # layer forward: attention output as a bf16 hi + lo pair
+    rotary_dim: Optional[int] = None  # partial rotary width; None = head_dim
 
     def c(self) -> _CConfig:
         return _CConfig(self.hidden_size, self.num_heads, self.num_kv_heads or 0,
                         self.head_dim or 0, float(self.rope_theta), float(self.rms_eps),
                         int(bool(self.qk_norm)), int(bool(self.causal)),
                         GQA_BF16 if self.dtype == "bf16" else GQA_F32, int(bool(self.out_f32)),
-                        int(bool(self.o_split)))
+                        int(bool(self.o_split)), int(self.rotary_dim or 0))
 
 
 _lib = None

@@ -49,15 +49,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args a) {
 }
 
 // One workgroup per (token, head of the fused projection); thread j < d/2
-// owns the RoPE pair (j, j + d/2).  T is the element type of the norm
-// weights and of q / the caches (float, or bf16 for the few-token bf16 path).
+// holds features j and j + d/2.  The normalised head goes through shared
+// memory so that any rotary width r works: output feature e < r/2 pairs with
+// e + r/2; features r .. d-1 pass through.  T is the element type of the
+// norm weights and of q / the caches (float, or bf16 for the bf16 path).
 template <typename T>
 __global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
   __shared__ float red[128];
+  __shared__ float xs[256];
   const int m = blockIdx.x;       // token
   const int head = blockIdx.y;    // 0 .. Hq + 2 Hkv - 1
   const int j = threadIdx.x;
-  const int d = a.d, half = d >> 1;
+  const int d = a.d, half = d >> 1, rh = a.rot >> 1;
   const int b = m / a.L, tok = m - b * a.L;
   const int n_qkv = (a.Hq + 2 * a.Hkv) * d;
   const float* y = a.y + (size_t)m * n_qkv + (size_t)head * d;
@@ -85,14 +88,23 @@ __global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
       }
     }
     if (act) {
-      const double ang = (double)pos * pow(a.theta, -2.0 * (double)j / (double)d);
+      xs[j] = x1;
+      xs[j + half] = x2;
+    }
+    __syncthreads();
+    // rotated value of feature e (the pair's angle uses its lower index)
+    auto rot_of = [&](int e) {
+      if (e >= a.rot) return xs[e];
+      const int i = e < rh ? e : e - rh;
+      const double ang = (double)pos * pow(a.theta, -2.0 * (double)i / (double)a.rot);
       double sd, cd;
       sincos(ang, &sd, &cd);
       const float c = (float)cd, s = (float)sd;
-      const float y1 = x1 * c - x2 * s;
-      const float y2 = x2 * c + x1 * s;
-      x1 = y1;
-      x2 = y2;
+      return e < rh ? xs[e] * c - xs[e + rh] * s : xs[e] * c + xs[e - rh] * s;
+    };
+    if (act) {
+      x1 = rot_of(j);
+      x2 = rot_of(j + half);
     }
   }
   if (!act) return;

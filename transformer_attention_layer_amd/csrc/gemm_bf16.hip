@@ -332,8 +332,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     }
 
   // One token block (32 tokens) at a time; within it, a lane handles four
-  // consecutive features i..i+3 of the first half together with their RoPE
-  // partners i+64..i+67, so only a few values are live at once.
+  // consecutive features i..i+3 together with their RoPE partners
+  // i+rot/2..i+rot/2+3, so only a few values are live at once.
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int row = 32 * t + l32;
@@ -362,37 +362,59 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         }
       continue;
     }
-    // rotate-half RoPE: feature i (< 64) pairs with i + 64 (block f + 2)
-    const float2* cs = a.rope + (size_t)(a.start_pos ? mm : tok) * 64;
+    // rotate-half RoPE over the first `rot` features: feature i < rot/2
+    // pairs with i + rot/2 (rot 128: block f with f + 2; rot 64: block 0
+    // with block 1, blocks 2 and 3 pass through)
+    const int half = a.rot >> 1;
+    const float2* cs = a.rope + (size_t)(a.start_pos ? mm : tok) * half;
+    auto rope_pair = [&](int f1, int f2, int j) {
+      const int i0 = 32 * f1 + 8 * j + 4 * hh;
+      // (cos, sin) of features i0 .. i0+3: two 16-byte loads
+      const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
+      const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
+      const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
+      const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+      const u32x2 w1 = wpk[f1][j], w2 = wpk[f2][j];
+      const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
+      const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
+      float y1[4], y2[4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int e = 0; e < 4; ++e) {
+        const float x1 = acc[f1][t][4 * j + e] * inv * g1[e];
+        const float x2 = acc[f2][t][4 * j + e] * inv * g2[e];
+        y1[e] = x1 * cc[e] - x2 * sn[e];
+        y2[e] = x2 * cc[e] + x1 * sn[e];
+      }
+      u32x2 o1, o2;
+      o1.x = pack_bf16x2(y1[0], y1[1]);
+      o1.y = pack_bf16x2(y1[2], y1[3]);
+      o2.x = pack_bf16x2(y2[0], y2[1]);
+      o2.y = pack_bf16x2(y2[2], y2[3]);
+      put8(row, i0, o1);
+      put8(row, i0 + half, o2);
+    };
+    auto norm_only = [&](int f, int j) {
+      const u32x2 w = wpk[f][j];
+      u32x2 o;
+      o.x = pack_bf16x2(acc[f][t][4 * j + 0] * inv * lo_bf16(w.x),
+                        acc[f][t][4 * j + 1] * inv * hi_bf16(w.x));
+      o.y = pack_bf16x2(acc[f][t][4 * j + 2] * inv * lo_bf16(w.y),
+                        acc[f][t][4 * j + 3] * inv * hi_bf16(w.y));
+      put8(row, 32 * f + 8 * j + 4 * hh, o);
+    };
+    if (a.rot == 128) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rope_pair(f, f + 2, j);
+    } else {  // rot == 64
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int i0 = 32 * f + 8 * j + 4 * hh;
-        // (cos, sin) of features i0 .. i0+3: two 16-byte loads
-        const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
-        const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
-        const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
-        const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-        const u32x2 w1 = wpk[f][j], w2 = wpk[f + 2][j];
-        const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
-        const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
-        float y1[4], y2[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x1 = acc[f][t][4 * j + e] * inv * g1[e];
-          const float x2 = acc[f + 2][t][4 * j + e] * inv * g2[e];
-          y1[e] = x1 * cc[e] - x2 * sn[e];
-          y2[e] = x2 * cc[e] + x1 * sn[e];
-        }
-        u32x2 o1, o2;
-        o1.x = pack_bf16x2(y1[0], y1[1]);
-        o1.y = pack_bf16x2(y1[2], y1[3]);
-        o2.x = pack_bf16x2(y2[0], y2[1]);
-        o2.y = pack_bf16x2(y2[2], y2[3]);
-        put8(row, i0, o1);
-        put8(row, i0 + 64, o2);
+        rope_pair(0, 1, j);
+        norm_only(2, j);
+        norm_only(3, j);
       }
+    }
   }
 
   // Store: lane l moves chunk l % 16 of row 4 i + l / 16.

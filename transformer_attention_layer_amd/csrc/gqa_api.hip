@@ -39,7 +39,9 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Shape {
   int H, Hq, Hkv, d, G, n_qkv;
   bool bf16;
-  bool mfma;     // bf16 with head_dim 128: the matrix-core attention and fused QKV epilogue
+  bool mfma;     // bf16 with head_dim 128: the matrix-core attention
+  int rot;       // rotary width
+  bool fused;    // mfma, and the rotary width (128 or 64) fits the fused QKV epilogue
   bool out_f32;  // o_proj output in fp32
   bool o_split;  // layer forward: attention output as a bf16 hi + lo pair
 };
@@ -68,6 +70,10 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
                 c.head_dim);
   if (c.dtype != GQA_F32 && c.dtype != GQA_BF16)
     return fail(GQA_ERR_UNSUPPORTED_DTYPE, "dtype %d is not GQA_F32 or GQA_BF16", c.dtype);
+  if (c.rotary_dim < 0 || c.rotary_dim > c.head_dim || c.rotary_dim % 2 != 0)
+    return fail(GQA_ERR_INVALID_ARG, "rotary_dim %d must be even and in [0, head_dim %d]",
+                c.rotary_dim, c.head_dim);
+  if (c.rotary_dim == 0) c.rotary_dim = c.head_dim;
   if (c.head_dim > 256)
     return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
                 "Unsupported head_dim %d: the kernels take even head_dim up to 256", c.head_dim);
@@ -106,6 +112,8 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->n_qkv = (int)n_qkv;
     sh->bf16 = c.dtype == GQA_BF16;
     sh->mfma = sh->bf16 && c.head_dim == 128;
+    sh->rot = c.rotary_dim;
+    sh->fused = sh->mfma && (c.rotary_dim == 128 || c.rotary_dim == 64);
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
     sh->o_split = c.o_split && c.dtype == GQA_BF16;
   }
@@ -140,8 +148,8 @@ bool use_skinny(const Shape& s, long long tokens) { return s.bf16 && tokens <= k
 
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
-  if (s.mfma && !use_skinny(s, (long long)T))
-    return align_up(T * (s.d / 2) * sizeof(float) * 2);  // rope table, T rows max
+  if (s.fused && !use_skinny(s, (long long)T))
+    return align_up(T * (s.rot / 2) * sizeof(float) * 2);  // rope table, T rows max
   return align_up(T * (size_t)s.n_qkv * sizeof(float));   // fp32 projection output
 }
 
@@ -180,11 +188,11 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
                    const void* w_qkv, const void* qn, const void* kn, const int32_t* start_pos,
                    void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st) {
   const int T = batch * q_len;
-  if (s.mfma && !use_skinny(s, T)) {
+  if (s.fused && !use_skinny(s, T)) {
     float2* table = reinterpret_cast<float2*>(ws);
     const int rows = start_pos ? T : q_len;
     gqa_status r = check_launch(
-        gqa::launch_rope_table(table, start_pos, rows, q_len, s.d / 2, (double)c.rope_theta, st),
+        gqa::launch_rope_table(table, start_pos, rows, q_len, s.rot / 2, (double)c.rope_theta, st),
         "rope table");
     if (r != GQA_OK) return r;
     gqa::GemmArgs g{};
@@ -205,6 +213,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     g.Hkv = s.Hkv;
     g.cap = cap;
     g.qk_norm = c.qk_norm;
+    g.rot = s.rot;
     g.eps = c.rms_eps;
     return check_launch(gqa::launch_gemm_qkv_bf16(g, st), "qkv projection");
   }
@@ -241,6 +250,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   n.Hq = s.Hq;
   n.Hkv = s.Hkv;
   n.d = s.d;
+  n.rot = s.rot;
   n.cap = cap;
   n.qk_norm = c.qk_norm;
   n.bf16 = s.bf16;

@@ -25,9 +25,10 @@ struct GemmArgs {
   __bf16* v_cache;
   const __bf16* q_norm_w;
   const __bf16* k_norm_w;
-  const float2* rope;     // [rows, 64] (cos, sin); rows = T if start_pos else L
+  const float2* rope;     // [rows, rot / 2] (cos, sin); rows = T if start_pos else L
   const int* start_pos;   // [B] or null
   int L, Hq, Hkv, cap, qk_norm;
+  int rot;                // rotary width: 128 (full) or 64 (first half of each head)
   float eps;
 };
 
@@ -71,7 +72,7 @@ struct NormRopeArgs {
   const void* q_norm_w; const void* k_norm_w;
   const int* start_pos;
   void* q; void* k_cache; void* v_cache;
-  int B, L, Hq, Hkv, d, cap, qk_norm, bf16;
+  int B, L, Hq, Hkv, d, rot, cap, qk_norm, bf16;
   float eps; double theta;
 };
 hipError_t launch_normrope(const NormRopeArgs& args, hipStream_t stream);
