@@ -60,8 +60,15 @@ def kv_bytes_of(w):
 
 KERNEL_OF_PART = {"qkv": "qkv_gemm", "attn": "attn_prefill", "oproj": "oproj_gemm",
                   "attn_decode": "attn_decode"}
+# bf16 head sizes other than 128: projection GEMM + separate norm/RoPE pass,
+# vector-unit attention
+KERNEL_OF_PART_FALLBACK = {"qkv": "qkv_gemm_normrope", "attn": "attn_vec", "oproj": "oproj_gemm"}
 SOURCES_OF_KERNEL = {"qkv_gemm": "gemm_bf16.hip", "oproj_gemm": "gemm_bf16.hip",
-                     "attn_prefill": "attn_bf16.hip", "attn_decode": "attn_bf16.hip"}
+                     "attn_prefill": "attn_bf16.hip", "attn_decode": "attn_bf16.hip",
+                     "qkv_gemm_normrope": "gemm_bf16.hip", "attn_vec": "f32_kernels.hip"}
+# MI355X fp32 vector peak as published (it counts packed-fp32 issue; plain
+# FMAs, which these kernels use, reach half of it)
+PEAK_F32_VALU_TFLOPS = 157.3
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -285,9 +292,13 @@ def main():
                        "ms_per_step": round(ms, 4), "frac_of_peak": round(value / peak, 4)})
         result["config"] = cfgd
         result["kernels_ms"] = {k: round(v, 4) for k, v in part_ms.items()}
-        kern = KERNEL_OF_PART[dom]
-        result["roofline"] = {"bound": "mfma", "kernel": kern, "achieved": round(ach, 2),
-                              "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+        fallback = w.dtype == "bf16" and w.d != 128
+        kern = (KERNEL_OF_PART_FALLBACK if fallback else KERNEL_OF_PART)[dom]
+        bound, kpeak = "mfma", peak
+        if kern == "attn_vec":  # fp32 FMAs on the vector units
+            bound, kpeak = "alu", PEAK_F32_VALU_TFLOPS
+        result["roofline"] = {"bound": bound, "kernel": kern, "achieved": round(ach, 2),
+                              "peak": kpeak, "unit": "TFLOP/s", "frac": round(ach / kpeak, 4),
                               "traffic": stored_traffic(w.name, kern),
                               "algorithmic_flop": fl[dom], "avg_launch_ms": round(part_ms[dom], 5)}
     else:

@@ -74,6 +74,11 @@ WORKLOADS = {
     "decode_h2560_mqa": Workload("decode_h2560_mqa", 64, 1, 2560, 32, 1, 128,
                                  True, 1e6, 1e-6, "bf16", 4, cache_len=32768,
                                  o_split=True),
+    # The explicit head_dim the pages cite for Gemma 3 (hidden 640, four
+    # query heads, head_dim 256 rather than 160); one KV head.  Head sizes
+    # other than 128 run the fallback path.
+    "gemma_h640_d256": Workload("gemma_h640_d256", 4, 2048, 640, 4, 1, 256, True,
+                                1e6, 1e-6, "bf16", 5),
 }
 
 

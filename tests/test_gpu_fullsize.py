@@ -35,6 +35,7 @@ PREFILL_ROWS = {
     "prefill_h1024": [(0, 0), (0, 1), (0, 63), (0, 64), (3, 1000), (5, 2046), (7, 2047)],
     "quotient_h4096": [(0, 0), (0, 129), (1, 4095), (2, 77), (3, 8191)],
     "wide_h5120": [(0, 0), (0, 5000), (1, 1), (1, 16383)],
+    "gemma_h640_d256": [(0, 0), (1, 777), (2, 64), (3, 2047)],
 }
 
 
@@ -56,7 +57,7 @@ def test_prefill_full_size(name):
     del out
     ref = O.layer_forward_rows(resolved(w), h["x"], h["w_qkv"], h["q_norm_w"], h["k_norm_w"],
                                h["w_o"], rows, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
-                               qk_norm=w.qk_norm, dtype=np.float32)
+                               qk_norm=w.qk_norm, rotary_dim=w.rotary_dim, dtype=np.float32)
     assert_close(got, ref, w.dtype, "sampled rows")
 
 
