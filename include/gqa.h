@@ -28,10 +28,10 @@
  *   thread).  A launch failure returns GQA_ERR_HIP.
  * - batch == 0 or q_len == 0 is a no-op returning GQA_OK.
  * - Supported head_dim: any even value from 2 to 256; others return
- *   GQA_ERR_UNSUPPORTED_HEAD_DIM.  With GQA_BF16, head_dim 128 runs the
- *   matrix-core attention and the fused QKV epilogue; other sizes run the
- *   same projections with a separate norm/RoPE pass and a vector-unit
- *   attention (correct, much slower).  bf16 also needs num_heads*head_dim and
+ *   GQA_ERR_UNSUPPORTED_HEAD_DIM.  With GQA_BF16, head_dim 64, 128 and 256
+ *   run the matrix-core attention; 128 also fuses QK-norm and RoPE into the
+ *   QKV GEMM (other sizes take a separate norm/RoPE pass); any other size
+ *   runs a vector-unit attention (correct, much slower).  bf16 also needs num_heads*head_dim and
  *   (num_heads + 2*num_kv_heads)*head_dim to be multiples of 8, and o_split
  *   needs num_heads*head_dim to be a multiple of 32 (GQA_ERR_UNSUPPORTED_SHAPE).
  */

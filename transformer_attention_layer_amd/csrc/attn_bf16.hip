@@ -1,4 +1,5 @@
-// Grouped causal attention on the bf16 matrix cores of gfx950, head_dim 128.
+// Grouped causal attention on the bf16 matrix cores of gfx950, head_dim 64,
+// 128 or 256 (the template parameter KD).
 //
 // Computes softmax(q k^T * d^-0.5 + mask) v with query head h reading KV
 // head h / (Hq/Hkv) (tutorial "Multi-Head and Grouped-Query Attention (Full
@@ -14,8 +15,8 @@
 // lane l holds one query (l % 32) and half of each 32-key block; the row max
 // and sum need a single exchange with lane l ^ 32, and the rescale factor is
 // one scalar per lane.  O^T = V^T P^T then takes P^T straight from the score
-// registers; V^T is built in LDS while the tile is stored, with the keys of
-// each 16-key group in the order the score registers hold them.
+// registers; the V^T operand is read from V (stored as in memory) with
+// transposing LDS reads, keys in the order the score registers hold them.
 //
 // Softmax bookkeeping per key tile: the tile's row max is taken on the raw
 // scores (the scale is positive), exp2(s * scale*log2(e) - m) is one FMA and
@@ -40,44 +41,71 @@
 namespace gqa {
 namespace {
 
-constexpr int kD = 128;
 constexpr float kLazyRescale = 8.0f;  // log2 of the growth allowed before rescaling
 
-// K tile: rows = keys, 256 B = 16 chunks each; chunk c of row r at slot
-// c ^ (r & 15).
-__device__ __forceinline__ int kslot(int row, int chunk) { return (row << 4) + (chunk ^ (row & 15)); }
+// LDS pointers are kept in the LDS address space from the arrays on, so no
+// generic-to-LDS conversion (and its null check) is left for the compiler.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const char lds_cchar;
 
-// V tile: rows = keys, 256 B = 16 chunks each, as in memory.  The PV
-// product reads it transposed with ds_read_b64_tr_b16 (below); one such read
-// by 32 lanes touches 4 consecutive rows x 64 bytes, so chunk c of row r
-// sits at slot c ^ (4 (r & 3)): the 4 rows land on disjoint bank ranges.
-__device__ __forceinline__ int vslot(int row, int chunk) {
-  return (row << 4) + (chunk ^ ((row & 3) << 2));
-}
+// Geometry of a K or V tile row for head size KD: KD bf16 = NCH 16-byte
+// chunks; one 64-lane load instruction (64 x 16 B) fills RPI rows.
+template <int KD>
+struct Geo {
+  static_assert(KD == 64 || KD == 128 || KD == 256, "head_dim 64, 128 or 256");
+  static constexpr int NCH = KD / 8;
+  static constexpr int RB = KD * 2;     // bytes per row
+  static constexpr int RPI = 64 / NCH;  // rows per load instruction
+  static constexpr int NB = KD / 32;    // 32-feature blocks of O^T
+  static constexpr int NC = KD / 16;    // 16-feature steps of the QK product
+
+  // K tile: a fragment read has 16 lanes on 16 consecutive rows at one chunk;
+  // gfx950's LDS serves them over 64 banks (256 B).  Chunk c of row r sits at
+  // slot c ^ kswz(r): 128-byte rows pair up in a bank window, so the 8 even
+  // and the 8 odd rows each take 8 slots; 256- and 512-byte rows start on the
+  // same bank, so 16 rows take 16 slots (the XOR keeps a 512-byte row's
+  // chunks in their 256-byte half).
+  __device__ static __forceinline__ int kswz(int row) {
+    return KD == 64 ? ((row >> 1) & 7) : (row & 15);
+  }
+  // V tile: one transposing read by 32 lanes touches 4 consecutive rows x 4
+  // chunks; chunk c of row r sits at slot c ^ vswz(r) so that the 16 chunks
+  // land on 16 distinct bank groups (rows r and r + 2 share a bank window
+  // when rows are 128 bytes).
+  __device__ static __forceinline__ int vswz(int row) {
+    return KD == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
+  }
+  __device__ static __forceinline__ int kslot(int row, int chunk) {
+    return row * NCH + (chunk ^ kswz(row));
+  }
+  __device__ static __forceinline__ int vslot(int row, int chunk) {
+    return row * NCH + (chunk ^ vswz(row));
+  }
+};
 
 // K or V tile straight into LDS (buffer_load ... lds): one instruction fills
-// 64 consecutive slots = 4 key rows; lane i writes slot i, so it loads the
+// 64 consecutive slots = RPI key rows; lane i writes slot i, so it loads the
 // chunk that the tile's swizzle puts there.  Keys past the descriptor's
-// range read as 0.  A wave issues JW = TK / 4 / (NT / 64) instructions per
-// tile and per operand; the per-lane byte offsets within a tile are fixed.
-// Each tile gets descriptors based at its first key, so that the hardware
-// range check (which covers the per-lane offset only, not a scalar offset)
-// still zero-fills the keys past the end.
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
-__device__ __forceinline__ int vswz(int row) { return (row & 3) << 2; }
-
-template <int NT, int TK>
+// range read as 0.  A wave issues JW instructions per tile and per operand;
+// the per-lane byte offsets within a tile are fixed.  Each tile gets
+// descriptors based at its first key, so that the hardware range check
+// (which covers the per-lane offset only, not a scalar offset) still
+// zero-fills the keys past the end.
+template <int KD, int NT, int TK>
 struct TileLoads {
-  static constexpr int JW = TK / 4 / (NT / 64);
+  using G = Geo<KD>;
+  static constexpr int JW = TK / G::RPI / (NT / 64);
+  static_assert(JW >= 1 && JW * G::RPI * (NT / 64) == TK, "tile rows split evenly over waves");
   unsigned ko[JW], vo[JW];  // per-lane byte offsets of instruction j
   int slot0;                // first LDS slot of this wave's rows
 
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
-      const int row = (wave * JW + j) * 4 + (lane >> 4);
-      ko[j] = (unsigned)(row * (kD * 2) + (((lane & 15) ^ kswz(row)) << 4));
-      vo[j] = (unsigned)(row * (kD * 2) + (((lane & 15) ^ vswz(row)) << 4));
+      const int row = (wave * JW + j) * G::RPI + lane / G::NCH;
+      const int slot = lane % G::NCH;
+      ko[j] = (unsigned)(row * G::RB + ((slot ^ G::kswz(row)) << 4));
+      vo[j] = (unsigned)(row * G::RB + ((slot ^ G::vswz(row)) << 4));
     }
     slot0 = wave * JW * 64;
   }
@@ -85,30 +113,28 @@ struct TileLoads {
 
 // The loads of one tile into one buffer; rk / rv start at the tile's first
 // key and end at the last valid key.
-template <int NT, int TK>
+template <int KD, int NT, int TK>
 struct TileDst {
-  const TileLoads<NT, TK>* plan;
+  const TileLoads<KD, NT, TK>* plan;
   __amdgpu_buffer_rsrc_t rk, rv;
-  u32x4* sk;
-  u32x4* sv;
+  lds_u32x4* sk;
+  lds_u32x4* sv;
   bool live;  // the tile exists
   __device__ __forceinline__ void k(int j) const {
     if (live)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(sk + plan->slot0 + 64 * j), 16, plan->ko[j],
-          0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, sk + plan->slot0 + 64 * j, 16, plan->ko[j], 0, 0,
+                                               0);
   }
   __device__ __forceinline__ void v(int j) const {
     if (live)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(sv + plan->slot0 + 64 * j), 16, plan->vo[j],
-          0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, sv + plan->slot0 + 64 * j, 16, plan->vo[j], 0, 0,
+                                               0);
   }
   __device__ __forceinline__ void all() const {
 #pragma unroll
-    for (int j = 0; j < TileLoads<NT, TK>::JW; ++j) k(j);
+    for (int j = 0; j < TileLoads<KD, NT, TK>::JW; ++j) k(j);
 #pragma unroll
-    for (int j = 0; j < TileLoads<NT, TK>::JW; ++j) v(j);
+    for (int j = 0; j < TileLoads<KD, NT, TK>::JW; ++j) v(j);
   }
 };
 
@@ -118,7 +144,7 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 // lane i receives element i % 4 of the 8 bytes that lane 4e + i / 4 of the
 // group points at, as its element e (a 16 x 4 block of 16-bit values comes
 // back transposed).
-GQA_DEV u32x2 lds_read_tr16(const void* p) {
+GQA_DEV u32x2 lds_read_tr16(lds_cchar* p) {
   const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) shortx4*)(p));
   return __builtin_bit_cast(u32x2, v);
@@ -126,9 +152,10 @@ GQA_DEV u32x2 lds_read_tr16(const void* p) {
 
 // Per-lane LDS offsets of the MFMA fragments; the same for every tile and
 // buffer.
+template <int KD>
 struct LaneOffsets {
-  int k[8];  // K fragment of d-chunk c (16-byte slots): key row l32
-  int v[4];  // V^T fragment of feature block d (bytes), first read of key group 0
+  int k[Geo<KD>::NC];  // K fragment of feature step c (16-byte slots): key row l32
+  int v[Geo<KD>::NB];  // V^T fragment of feature block d (bytes), first read of key group 0
 };
 
 // V^T fragment (A operand of O^T = V^T P^T) for 32 features x 16 keys: lane
@@ -138,31 +165,35 @@ struct LaneOffsets {
 // points at row (key) 4 (G / 2) + j / 4, features 16 (G % 2) + 4 (j % 4)
 // + 0..3, hands lane i features 16 (G % 2) + i of the 4 keys 4 (G / 2) + e;
 // the second read is the same, 8 keys (rows) further on.  The swizzle term
-// of those rows is 4 (j / 4) for every key group, so only the feature block
-// changes the lane offset.
-__device__ __forceinline__ void lane_offsets(LaneOffsets& o, int lane) {
+// of those rows depends on the row modulo 4, the same for every key group,
+// so only the feature block changes the lane offset.
+template <int KD>
+__device__ __forceinline__ void lane_offsets(LaneOffsets<KD>& o, int lane) {
+  using G = Geo<KD>;
   const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) o.k[c] = kslot(l32, 2 * c + hh);
-  const int G = lane >> 4, j = lane & 15;
-  const int row = 4 * (G >> 1) + (j >> 2);
+  for (int c = 0; c < G::NC; ++c) o.k[c] = G::kslot(l32, 2 * c + hh);
+  const int Gq = lane >> 4, j = lane & 15;
+  const int row = 4 * (Gq >> 1) + (j >> 2);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int feat = 32 * d + 16 * (G & 1) + 4 * (j & 3);
-    o.v[d] = vslot(row, feat >> 3) * 16 + (feat & 7) * 2;
+  for (int d = 0; d < G::NB; ++d) {
+    const int feat = 32 * d + 16 * (Gq & 1) + 4 * (j & 3);
+    o.v[d] = G::vslot(row, feat >> 3) * 16 + (feat & 7) * 2;
   }
 }
 
 // Running state of one wave: 32 query rows, lane = row (l % 32).
+template <int KD>
 struct RowState {
-  floatx16 o[4];   // O^T: value feature 32*db + 8*(r/4) + 4*(l/32) + r%4
-  float m;         // running max (log2 units, scaled scores)
-  float l;         // running sum, this lane-half's keys only
+  floatx16 o[Geo<KD>::NB];  // O^T: value feature 32*db + 8*(r/4) + 4*(l/32) + r%4
+  float m;                  // running max (log2 units, scaled scores)
+  float l;                  // running sum, this lane-half's keys only
 };
 
-__device__ __forceinline__ void init_state(RowState& st) {
+template <int KD>
+__device__ __forceinline__ void init_state(RowState<KD>& st) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < Geo<KD>::NB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o[d][r] = 0.f;
   st.m = -INFINITY;
@@ -178,24 +209,25 @@ __device__ __forceinline__ void init_state(RowState& st) {
 // LDS reads are issued a whole phase ahead of their MFMAs: all K fragments of
 // the tile before the QK product, all V^T fragments (into the same registers)
 // while the QK MFMAs drain and the softmax runs.
-template <int TK, int JW, typename Loads>
-__device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], const u32x4* sk,
-                                            const u32x4* sv, const LaneOffsets& lo, int key0,
-                                            int kend_row, bool masked, float c_log2, int hh,
-                                            const Loads& loads) {
+template <int KD, int TK, int JW, typename Loads>
+__device__ __forceinline__ void attend_tile(RowState<KD>& st, const u32x4 (&qf)[Geo<KD>::NC],
+                                            const lds_u32x4* sk, const lds_u32x4* sv,
+                                            const LaneOffsets<KD>& lo, int key0, int kend_row,
+                                            bool masked, float c_log2, int hh, const Loads& loads) {
+  using G = Geo<KD>;
   constexpr int KB = TK / 32;
-  constexpr int NF = KB * 8;  // K fragments per tile = V^T fragments per tile
-  static_assert(NF == TK / 16 * 4, "as many V^T as K fragments");
+  constexpr int NF = KB * G::NC;  // K fragments per tile = V^T fragments per tile
+  static_assert(NF == TK / 16 * G::NB, "as many V^T as K fragments");
   constexpr int kPer = (2 * JW + NF - 1) / NF;  // loads per leading QK MFMA
   u32x4 fr[NF];
 #pragma unroll
-  for (int m = 0; m < NF; ++m) fr[m] = sk[(m >> 3) * 512 + lo.k[m & 7]];
+  for (int m = 0; m < NF; ++m) fr[m] = sk[(m / G::NC) * 32 * G::NCH + lo.k[m % G::NC]];
   __builtin_amdgcn_sched_barrier(0);
   floatx16 s[KB];
   // the KB accumulation chains are interleaved
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
-    const int kb = i % KB, c = i / KB, m = kb * 8 + c;
+    const int kb = i % KB, c = i / KB, m = kb * G::NC + c;
     const floatx16 z = {};
     s[kb] = mfma32x32x16(fr[m], qf[c], c == 0 ? z : s[kb]);
     if (i * kPer < 2 * JW) {
@@ -214,12 +246,12 @@ __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], 
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int g = 0; g < TK / 16; ++g) {
-    const char* vg = reinterpret_cast<const char*>(sv) + g * 16 * (kD * 2);
+    lds_cchar* vg = reinterpret_cast<lds_cchar*>(sv) + g * 16 * G::RB;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < G::NB; ++d) {
       const u32x2 k0 = lds_read_tr16(vg + lo.v[d]);
-      const u32x2 k1 = lds_read_tr16(vg + lo.v[d] + 8 * (kD * 2));
-      fr[g * 4 + d] = u32x4{k0.x, k0.y, k1.x, k1.y};
+      const u32x2 k1 = lds_read_tr16(vg + lo.v[d] + 8 * G::RB);
+      fr[g * G::NB + d] = u32x4{k0.x, k0.y, k1.x, k1.y};
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -243,7 +275,7 @@ __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], 
     const float mn = fmaxf(st.m, mt);
     const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(st.m - mn);
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < G::NB; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[d][r] *= alpha;
     st.l *= alpha;
@@ -267,7 +299,7 @@ __device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[8], 
     st.l = sum_bf16x2(pf.z, st.l);
     st.l = sum_bf16x2(pf.w, st.l);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st.o[d] = mfma32x32x16(fr[g * 4 + d], pf, st.o[d]);
+    for (int d = 0; d < G::NB; ++d) st.o[d] = mfma32x32x16(fr[g * G::NB + d], pf, st.o[d]);
   }
 }
 
@@ -276,9 +308,11 @@ __device__ __forceinline__ int kv_len_of(const AttnArgs& a, int b) {
   return n < 0 ? 0 : (n > a.cap ? a.cap : n);
 }
 
-__device__ __forceinline__ void load_q(u32x4 (&qf)[8], const bf16* qrow, bool valid, int hh) {
+template <int KD>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[Geo<KD>::NC], const bf16* qrow, bool valid,
+                                       int hh) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < Geo<KD>::NC; ++c) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (valid) v = ld16(qrow + 16 * c + 8 * hh);
     qf[c] = v;
@@ -300,18 +334,28 @@ __device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)
   }
 }
 
-constexpr int kPrefillTK = 64;
-constexpr int kPrefillNT = 256;
+// Prefill tile sizes: 64 keys (32 for head_dim 256, whose fragments would
+// not fit the registers of two waves per SIMD otherwise).
+template <int KD>
+struct PrefillCfg {
+  static constexpr int TK = KD == 256 ? 32 : 64;
+  static constexpr int NT = 256;
+  static constexpr int MIN_BLOCKS = KD == 256 ? 1 : 2;
+};
 
-__global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a) {
-  constexpr int TK = kPrefillTK, NT = kPrefillNT;
+template <int KD>
+__global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) void attn_prefill_kernel(
+    AttnArgs a) {
+  using G = Geo<KD>;
+  constexpr int TK = PrefillCfg<KD>::TK, NT = PrefillCfg<KD>::NT;
+  using Plan = TileLoads<KD, NT, TK>;
   // Separate arrays per buffer: the compiler then knows that the loads into
   // one buffer cannot touch the other, and does not make reads of the
   // current tile wait for the loads of the next.
-  __shared__ u32x4 sk0[TK * 16], sk1[TK * 16];
-  __shared__ u32x4 sv0[kD * TK / 8], sv1[kD * TK / 8];
-  u32x4* const sk[2] = {sk0, sk1};
-  u32x4* const sv[2] = {sv0, sv1};
+  __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
+  __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
+  lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -340,23 +384,23 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   const bool row_valid = tq < a.Lq;
   const int kend_row = row_valid ? (a.causal ? min(kvl, off + tq + 1) : kvl) : 0;
 
-  u32x4 qf[8];
-  load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + (row_valid ? tq : 0)) * kD, row_valid, hh);
+  u32x4 qf[G::NC];
+  load_q<KD>(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + (row_valid ? tq : 0)) * KD, row_valid, hh);
 
-  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * KD;
   const bf16* kb = a.k + kv_base;
   const bf16* vb = a.v + kv_base;
   // descriptors of the tile starting at key k0 (keys k0 .. kvl - 1 valid)
-  auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * kD, (long long)(kvl - k0) * kD * 2); };
-  auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * kD, (long long)(kvl - k0) * kD * 2); };
-  LaneOffsets lo;
-  lane_offsets(lo, lane);
+  auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * KD, (long long)(kvl - k0) * G::RB); };
+  auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * KD, (long long)(kvl - k0) * G::RB); };
+  LaneOffsets<KD> lo;
+  lane_offsets<KD>(lo, lane);
 
-  RowState st;
-  init_state(st);
-  TileLoads<NT, TK> plan;
+  RowState<KD> st;
+  init_state<KD>(st);
+  Plan plan;
   plan.init(wave, lane);
-  const TileDst<NT, TK> first{&plan, rk_at(0), rv_at(0), sk[0], sv[0], n_tiles > 0};
+  const TileDst<KD, NT, TK> first{&plan, rk_at(0), rv_at(0), sk[0], sv[0], n_tiles > 0};
   first.all();
   __syncthreads();
   // two tiles per trip, so each buffer's LDS addresses are constants
@@ -364,13 +408,13 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
     constexpr int B = decltype(bufc)::value;
     // the next tile goes to the other buffer, last read before the barrier
     // that ended the previous trip
-    const TileDst<NT, TK> next{&plan, rk_at((it + 1) * TK), rv_at((it + 1) * TK), sk[B ^ 1],
-                               sv[B ^ 1], it + 1 < n_tiles};
+    const TileDst<KD, NT, TK> next{&plan, rk_at((it + 1) * TK), rv_at((it + 1) * TK), sk[B ^ 1],
+                                   sv[B ^ 1], it + 1 < n_tiles};
     const int key0 = it * TK;
     if (key0 < key_end_w) {
       const bool masked = key0 + TK > kmin_w;
-      attend_tile<TK, TileLoads<NT, TK>::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked,
-                                             a.scale_log2, hh, next);
+      attend_tile<KD, TK, Plan::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked,
+                                    a.scale_log2, hh, next);
     } else {
       next.all();  // the other waves still need this wave's share
     }
@@ -384,10 +428,10 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
   const float lt = sum_xor32(st.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (!row_valid) return;
-  const size_t width = (size_t)a.Hq * kD;
-  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * kD;
+  const size_t width = (size_t)a.Hq * KD;
+  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < G::NB; ++d)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float v[4];
@@ -400,15 +444,15 @@ __global__ __launch_bounds__(kPrefillNT, 2) void attn_prefill_kernel(AttnArgs a)
 constexpr int kDecodeTK = 32;
 constexpr int kDecodeNT = 64;
 
+template <int KD>
 __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
+  using G = Geo<KD>;
   constexpr int TK = kDecodeTK, NT = kDecodeNT;
-  // Separate arrays per buffer: the compiler then knows that the loads into
-  // one buffer cannot touch the other, and does not make reads of the
-  // current tile wait for the loads of the next.
-  __shared__ u32x4 sk0[TK * 16], sk1[TK * 16];
-  __shared__ u32x4 sv0[kD * TK / 8], sv1[kD * TK / 8];
-  u32x4* const sk[2] = {sk0, sk1};
-  u32x4* const sv[2] = {sv0, sv1};
+  using Plan = TileLoads<KD, NT, TK>;
+  __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
+  __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
+  lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -428,33 +472,33 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   const int kend_row = row_valid ? min(ke, a.causal ? min(kvl, off + tq + 1) : kvl) : 0;
   const int kmin = min(ke, a.causal ? min(kvl, off + 1) : kvl);
 
-  u32x4 qf[8];
-  load_q(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + tq) * kD, row_valid, hh);
+  u32x4 qf[G::NC];
+  load_q<KD>(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + tq) * KD, row_valid, hh);
 
-  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * kD;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * KD;
   const bf16* kb = a.k + kv_base;
   const bf16* vb = a.v + kv_base;
   // descriptors of the tile starting at key k0 (keys k0 .. ke - 1 valid)
-  auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * kD, (long long)(ke - k0) * kD * 2); };
-  auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * kD, (long long)(ke - k0) * kD * 2); };
-  LaneOffsets lo;
-  lane_offsets(lo, lane);
+  auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * KD, (long long)(ke - k0) * G::RB); };
+  auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * KD, (long long)(ke - k0) * G::RB); };
+  LaneOffsets<KD> lo;
+  lane_offsets<KD>(lo, lane);
 
-  RowState st;
-  init_state(st);
-  TileLoads<NT, TK> plan;
+  RowState<KD> st;
+  init_state<KD>(st);
+  Plan plan;
   plan.init(0, lane);
-  const TileDst<NT, TK> first{&plan, rk_at(ks), rv_at(ks), sk[0], sv[0], n_tiles > 0};
+  const TileDst<KD, NT, TK> first{&plan, rk_at(ks), rv_at(ks), sk[0], sv[0], n_tiles > 0};
   first.all();
   __syncthreads();
   auto step = [&](auto bufc, int it) {
     constexpr int B = decltype(bufc)::value;
     const int key0 = ks + it * TK;
-    const TileDst<NT, TK> next{&plan, rk_at(key0 + TK), rv_at(key0 + TK), sk[B ^ 1], sv[B ^ 1],
-                               it + 1 < n_tiles};
+    const TileDst<KD, NT, TK> next{&plan, rk_at(key0 + TK), rv_at(key0 + TK), sk[B ^ 1],
+                                   sv[B ^ 1], it + 1 < n_tiles};
     const bool masked = key0 + TK > kmin;
-    attend_tile<TK, TileLoads<NT, TK>::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked,
-                                           a.scale_log2, hh, next);
+    attend_tile<KD, TK, Plan::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2,
+                                  hh, next);
     __syncthreads();
   };
   for (int it = 0; it < n_tiles; it += 2) {
@@ -466,9 +510,9 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   if (!row_valid) return;  // only the group's real rows are merged
   const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * 32 + l32;
   if (hh == 0) a.part_ml[pidx] = make_float2(st.m, lt);
-  float* po = a.part_o + pidx * kD;
+  float* po = a.part_o + pidx * KD;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < G::NB; ++d)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       floatx4 w = {st.o[d][4 * j + 0], st.o[d][4 * j + 1], st.o[d][4 * j + 2], st.o[d][4 * j + 3]};
@@ -476,9 +520,12 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
     }
 }
 
-// Merge the per-split partials of one (sequence, KV head, row) with their
-// log-sum-exp weights.
+// Merge of the decode splits: one workgroup per (query row, KV head,
+// sequence); lane s first holds split s for the maxima and sums, then lane
+// e accumulates features e, e + 64, ... of every split's partial output.
+template <int KD>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  constexpr int FPL = (KD + 63) / 64;  // features per lane
   __shared__ float wsh[64];
   const int lane = threadIdx.x;
   const int row = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -486,14 +533,16 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const int tq = row - head_local * a.Lq;
   const int hq = kvh * a.G + head_local;
   const size_t base = (((size_t)b * a.Hkv + kvh) * a.n_splits) * 32 + row;
-  // split maxima and sums: lane s holds split s (then s + 64, ...)
   float mmax = -INFINITY;
   for (int s = lane; s < a.n_splits; s += 64) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
 #pragma unroll
   for (int x = 32; x > 0; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x, 64));
   const float muse = mmax == -INFINITY ? 0.f : mmax;
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  const float* po = a.part_o + base * kD + 2 * lane;
+  float lsum = 0.f;
+  float o[FPL];
+#pragma unroll
+  for (int f = 0; f < FPL; ++f) o[f] = 0.f;
+  const float* po = a.part_o + base * KD;
   for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
     const int s = s0 + lane;
     float w = 0.f;
@@ -506,54 +555,68 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
     wsh[lane] = w;
     __syncthreads();
     const int n = min(64, a.n_splits - s0);
-    // lane holds features 2 lane, 2 lane + 1 of every split row
-    int i = 0;
-    for (; i + 4 <= n; i += 4) {
-      float2 v[4];
+    for (int i = 0; i < n; ++i) {
+      const float wi = wsh[i];
+      const float* pr = po + (size_t)(s0 + i) * 32 * KD;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        v[u] = *reinterpret_cast<const float2*>(po + (size_t)(s0 + i + u) * 32 * kD);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        o0 += wsh[i + u] * v[u].x;
-        o1 += wsh[i + u] * v[u].y;
+      for (int f = 0; f < FPL; ++f) {
+        const int e = lane + 64 * f;
+        if (e < KD) o[f] += wi * pr[e];
       }
-    }
-    for (; i < n; ++i) {
-      const float2 v = *reinterpret_cast<const float2*>(po + (size_t)(s0 + i) * 32 * kD);
-      o0 += wsh[i] * v.x;
-      o1 += wsh[i] * v.y;
     }
   }
 #pragma unroll
   for (int x = 32; x > 0; x >>= 1) lsum += __shfl_xor(lsum, x, 64);
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  const size_t width = (size_t)a.Hq * kD;
-  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * kD;
-  const float h0 = o0 * inv, h1 = o1 * inv;
-  const unsigned int hi = pack_bf16x2(h0, h1);
-  *reinterpret_cast<unsigned int*>(orow + 2 * lane) = hi;
-  if (a.o_split)
-    *reinterpret_cast<unsigned int*>(orow + width + 2 * lane) =
-        pack_bf16x2(h0 - lo_bf16(hi), h1 - hi_bf16(hi));
+  const size_t width = (size_t)a.Hq * KD;
+  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
+#pragma unroll
+  for (int f = 0; f < FPL; ++f) {
+    const int e = lane + 64 * f;
+    if (e >= KD) continue;
+    const float h = o[f] * inv;
+    const bf16 hb = (bf16)h;
+    orow[e] = hb;
+    if (a.o_split) orow[width + e] = (bf16)(h - (float)hb);
+  }
+}
+
+template <int KD>
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
+  dim3 grid(a.Hkv * a.n_hsub, a.B, a.n_qtiles);
+  attn_prefill_kernel<KD><<<grid, PrefillCfg<KD>::NT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int KD>
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_splits, a.Hkv, a.B);
+  attn_decode_kernel<KD><<<grid, kDecodeNT, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid2(a.G * a.Lq, a.Hkv, a.B);
+  attn_combine_kernel<KD><<<grid2, 64, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
-  dim3 grid(a.Hkv * a.n_hsub, a.B, a.n_qtiles);
-  attn_prefill_kernel<<<grid, kPrefillNT, 0, stream>>>(a);
-  return hipGetLastError();
+  switch (a.d) {
+    case 64: return launch_prefill<64>(a, stream);
+    case 128: return launch_prefill<128>(a, stream);
+    case 256: return launch_prefill<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_decode_bf16(const AttnArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_splits, a.Hkv, a.B);
-  attn_decode_kernel<<<grid, kDecodeNT, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 grid2(a.G * a.Lq, a.Hkv, a.B);
-  attn_combine_kernel<<<grid2, 64, 0, stream>>>(a);
-  return hipGetLastError();
+  switch (a.d) {
+    case 64: return launch_decode<64>(a, stream);
+    case 128: return launch_decode<128>(a, stream);
+    case 256: return launch_decode<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gqa

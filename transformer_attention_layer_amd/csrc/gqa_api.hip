@@ -39,7 +39,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Shape {
   int H, Hq, Hkv, d, G, n_qkv;
   bool bf16;
-  bool mfma;     // bf16 with head_dim 128: the matrix-core attention
+  bool mfma;     // bf16 with head_dim 64, 128 or 256: the matrix-core attention
   int rot;       // rotary width
   bool fused;    // mfma, and the rotary width (128 or 64) fits the fused QKV epilogue
   bool out_f32;  // o_proj output in fp32
@@ -111,9 +111,9 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->G = c.num_heads / c.num_kv_heads;
     sh->n_qkv = (int)n_qkv;
     sh->bf16 = c.dtype == GQA_BF16;
-    sh->mfma = sh->bf16 && c.head_dim == 128;
+    sh->mfma = sh->bf16 && (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256);
     sh->rot = c.rotary_dim;
-    sh->fused = sh->mfma && (c.rotary_dim == 128 || c.rotary_dim == 64);
+    sh->fused = sh->bf16 && c.head_dim == 128 && (c.rotary_dim == 128 || c.rotary_dim == 64);
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
     sh->o_split = c.o_split && c.dtype == GQA_BF16;
   }
@@ -158,7 +158,7 @@ size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
   int ns, ch;
   decode_split(s, batch, cap, &ns, &ch);
   const size_t parts = (size_t)batch * s.Hkv * ns * 32;
-  return align_up(parts * 128 * sizeof(float)) + align_up(parts * 2 * sizeof(float));
+  return align_up(parts * s.d * sizeof(float)) + align_up(parts * 2 * sizeof(float));
 }
 
 size_t ws_layer(const Shape& s, int batch, int q_len, int cap) {
@@ -263,7 +263,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
                     const void* kc, const void* vc, const int32_t* kv_base, int kv_add, int cap,
                     void* o, bool o_split, void* ws, hipStream_t st) {
   const double scale = 1.0 / sqrt((double)s.d);
-  if (!s.mfma) {  // fp32, or bf16 with a head_dim other than 128
+  if (!s.mfma) {  // fp32, or bf16 with a head_dim other than 64, 128, 256
     gqa::F32AttnArgs a{};
     a.q = q;
     a.k = kc;
@@ -284,6 +284,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
     return check_launch(gqa::launch_attn_vec(a, st), "attention (vector path)");
   }
   gqa::AttnArgs a{};
+  a.d = s.d;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(kc);
   a.v = static_cast<const __bf16*>(vc);
@@ -303,7 +304,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
     decode_split(s, batch, cap, &a.n_splits, &a.chunk);
     const size_t parts = (size_t)batch * s.Hkv * a.n_splits * 32;
     a.part_o = reinterpret_cast<float*>(ws);
-    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(parts * 128 * sizeof(float)));
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(parts * s.d * sizeof(float)));
     return check_launch(gqa::launch_attn_decode_bf16(a, st), "decode attention");
   }
   int hpw = 1;

@@ -33,10 +33,11 @@ struct GemmArgs {
 };
 
 struct AttnArgs {
-  const __bf16* q;  // [B, Hq, Lq, 128]
-  const __bf16* k;  // [B, Hkv, cap, 128]
+  int d;            // head_dim: 64, 128 or 256
+  const __bf16* q;  // [B, Hq, Lq, d]
+  const __bf16* k;  // [B, Hkv, cap, d]
   const __bf16* v;
-  __bf16* o;        // [B, Lq, Hq * 128], or [B, Lq, 2, Hq * 128] (hi | lo) when o_split
+  __bf16* o;        // [B, Lq, Hq * d], or [B, Lq, 2, Hq * d] (hi | lo) when o_split
   int o_split;
   const int* kv_base;  // kv_len[b] = (kv_base ? kv_base[b] : 0) + kv_add, clamped to [0, cap]
   int kv_add;
@@ -45,7 +46,7 @@ struct AttnArgs {
   // prefill work split
   int hpw, pb, n_qtiles, n_hsub;
   // split-KV decode
-  float* part_o;       // [B, Hkv, n_splits, 32, 128]
+  float* part_o;       // [B, Hkv, n_splits, 32, d]
   float2* part_ml;     // [B, Hkv, n_splits, 32] (running max in log2 units, sum)
   int n_splits, chunk;
 };
