@@ -60,9 +60,22 @@ def kv_bytes_of(w):
 
 KERNEL_OF_PART = {"qkv": "qkv_gemm", "attn": "attn_prefill", "oproj": "oproj_gemm",
                   "attn_decode": "attn_decode"}
-# bf16 head sizes other than 128: projection GEMM + separate norm/RoPE pass,
-# vector-unit attention
-KERNEL_OF_PART_FALLBACK = {"qkv": "qkv_gemm_normrope", "attn": "attn_vec", "oproj": "oproj_gemm"}
+
+
+def kernel_of_part(w, part: str) -> str:
+    """Kernel that runs a layer part for a workload, by the library's path
+    rules: the fused QKV epilogue needs bf16, head_dim 128 and a rotary width
+    of 64 or 128 (else projection GEMM + separate norm/RoPE pass); matrix-core
+    attention needs bf16 and head_dim 64, 128 or 256 (else the vector-unit
+    attention)."""
+    rot = w.rotary_dim or w.d
+    if part == "qkv" and not (w.dtype == "bf16" and w.d == 128 and rot in (64, 128)):
+        return "qkv_gemm_normrope"
+    if part in ("attn", "attn_decode") and not (w.dtype == "bf16" and w.d in (64, 128, 256)):
+        return "attn_vec"
+    return KERNEL_OF_PART[part]
+
+
 SOURCES_OF_KERNEL = {"qkv_gemm": "gemm_bf16.hip", "oproj_gemm": "gemm_bf16.hip",
                      "attn_prefill": "attn_bf16.hip", "attn_decode": "attn_bf16.hip",
                      "qkv_gemm_normrope": "gemm_bf16.hip", "attn_vec": "f32_kernels.hip"}
@@ -188,26 +201,37 @@ def bench_decode(w, steps, warmup, torch, T, GI):
 
 
 def measured_peaks(torch):
-    """What this machine delivers to a library GEMM and to a plain streaming read,
-    as references beside the vendor peaks: a bf16 8192^3 torch.matmul
-    (hipBLASLt) and a torch.sum over 2 GiB of fp32."""
+    """What this machine delivers to a library GEMM and to a library streaming
+    read, as references beside the vendor peaks: a bf16 8192^3 torch.matmul
+    with both operands K-contiguous (the layer's layout; hipBLASLt) and a
+    row-sum over 2 GiB of fp32 (8192-wide rows).  Each is the best of 10
+    timed calls after 3 untimed ones."""
+    def best_ms(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return min(times)
     n = 8192
     a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
-    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
-    for _ in range(3):  # library setup and clocks
-        torch.matmul(a, b)
-    gemm_ms = _time_loop(lambda: torch.matmul(a, b), 10, torch)
-    del a, b
+    bt = torch.randn(n, n, device="cuda").to(torch.bfloat16)  # [N, K]
+    gemm_ms = best_ms(lambda: torch.matmul(a, bt.t()))
+    del a, bt
     x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        x.sum()
-    read_ms = _time_loop(lambda: x.sum(), 10, torch)
+    read_ms = best_ms(lambda: x.view(-1, 8192).sum(1))
     del x
     torch.cuda.empty_cache()
     return {"gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
-            "gemm": "torch.matmul bf16 8192x8192x8192 (hipBLASLt)",
+            "gemm": "torch.matmul bf16 8192^3, A [M,K] x B[N,K]^T (hipBLASLt), best of 10",
             "hbm_read_gbs": round((1 << 31) / (read_ms * 1e-3) / 1e9, 1),
-            "read": "torch.sum over 2 GiB fp32"}
+            "read": "torch row-sum over 2 GiB fp32, best of 10"}
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -292,8 +316,7 @@ def main():
                        "ms_per_step": round(ms, 4), "frac_of_peak": round(value / peak, 4)})
         result["config"] = cfgd
         result["kernels_ms"] = {k: round(v, 4) for k, v in part_ms.items()}
-        fallback = w.dtype == "bf16" and w.d != 128
-        kern = (KERNEL_OF_PART_FALLBACK if fallback else KERNEL_OF_PART)[dom]
+        kern = kernel_of_part(w, dom)
         bound, kpeak = "mfma", peak
         if kern == "attn_vec":  # fp32 FMAs on the vector units
             bound, kpeak = "alu", PEAK_F32_VALU_TFLOPS

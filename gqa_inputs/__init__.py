@@ -75,8 +75,9 @@ WORKLOADS = {
                                  True, 1e6, 1e-6, "bf16", 4, cache_len=32768,
                                  o_split=True),
     # The explicit head_dim the pages cite for Gemma 3 (hidden 640, four
-    # query heads, head_dim 256 rather than 160); one KV head.  Head sizes
-    # other than 128 run the fallback path.
+    # query heads, head_dim 256 rather than 160); one KV head.  Runs the
+    # matrix-core attention, with the projection GEMM followed by a separate
+    # norm/RoPE pass.
     "gemma_h640_d256": Workload("gemma_h640_d256", 4, 2048, 640, 4, 1, 256, True,
                                 1e6, 1e-6, "bf16", 5),
 }

@@ -38,18 +38,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kCPR + (chunk ^ ((row / kRPW) & (kCPR - 1)));
 }
 
-// Raw buffer descriptor over rows [row0, nrows) of a row-major bf16 matrix
-// with `ld` elements per row.  Loads past the end of the range return zero
-// (hardware bounds check), which zero-fills ragged row and K tails.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int row0, int nrows,
-                                                            int ld) {
-  long long bytes = (long long)(nrows - row0) * ld * 2;
-  if (bytes < 0) bytes = 0;
-  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * ld), 0, (int)bytes,
-                                           0x00020000);
-}
-
 // One operand's share of a K stage, staged straight from global memory into
 // LDS (buffer_load ... lds, no register staging).  One instruction fills 64
 // consecutive 16-byte LDS slots = kRowsPerDma rows; lane i writes slot i, so
@@ -101,43 +89,74 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LDS ? 0 : 15) << 8));
 }
 
-// Workgroup -> output tile.  The grid is 1-D and padded to a multiple of the
-// 8 XCDs; workgroup i runs on XCD i % 8, so each XCD is handed one
-// contiguous run of the tile order below.  That order walks groups of
-// kGroupM token tiles and, inside a group, the feature tiles token tile by
-// token tile, so the tiles an XCD works on at one time share activations
-// and weights through its L2.
+// Output tiles and their order.  The tile order walks groups of kGroupM
+// token tiles and, inside a group, the feature tiles token tile by token
+// tile, so that tiles close in the order share activations and weights.
+// The order is cut into kXcds contiguous runs, one per XCD: workgroup i
+// runs on XCD i % 8 and takes tiles i / 8, i / 8 + G, i / 8 + 2 G, ... of
+// its XCD's run, where G is the number of workgroups per XCD, so the G
+// tiles an XCD works on at one time are neighbours in the order and share
+// its L2.
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
-__device__ __forceinline__ bool tile_of(const GemmArgs& a, int BN, int BM, int& tn, int& tm) {
-  const int ntn = (a.N + BN - 1) / BN;
-  const int ntm = (a.M + BM - 1) / BM;
-  const int total = ntn * ntm;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int id = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (id >= total) return false;
-  const int group = id / (kGroupM * ntn);
-  const int first_m = group * kGroupM;
-  const int gm = min(ntm - first_m, kGroupM);
-  const int in = id - group * kGroupM * ntn;
-  tm = first_m + in % gm;
-  tn = in / gm;
-  return true;
+struct TileOrder {
+  int ntn, ntm, total, per_xcd;
+  __device__ __forceinline__ TileOrder(int N, int M, int BN, int BM) {
+    ntn = (N + BN - 1) / BN;
+    ntm = (M + BM - 1) / BM;
+    total = ntn * ntm;
+    per_xcd = (total + kXcds - 1) / kXcds;
+  }
+  // position id of the order -> (feature tile, token tile)
+  __device__ __forceinline__ void at(int id, int& tn, int& tm) const {
+    const int group = id / (kGroupM * ntn);
+    const int first_m = group * kGroupM;
+    const int gm = min(ntm - first_m, kGroupM);
+    const int in = id - group * kGroupM * ntn;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  }
+};
+
+__host__ __device__ constexpr int gemm_tiles(int N, int M, int BN, int BM) {
+  return ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
 }
 
-__host__ __device__ constexpr int gemm_grid(int N, int M, int BN, int BM) {
-  return ((((N + BN - 1) / BN) * ((M + BM - 1) / BM) + kXcds - 1) / kXcds) * kXcds;
+// Bytes of the operands' bf16 rows [row0, nrows) with `ld` elements per row,
+// clamped to what one buffer descriptor addresses.
+__device__ __forceinline__ int rows_bytes(int row0, int nrows, int ld) {
+  long long bytes = (long long)(nrows - row0) * ld * 2;
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+  return (int)bytes;
 }
 
+// A persistent workgroup computes its tiles one after the other through one
+// continuous LDS pipeline: its K stages are numbered across tiles, the ring
+// slot of stage s is s % kStages, and the loads that run kStages - 1 stages
+// ahead cross into the next tile during the last trips of the current one,
+// so the next tile's first two stages are in LDS when the current tile's
+// epilogue starts (the third is loaded right after it).  The epilogue
+// stages its output through LDS rows past the ring (32 tokens x 128
+// features per wave at a time) and needs no barrier; a barrier after it
+// makes the next tile's first stage visible.  Compared with one workgroup
+// per tile, the next tile's prologue and the workgroup launch are off the
+// critical path, which pays at short K (a few stages per tile).
 template <int BN, int BM, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FB = WN / 32, TB = WM / 32;
-  static_assert(EPI != kEpiQKV || WN == 128, "QKV epilogue needs one head (128 features) per wave");
+  static_assert(WN == 128, "the epilogues stage 128 features per wave");
   static_assert(kBK == 32 && kStages == 4, "the pipeline below is written for 2 substeps x 4 stages");
   static_assert(FB == 4 && TB == 4, "16 MFMAs per substep");
-  __shared__ u32x4 lds[kStages][(BN + BM) * kCPR];
+  // One LDS array: the K-stage ring, then the epilogue's staging rows (per
+  // wave 32 rows x 256 B).  A second __shared__ array would give the
+  // compiler alias scopes under which it waits for every LDS DMA in flight
+  // before each fragment read; the waits below already order them.
+  constexpr int kStageSlots = (BN + BM) * kCPR;
+  __shared__ u32x4 lds[kStages * kStageSlots + (kThreads / 64) * 32 * 16];
+  auto ring = [&](int slot) { return &lds[slot * kStageSlots]; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,34 +165,78 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int N = a.N, M = a.M, K = a.K;
-  int tn, tm;
-  if (!tile_of(a, BN, BM, tn, tm)) return;  // padding workgroup
-  const int n0 = tn * BN;
-  const int m0 = tm * BM;
-
-  floatx16 acc[FB][TB];
-#pragma unroll
-  for (int f = 0; f < FB; ++f)
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[f][t][r] = 0.f;
+  const TileOrder order(N, M, BN, BM);
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int per_wg = (int)(gridDim.x / kXcds);  // workgroups on this XCD
+  const int run_end = min((xcd + 1) * order.per_xcd, order.total);
+  int id = xcd * order.per_xcd + (int)(blockIdx.x / kXcds);
+  if (id >= run_end) return;  // no tile for this workgroup
 
   const int nk = (K + kBK - 1) / kBK;
   // W may be narrower than X along K (w_kmod): X = [hi | lo] reads W twice
   const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
-  const __amdgpu_buffer_rsrc_t rw = rows_rsrc(a.W, n0, N, Kw);
-  const __amdgpu_buffer_rsrc_t rx = rows_rsrc(a.X, m0, M, K);
   DmaPlan<BN> pw;
   DmaPlan<BM> px;
   pw.init(Kw, wave, lane);
   px.init(K, wave, lane);
   constexpr int kLw = DmaPlan<BN>::kInstr, kLx = DmaPlan<BM>::kInstr;
   static_assert(kLw == 4 && kLx == 4, "one load per two MFMAs in each substep's second half");
-  // K offset into W of stage kt (K <= 2 Kw: X = [hi | lo] reads W at most twice)
+  // K offset into W of a tile's stage kt (K <= 2 Kw: X = [hi | lo] reads W at most twice)
   auto w_k0 = [&](int kt) { const int k0 = kt * kBK; return k0 >= Kw ? k0 - Kw : k0; };
-  auto stage_w = [&](int kt) { return &lds[kt % kStages][0]; };
-  auto stage_x = [&](int kt) { return &lds[kt % kStages][BN * kCPR]; };
+
+  // Operand rows of the current tile (cur) and of this workgroup's next
+  // tile (nxt; zero bytes when there is none: its loads then read zeros
+  // into ring slots nobody reads).
+  struct Src { const bf16* w; const bf16* x; int wbytes, xbytes; int n0, m0; };
+  auto src_of = [&](int tile) {
+    Src s;
+    if (tile >= run_end) {
+      s.w = a.W; s.x = a.X; s.wbytes = 0; s.xbytes = 0; s.n0 = 0; s.m0 = 0;
+      return s;
+    }
+    int tn, tm;
+    order.at(tile, tn, tm);
+    s.n0 = tn * BN;
+    s.m0 = tm * BM;
+    s.w = a.W + (size_t)s.n0 * Kw;
+    s.x = a.X + (size_t)s.m0 * K;
+    s.wbytes = rows_bytes(s.n0, N, Kw);
+    s.xbytes = rows_bytes(s.m0, M, K);
+    return s;
+  };
+  Src cur = src_of(id);
+  Src nxt = src_of(id + per_wg);
+
+  // A tile's two buffer descriptors, and the loads of its stage kt into
+  // ring slot `slot` (8 instructions, issued one at a time: half 0 = W,
+  // 1 = X).
+  struct Rsrc {
+    __amdgpu_buffer_rsrc_t w, x;
+  };
+  auto rsrc_of = [&](const Src& s) {
+    Rsrc r;
+    r.w = __builtin_amdgcn_make_buffer_rsrc((void*)s.w, 0, s.wbytes, 0x00020000);
+    r.x = __builtin_amdgcn_make_buffer_rsrc((void*)s.x, 0, s.xbytes, 0x00020000);
+    return r;
+  };
+  struct StageLoad {
+    u32x4* dst;
+    int kw, kx;
+  };
+  auto stage_load = [&](int slot, int kt) {
+    StageLoad l;
+    l.dst = ring(slot);
+    l.kw = w_k0(kt);
+    l.kx = kt * kBK;
+    return l;
+  };
+  auto issue = [&](const Rsrc& r, const StageLoad& l, int j, int half) {
+    if (half == 0) pw.issue(r.w, l.dst, j, l.kw, Kw);
+    else px.issue(r.x, l.dst + BN * kCPR, j, l.kx, K);
+  };
+  auto load = [&](const Src& s, int slot, int kt, int j, int half) {
+    issue(rsrc_of(s), stage_load(slot, kt), j, half);
+  };
 
   // LDS offsets (16-byte slots) of this lane's fragments: row-major
   // fragments of W (features) and X (tokens), chunk = 2 * substep + hh
@@ -186,54 +249,63 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     for (int t = 0; t < TB; ++t) ob[sub][t] = BN * kCPR + swz(wm * WM + 32 * t + l32, 2 * sub + hh);
   }
 
-  // Prologue: stages 0 .. kStages - 2 in flight, stage 0 landed and visible.
+  // Prologue: the first tile's stages 0 .. kStages - 2 (or, for K of fewer
+  // stages, whatever follows them) in flight, stage 0 landed and visible.
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p) {
-    if (p < nk) {
+    const bool in_cur = p < nk;
 #pragma unroll
-      for (int j = 0; j < kLw; ++j) pw.issue(rw, stage_w(p), j, w_k0(p), Kw);
+    for (int j = 0; j < kLw; ++j) load(in_cur ? cur : nxt, p, in_cur ? p : p - nk, j, 0);
 #pragma unroll
-      for (int j = 0; j < kLx; ++j) px.issue(rx, stage_x(p), j, p * kBK, K);
-    }
+    for (int j = 0; j < kLx; ++j) load(in_cur ? cur : nxt, p, in_cur ? p : p - nk, j, 1);
   }
-  if (nk >= 3) wait_vmem<2 * (kLw + kLx)>();
-  else if (nk == 2) wait_vmem<kLw + kLx>();
-  else wait_vmem<0>();
+  wait_vmem<2 * (kLw + kLx)>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
   u32x4 fa[2][FB], fb[2][TB];
   {
-    const u32x4* st = &lds[0][0];
+    const u32x4* st = ring(0);
 #pragma unroll
     for (int f = 0; f < FB; ++f) fa[0][f] = st[oa[0][f]];
 #pragma unroll
     for (int t = 0; t < TB; ++t) fb[0][t] = st[ob[0][t]];
   }
 
-  // Main loop, one K stage (two 16-wide substeps) per trip.  Each substep
-  // issues its 16 MFMAs interleaved with the 8 LDS reads of the next
-  // substep's fragments (first half) and 4 of the loads of stage kt + 3
-  // (second half), so that no wave stalls for long on a queue of loads.
-  // Stage kt + 3 goes to the LDS stage of kt - 1.  Every wave's reads of
-  // that stage had completed (s_waitcnt lgkmcnt(0)) before it reached the
-  // barrier in the middle of trip kt - 1, which in turn makes stage kt
-  // visible.  LOAD: stage kt + 3 exists; NEXT: stage kt + 1 exists.
-  auto trip = [&](int kt, auto LOAD, auto NEXT) {
-    const int kn = kt + kStages - 1;
-    const int kwn = w_k0(kn);
-    const u32x4* st = &lds[kt % kStages][0];
-    const u32x4* st1 = &lds[(kt + 1) % kStages][0];
+  // One K stage (two 16-wide substeps) per trip; g is the stage's number
+  // in this workgroup's sequence and kt its index in the current tile.
+  // Each substep issues its 16 MFMAs interleaved with the 8 LDS reads of
+  // the next substep's fragments (first half) and 4 of the loads of stage
+  // g + 3 (second half), so that no wave stalls for long on a queue of
+  // loads.  Stage g + 3 goes to the ring slot of stage g - 1.  Every wave's
+  // reads of that slot had completed (s_waitcnt lgkmcnt(0)) before it
+  // reached the barrier in the middle of trip g - 1 (or, for a tile's last
+  // trip, the barrier after its epilogue), which in turn makes stage g
+  // visible.  Stage g + 3 is stage kt + 3 of this tile or, past its end, a
+  // stage of the next one.  A tile's last trip (NEXT false) issues no loads,
+  // reads no fragments in its second substep and has no barrier in the
+  // middle: its stage g + 3 (the next tile's stage 2) is loaded, and the
+  // next tile's first fragments are read, after the epilogue.  Loads
+  // complete in order, so a load the epilogue itself issues then waits
+  // only for stages issued a trip or more earlier.
+  floatx16 acc[FB][TB];
+  unsigned g = 0;  // unsigned: the ring slot g % kStages is a mask
+  // A trip loads stage kt + kofs of the tile whose descriptors are rl
+  // (kofs = 3 with this tile's, 3 - nk with the next tile's); a tile's
+  // last trip (NEXT false) loads nothing.
+  auto trip = [&](int kt, const Rsrc& rl, int kofs, auto NEXT) {
+    const int sl = (int)((g + kStages - 1) % kStages);
+    const StageLoad ld = stage_load(sl, kt + kofs);
+    const u32x4* st = ring((int)(g % kStages));
+    const u32x4* st1 = ring((int)((g + 1) % kStages));
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       if (sub == 1) {
         if constexpr (NEXT) {
-          // stage kt + 1 landed: at most stage kt + 2 (8 loads) and the
-          // first half of stage kt + 3 (4 loads) may still be in flight;
-          // this wave's reads of stage kt are done
-          if constexpr (LOAD) wait_vmem<kLw + kLx + kLw, true>();
-          else if (kt + 2 < nk) wait_vmem<kLw + kLx, true>();
-          else wait_vmem<0, true>();
+          // stage g + 1 landed: stage g + 2 (8 loads) and the first half of
+          // stage g + 3 (4 loads) may still be in flight; this wave's reads
+          // of stage g are done
+          wait_vmem<kLw + kLx + kLw, true>();
           __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -254,188 +326,305 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             else fa[sub ^ 1][i - 4] = rs[ra[i - 4]];
           }
         } else if ((i & 1) == 0) {
-          if constexpr (LOAD) {
-            const int j = (i - 8) / 2;
-            if (sub == 0) pw.issue(rw, stage_w(kn), j, kwn, Kw);
-            else px.issue(rx, stage_x(kn), j, kn * kBK, K);
-          }
+          if constexpr (NEXT) issue(rl, ld, (i - 8) / 2, sub);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    ++g;
   };
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
-  int kt = 0;
-  for (; kt < nk - (kStages - 1); ++kt) trip(kt, True(), True());
-  for (; kt < nk - 1; ++kt) trip(kt, False(), True());
-  trip(kt, False(), False());
 
-  const int nw = n0 + wn * WN;  // first feature of this wave
-  if (EPI == kEpiPlain) {
+  for (;;) {
 #pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      const int m = m0 + wm * WM + 32 * t + l32;
-      if (m >= M) continue;
+    for (int f = 0; f < FB; ++f)
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[f][t][r] = 0.f;
+
+    const int n0 = cur.n0, m0 = cur.m0;
+    const int nw = n0 + wn * WN;  // first feature of this wave
+
+    {
+      // from trip nk - 3 on, the loads run into the next tile (one uniform
+      // branch per trip; the descriptors change once per tile)
+      Rsrc rl = rsrc_of(cur);
+      int kofs = kStages - 1;
+      for (int kt = 0; kt < nk - 1; ++kt) {
+        if (kt == nk - kStages + 1) {
+          // a real branch, not selects executed on every trip
+          asm volatile("");
+          rl = rsrc_of(nxt);
+          kofs -= nk;
+        }
+        trip(kt, rl, kofs, True());
+      }
+      trip(nk - 1, rl, kofs, False());
+    }
+
+    // The accumulators of token blocks t0 .. TB - 1 stay in the
+    // matrix-core registers until block t0's epilogue starts: the compiler
+    // would otherwise copy all of them into vector registers at once (right
+    // after their last MFMA, stalling on each result) and spill.
+    auto pin_from = [&](int t0) {
 #pragma unroll
       for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = nw + 32 * f + 8 * j + 4 * hh;
-          if (n >= N) continue;
-          if (a.out_f32) {
+        for (int t = 0; t < TB; ++t)
+          if (t >= t0) asm volatile("" : "+a"(acc[f][t]));
+    };
+
+    u32x4* const stage = &lds[kStages * kStageSlots + wave * 32 * 16];  // 32 rows x 16 chunks
+    // lane-derived epilogue addresses are computed here, not kept live
+    // (and spilled) across the K loop
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    const int l32 = lane & 31, hh = lane >> 5;
+    u32x2* const stage8 = reinterpret_cast<u32x2*>(stage);
+    // 4 features at feat (a multiple of 4) of row `row`; chunk c of row r
+    // sits at slot c ^ (r & 15)
+    auto put8 = [&](int row, int feat, u32x2 v) {
+      stage8[(row * 16 + ((feat >> 3) ^ (row & 15))) * 2 + ((feat >> 2) & 1)] = v;
+    };
+    if constexpr (EPI == kEpiPlainF32) {
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        pin_from(t);
+        const int m = m0 + wm * WM + 32 * t + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int f = 0; f < FB; ++f)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = nw + 32 * f + 8 * j + 4 * hh;
+            if (n >= N) continue;
             floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
                          acc[f][t][4 * j + 3]};
             *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + (size_t)m * N + n) = w;
-          } else {
+          }
+      }
+    } else if constexpr (EPI == kEpiPlain) {
+      // per 32-token block: rows of 128 bf16 features per token in LDS,
+      // then stored 16 bytes per lane, 4 whole rows per instruction
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        pin_from(t);
+#pragma unroll
+        for (int f = 0; f < FB; ++f)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
             u32x2 w;
             w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
             w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
-            st8(static_cast<bf16*>(a.out) + (size_t)m * N + n, w);
+            put8(l32, 32 * f + 8 * j + 4 * hh, w);
           }
+        const int c = lane & 15;
+        const int n = nw + 8 * c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const int m = m0 + wm * WM + 32 * t + row;
+          const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
+          if (m < M && n < N) st16(static_cast<bf16*>(a.out) + (size_t)m * N + n, v);
         }
-    }
-    return;
-  }
-
-  // ---- QKV epilogue: one head of 128 features per wave ----
-  // Per 32-token block the lane's values are normalised and rotated in
-  // registers and written to this wave's 32 KB of LDS as rows of 128 bf16
-  // per token; the rows are then stored 16 bytes per lane, 4 whole rows per
-  // instruction (a head's rows are contiguous in q and in the caches).
-  // Row r's 16-byte chunk c sits at slot c ^ (r & 15).
-  __syncthreads();  // every wave is done reading the last K stages
-  if (nw >= N) return;  // wave-uniform
-  const int head = nw >> 7;
-  const int Hq = a.Hq, Hkv = a.Hkv;
-  int kind;       // 0 = q, 1 = k, 2 = v
-  int h;
-  if (head < Hq) { kind = 0; h = head; }
-  else if (head < Hq + Hkv) { kind = 1; h = head - Hq; }
-  else { kind = 2; h = head - Hq - Hkv; }
-  u32x4* const stage = &lds[wave][0];   // 128 rows x 16 chunks
-  u32x2* const stage8 = reinterpret_cast<u32x2*>(stage);
-  auto put8 = [&](int row, int feat, u32x2 v) {  // 4 features at feat (multiple of 4)
-    stage8[(row * 16 + ((feat >> 3) ^ (row & 15))) * 2 + ((feat >> 2) & 1)] = v;
-  };
-
-  const bool do_norm = (kind != 2) && a.qk_norm;
-  const bf16* wsrc = kind == 0 ? a.q_norm_w : a.k_norm_w;
-  // norm weights of this lane's features 32f + 8j + 4hh + (0..3), kept packed
-  u32x2 wpk[4][4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x2 z = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
-      wpk[f][j] = do_norm ? ld8(wsrc + 32 * f + 8 * j + 4 * hh) : z;
-    }
-
-  // One token block (32 tokens) at a time; within it, a lane handles four
-  // consecutive features i..i+3 together with their RoPE partners
-  // i+rot/2..i+rot/2+3, so only a few values are live at once.
-#pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int row = 32 * t + l32;
-    const int m = m0 + wm * WM + row;
-    const int mm = m < M ? m : 0;
-    const int tok = mm % a.L;
-    float inv = 1.0f;
-    if (do_norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
-      ss = sum_xor32(ss);
-      inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
-    }
-    if (kind == 2) {
+      }
+    } else if (nw < N) {  // wave-uniform
+      // ---- QKV epilogue: one head of 128 features per wave ----
+      // Per 32-token block the lane's values are normalised and rotated in
+      // registers, written to LDS as rows of 128 bf16 per token and stored
+      // 16 bytes per lane, 4 whole rows per instruction (a head's rows are
+      // contiguous in q and in the caches).  Within a block, a lane handles
+      // four consecutive features i..i+3 together with their RoPE partners
+      // i+rot/2..i+rot/2+3, so only a few values are live at once.
+      const int head = nw >> 7;
+      const int Hq = a.Hq, Hkv = a.Hkv;
+      int kind;  // 0 = q, 1 = k, 2 = v
+      int h;
+      if (head < Hq) { kind = 0; h = head; }
+      else if (head < Hq + Hkv) { kind = 1; h = head - Hq; }
+      else { kind = 2; h = head - Hq - Hkv; }
+      const bool do_norm = (kind != 2) && a.qk_norm;
+      const bf16* wsrc = kind == 0 ? a.q_norm_w : a.k_norm_w;
+      // norm weights of this lane's features 32f + 8j + 4hh + (0..3), kept packed
+      u32x2 wpk[4][4];
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          u32x2 w;
-          w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
-          w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
-          put8(row, 32 * f + 8 * j + 4 * hh, w);
+          u32x2 z = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+          wpk[f][j] = do_norm ? ld8(wsrc + 32 * f + 8 * j + 4 * hh) : z;
         }
-      continue;
-    }
-    // rotate-half RoPE over the first `rot` features: feature i < rot/2
-    // pairs with i + rot/2 (rot 128: block f with f + 2; rot 64: block 0
-    // with block 1, blocks 2 and 3 pass through)
-    const int half = a.rot >> 1;
-    const float2* cs = a.rope + (size_t)(a.start_pos ? mm : tok) * half;
-    auto rope_pair = [&](int f1, int f2, int j) {
-      const int i0 = 32 * f1 + 8 * j + 4 * hh;
-      // (cos, sin) of features i0 .. i0+3: two 16-byte loads
-      const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
-      const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
-      const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
-      const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-      const u32x2 w1 = wpk[f1][j], w2 = wpk[f2][j];
-      const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
-      const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
-      float y1[4], y2[4];
+      const int half = a.rot >> 1;
+      const int L = a.L;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x1 = acc[f1][t][4 * j + e] * inv * g1[e];
-        const float x2 = acc[f2][t][4 * j + e] * inv * g2[e];
-        y1[e] = x1 * cc[e] - x2 * sn[e];
-        y2[e] = x2 * cc[e] + x1 * sn[e];
+      for (int t = 0; t < TB; ++t) {
+        pin_from(t);
+        // Token rows mb .. mb + 31 of this block: row m is token tok of
+        // sequence b (m = b L + tok).  One division per block (wave-uniform);
+        // a row's (b, tok) follows by carrying over sequence ends, which
+        // takes at most one step per row when L >= 32.
+        const int mb = m0 + wm * WM + 32 * t;
+        const int b0 = mb / L;
+        const int tok0 = mb - b0 * L;
+        const bool long_seq = L >= 32;
+        auto locate = [&](int r, int& b, int& tok) {  // row mb + r, 0 <= r < 32
+          if (long_seq) {
+            tok = tok0 + r;
+            b = b0;
+            if (tok >= L) { tok -= L; ++b; }
+          } else {
+            b = (mb + r) / L;
+            tok = mb + r - b * L;
+          }
+        };
+        const int mr = mb + l32;
+        int rb, rtok;
+        locate(l32, rb, rtok);
+        const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
+        float inv = 1.0f;
+        if (do_norm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
+          ss = sum_xor32(ss);
+          inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
+        }
+        if (kind == 2) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              u32x2 w;
+              w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
+              w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
+              put8(l32, 32 * f + 8 * j + 4 * hh, w);
+            }
+        } else {
+          // Rotate-half RoPE over the first `rot` features: feature i <
+          // rot/2 pairs with i + rot/2 (rot 128: block f with f + 2; rot
+          // 64: block 0 with block 1, blocks 2 and 3 pass through).  Each
+          // rope_pair call needs the (cos, sin) of features i0 .. i0+3,
+          // i0 = 32 f1 + 8 j + 4 hh: two 16-byte loads, issued four calls
+          // ahead so that the table's latency is paid about once per block.
+          floatx4 pre[4][2];
+          auto fetch = [&](int k, int f1, int j) {
+            const int i0 = 32 * f1 + 8 * j + 4 * hh;
+            pre[k & 3][0] = *reinterpret_cast<const floatx4*>(cs + i0);
+            pre[k & 3][1] = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
+          };
+          auto rope_pair = [&](int f1, int f2, int j, const floatx4& c01, const floatx4& c23) {
+            const int i0 = 32 * f1 + 8 * j + 4 * hh;
+            const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
+            const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+            const u32x2 w1 = wpk[f1][j], w2 = wpk[f2][j];
+            const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
+            const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
+            float y1[4], y2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x1 = acc[f1][t][4 * j + e] * inv * g1[e];
+              const float x2 = acc[f2][t][4 * j + e] * inv * g2[e];
+              y1[e] = x1 * cc[e] - x2 * sn[e];
+              y2[e] = x2 * cc[e] + x1 * sn[e];
+            }
+            u32x2 o1, o2;
+            o1.x = pack_bf16x2(y1[0], y1[1]);
+            o1.y = pack_bf16x2(y1[2], y1[3]);
+            o2.x = pack_bf16x2(y2[0], y2[1]);
+            o2.y = pack_bf16x2(y2[2], y2[3]);
+            put8(l32, i0, o1);
+            put8(l32, i0 + half, o2);
+          };
+          auto norm_only = [&](int f, int j) {
+            const u32x2 w = wpk[f][j];
+            u32x2 o;
+            o.x = pack_bf16x2(acc[f][t][4 * j + 0] * inv * lo_bf16(w.x),
+                              acc[f][t][4 * j + 1] * inv * hi_bf16(w.x));
+            o.y = pack_bf16x2(acc[f][t][4 * j + 2] * inv * lo_bf16(w.y),
+                              acc[f][t][4 * j + 3] * inv * hi_bf16(w.y));
+            put8(l32, 32 * f + 8 * j + 4 * hh, o);
+          };
+          if (a.rot == 128) {  // call k: f1 = k / 4, j = k % 4
+#pragma unroll
+            for (int k = 0; k < 4; ++k) fetch(k, 0, k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              rope_pair(k / 4, k / 4 + 2, k % 4, pre[k & 3][0], pre[k & 3][1]);
+              if (k + 4 < 8) fetch(k + 4, 1, k % 4);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {  // rot == 64: call j pairs block 0 with block 1
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fetch(j, 0, j);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              rope_pair(0, 1, j, pre[j][0], pre[j][1]);
+              norm_only(2, j);
+              norm_only(3, j);
+            }
+          }
+        }
+        // cache offsets of the (at most two, when L >= 32) sequences the
+        // block's rows belong to, read once per block
+        int sp0 = 0, sp1 = 0;
+        if (kind != 0 && a.start_pos && long_seq) {
+          sp0 = a.start_pos[b0];
+          if ((b0 + 1) * L < M) sp1 = a.start_pos[b0 + 1];
+        }
+        // Store the block: lane l moves chunk l % 16 of row 4 i + l / 16.
+        const int c = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const int m = mb + row;
+          const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
+          if (m >= M) continue;
+          int b, tok;
+          locate(row, b, tok);
+          bf16* dst;
+          if (kind == 0) {
+            dst = a.q + (((size_t)b * Hq + h) * L + tok) * 128;
+          } else {
+            const int base = !a.start_pos ? 0 : long_seq ? (b == b0 ? sp0 : sp1) : a.start_pos[b];
+            const int pos = base + tok;
+            if (pos < 0 || pos >= a.cap) continue;
+            bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
+            dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
+          }
+          st16(dst + 8 * c, v);
+        }
       }
-      u32x2 o1, o2;
-      o1.x = pack_bf16x2(y1[0], y1[1]);
-      o1.y = pack_bf16x2(y1[2], y1[3]);
-      o2.x = pack_bf16x2(y2[0], y2[1]);
-      o2.y = pack_bf16x2(y2[2], y2[3]);
-      put8(row, i0, o1);
-      put8(row, i0 + half, o2);
-    };
-    auto norm_only = [&](int f, int j) {
-      const u32x2 w = wpk[f][j];
-      u32x2 o;
-      o.x = pack_bf16x2(acc[f][t][4 * j + 0] * inv * lo_bf16(w.x),
-                        acc[f][t][4 * j + 1] * inv * hi_bf16(w.x));
-      o.y = pack_bf16x2(acc[f][t][4 * j + 2] * inv * lo_bf16(w.y),
-                        acc[f][t][4 * j + 3] * inv * hi_bf16(w.y));
-      put8(row, 32 * f + 8 * j + 4 * hh, o);
-    };
-    if (a.rot == 128) {
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rope_pair(f, f + 2, j);
-    } else {  // rot == 64
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rope_pair(0, 1, j);
-        norm_only(2, j);
-        norm_only(3, j);
-      }
     }
-  }
 
-  // Store: lane l moves chunk l % 16 of row 4 i + l / 16.
-  const int c = lane & 15;
-#pragma unroll 4
-  for (int i = 0; i < WM / 4; ++i) {
-    const int row = 4 * i + (lane >> 4);
-    const int m = m0 + wm * WM + row;
-    if (m >= M) continue;
-    const int b = m / a.L;
-    const int tok = m - b * a.L;
-    bf16* dst;
-    if (kind == 0) {
-      dst = a.q + (((size_t)b * Hq + h) * a.L + tok) * 128;
-    } else {
-      const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
-      if (pos < 0 || pos >= a.cap) continue;
-      bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
-      dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
-    }
-    st16(dst + 8 * c, stage[row * 16 + (c ^ (row & 15))]);
+    // every load and store of this wave done (the next tile's stages 0
+    // and 1 landed), on the way out of the loop too
+    wait_vmem<0, true>();
+    id += per_wg;
+    if (id >= run_end) break;
+    cur = nxt;
+    nxt = src_of(id + per_wg);
+    // stage 0 of the next tile (ring slot g % kStages) visible; every
+    // wave's reads of the last stage are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // the next tile's stage 2 (held back by the last trip) into the slot
+    // of the last trip's stage; the stage index is opaque so that its load
+    // offsets are not hoisted out of the tile loop
+    int k2 = kStages - 2;
+    asm volatile("" : "+s"(k2));
+#pragma unroll
+    for (int j = 0; j < kLw; ++j) load(cur, (int)((g + kStages - 2) % kStages), k2, j, 0);
+#pragma unroll
+    for (int j = 0; j < kLx; ++j) load(cur, (int)((g + kStages - 2) % kStages), k2, j, 1);
+    const u32x4* st = ring((int)(g % kStages));
+#pragma unroll
+    for (int f = 0; f < FB; ++f) fa[0][f] = st[oa[0][f]];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) fb[0][t] = st[ob[0][t]];
   }
 }
 
@@ -551,15 +740,43 @@ hipError_t launch_rope_table(float2* table, const int* start_pos, int rows, int 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
+namespace {
+
+// Workgroups of the large GEMMs: one per tile (padded to a multiple of the
+// XCDs), at most one per compute unit (each holds 160 KB of LDS), rounded
+// down to a multiple of the XCDs.  With fewer than kStages - 1 K stages a
+// load that runs ahead could reach two tiles further, so every workgroup
+// then gets exactly one tile.
+int gemm_workgroups(int N, int M, int K) {
   constexpr int BN = 256, BM = 256;
-  gemm_bf16_kernel<BN, BM, kEpiQKV><<<gemm_grid(args.N, args.M, BN, BM), kThreads, 0, stream>>>(args);
+  const int tiles = gemm_tiles(N, M, BN, BM);
+  int grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  if ((K + kBK - 1) / kBK < kStages - 1) return grid;
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return grid;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n >= kXcds ? n / kXcds * kXcds : -1;
+  }
+  return cus[dev] > 0 ? min(grid, cus[dev]) : grid;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
+  gemm_bf16_kernel<256, 256, kEpiQKV>
+      <<<gemm_workgroups(args.N, args.M, args.K), kThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream) {
-  constexpr int BN = 256, BM = 256;
-  gemm_bf16_kernel<BN, BM, kEpiPlain><<<gemm_grid(args.N, args.M, BN, BM), kThreads, 0, stream>>>(args);
+  const int grid = gemm_workgroups(args.N, args.M, args.K);
+  if (args.out_f32)
+    gemm_bf16_kernel<256, 256, kEpiPlainF32><<<grid, kThreads, 0, stream>>>(args);
+  else
+    gemm_bf16_kernel<256, 256, kEpiPlain><<<grid, kThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 

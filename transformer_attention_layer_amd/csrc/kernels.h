@@ -8,7 +8,7 @@
 
 namespace gqa {
 
-enum { kEpiPlain = 0, kEpiQKV = 1 };
+enum { kEpiPlain = 0, kEpiQKV = 1, kEpiPlainF32 = 2 };  // GEMM epilogue kinds
 
 // C^T[n, m] = sum_k W[n, k] X[m, k]  (bf16 in, fp32 accumulate)
 struct GemmArgs {
