@@ -70,10 +70,15 @@ struct DmaPlan {
   }
 
   // instruction j of the stage whose K offset is k0, into `stage` (the
-  // operand's first slot in that LDS stage)
+  // operand's first slot in that LDS stage).  kalign (the row length is a
+  // multiple of kBK, so no stage has a K tail; a compile-time constant at
+  // every call): the descriptor is already based at the stage's K offset,
+  // and the per-lane offset alone decides whether the row exists.
+  // Otherwise chunks at or past column `kcols` are redirected out of range.
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, u32x4* stage, int j, int k0,
-                                        int kcols) const {
-    const unsigned v = k0 + kc < kcols ? voff[j] + (unsigned)(k0 * 2) : 0x80000000u;
+                                        int kcols, bool kalign) const {
+    const unsigned v = kalign ? voff[j]
+                              : k0 + kc < kcols ? voff[j] + (unsigned)(k0 * 2) : 0x80000000u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(stage + slot0 + j * kRowsPerDma * kCPR), 16,
         v, 0, 0, 0);
@@ -143,7 +148,7 @@ __device__ __forceinline__ int rows_bytes(int row0, int nrows, int ld) {
 // makes the next tile's first stage visible.  Compared with one workgroup
 // per tile, the next tile's prologue and the workgroup launch are off the
 // critical path, which pays at short K (a few stages per tile).
-template <int BN, int BM, int EPI>
+template <int BN, int BM, int EPI, bool KALIGN>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FB = WN / 32, TB = WM / 32;
@@ -207,35 +212,32 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   Src cur = src_of(id);
   Src nxt = src_of(id + per_wg);
 
-  // A tile's two buffer descriptors, and the loads of its stage kt into
-  // ring slot `slot` (8 instructions, issued one at a time: half 0 = W,
-  // 1 = X).
-  struct Rsrc {
-    __amdgpu_buffer_rsrc_t w, x;
-  };
-  auto rsrc_of = [&](const Src& s) {
-    Rsrc r;
-    r.w = __builtin_amdgcn_make_buffer_rsrc((void*)s.w, 0, s.wbytes, 0x00020000);
-    r.x = __builtin_amdgcn_make_buffer_rsrc((void*)s.x, 0, s.xbytes, 0x00020000);
-    return r;
-  };
+  // The loads of stage kt of a tile into ring slot `slot`: two buffer
+  // descriptors (rebased to the stage's K offset when K is aligned) and 8
+  // instructions, issued one at a time (half 0 = W, 1 = X).
   struct StageLoad {
+    __amdgpu_buffer_rsrc_t w, x;
     u32x4* dst;
     int kw, kx;
   };
-  auto stage_load = [&](int slot, int kt) {
+  auto stage_load = [&](const Src& s, int slot, int kt) {
     StageLoad l;
     l.dst = ring(slot);
     l.kw = w_k0(kt);
     l.kx = kt * kBK;
+    const int ow = KALIGN ? l.kw : 0, ox = KALIGN ? l.kx : 0;
+    l.w = __builtin_amdgcn_make_buffer_rsrc((void*)(s.w + ow), 0, max(s.wbytes - 2 * ow, 0),
+                                            0x00020000);
+    l.x = __builtin_amdgcn_make_buffer_rsrc((void*)(s.x + ox), 0, max(s.xbytes - 2 * ox, 0),
+                                            0x00020000);
     return l;
   };
-  auto issue = [&](const Rsrc& r, const StageLoad& l, int j, int half) {
-    if (half == 0) pw.issue(r.w, l.dst, j, l.kw, Kw);
-    else px.issue(r.x, l.dst + BN * kCPR, j, l.kx, K);
+  auto issue = [&](const StageLoad& l, int j, int half) {
+    if (half == 0) pw.issue(l.w, l.dst, j, l.kw, Kw, KALIGN);
+    else px.issue(l.x, l.dst + BN * kCPR, j, l.kx, K, KALIGN);
   };
   auto load = [&](const Src& s, int slot, int kt, int j, int half) {
-    issue(rsrc_of(s), stage_load(slot, kt), j, half);
+    issue(stage_load(s, slot, kt), j, half);
   };
 
   // LDS offsets (16-byte slots) of this lane's fragments: row-major
@@ -290,12 +292,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   // only for stages issued a trip or more earlier.
   floatx16 acc[FB][TB];
   unsigned g = 0;  // unsigned: the ring slot g % kStages is a mask
-  // A trip loads stage kt + kofs of the tile whose descriptors are rl
-  // (kofs = 3 with this tile's, 3 - nk with the next tile's); a tile's
-  // last trip (NEXT false) loads nothing.
-  auto trip = [&](int kt, const Rsrc& rl, int kofs, auto NEXT) {
+  // A trip loads stage kt + kofs of tile rl (kofs = 3 with this tile,
+  // 3 - nk with the next one); a tile's last trip (NEXT false) loads
+  // nothing.
+  auto trip = [&](int kt, const Src& rl, int kofs, auto NEXT) {
     const int sl = (int)((g + kStages - 1) % kStages);
-    const StageLoad ld = stage_load(sl, kt + kofs);
+    const StageLoad ld = stage_load(rl, sl, kt + kofs);
     const u32x4* st = ring((int)(g % kStages));
     const u32x4* st1 = ring((int)((g + 1) % kStages));
 #pragma unroll
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             else fa[sub ^ 1][i - 4] = rs[ra[i - 4]];
           }
         } else if ((i & 1) == 0) {
-          if constexpr (NEXT) issue(rl, ld, (i - 8) / 2, sub);
+          if constexpr (NEXT) issue(ld, (i - 8) / 2, sub);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -350,13 +352,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     {
       // from trip nk - 3 on, the loads run into the next tile (one uniform
       // branch per trip; the descriptors change once per tile)
-      Rsrc rl = rsrc_of(cur);
+      Src rl = cur;
       int kofs = kStages - 1;
       for (int kt = 0; kt < nk - 1; ++kt) {
         if (kt == nk - kStages + 1) {
           // a real branch, not selects executed on every trip
           asm volatile("");
-          rl = rsrc_of(nxt);
+          rl = nxt;
           kofs -= nk;
         }
         trip(kt, rl, kofs, True());
@@ -763,20 +765,36 @@ int gemm_workgroups(int N, int M, int K) {
   return cus[dev] > 0 ? min(grid, cus[dev]) : grid;
 }
 
+// No stage of either operand has a K tail.
+bool k_aligned(const GemmArgs& a) {
+  return a.K % kBK == 0 && (a.w_kmod <= 0 || a.w_kmod % kBK == 0);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
-  gemm_bf16_kernel<256, 256, kEpiQKV>
-      <<<gemm_workgroups(args.N, args.M, args.K), kThreads, 0, stream>>>(args);
+  const int grid = gemm_workgroups(args.N, args.M, args.K);
+  if (k_aligned(args))
+    gemm_bf16_kernel<256, 256, kEpiQKV, true><<<grid, kThreads, 0, stream>>>(args);
+  else
+    gemm_bf16_kernel<256, 256, kEpiQKV, false><<<grid, kThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream) {
   const int grid = gemm_workgroups(args.N, args.M, args.K);
-  if (args.out_f32)
-    gemm_bf16_kernel<256, 256, kEpiPlainF32><<<grid, kThreads, 0, stream>>>(args);
-  else
-    gemm_bf16_kernel<256, 256, kEpiPlain><<<grid, kThreads, 0, stream>>>(args);
+  const bool kal = k_aligned(args);
+  if (args.out_f32) {
+    if (kal)
+      gemm_bf16_kernel<256, 256, kEpiPlainF32, true><<<grid, kThreads, 0, stream>>>(args);
+    else
+      gemm_bf16_kernel<256, 256, kEpiPlainF32, false><<<grid, kThreads, 0, stream>>>(args);
+  } else {
+    if (kal)
+      gemm_bf16_kernel<256, 256, kEpiPlain, true><<<grid, kThreads, 0, stream>>>(args);
+    else
+      gemm_bf16_kernel<256, 256, kEpiPlain, false><<<grid, kThreads, 0, stream>>>(args);
+  }
   return hipGetLastError();
 }
 
