@@ -46,6 +46,15 @@ Readings where the pages are silent (each also listed in the design doc):
    with i + r/2 and turns by ``p * theta**(-2i/r)``); entries r .. d-1 pass
    through.  r = d is reading 3.
 
+10. FP8 K/V cache ("Head Dimension" article, section 5.2: K and V are cached
+   in FP8 precision; nothing more is said): cache entries are OCP E4M3
+   codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+   finite value 448, no infinities, 0x7F/0xFF are NaN).  An entry holds
+   ``value(code) * scale`` with one scale per tensor (K, V).  Appending x
+   stores the code nearest to x / scale, ties to an even mantissa, with
+   magnitudes above 448 saturated to 448.  Attention runs on the stored
+   values.
+
 parity unpinned: reading 1 (the exact RMSNorm formula: eps placement),
 reading 3 (the RoPE pairing convention) and reading 9 (which entries a
 partial rotary turns) are not fixed by the pages.  The
@@ -250,6 +259,59 @@ def merge_heads(o: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# FP8 (E4M3) cache entries (reading 10)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Value of OCP E4M3 codes (reading 10), from the bit fields: sign s,
+    exponent e (4 bits, bias 7), mantissa m (3 bits).  e > 0: (1 + m/8) *
+    2^(e-7); e = 0: m/8 * 2^-6 (subnormal); e = 15 with m = 7: NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e > 0, (1.0 + m / 8.0) * np.exp2(e - 7.0), m / 8.0 * 2.0 ** -6)
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def quantize_e4m3(x) -> np.ndarray:
+    """Code of the E4M3 value nearest to x, ties to an even mantissa,
+    magnitudes above 448 saturated (reading 10).  Within a binade the
+    representable magnitudes are multiples of the quantum 2^(e-10) (e the
+    biased exponent, at least 1; the subnormals share the quantum 2^-9 of the
+    lowest binade), so rounding |x| to the nearest multiple of the quantum,
+    half to even, picks the nearest value; a result that reaches the next
+    power of two is that power's code.  Returns uint8 codes; x must be
+    finite."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_e4m3 needs finite inputs")
+    sign = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # biased exponent of |x| (1 for the subnormal range and zero)
+    with np.errstate(divide="ignore"):
+        e = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0))) + 7.0, 1.0)
+    e = np.clip(e, 1.0, 15.0)
+    q = np.exp2(e - 10.0)                       # quantum of the binade
+    n = np.rint(a / q)                          # half to even
+    # n counts quanta: 8..15 within a normal binade; 16 is the next binade's
+    # first value; below 8 (only in the lowest binade) a subnormal
+    n = n.astype(np.int64)
+    e = e.astype(np.int64)
+    up = n >= 16
+    e = np.where(up, e + 1, e)
+    n = np.where(up, n // 2, n)
+    normal = n >= 8
+    code = np.where(normal, (e << 3) | (n - 8), n)  # subnormal: e field 0, m = n
+    code = np.where(sign, code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
 
@@ -275,7 +337,9 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
                   rope_theta: float, rms_eps: float, qk_norm: bool = True,
                   causal: bool = True, rope: bool = True,
                   k_cache=None, v_cache=None, cache_len=None,
-                  rotary_dim: Optional[int] = None, dtype=np.float64):
+                  rotary_dim: Optional[int] = None, kv_fp8: bool = False,
+                  k_scale: float = 1.0, v_scale: float = 1.0,
+                  dtype=np.float64):
     """The layer forward (tutorial section 4, steps 1 to 7).
 
     x [B, L, hidden]; w_qkv [(Hq+2Hkv)d, hidden]; w_o [hidden, Hq*d].
@@ -289,6 +353,11 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
     updated copies (None without a cache).  ``rope=False`` drops step 3 and
     exists only to reduce the layer to textbook multi-head attention in the
     tests; ``rotary_dim`` is reading 9.
+
+    ``kv_fp8`` (reading 10): the caches hold E4M3 codes (uint8) standing for
+    code value * k_scale (resp. v_scale); the new rows are appended as the
+    codes of k / k_scale and v / v_scale, and attention runs on the stored
+    values.  The returned caches are then the updated code arrays.
     """
     x = np.asarray(x, dtype=dtype)
     w_qkv = np.asarray(w_qkv, dtype=dtype)
@@ -308,6 +377,22 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
         kk, vv = k, v
         kv_len = np.full(bsz, seq, dtype=np.int64)
         k_out = v_out = None
+    elif kv_fp8:
+        kc = np.array(k_cache, dtype=np.uint8, copy=True)
+        vc = np.array(v_cache, dtype=np.uint8, copy=True)
+        for b in range(bsz):
+            s0 = int(start[b])
+            kc[b, :, s0:s0 + seq] = quantize_e4m3(np.asarray(k[b], np.float64) / k_scale)
+            vc[b, :, s0:s0 + seq] = quantize_e4m3(np.asarray(v[b], np.float64) / v_scale)
+        kv_len = start + seq
+        # rows at or past kv_len are never read; their codes may be anything
+        kk = np.zeros(kc.shape, dtype=dtype)
+        vv = np.zeros(vc.shape, dtype=dtype)
+        for b in range(bsz):
+            n = int(kv_len[b])
+            kk[b, :, :n] = e4m3_value(kc[b, :, :n]) * k_scale
+            vv[b, :, :n] = e4m3_value(vc[b, :, :n]) * v_scale
+        k_out, v_out = kc, vc
     else:
         kk = np.array(k_cache, dtype=dtype, copy=True)
         vv = np.array(v_cache, dtype=dtype, copy=True)

@@ -504,6 +504,97 @@ def check_rows_mode():
         assert np.max(np.abs(got[i] - full[b, t])) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) cache entries (reading 10)
+# ---------------------------------------------------------------------------
+
+def check_e4m3_closed_forms():
+    """Values fixed by the format's definition (1 sign bit, 4 exponent bits
+    with bias 7, 3 mantissa bits, no infinities): 1.0, the largest finite
+    448, the smallest normal 2^-6, the smallest subnormal 2^-9, the NaN
+    codes, signed zero, 254 finite values in increasing order."""
+    v = O.e4m3_value(np.arange(256))
+    fixed = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0x08: 2.0 ** -6,
+             0x07: 7 * 2.0 ** -9, 0x01: 2.0 ** -9, 0x30: 0.5, 0xB8: -1.0, 0xFE: -448.0}
+    for c, want in fixed.items():
+        assert v[c] == want, (hex(c), v[c], want)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v[0x80:0xFF], -pos)
+
+
+def _e4m3_nearest_bruteforce(x):
+    """Nearest finite E4M3 value by searching the value table: saturate,
+    take the smallest distance, break ties toward the even code."""
+    table = O.e4m3_value(np.arange(0x7F))  # the 127 non-negative finite values
+    out = []
+    for xi in np.asarray(x, dtype=np.float64):
+        a = min(abs(xi), 448.0)
+        dist = np.abs(table - a)
+        best = np.flatnonzero(dist == dist.min())
+        c = int(best[0]) if len(best) == 1 else int([b for b in best if b % 2 == 0][0])
+        if np.signbit(xi):
+            c |= 0x80
+        out.append(c)
+    return np.array(out, dtype=np.uint8)
+
+
+def check_e4m3_quantize_bruteforce():
+    """The quantizer against a search over the value table: every finite
+    value, every midpoint between neighbours (ties), points just either side
+    of them, out-of-range magnitudes and random values over the range."""
+    v = O.e4m3_value(np.arange(0x7F))
+    mids = 0.5 * (v[:-1] + v[1:])
+    pts = np.concatenate([v, mids, np.nextafter(mids, 0.0), np.nextafter(mids, 1e9),
+                          [448.0, 460.0, 464.0, 500.0, 1e6, 2.0 ** -10, 1e-30, 0.0]])
+    rng = np.random.default_rng(40)
+    pts = np.concatenate([pts, rng.standard_normal(4000) * np.exp2(rng.integers(-12, 10, 4000))])
+    pts = np.concatenate([pts, -pts])
+    got = O.quantize_e4m3(pts)
+    want = _e4m3_nearest_bruteforce(pts)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(pts[i], int(got[i]), int(want[i])) for i in bad[:5]]
+    # the stored value is within half a quantum of the (saturated) input
+    a = np.minimum(np.abs(pts), 448.0)
+    err = np.abs(np.abs(O.e4m3_value(got)) - a)
+    q = np.exp2(np.clip(np.floor(np.log2(np.maximum(a, 2.0 ** -9))), -6, 8) - 3)
+    assert np.all(err <= q / 2 + 1e-300)
+
+
+def check_fp8_cache_layer():
+    """With kv_fp8, the appended rows are the codes of k / k_scale and
+    v / v_scale, and the output is the plain layer's run on caches holding
+    the stored values (attention reads the cache, not the fresh rows); with
+    a power-of-two scale the codes are the unscaled codes' exponents
+    shifted."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=41, b=2, l=3)
+    kw = dict(rope_theta=1e4, rms_eps=1e-6)
+    cap, c0 = 9, np.array([4, 6])
+    rng = np.random.default_rng(42)
+    kc = O.quantize_e4m3(rng.standard_normal((2, res.hkv, cap, res.d)))
+    vc = O.quantize_e4m3(rng.standard_normal((2, res.hkv, cap, res.d)))
+    ks, vs = 0.5, 3.0
+    out, kc2, vc2 = O.layer_forward(res, x, w_qkv, qn, kn, w_o, k_cache=kc, v_cache=vc,
+                                    cache_len=c0, kv_fp8=True, k_scale=ks, v_scale=vs, **kw)
+    pos = c0[:, None] + np.arange(3)[None, :]
+    q, k, v = O.qkv_normrope(res, x, w_qkv, qn, kn, pos, kw["rope_theta"], kw["rms_eps"])
+    for b in range(2):
+        s0 = int(c0[b])
+        assert np.array_equal(kc2[b, :, s0:s0 + 3], O.quantize_e4m3(k[b] / ks))
+        assert np.array_equal(vc2[b, :, s0:s0 + 3], O.quantize_e4m3(v[b] / vs))
+        assert np.array_equal(kc2[b, :, :s0], kc[b, :, :s0])
+    kvals = O.e4m3_value(kc2) * ks
+    vvals = O.e4m3_value(vc2) * vs
+    o = O.grouped_attention(q, kvals, vvals, pos, c0 + 3, res.scale, True)
+    ref = O.project(O.merge_heads(o), w_o)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # scale 1/2 on values in the normal range doubles them: exponent + 1
+    xs = np.array([0.3, -1.7, 5.0, 100.0])
+    assert np.array_equal(O.quantize_e4m3(xs / 0.5), O.quantize_e4m3(xs) + 8)
+
+
 ALL_CHECKS = [
     check_geometries, check_resolve_errors, check_param_counts, check_macs,
     check_projection_bruteforce, check_attention_bruteforce,
@@ -513,4 +604,5 @@ ALL_CHECKS = [
     check_gqa_equals_repeated_kv, check_rank_ceiling, check_one_dim_head,
     check_sum_over_heads, check_prefill_equals_decode,
     check_quotient_equals_explicit, check_rows_mode,
+    check_e4m3_closed_forms, check_e4m3_quantize_bruteforce, check_fp8_cache_layer,
 ]

@@ -14,7 +14,7 @@ from oracle import gqa_oracle as O  # noqa: E402
 _orig = {name: getattr(O, name) for name in (
     "resolve_config", "attention_param_count", "macs_per_token", "project",
     "split_heads", "rms_norm_heads", "rope_inv_freq", "apply_rope",
-    "grouped_attention", "merge_heads", "qkv_normrope")}
+    "grouped_attention", "merge_heads", "qkv_normrope", "e4m3_value", "quantize_e4m3")}
 
 
 def _k_norm_uses_q_weight(res, x, w_qkv, qn, kn, positions, theta, eps,
@@ -96,6 +96,28 @@ def _macs_score_only(res, n):
     return {"projection": m["projection"], "score_value": m["score_value"] // 2}
 
 
+def _e4m3_value_bias8(codes):
+    """FNUZ-style reading of the codes (bias 8): every value halved."""
+    return _orig["e4m3_value"](codes) / 2.0
+
+
+def _quantize_half_up(x):
+    """Rounds halves away from zero instead of to even."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    e = np.clip(np.floor(np.log2(np.where(a > 0, a, 1.0))) + 7.0, 1.0, 15.0)
+    q = np.exp2(e - 10.0)
+    y = np.sign(x) * np.floor(a / q + 0.5) * q
+    return _orig["quantize_e4m3"](y)
+
+
+def _quantize_no_saturation(x):
+    """Values above 448 become NaN codes instead of saturating."""
+    x = np.asarray(x, dtype=np.float64)
+    c = _orig["quantize_e4m3"](x)
+    return np.where(np.abs(x) > 464.0, np.where(x < 0, 0xFF, 0x7F), c).astype(np.uint8)
+
+
 MUTATIONS = {
     "k_norm_with_q_weight": ("qkv_normrope", _k_norm_uses_q_weight),
     "group_map_modulo": ("grouped_attention",
@@ -128,6 +150,9 @@ MUTATIONS = {
     "head_dim_always_derived": ("resolve_config", _resolve_always_quotient),
     "params_miss_o_proj": ("attention_param_count", _params_without_o_proj),
     "macs_miss_value_term": ("macs_per_token", _macs_score_only),
+    "e4m3_bias_8": ("e4m3_value", _e4m3_value_bias8),
+    "e4m3_ties_away_from_zero": ("quantize_e4m3", _quantize_half_up),
+    "e4m3_no_saturation": ("quantize_e4m3", _quantize_no_saturation),
 }
 
 
@@ -136,6 +161,8 @@ def _run_all_checks():
     for chk in P.ALL_CHECKS:
         try:
             chk()
+        except KeyError:  # a broken mutation, not a caught mistake
+            raise
         except Exception as e:  # AssertionError, or a crash from bad shapes
             failed.append((chk.__name__, type(e).__name__))
     return failed
