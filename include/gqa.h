@@ -98,6 +98,24 @@ typedef struct {
                             i + r/2, angle pos * theta^(-2i/r)); entries r ..
                             head_dim-1 pass through.  Must be even and at most
                             head_dim, else GQA_ERR_INVALID_ARG. */
+  int32_t kv_fp8;        /* 1: the K and V caches hold FP8 codes, one byte per
+                            element ("Head Dimension" article, section 5.2:
+                            K, V cached in FP8 precision).  Format: OCP E4M3
+                            (sign, 4 exponent bits with bias 7, 3 mantissa
+                            bits; largest finite 448; 0x7F/0xFF NaN).  An
+                            entry stands for value(code) * k_scale (K) or
+                            * v_scale (V).  Appending x (qkv_proj_normrope,
+                            gqa_layer_forward) stores the code nearest to
+                            x / scale, ties to even, magnitudes above 448
+                            saturated; attention reads the stored values.
+                            bf16 with head_dim 64 or 128 only
+                            (GQA_ERR_UNSUPPORTED_DTYPE / _HEAD_DIM), and
+                            gqa_attn_core / gqa_layer_forward
+                            only for calls whose Hq/Hkv * q_len <= 32 (decode
+                            and short chunks); else GQA_ERR_UNSUPPORTED_SHAPE.
+                            0: the caches hold `dtype` values. */
+  float k_scale;         /* kv_fp8 only: per-tensor scales, 0 = 1.0; positive */
+  float v_scale;         /* and finite, else GQA_ERR_INVALID_ARG */
 } gqa_config;
 
 /* Host only (no device needed): copy *in to *out with num_kv_heads and
@@ -124,7 +142,8 @@ size_t gqa_workspace_bytes(const gqa_config* cfg, int32_t batch, int32_t q_len,
  *            its k, v go to cache row start_pos[b] + t.
  *   q        [batch, Hq, q_len, d]   (after norm and RoPE)
  *   k_cache, v_cache [batch, Hkv, kv_capacity, d]; only the rows above are
- *            written (k after norm and RoPE, v raw).
+ *            written (k after norm and RoPE, v raw), as FP8 codes with
+ *            cfg->kv_fp8.
  * The caller guarantees start_pos[b] + q_len <= kv_capacity.
  */
 gqa_status qkv_proj_normrope(const gqa_config* cfg, int32_t batch, int32_t q_len,
@@ -139,7 +158,8 @@ gqa_status qkv_proj_normrope(const gqa_config* cfg, int32_t batch, int32_t q_len
  * Grouped attention core (tutorial section 4 step 6; GPT-NeoX issue
  * "Scaling and RoPE": scale = d^-0.5 of the effective head_dim).
  *   q        [batch, Hq, q_len, d]
- *   k_cache, v_cache [batch, Hkv, kv_capacity, d]
+ *   k_cache, v_cache [batch, Hkv, kv_capacity, d] (FP8 codes with
+ *            cfg->kv_fp8)
  *   kv_len   [batch] int32 device array of valid key rows, or NULL for
  *            q_len.  Query i of sequence b sits at position
  *            kv_len[b] - q_len + i (bottom-right alignment) and, when

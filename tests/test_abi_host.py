@@ -82,6 +82,12 @@ def test_resolve_explicit_and_quotient():
     (dict(rotary_dim=130), "GQA_ERR_INVALID_ARG"),
     (dict(rope_theta=0.0), "GQA_ERR_INVALID_ARG"),
     (dict(rms_eps=-1.0), "GQA_ERR_INVALID_ARG"),
+    # FP8 caches: bf16 only, head_dim 64 or 128, positive finite scales
+    (dict(kv_fp8=True, dtype="f32"), "GQA_ERR_UNSUPPORTED_DTYPE"),
+    (dict(kv_fp8=True, head_dim=256), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(kv_fp8=True, head_dim=80), "GQA_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(kv_fp8=True, k_scale=-1.0), "GQA_ERR_INVALID_ARG"),
+    (dict(kv_fp8=True, v_scale=float("inf")), "GQA_ERR_INVALID_ARG"),
 ])
 def test_resolve_rejects(kw, name):
     _lib_or_skip()
@@ -89,6 +95,32 @@ def test_resolve_rejects(kw, name):
         T.gqa_resolve(cfg(**kw))
     assert e.value.name == name
     assert T.lib().gqa_last_error().decode()
+
+
+def test_resolve_fp8_cache_scales():
+    _lib_or_skip()
+    r = T.gqa_resolve(cfg(kv_fp8=True, k_scale=0.0, v_scale=0.0))
+    assert (r["kv_fp8"], r["k_scale"], r["v_scale"]) == (1, 1.0, 1.0)   # 0 means 1
+    r = T.gqa_resolve(cfg(kv_fp8=True, k_scale=0.25, v_scale=3.0, head_dim=64))
+    assert (r["k_scale"], r["v_scale"], r["head_dim"]) == (0.25, 3.0, 64)
+    cc = cfg().c()
+    cc.kv_fp8 = 2
+    out = T._CConfig()
+    assert T.STATUS_NAMES[T.lib().gqa_resolve(ctypes.byref(cc), ctypes.byref(out))] == \
+        "GQA_ERR_INVALID_ARG"
+
+
+def test_fp8_cache_rejects_prefill_attention_before_launch():
+    """An FP8 cache is read by the split-KV decode kernel only: attention
+    calls whose group * q_len exceeds 32 are rejected on the host."""
+    _lib_or_skip()
+    L = T.lib()
+    c = cfg(kv_fp8=True)  # group 2: q_len up to 16
+    assert T.STATUS_NAMES[_raw_call_layer(c, 2, 17, 64)] == "GQA_ERR_UNSUPPORTED_SHAPE"
+    cc = c.c()
+    st = L.gqa_attn_core(ctypes.byref(cc), 2, 17, 1, 1, 1, None, 64, 1, 1, 1 << 40, None)
+    assert T.STATUS_NAMES[st] == "GQA_ERR_UNSUPPORTED_SHAPE"
+    assert "decode" in L.gqa_last_error().decode()
 
 
 def test_unsupported_head_dim_message_names_the_dimension():

@@ -48,7 +48,9 @@ class _CConfig(ctypes.Structure):
                 ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("qk_norm", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_f32", ctypes.c_int32),
-                ("o_split", ctypes.c_int32), ("rotary_dim", ctypes.c_int32)]
+                ("o_split", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
+                ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 @dataclass(frozen=True)
@@ -67,13 +69,17 @@ class GQAConfig:
     out_f32: bool = False   # o_proj output in fp32 (the accumulator) instead of dtype
     o_split: bool = False   # layer forward: attention output as a bf16 hi + lo pair
     rotary_dim: Optional[int] = None  # partial rotary width; None = head_dim
+    kv_fp8: bool = False    # K/V caches hold FP8 (E4M3) codes as torch.uint8
+    k_scale: float = 1.0    # kv_fp8: an entry stands for value(code) * scale
+    v_scale: float = 1.0
 
     def c(self) -> _CConfig:
         return _CConfig(self.hidden_size, self.num_heads, self.num_kv_heads or 0,
                         self.head_dim or 0, float(self.rope_theta), float(self.rms_eps),
                         int(bool(self.qk_norm)), int(bool(self.causal)),
                         GQA_BF16 if self.dtype == "bf16" else GQA_F32, int(bool(self.out_f32)),
-                        int(bool(self.o_split)), int(self.rotary_dim or 0))
+                        int(bool(self.o_split)), int(self.rotary_dim or 0),
+                        int(bool(self.kv_fp8)), float(self.k_scale), float(self.v_scale))
 
 
 _lib = None
@@ -140,6 +146,12 @@ def _dt(cfg: GQAConfig):
     return t.bfloat16 if cfg.dtype == "bf16" else t.float32
 
 
+def _cache_dt(cfg: GQAConfig):
+    """Element type of the K/V caches: FP8 codes are stored as uint8."""
+    t = _torch()
+    return t.uint8 if cfg.kv_fp8 else _dt(cfg)
+
+
 def _out_dt(cfg: GQAConfig):
     t = _torch()
     return t.float32 if cfg.out_f32 else _dt(cfg)
@@ -201,12 +213,13 @@ def qkv_proj_normrope(cfg: GQAConfig, x, w_qkv, q_norm_w=None, k_norm_w=None, *,
     if cfg.qk_norm:
         _need(q_norm_w, "q_norm_w", dt, (d,))
         _need(k_norm_w, "k_norm_w", dt, (d,))
+    cdt = _cache_dt(cfg)
     if k_cache is None:
-        k_cache = torch.zeros((B, hkv, L, d), dtype=dt, device=x.device)
-        v_cache = torch.zeros((B, hkv, L, d), dtype=dt, device=x.device)
+        k_cache = torch.zeros((B, hkv, L, d), dtype=cdt, device=x.device)
+        v_cache = torch.zeros((B, hkv, L, d), dtype=cdt, device=x.device)
     cap = k_cache.shape[2]
-    _need(k_cache, "k_cache", dt, (B, hkv, cap, d))
-    _need(v_cache, "v_cache", dt, (B, hkv, cap, d))
+    _need(k_cache, "k_cache", cdt, (B, hkv, cap, d))
+    _need(v_cache, "v_cache", cdt, (B, hkv, cap, d))
     if q is None:
         q = torch.empty((B, cfg.num_heads, L, d), dtype=dt, device=x.device)
     _need(q, "q", dt, (B, cfg.num_heads, L, d))
@@ -229,8 +242,8 @@ def gqa_attn_core(cfg: GQAConfig, q, k_cache, v_cache, *, kv_len=None, o=None, s
     B, Hq, Lq, _ = q.shape
     _need(q, "q", dt, (B, cfg.num_heads, Lq, d))
     cap = k_cache.shape[2]
-    _need(k_cache, "k_cache", dt, (B, hkv, cap, d))
-    _need(v_cache, "v_cache", dt, (B, hkv, cap, d))
+    _need(k_cache, "k_cache", _cache_dt(cfg), (B, hkv, cap, d))
+    _need(v_cache, "v_cache", _cache_dt(cfg), (B, hkv, cap, d))
     if o is None:
         o = torch.empty((B, Lq, Hq * d), dtype=dt, device=q.device)
     _need(o, "o", dt, (B, Lq, Hq * d))
@@ -289,12 +302,13 @@ def gqa_layer_forward(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *, k_ca
     if cfg.qk_norm:
         _need(q_norm_w, "q_norm_w", dt, (d,))
         _need(k_norm_w, "k_norm_w", dt, (d,))
+    cdt = _cache_dt(cfg)
     if k_cache is None:
-        k_cache = torch.empty((B, hkv, L, d), dtype=dt, device=x.device)
-        v_cache = torch.empty((B, hkv, L, d), dtype=dt, device=x.device)
+        k_cache = torch.empty((B, hkv, L, d), dtype=cdt, device=x.device)
+        v_cache = torch.empty((B, hkv, L, d), dtype=cdt, device=x.device)
     cap = k_cache.shape[2]
-    _need(k_cache, "k_cache", dt, (B, hkv, cap, d))
-    _need(v_cache, "v_cache", dt, (B, hkv, cap, d))
+    _need(k_cache, "k_cache", cdt, (B, hkv, cap, d))
+    _need(v_cache, "v_cache", cdt, (B, hkv, cap, d))
     cl = _i32(cache_len, "cache_len", B)
     if out is None:
         out = torch.empty((B, L, H), dtype=_out_dt(cfg), device=x.device)

@@ -520,6 +520,145 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
     }
 }
 
+// FP8 (E4M3) caches: the decode kernel above with K and V tiles staged
+// through registers.  A tile's codes (KD bytes per key) arrive by 16-byte
+// register loads issued during the first QK MFMAs of the previous tile;
+// after that tile the codes are widened to bf16 (exact: every E4M3 value is
+// a bf16 value) and written into the other LDS buffer in the layout the
+// DMA path produces, so the same attend_tile runs on them.  The scales are
+// applied outside the products: the K scale is part of the score scale,
+// the V scale is applied when the splits are merged.
+template <int KD, int TK>
+struct Fp8TileLoads {
+  static constexpr int P = KD / 16;     // 16-byte pieces of one key's codes
+  static constexpr int RPL = 64 / P;    // keys per load instruction
+  static constexpr int NI = TK / RPL;   // load instructions per tile and operand
+  static_assert(NI * RPL == TK, "a tile splits into whole load instructions");
+  __amdgpu_buffer_rsrc_t rk, rv;        // the tile's codes, from its first key
+  unsigned off[NI];                     // per-lane byte offsets within a tile
+  bool live;
+  mutable u32x4 kc[NI], vc[NI];         // codes in flight
+  __device__ __forceinline__ void k(int j) const {
+    if (live) kc[j] = buf_ld16(rk, off[j]);
+  }
+  __device__ __forceinline__ void v(int j) const {
+    if (live) vc[j] = buf_ld16(rv, off[j]);
+  }
+  __device__ __forceinline__ void all() const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) k(j);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) v(j);
+  }
+};
+
+// 8 E4M3 codes (two dwords) -> 8 bf16 (one 16-byte LDS chunk)
+GQA_DEV unsigned widen_e4m3_lo(unsigned w) {  // codes in bytes 0, 1
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+GQA_DEV unsigned widen_e4m3_hi(unsigned w) {  // codes in bytes 2, 3
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+GQA_DEV u32x4 widen_e4m3(unsigned lo, unsigned hi) {
+  return u32x4{widen_e4m3_lo(lo), widen_e4m3_hi(lo), widen_e4m3_lo(hi), widen_e4m3_hi(hi)};
+}
+
+template <int KD>
+__global__ __launch_bounds__(kDecodeNT) void attn_decode_fp8_kernel(AttnArgs a) {
+  using G = Geo<KD>;
+  constexpr int TK = kDecodeTK, NT = kDecodeNT;
+  using L8 = Fp8TileLoads<KD, TK>;
+  __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
+  __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
+  lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int rows = a.G * a.Lq;
+  const bool row_valid = l32 < rows;
+  const int head_local = row_valid ? l32 / a.Lq : 0;
+  const int tq = row_valid ? l32 - head_local * a.Lq : 0;
+  const int hq = kvh * a.G + head_local;
+
+  const int kvl = kv_len_of(a, b);
+  const int off = kvl - a.Lq;
+  const int ks = split * a.chunk;
+  int ke = min(ks + a.chunk, kvl);
+  if (a.causal) ke = min(ke, off + a.Lq);
+  const int n_tiles = ke > ks ? (ke - ks + TK - 1) / TK : 0;
+  const int kend_row = row_valid ? min(ke, a.causal ? min(kvl, off + tq + 1) : kvl) : 0;
+  const int kmin = min(ke, a.causal ? min(kvl, off + 1) : kvl);
+
+  u32x4 qf[G::NC];
+  load_q<KD>(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + tq) * KD, row_valid, hh);
+
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * KD;  // one byte per element
+  const unsigned char* kb = a.k8 + kv_base;
+  const unsigned char* vb = a.v8 + kv_base;
+  LaneOffsets<KD> lo;
+  lane_offsets<KD>(lo, lane);
+
+  // lane -> (key row_in + RPL i, piece p) of a tile: 16 codes, features
+  // 16 p .. 16 p + 15 = bf16 chunks 2 p and 2 p + 1
+  const int row_in = lane / L8::P, piece = lane % L8::P;
+  L8 ld;
+#pragma unroll
+  for (int i = 0; i < L8::NI; ++i) ld.off[i] = (unsigned)((row_in + L8::RPL * i) * KD + 16 * piece);
+  auto aim = [&](int k0, bool live) {  // the loads of the tile starting at key k0
+    const long long bytes = live ? (long long)(ke - k0) * KD : 0;
+    ld.rk = make_rsrc(kb + (size_t)k0 * KD, bytes);
+    ld.rv = make_rsrc(vb + (size_t)k0 * KD, bytes);
+    ld.live = live;
+  };
+  auto widen_into = [&](lds_u32x4* dk, lds_u32x4* dv) {
+#pragma unroll
+    for (int i = 0; i < L8::NI; ++i) {
+      const int row = row_in + L8::RPL * i;
+      dk[G::kslot(row, 2 * piece)] = widen_e4m3(ld.kc[i].x, ld.kc[i].y);
+      dk[G::kslot(row, 2 * piece + 1)] = widen_e4m3(ld.kc[i].z, ld.kc[i].w);
+      dv[G::vslot(row, 2 * piece)] = widen_e4m3(ld.vc[i].x, ld.vc[i].y);
+      dv[G::vslot(row, 2 * piece + 1)] = widen_e4m3(ld.vc[i].z, ld.vc[i].w);
+    }
+  };
+
+  RowState<KD> st;
+  init_state<KD>(st);
+  aim(ks, n_tiles > 0);
+  ld.all();
+  widen_into(sk[0], sv[0]);
+  __syncthreads();
+  auto step = [&](auto bufc, int it) {
+    constexpr int B = decltype(bufc)::value;
+    const int key0 = ks + it * TK;
+    const bool more = it + 1 < n_tiles;
+    aim(key0 + TK, more);
+    const bool masked = key0 + TK > kmin;
+    attend_tile<KD, TK, L8::NI>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2,
+                                hh, ld);
+    if (more) widen_into(sk[B ^ 1], sv[B ^ 1]);
+    __syncthreads();
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  const float lt = sum_xor32(st.l);
+  if (!row_valid) return;  // only the group's real rows are merged
+  const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * 32 + l32;
+  if (hh == 0) a.part_ml[pidx] = make_float2(st.m, lt);
+  float* po = a.part_o + pidx * KD;
+#pragma unroll
+  for (int d = 0; d < G::NB; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      floatx4 w = {st.o[d][4 * j + 0], st.o[d][4 * j + 1], st.o[d][4 * j + 2], st.o[d][4 * j + 3]};
+      *reinterpret_cast<floatx4*>(po + 32 * d + 8 * j + 4 * hh) = w;
+    }
+}
+
 // Merge of the decode splits: one workgroup per (query row, KV head,
 // sequence); lane s first holds split s for the maxima and sums, then lane
 // e accumulates features e, e + 64, ... of every split's partial output.
@@ -567,7 +706,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int x = 32; x > 0; x >>= 1) lsum += __shfl_xor(lsum, x, 64);
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
   const size_t width = (size_t)a.Hq * KD;
   bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
 #pragma unroll
@@ -591,7 +730,17 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
 template <int KD>
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(a.n_splits, a.Hkv, a.B);
-  attn_decode_kernel<KD><<<grid, kDecodeNT, 0, stream>>>(a);
+  if constexpr (KD <= 128) {
+    if (a.k8)
+      attn_decode_fp8_kernel<KD><<<grid, kDecodeNT, 0, stream>>>(a);
+    else
+      attn_decode_kernel<KD><<<grid, kDecodeNT, 0, stream>>>(a);
+  } else {
+    // FP8 caches: head_dim 64 and 128 (the host rejects 256: its staged
+    // codes would not fit the registers next to the kernel's own)
+    if (a.k8) return hipErrorInvalidValue;
+    attn_decode_kernel<KD><<<grid, kDecodeNT, 0, stream>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2(a.G * a.Lq, a.Hkv, a.B);

@@ -108,6 +108,21 @@ __global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
     }
   }
   if (!act) return;
+  if (kind != 0 && a.kv_fp8) {
+    // E4M3 code of x / scale: the conversion rounds to nearest even but
+    // turns magnitudes past the largest finite value into NaN, so they are
+    // clamped to 448 first
+    if (pos < 0 || pos >= a.cap) return;
+    const float inv = kind == 1 ? a.inv_k_scale : a.inv_v_scale;
+    const float y1 = fminf(fmaxf(x1 * inv, -448.0f), 448.0f);
+    const float y2 = fminf(fmaxf(x2 * inv, -448.0f), 448.0f);
+    const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y1, y2, 0, false);
+    unsigned char* dst = static_cast<unsigned char*>(kind == 1 ? a.k_cache : a.v_cache) +
+                         (((size_t)b * a.Hkv + h) * a.cap + pos) * d;
+    dst[j] = (unsigned char)(codes & 0xff);
+    dst[j + half] = (unsigned char)((codes >> 8) & 0xff);
+    return;
+  }
   T* dst;
   if (kind == 0) {
     dst = static_cast<T*>(a.q) + (((size_t)b * a.Hq + h) * a.L + tok) * d;

@@ -44,6 +44,8 @@ struct Shape {
   bool fused;    // mfma, and the rotary width (128 or 64) fits the fused QKV epilogue
   bool out_f32;  // o_proj output in fp32
   bool o_split;  // layer forward: attention output as a bf16 hi + lo pair
+  bool kv_fp8;   // caches hold E4M3 codes
+  float k_scale, v_scale;
 };
 
 gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
@@ -91,6 +93,20 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
       return fail(GQA_ERR_UNSUPPORTED_SHAPE,
                   "o_split needs num_heads*head_dim to be a multiple of 32");
   }
+  if (c.kv_fp8 != 0 && c.kv_fp8 != 1)
+    return fail(GQA_ERR_INVALID_ARG, "kv_fp8 must be 0 or 1");
+  if (c.kv_fp8) {
+    if (c.dtype != GQA_BF16)
+      return fail(GQA_ERR_UNSUPPORTED_DTYPE, "kv_fp8 needs dtype GQA_BF16");
+    if (c.head_dim != 64 && c.head_dim != 128)
+      return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
+                  "Unsupported head_dim %d with kv_fp8: the FP8 cache is read by the "
+                  "matrix-core decode kernel for head_dim 64 and 128", c.head_dim);
+    if (c.k_scale == 0.f) c.k_scale = 1.f;
+    if (c.v_scale == 0.f) c.v_scale = 1.f;
+    if (!(c.k_scale > 0.f) || !isfinite(c.k_scale) || !(c.v_scale > 0.f) || !isfinite(c.v_scale))
+      return fail(GQA_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+  }
   if (!(c.rope_theta > 0.f) || !isfinite(c.rope_theta))
     return fail(GQA_ERR_INVALID_ARG, "rope_theta must be positive and finite");
   if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
@@ -116,6 +132,9 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->fused = sh->bf16 && c.head_dim == 128 && (c.rotary_dim == 128 || c.rotary_dim == 64);
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
     sh->o_split = c.o_split && c.dtype == GQA_BF16;
+    sh->kv_fp8 = c.kv_fp8 != 0;
+    sh->k_scale = c.kv_fp8 ? c.k_scale : 1.f;
+    sh->v_scale = c.kv_fp8 ? c.v_scale : 1.f;
   }
   return GQA_OK;
 }
@@ -146,9 +165,24 @@ void decode_split(const Shape& s, int batch, int cap, int* n_splits, int* chunk)
 constexpr long long kSkinnyMaxTokens = 256;
 bool use_skinny(const Shape& s, long long tokens) { return s.bf16 && tokens <= kSkinnyMaxTokens; }
 
+// The QKV GEMM's own epilogue (norm, RoPE, scatter) writes bf16 caches only;
+// FP8 caches take the projection + norm/RoPE pass.
+bool use_fused_qkv(const Shape& s, long long tokens) {
+  return s.fused && !use_skinny(s, tokens) && !s.kv_fp8;
+}
+
+// FP8 caches are read by the split-KV decode kernel only.
+gqa_status check_fp8_attn(const Shape& s, int q_len) {
+  if (s.kv_fp8 && !use_decode(s, q_len))
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE,
+                "kv_fp8: attention over an FP8 cache needs (num_heads/num_kv_heads) * q_len "
+                "<= 32 (decode); got %d * %d", s.G, q_len);
+  return GQA_OK;
+}
+
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
-  if (s.fused && !use_skinny(s, (long long)T))
+  if (use_fused_qkv(s, (long long)T))
     return align_up(T * (s.rot / 2) * sizeof(float) * 2);  // rope table, T rows max
   return align_up(T * (size_t)s.n_qkv * sizeof(float));   // fp32 projection output
 }
@@ -188,7 +222,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
                    const void* w_qkv, const void* qn, const void* kn, const int32_t* start_pos,
                    void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st) {
   const int T = batch * q_len;
-  if (s.fused && !use_skinny(s, T)) {
+  if (use_fused_qkv(s, T)) {
     float2* table = reinterpret_cast<float2*>(ws);
     const int rows = start_pos ? T : q_len;
     gqa_status r = check_launch(
@@ -254,6 +288,9 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   n.cap = cap;
   n.qk_norm = c.qk_norm;
   n.bf16 = s.bf16;
+  n.kv_fp8 = s.kv_fp8;
+  n.inv_k_scale = 1.0f / s.k_scale;
+  n.inv_v_scale = 1.0f / s.v_scale;
   n.eps = c.rms_eps;
   n.theta = (double)c.rope_theta;
   return check_launch(gqa::launch_normrope(n, st), "norm + rope");
@@ -299,7 +336,16 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   a.Lq = q_len;
   a.cap = cap;
   a.causal = c.causal;
-  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  // with FP8 caches the K scale multiplies every score and the V scale the
+  // output: the kernels work on the codes' values
+  a.scale_log2 = (float)(scale * 1.4426950408889634 * (double)s.k_scale);
+  a.v_scale = s.v_scale;
+  if (s.kv_fp8) {
+    a.k = nullptr;
+    a.v = nullptr;
+    a.k8 = static_cast<const unsigned char*>(kc);
+    a.v8 = static_cast<const unsigned char*>(vc);
+  }
   if (use_decode(s, q_len)) {
     decode_split(s, batch, cap, &a.n_splits, &a.chunk);
     const size_t parts = (size_t)batch * s.Hkv * a.n_splits * 32;
@@ -398,6 +444,7 @@ gqa_status gqa_attn_core(const gqa_config* cfg, int32_t batch, int32_t q_len, co
   if (batch == 0 || q_len == 0) return ok();
   if (!q || !k_cache || !v_cache || !o)
     return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-null");
+  if ((r = check_fp8_attn(s, q_len)) != GQA_OK) return r;
   const size_t need = ws_attn(s, batch, q_len, kv_capacity);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
@@ -436,6 +483,7 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
     return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, w_o, k_cache, v_cache and out must be non-null");
   if (c.qk_norm && (!q_norm_w || !k_norm_w))
     return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
+  if ((r = check_fp8_attn(s, q_len)) != GQA_OK) return r;
   const size_t need = ws_layer(s, batch, q_len, kv_capacity);
   if (!workspace || workspace_bytes < need)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,

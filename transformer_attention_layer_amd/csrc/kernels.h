@@ -37,6 +37,9 @@ struct AttnArgs {
   const __bf16* q;  // [B, Hq, Lq, d]
   const __bf16* k;  // [B, Hkv, cap, d]
   const __bf16* v;
+  const unsigned char* k8;  // FP8 (E4M3) caches [B, Hkv, cap, d] (decode only), else null
+  const unsigned char* v8;
+  float v_scale;            // multiplies the output (FP8 V scale; 1 otherwise)
   __bf16* o;        // [B, Lq, Hq * d], or [B, Lq, 2, Hq * d] (hi | lo) when o_split
   int o_split;
   const int* kv_base;  // kv_len[b] = (kv_base ? kv_base[b] : 0) + kv_add, clamped to [0, cap]
@@ -74,6 +77,8 @@ struct NormRopeArgs {
   const int* start_pos;
   void* q; void* k_cache; void* v_cache;
   int B, L, Hq, Hkv, d, rot, cap, qk_norm, bf16;
+  int kv_fp8;                       // caches take E4M3 codes of x * inv_scale
+  float inv_k_scale, inv_v_scale;
   float eps; double theta;
 };
 hipError_t launch_normrope(const NormRopeArgs& args, hipStream_t stream);
