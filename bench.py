@@ -54,7 +54,7 @@ def flops_of(w):
 def kv_bytes_of(w):
     """Bytes of K and V a decode step must read: every valid row of the
     cache including the appended one, for every sequence and KV head."""
-    el = 2 if w.dtype == "bf16" else 4
+    el = 1 if w.kv_fp8 else 2 if w.dtype == "bf16" else 4
     return 2.0 * w.batch * w.hkv * (w.cache_len + w.seq) * w.d * el
 
 
@@ -167,7 +167,7 @@ def bench_decode(w, steps, warmup, torch, T, GI):
     cfg = T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
                       head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
                       qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True,
-                      o_split=w.o_split)
+                      o_split=w.o_split, kv_fp8=w.kv_fp8)
     h = GI.device_layer_inputs(w)
     c = GI.device_cache(w)
     cl = torch.full((w.batch,), w.cache_len, dtype=torch.int32, device="cuda")
@@ -304,7 +304,8 @@ def main():
             "num_heads": w.hq, "num_kv_heads": w.hkv, "head_dim": w.d,
             "head_dim_explicit": w.head_dim is not None, "qk_norm": w.qk_norm,
             "rope_theta": w.rope_theta, "causal": w.causal, "cache_len": w.cache_len,
-            "out_dtype": "f32", "o_split": w.o_split}
+            "out_dtype": "f32", "o_split": w.o_split,
+            "kv_cache": "fp8_e4m3" if w.kv_fp8 else w.dtype}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     if w.cache_len == 0:
         ms, part_ms = bench_prefill(w, args.steps, args.warmup, torch, T, GI)
@@ -338,7 +339,8 @@ def main():
 
     if w.cache_len == 0 and not args.no_decode:
         dec = {}
-        for name in ("decode_h2560_gqa", "decode_h2560_mqa"):
+        for name in ("decode_h2560_gqa", "decode_h2560_mqa", "decode_h2560_gqa_fp8",
+                     "decode_h2560_mqa_fp8"):
             wd = GI.WORKLOADS[name]
             dms, attn_ms = bench_decode(wd, args.steps, args.warmup, torch, T, GI)
             gbs = kv_bytes_of(wd) / (attn_ms * 1e-3) / 1e9

@@ -43,6 +43,7 @@ class Workload:
     # the attention output alone moves outputs by ~1e-2.
     o_split: bool = False
     rotary_dim: Optional[int] = None  # partial rotary width; None = head_dim
+    kv_fp8: bool = False      # K/V caches hold FP8 (E4M3) codes, scales 1
 
     @property
     def d(self) -> int:
@@ -74,6 +75,13 @@ WORKLOADS = {
     "decode_h2560_mqa": Workload("decode_h2560_mqa", 64, 1, 2560, 32, 1, 128,
                                  True, 1e6, 1e-6, "bf16", 4, cache_len=32768,
                                  o_split=True),
+    # The decode workloads with FP8 (E4M3) K/V caches: half the cache bytes.
+    "decode_h2560_gqa_fp8": Workload("decode_h2560_gqa_fp8", 64, 1, 2560, 32, 8, 128, True,
+                                     1e6, 1e-6, "bf16", 4, cache_len=32768, o_split=True,
+                                     kv_fp8=True),
+    "decode_h2560_mqa_fp8": Workload("decode_h2560_mqa_fp8", 64, 1, 2560, 32, 1, 128, True,
+                                     1e6, 1e-6, "bf16", 4, cache_len=32768, o_split=True,
+                                     kv_fp8=True),
     # The explicit head_dim the pages cite for Gemma 3 (hidden 640, four
     # query heads, head_dim 256 rather than 160); one KV head.  Runs the
     # matrix-core attention, with the projection GEMM followed by a separate
@@ -170,20 +178,21 @@ def device_layer_inputs(w: Workload, device="cuda", seed: Optional[int] = None):
 
 def device_cache(w: Workload, device="cuda", seed: Optional[int] = None):
     """K/V caches [B, Hkv, capacity, d] drawn on the device: rows below
-    ``cache_len`` ~ N(0, 1), the rest zero."""
+    ``cache_len`` ~ N(0, 1), the rest zero.  With ``kv_fp8`` the caches are
+    uint8 E4M3 codes of those values (torch's float8_e4m3fn conversion)."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed((w.seed if seed is None else seed) + 1000)
-    dt = torch_dtype(w)
+    dt = torch.float8_e4m3fn if w.kv_fp8 else torch_dtype(w)
     shape = (w.batch, w.hkv, w.kv_capacity, w.d)
     out = {}
     for name in ("k_cache", "v_cache"):
-        t = torch.zeros(shape, device=device, dtype=dt)
+        t = torch.zeros(shape, device=device, dtype=torch.uint8 if w.kv_fp8 else dt)
         if w.cache_len:
             # fill one sequence at a time to bound the float32 staging buffer
             for b in range(w.batch):
-                t[b, :, :w.cache_len] = torch.randn(
-                    (w.hkv, w.cache_len, w.d), generator=g, device=device,
-                    dtype=torch.float32).to(dt)
+                vals = torch.randn((w.hkv, w.cache_len, w.d), generator=g, device=device,
+                                   dtype=torch.float32).to(dt)
+                t[b, :, :w.cache_len] = vals.view(torch.uint8) if w.kv_fp8 else vals
         out[name] = t
     return out
