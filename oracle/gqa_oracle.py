@@ -54,6 +54,13 @@ Readings where the pages are silent (each also listed in the design doc):
    stores the code nearest to x / scale, ties to an even mantissa, with
    magnitudes above 448 saturated to 448.  Attention runs on the stored
    values.
+11. Backward pass (GPT-NeoX issue, "Tests and acceptance criteria": forward
+   and backward passes; "Attention head partitions ...": gradients of the
+   shared KV parameters): the pages name the gradients but print no formula.
+   They are read as the exact derivatives of this forward without a cache
+   (positions 0..L-1), taken by the chain rule through the steps in reverse;
+   a KV head's gradient sums over the query heads it serves, and the shared
+   QK-norm weights sum over every token and head.
 
 parity unpinned: reading 1 (the exact RMSNorm formula: eps placement),
 reading 3 (the RoPE pairing convention) and reading 9 (which entries a
@@ -451,3 +458,139 @@ def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
         for j, (i, _) in enumerate(items):
             out[i] = o_rows[j]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (reading 11): gradients of the layer without a cache
+# ---------------------------------------------------------------------------
+
+def project_backward(x, w, dy):
+    """Gradients of y = x @ W.T (tutorial section 4, steps 1 and 7) for the
+    upstream gradient dy: dx = dy @ W and dW = dy^T x, summed over every
+    token.  Returns (dx, dW)."""
+    dx = np.matmul(dy, w)
+    dw = np.matmul(dy.reshape(-1, dy.shape[-1]).T, x.reshape(-1, x.shape[-1]))
+    return dx, dw
+
+
+def rms_norm_heads_backward(v, w, eps, dy):
+    """Gradients of ``rms_norm_heads(v, w, eps)`` (reading 1) for dy.
+
+    With r = (mean(v*v) + eps)^(-1/2) per head row, out_j = v_j r w_j and
+    d out_j / d v_i = w_j r (delta_ij - v_i v_j r^2 / d).  Hence
+    dv_i = r (w_i dy_i - v_i r^2 mean_j(w_j dy_j v_j)), and the weight, shared
+    by all rows, gets dw_j = sum over rows of dy_j v_j r.  Returns (dv, dw)."""
+    r = 1.0 / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    wd = w * dy
+    dv = r * (wd - v * r * r * np.mean(wd * v, axis=-1, keepdims=True))
+    dw = np.sum((dy * v * r).reshape(-1, v.shape[-1]), axis=0)
+    return dv, dw
+
+
+def apply_rope_backward(g, positions, theta: float,
+                        rotary_dim: Optional[int] = None):
+    """Gradient through ``apply_rope`` (readings 3 and 9) for g [B, L, heads,
+    d].  Each pair (i, i + r/2) is turned by a rotation matrix
+    [[cos, -sin], [sin, cos]]; its transpose [[cos, sin], [-sin, cos]] carries
+    the gradient back.  Entries past the rotary width pass through."""
+    d = g.shape[-1]
+    r = d if rotary_dim is None else int(rotary_dim)
+    half = r // 2
+    ang = positions.astype(np.float64)[..., None] * rope_inv_freq(r, theta)
+    cos = np.cos(ang).astype(g.dtype)[:, :, None, :]
+    sin = np.sin(ang).astype(g.dtype)[:, :, None, :]
+    g1 = g[..., :half]
+    g2 = g[..., half:r]
+    return np.concatenate([g1 * cos + g2 * sin, g2 * cos - g1 * sin, g[..., r:]], axis=-1)
+
+
+def grouped_attention_backward(q, k, v, q_pos, kv_len, scale: float,
+                               causal: bool, do):
+    """Gradients of ``grouped_attention`` for the upstream gradient do
+    [B, Hq, Lq, d] (tutorial section 4, step 6; the group map of reading 5).
+
+    Per query head h with KV head g = h // (Hq/Hkv): s = q k^T * scale over
+    the visible keys, p = softmax(s) by rows, o = p v.  Then dv_g += p^T do,
+    dp = do v^T, and the softmax Jacobian gives ds = p * (dp - sum_j p dp)
+    row by row; dq = ds k * scale and dk_g += ds^T q * scale.  A KV head's
+    gradients sum the contributions of every query head it serves.
+    Returns (dq, dk, dv) shaped like q, k, v."""
+    bsz, hq, lq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(bsz):
+        n = int(kv_len[b])
+        key_idx = np.arange(n)
+        visible = np.ones((lq, n), dtype=bool)
+        if causal:
+            visible = key_idx[None, :] <= q_pos[b][:, None]
+        for h in range(hq):
+            g = h // group
+            s = np.matmul(q[b, h], k[b, g, :n].T) * scale
+            s = np.where(visible, s, -np.inf)
+            m = np.max(s, axis=-1, keepdims=True)
+            p = np.exp(s - m)
+            p = p / np.sum(p, axis=-1, keepdims=True)
+            dv[b, g, :n] += np.matmul(p.T, do[b, h])
+            dp = np.matmul(do[b, h], v[b, g, :n].T)
+            ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+            dq[b, h] = np.matmul(ds, k[b, g, :n]) * scale
+            dk[b, g, :n] += np.matmul(ds.T, q[b, h]) * scale
+    return dq, dk, dv
+
+
+def layer_backward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, dout, *,
+                   rope_theta: float, rms_eps: float, qk_norm: bool = True,
+                   causal: bool = True, rotary_dim: Optional[int] = None,
+                   dtype=np.float64):
+    """Gradients of ``layer_forward`` without a cache (positions 0..L-1) for
+    the upstream gradient dout [B, L, hidden] (reading 11): the chain rule
+    through the forward's steps in reverse order -- o_proj, attention, RoPE,
+    QK-norm, the fused projection.
+
+    Returns a dict with dx [B, L, hidden], dw_qkv [(Hq+2Hkv)d, hidden],
+    dq_norm_w and dk_norm_w [d] (None without QK-norm) and dw_o
+    [hidden, Hq*d]."""
+    x = np.asarray(x, dtype=dtype)
+    w_qkv = np.asarray(w_qkv, dtype=dtype)
+    w_o = np.asarray(w_o, dtype=dtype)
+    dout = np.asarray(dout, dtype=dtype)
+    bsz, seq, _ = x.shape
+    positions = np.tile(np.arange(seq, dtype=np.int64), (bsz, 1))
+    kw = {} if rotary_dim is None else {"rotary_dim": rotary_dim}
+    # forward, keeping what the backward reads
+    y = project(x, w_qkv)
+    q0, k0, v0 = split_heads(y, res)
+    qn, kn = q0, k0
+    if qk_norm:
+        qnw = np.asarray(q_norm_w, dtype=dtype)
+        knw = np.asarray(k_norm_w, dtype=dtype)
+        qn = rms_norm_heads(q0, qnw, rms_eps)
+        kn = rms_norm_heads(k0, knw, rms_eps)
+    qr = apply_rope(qn, positions, rope_theta, **kw)
+    kr = apply_rope(kn, positions, rope_theta, **kw)
+    qh, kh, vh = (qr.transpose(0, 2, 1, 3), kr.transpose(0, 2, 1, 3),
+                  v0.transpose(0, 2, 1, 3))
+    kv_len = np.full(bsz, seq, dtype=np.int64)
+    o = grouped_attention(qh, kh, vh, positions, kv_len, res.scale, causal)
+    om = merge_heads(o)
+    # backward
+    dom, dw_o = project_backward(om, w_o, dout)
+    do = dom.reshape(bsz, seq, res.hq, res.d).transpose(0, 2, 1, 3)
+    dqh, dkh, dvh = grouped_attention_backward(qh, kh, vh, positions, kv_len,
+                                               res.scale, causal, do)
+    dqn = apply_rope_backward(dqh.transpose(0, 2, 1, 3), positions, rope_theta, **kw)
+    dkn = apply_rope_backward(dkh.transpose(0, 2, 1, 3), positions, rope_theta, **kw)
+    dq_norm_w = dk_norm_w = None
+    dq0, dk0 = dqn, dkn
+    if qk_norm:
+        dq0, dq_norm_w = rms_norm_heads_backward(q0, qnw, rms_eps, dqn)
+        dk0, dk_norm_w = rms_norm_heads_backward(k0, knw, rms_eps, dkn)
+    dy = np.concatenate([dq0.reshape(bsz, seq, -1), dk0.reshape(bsz, seq, -1),
+                         dvh.transpose(0, 2, 1, 3).reshape(bsz, seq, -1)], axis=-1)
+    dx, dw_qkv = project_backward(x, w_qkv, dy)
+    return {"dx": dx, "dw_qkv": dw_qkv, "dq_norm_w": dq_norm_w,
+            "dk_norm_w": dk_norm_w, "dw_o": dw_o}

@@ -595,6 +595,158 @@ def check_fp8_cache_layer():
     assert np.array_equal(O.quantize_e4m3(xs / 0.5), O.quantize_e4m3(xs) + 8)
 
 
+# ---------------------------------------------------------------------------
+# Backward pass (reading 11)
+# ---------------------------------------------------------------------------
+
+def _layer_loss(res, x, w_qkv, qn, kn, w_o, dout, **kw):
+    out, _, _ = O.layer_forward(res, x, w_qkv, qn, kn, w_o, **kw)
+    return float(np.sum(out * dout))
+
+
+BWD_CASES = [
+    # (seed, b, l, hidden, hq, hkv, d, qk_norm, causal, rotary_dim)
+    (20, 2, 5, 12, 4, 2, 6, True, True, None),     # GQA, Hq*d != hidden
+    (21, 1, 6, 16, 4, 1, 8, True, False, 4),       # MQA, no mask, partial rotary
+    (22, 2, 4, 8, 2, 2, 4, False, True, None),     # MHA without QK-norm
+]
+
+
+def check_layer_backward_finite_differences():
+    """Every gradient of the layer against central differences of
+    sum(dout * layer_forward(...)) in float64, on sampled entries of each
+    input and parameter (step 1e-6: truncation and rounding stay near 1e-9
+    for these O(1) values).  The difference quotient uses only the forward,
+    so a mistake anywhere in the backward shows."""
+    for seed, b, l, hid, hq, hkv, d, qkn, causal, rot in BWD_CASES:
+        rng = np.random.default_rng(seed)
+        res, x, w_qkv, qn, kn, w_o = _layer_case(seed=seed, b=b, l=l, hidden=hid,
+                                                 hq=hq, hkv=hkv, d=d)
+        dout = _rand(rng, b, l, hid)
+        kw = dict(rope_theta=100.0, rms_eps=1e-6, qk_norm=qkn, causal=causal,
+                  rotary_dim=rot)
+        g = O.layer_backward(res, x, w_qkv, qn if qkn else None, kn if qkn else None,
+                             w_o, dout, **kw)
+        args = {"x": x, "w_qkv": w_qkv, "qn": qn, "kn": kn, "w_o": w_o}
+        keys = {"x": "dx", "w_qkv": "dw_qkv", "qn": "dq_norm_w", "kn": "dk_norm_w",
+                "w_o": "dw_o"}
+        h = 1e-6
+        for name, key in keys.items():
+            if not qkn and name in ("qn", "kn"):
+                assert g[key] is None
+                continue
+            arr = args[name]
+            assert g[key].shape == arr.shape, (key, g[key].shape, arr.shape)
+            flat = rng.choice(arr.size, size=min(arr.size, 24), replace=False)
+            for fi in flat:
+                idx = np.unravel_index(fi, arr.shape)
+                vals = []
+                for sgn in (1.0, -1.0):
+                    a = arr.copy()
+                    a[idx] += sgn * h
+                    call = dict(args, **{name: a})
+                    vals.append(_layer_loss(res, call["x"], call["w_qkv"],
+                                            call["qn"] if qkn else None,
+                                            call["kn"] if qkn else None,
+                                            call["w_o"], dout, **kw))
+                fd = (vals[0] - vals[1]) / (2 * h)
+                assert abs(fd - g[key][idx]) < 1e-6 * max(1.0, abs(fd)), \
+                    (seed, key, idx, fd, g[key][idx])
+
+
+def check_layer_backward_vs_torch_autograd():
+    """All five gradients against torch autograd through an independent
+    float64 composition of library routines (F.linear, F.rms_norm, RoPE as
+    complex multiplication, SDPA with enable_gqa), GQA with a causal mask."""
+    res, x, w_qkv, qn, kn, w_o = _layer_case(seed=23, b=2, l=7, hidden=24, hq=6, hkv=2, d=8)
+    rng = np.random.default_rng(24)
+    dout = _rand(rng, 2, 7, 24)
+    theta, eps = 1e3, 1e-6
+    g = O.layer_backward(res, x, w_qkv, qn, kn, w_o, dout, rope_theta=theta, rms_eps=eps)
+    t = {n: torch.from_numpy(a.copy()).requires_grad_(True)
+         for n, a in (("x", x), ("w_qkv", w_qkv), ("qn", qn), ("kn", kn), ("w_o", w_o))}
+    b, l, _ = x.shape
+    y = F.linear(t["x"], t["w_qkv"])
+    q = y[..., :res.q_width].reshape(b, l, res.hq, res.d)
+    k = y[..., res.q_width:res.q_width + res.kv_width].reshape(b, l, res.hkv, res.d)
+    v = y[..., res.q_width + res.kv_width:].reshape(b, l, res.hkv, res.d)
+    q = F.rms_norm(q, (res.d,), t["qn"], eps)
+    k = F.rms_norm(k, (res.d,), t["kn"], eps)
+    half = res.d // 2
+    i = torch.arange(half, dtype=torch.float64)
+    ang = torch.arange(l, dtype=torch.float64)[:, None] * \
+        torch.pow(torch.tensor(theta, dtype=torch.float64), -2.0 * i / res.d)
+    rot = torch.polar(torch.ones_like(ang), ang)[None, :, None, :]
+
+    def rope(u):
+        z = torch.complex(u[..., :half], u[..., half:]) * rot
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    o = F.scaled_dot_product_attention(rope(q).transpose(1, 2), rope(k).transpose(1, 2),
+                                       v.transpose(1, 2), is_causal=True, enable_gqa=True)
+    out = F.linear(o.transpose(1, 2).reshape(b, l, res.q_width), t["w_o"])
+    out.backward(torch.from_numpy(dout))
+    for name, key in (("x", "dx"), ("w_qkv", "dw_qkv"), ("qn", "dq_norm_w"),
+                      ("kn", "dk_norm_w"), ("w_o", "dw_o")):
+        ref = t[name].grad.numpy()
+        assert np.max(np.abs(g[key] - ref)) < 1e-10 * max(1.0, np.abs(ref).max()), key
+
+
+def check_attention_backward_group_sum():
+    """The gradient of a shared KV head is the sum, over the query heads it
+    serves, of the gradients of the repeated-KV multi-head layer, and the
+    query gradients are those of that layer (per-head-distinguishable
+    values, causal, a ragged key range)."""
+    rng = np.random.default_rng(25)
+    hq, hkv, L, d = 6, 2, 8, 4
+    q = _rand(rng, 2, hq, L, d)
+    k = _rand(rng, 2, hkv, L, d) + np.arange(hkv)[None, :, None, None]
+    v = _rand(rng, 2, hkv, L, d) + 3.0 * np.arange(hkv)[None, :, None, None]
+    do = _rand(rng, 2, hq, L, d)
+    pos = np.tile(np.arange(L), (2, 1))
+    kvl = np.array([L, L])
+    dq, dk, dv = O.grouped_attention_backward(q, k, v, pos, kvl, 0.5, True, do)
+    grp = hq // hkv
+    rq, rk, rv = O.grouped_attention_backward(q, np.repeat(k, grp, axis=1),
+                                              np.repeat(v, grp, axis=1), pos, kvl, 0.5,
+                                              True, do)
+    assert np.max(np.abs(dq - rq)) < 1e-12
+    assert np.max(np.abs(dk - rk.reshape(2, hkv, grp, L, d).sum(2))) < 1e-12
+    assert np.max(np.abs(dv - rv.reshape(2, hkv, grp, L, d).sum(2))) < 1e-12
+    # under the causal mask the last key gets gradient only from the last query
+    only_last = do.copy()
+    only_last[:, :, :-1] = 0.0
+    _, _, dv_last = O.grouped_attention_backward(q, k, v, pos, kvl, 0.5, True, only_last)
+    do0 = do.copy()
+    do0[:, :, -1] = 0.0
+    _, dk0, dv0 = O.grouped_attention_backward(q, k, v, pos, kvl, 0.5, True, do0)
+    assert np.max(np.abs(dv0[:, :, -1])) < 1e-15 and np.max(np.abs(dk0[:, :, -1])) < 1e-15
+    assert np.max(np.abs(dv_last[:, :, -1])) > 1e-3
+
+
+def check_norm_rope_backward_invariants():
+    """RMSNorm with eps = 0 is invariant to scaling its input, so its input
+    gradient is orthogonal to the input row; RoPE is a rotation, so its
+    backward inverts it and keeps norms."""
+    rng = np.random.default_rng(26)
+    v = _rand(rng, 2, 3, 4, 16, scale=2.0)
+    w = 1.0 + _rand(rng, 16, scale=0.2)
+    dy = _rand(rng, 2, 3, 4, 16)
+    dv, dw = O.rms_norm_heads_backward(v, w, 0.0, dy)
+    assert np.max(np.abs(np.sum(dv * v, axis=-1))) < 1e-12
+    # the weight gradient is the upstream gradient times the normalised input
+    unit = O.rms_norm_heads(v, np.ones(16), 0.0)
+    assert np.max(np.abs(dw - np.sum((dy * unit).reshape(-1, 16), axis=0))) < 1e-12
+    pos = np.array([[0, 3, 40000], [1, 5, 65535]])
+    u = _rand(rng, 2, 3, 4, 16)
+    for rot in (None, 8):
+        back = O.apply_rope_backward(O.apply_rope(u, pos, 1e4, rotary_dim=rot), pos, 1e4,
+                                     rotary_dim=rot)
+        assert np.max(np.abs(back - u)) < 1e-12
+        gb = O.apply_rope_backward(u, pos, 1e4, rotary_dim=rot)
+        assert np.max(np.abs(np.linalg.norm(gb, axis=-1) - np.linalg.norm(u, axis=-1))) < 1e-12
+
+
 ALL_CHECKS = [
     check_geometries, check_resolve_errors, check_param_counts, check_macs,
     check_projection_bruteforce, check_attention_bruteforce,
@@ -605,4 +757,6 @@ ALL_CHECKS = [
     check_sum_over_heads, check_prefill_equals_decode,
     check_quotient_equals_explicit, check_rows_mode,
     check_e4m3_closed_forms, check_e4m3_quantize_bruteforce, check_fp8_cache_layer,
+    check_layer_backward_finite_differences, check_layer_backward_vs_torch_autograd,
+    check_attention_backward_group_sum, check_norm_rope_backward_invariants,
 ]

@@ -14,7 +14,9 @@ from oracle import gqa_oracle as O  # noqa: E402
 _orig = {name: getattr(O, name) for name in (
     "resolve_config", "attention_param_count", "macs_per_token", "project",
     "split_heads", "rms_norm_heads", "rope_inv_freq", "apply_rope",
-    "grouped_attention", "merge_heads", "qkv_normrope", "e4m3_value", "quantize_e4m3")}
+    "grouped_attention", "merge_heads", "qkv_normrope", "e4m3_value", "quantize_e4m3",
+    "project_backward", "rms_norm_heads_backward", "apply_rope_backward",
+    "grouped_attention_backward")}
 
 
 def _k_norm_uses_q_weight(res, x, w_qkv, qn, kn, positions, theta, eps,
@@ -118,7 +120,63 @@ def _quantize_no_saturation(x):
     return np.where(np.abs(x) > 464.0, np.where(x < 0, 0xFF, 0x7F), c).astype(np.uint8)
 
 
+def _norm_bwd_without_mean_term(v, w, eps, dy):
+    """Treats r as a constant: drops the term through mean(v*v)."""
+    dv, dw = _orig["rms_norm_heads_backward"](v, w, eps, dy)
+    r = 1.0 / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    return r * w * dy, dw
+
+
+def _rope_bwd_forward_rotation(g, positions, theta, rotary_dim=None):
+    """Carries the gradient back through the forward rotation, not its
+    transpose."""
+    return _orig["apply_rope"](g, positions, theta, rotary_dim=rotary_dim)
+
+
+def _attn_bwd_with(last_head_only=False, no_centering=False, dk_unscaled=False):
+    def bwd(q, k, v, q_pos, kv_len, scale, causal, do):
+        bsz, hq, lq, d = q.shape
+        hkv = k.shape[1]
+        group = hq // hkv
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(bsz):
+            n = int(kv_len[b])
+            vis = np.arange(n)[None, :] <= q_pos[b][:, None] if causal else \
+                np.ones((lq, n), dtype=bool)
+            for h in range(hq):
+                g = h // group
+                s = np.where(vis, q[b, h] @ k[b, g, :n].T * scale, -np.inf)
+                p = np.exp(s - s.max(-1, keepdims=True))
+                p /= p.sum(-1, keepdims=True)
+                dp = do[b, h] @ v[b, g, :n].T
+                ds = p * dp if no_centering else p * (dp - np.sum(p * dp, -1, keepdims=True))
+                dq[b, h] = ds @ k[b, g, :n] * scale
+                cdk = ds.T @ q[b, h] * (1.0 if dk_unscaled else scale)
+                cdv = p.T @ do[b, h]
+                if last_head_only:
+                    dk[b, g, :n], dv[b, g, :n] = cdk, cdv
+                else:
+                    dk[b, g, :n] += cdk
+                    dv[b, g, :n] += cdv
+        return dq, dk, dv
+    return bwd
+
+
+def _proj_bwd_first_sequence_only(x, w, dy):
+    """Weight gradient summed over the first sequence's tokens only."""
+    dx, _ = _orig["project_backward"](x, w, dy)
+    return dx, dy[0].reshape(-1, dy.shape[-1]).T @ x[0].reshape(-1, x.shape[-1])
+
+
 MUTATIONS = {
+    "norm_bwd_drops_mean_term": ("rms_norm_heads_backward", _norm_bwd_without_mean_term),
+    "rope_bwd_forward_rotation": ("apply_rope_backward", _rope_bwd_forward_rotation),
+    "attn_bwd_kv_grad_last_head_only": ("grouped_attention_backward",
+                                        _attn_bwd_with(last_head_only=True)),
+    "attn_bwd_softmax_not_centred": ("grouped_attention_backward",
+                                     _attn_bwd_with(no_centering=True)),
+    "attn_bwd_dk_unscaled": ("grouped_attention_backward", _attn_bwd_with(dk_unscaled=True)),
+    "proj_bwd_first_sequence_only": ("project_backward", _proj_bwd_first_sequence_only),
     "k_norm_with_q_weight": ("qkv_normrope", _k_norm_uses_q_weight),
     "group_map_modulo": ("grouped_attention",
                          _attention_with(group_map=lambda h, hkv, g: h % hkv)),
