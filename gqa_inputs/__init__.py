@@ -121,6 +121,24 @@ def host_layer_inputs(w: Workload, seed: Optional[int] = None) -> dict:
             "w_o": _finish(w_o, w.dtype)}
 
 
+def host_upstream_grad(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient of the layer output, dout [B, L, hidden] ~ N(0, 1),
+    from its own stream (seed + 2000), rounded to the workload's dtype."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 2000)
+    g = rng.standard_normal((w.batch, w.seq, w.hidden), dtype=np.float32)
+    return _finish(g, w.dtype)
+
+
+def device_upstream_grad(w: Workload, device="cuda", seed: Optional[int] = None):
+    """Same distribution as ``host_upstream_grad``, drawn on the device."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((w.seed if seed is None else seed) + 2000)
+    t = torch.randn((w.batch, w.seq, w.hidden), generator=g, device=device,
+                    dtype=torch.float32)
+    return t.to(torch_dtype(w))
+
+
 def host_cache(w: Workload, seed: Optional[int] = None,
                fill_unused: float = float("nan")) -> dict:
     """K/V caches [B, Hkv, capacity, d]: rows below ``cache_len`` ~ N(0, 1),

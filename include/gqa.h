@@ -124,7 +124,10 @@ typedef struct {
 gqa_status gqa_resolve(const gqa_config* in, gqa_config* out);
 
 /* Which entry point a workspace is sized for. */
-typedef enum { GQA_WS_QKV = 0, GQA_WS_ATTN = 1, GQA_WS_LAYER = 2, GQA_WS_OPROJ = 3 } gqa_ws_kind;
+typedef enum {
+  GQA_WS_QKV = 0, GQA_WS_ATTN = 1, GQA_WS_LAYER = 2, GQA_WS_OPROJ = 3,
+  GQA_WS_TRAIN_FORWARD = 4, GQA_WS_BACKWARD = 5
+} gqa_ws_kind;
 
 /* Bytes of workspace the entry point `kind` needs for this call shape
  * (0 if the config is invalid).  Host only. */
@@ -200,6 +203,64 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
                              int32_t kv_capacity, const int32_t* cache_len,
                              void* out, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * Training: a forward that keeps what the backward reads, and the backward
+ * (GPT-NeoX issue, "Tests and acceptance criteria": forward and backward
+ * passes; "Attention head partitions: keep each head's dependencies
+ * intact": gradients of the shared KV parameters).  No cache: the keys of
+ * sequence b are its own q_len tokens at positions 0 .. q_len - 1.
+ * Both need cfg->dtype GQA_BF16, head_dim 64 or 128, o_split 0 and kv_fp8 0
+ * (else GQA_ERR_UNSUPPORTED_DTYPE / _HEAD_DIM / _SHAPE).  All buffers are
+ * device memory owned by the caller.
+ */
+typedef struct {
+  float* qkv;  /* [batch, q_len, (Hq + 2*Hkv) * d]: the fused projection output
+                  before QK-norm and RoPE */
+  void* q;     /* [batch, Hq, q_len, d] after QK-norm and RoPE */
+  void* k;     /* [batch, Hkv, q_len, d] after QK-norm and RoPE */
+  void* v;     /* [batch, Hkv, q_len, d] */
+  void* o;     /* [batch, q_len, Hq * d] attention output (the o_proj input) */
+  float* lse;  /* [batch, Hq, q_len] natural log of each query row's softmax
+                  denominator, sum_j exp(q . k_j * d^-0.5) over its visible keys */
+} gqa_saved;
+
+typedef struct {
+  void* dx;          /* [batch, q_len, hidden], cfg->dtype */
+  float* dw_qkv;     /* [(Hq + 2*Hkv) * d, hidden] */
+  float* dq_norm_w;  /* [d]; not written (may be NULL) when cfg->qk_norm == 0 */
+  float* dk_norm_w;  /* [d] */
+  float* dw_o;       /* [hidden, Hq * d] */
+} gqa_grads;
+
+/*
+ * The layer forward of gqa_layer_forward without a cache, writing every
+ * buffer of *saved; out as there (fp32 when cfg->out_f32).  Needs
+ * gqa_workspace_bytes(..., GQA_WS_TRAIN_FORWARD) bytes of workspace.
+ */
+gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t q_len,
+                                   const void* x, const void* w_qkv,
+                                   const void* q_norm_w, const void* k_norm_w,
+                                   const void* w_o, const gqa_saved* saved, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gradients of the layer (the exact derivatives of the forward, taken
+ * through o_proj, the grouped attention, RoPE, QK-norm and the fused
+ * projection in reverse order) for the upstream gradient
+ *   dout [batch, q_len, hidden] (cfg->dtype),
+ * from the inputs of gqa_layer_forward_train and the *saved buffers it
+ * wrote.  Every buffer of *grads is overwritten (not accumulated into).
+ * A KV head's gradients sum over the Hq/Hkv query heads it serves; the norm
+ * weights' over every token and head.  Needs
+ * gqa_workspace_bytes(..., GQA_WS_BACKWARD) bytes of workspace; the
+ * results do not depend on timing (no atomics).
+ */
+gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_len,
+                              const void* x, const void* w_qkv, const void* q_norm_w,
+                              const void* k_norm_w, const void* w_o, const gqa_saved* saved,
+                              const void* dout, const gqa_grads* grads, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 const char* gqa_status_string(gqa_status s);
 /* Detail of the last error on the calling thread ("" if none). */

@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ["gqa_resolve", "gqa_workspace_bytes", "qkv_proj_normrope", "gqa_attn_core",
-              "gqa_o_proj", "gqa_layer_forward", "gqa_status_string", "gqa_last_error"]:
+              "gqa_o_proj", "gqa_layer_forward", "gqa_layer_forward_train",
+              "gqa_layer_backward", "gqa_status_string", "gqa_last_error"]:
         assert n in names
 
 
@@ -188,3 +189,54 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def _raw_train(c, batch, q_len, saved_ptr=1, ws_bytes=1 << 40, backward=False, null_saved=False):
+    L = T.lib()
+    cc = c.c()
+    p = ctypes.c_void_p(1)
+    sv = T._CSaved(*([0 if null_saved else saved_ptr] * 6))
+    if not backward:
+        return L.gqa_layer_forward_train(ctypes.byref(cc), batch, q_len, p, p, p, p, p,
+                                         ctypes.byref(sv), p, p, ws_bytes, None)
+    g = T._CGrads(1, 1, 1, 1, 1)
+    return L.gqa_layer_backward(ctypes.byref(cc), batch, q_len, p, p, p, p, p, ctypes.byref(sv),
+                                p, ctypes.byref(g), p, ws_bytes, None)
+
+
+@pytest.mark.parametrize("backward", [False, True])
+def test_training_entry_points_validate_before_launch(backward):
+    """The training pair takes bf16, head_dim 64 or 128, no o_split and no FP8
+    cache; bad calls are rejected on the host (no GPU here)."""
+    _lib_or_skip()
+    name = lambda st: T.STATUS_NAMES[st]  # noqa: E731
+    assert _raw_train(cfg(), 0, 16, backward=backward) == 0
+    assert _raw_train(cfg(), 2, 0, backward=backward) == 0
+    assert name(_raw_train(cfg(dtype="f32"), 2, 16, backward=backward)) == \
+        "GQA_ERR_UNSUPPORTED_DTYPE"
+    for d in (80, 256):
+        assert name(_raw_train(cfg(head_dim=d), 2, 16, backward=backward)) == \
+            "GQA_ERR_UNSUPPORTED_HEAD_DIM"
+    assert name(_raw_train(cfg(o_split=True), 2, 16, backward=backward)) == \
+        "GQA_ERR_UNSUPPORTED_SHAPE"
+    assert name(_raw_train(cfg(kv_fp8=True), 2, 16, backward=backward)) == \
+        "GQA_ERR_UNSUPPORTED_SHAPE"
+    assert name(_raw_train(cfg(), 2, 16, null_saved=True, backward=backward)) == \
+        "GQA_ERR_INVALID_ARG"
+    if backward:
+        assert name(_raw_train(cfg(), 2, 16, ws_bytes=64, backward=True)) == \
+            "GQA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_backward_workspace_covers_its_buffers():
+    """The backward's workspace holds at least dO and dy (bf16), dq/dk/dv
+    (fp32) and the chunked transposes of dout, o, dy and x."""
+    _lib_or_skip()
+    c = cfg()
+    B, L, H, qw, nq, kvw = 8, 2048, 1024, 2048, 4096, 1024
+    T_ = B * L
+    n = T.gqa_workspace_bytes(c, B, L, L, T.WS_BACKWARD)
+    floor = T_ * qw * 2 + T_ * nq * 2 + T_ * (qw + 2 * kvw) * 4 + T_ * (H + qw + nq + H) * 2
+    assert n >= floor
+    assert T.gqa_workspace_bytes(c, B, L, L, T.WS_TRAIN_FORWARD) == 0
+    assert T.gqa_workspace_bytes(cfg(dtype="f32"), B, L, L, T.WS_BACKWARD) > 0  # sized, then rejected

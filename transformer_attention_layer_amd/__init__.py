@@ -8,7 +8,8 @@ raises at the first call, and there is no fallback path.
 
 Entry points carry the names of the C ABI in ``include/gqa.h``:
 ``qkv_proj_normrope``, ``gqa_attn_core``, ``gqa_o_proj``,
-``gqa_layer_forward``, plus ``gqa_resolve`` and ``gqa_workspace_bytes``.
+``gqa_layer_forward``, the training pair ``gqa_layer_forward_train`` and
+``gqa_layer_backward``, plus ``gqa_resolve`` and ``gqa_workspace_bytes``.
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ LIB_PATH = os.environ.get("GQA_LIB", os.path.join(_HERE, "libgqa.so"))
 
 GQA_F32 = 0
 GQA_BF16 = 1
-WS_QKV, WS_ATTN, WS_LAYER, WS_OPROJ = 0, 1, 2, 3
+WS_QKV, WS_ATTN, WS_LAYER, WS_OPROJ, WS_TRAIN_FORWARD, WS_BACKWARD = 0, 1, 2, 3, 4, 5
 
 STATUS_NAMES = {
     0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_HEAD_DIM_INDIVISIBLE",
@@ -51,6 +52,17 @@ class _CConfig(ctypes.Structure):
                 ("o_split", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float)]
+
+
+class _CSaved(ctypes.Structure):
+    _fields_ = [("qkv", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+class _CGrads(ctypes.Structure):
+    _fields_ = [("dx", ctypes.c_void_p), ("dw_qkv", ctypes.c_void_p),
+                ("dq_norm_w", ctypes.c_void_p), ("dk_norm_w", ctypes.c_void_p),
+                ("dw_o", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -103,8 +115,11 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_core.argtypes = [CP, I32, I32, P, P, P, P, I32, P, P, SZ, P]
         L.gqa_o_proj.argtypes = [CP, I32, P, P, P, P]
         L.gqa_layer_forward.argtypes = [CP, I32, I32, P, P, P, P, P, P, P, I32, P, P, P, SZ, P]
+        SP, GP = ctypes.POINTER(_CSaved), ctypes.POINTER(_CGrads)
+        L.gqa_layer_forward_train.argtypes = [CP, I32, I32, P, P, P, P, P, SP, P, P, SZ, P]
+        L.gqa_layer_backward.argtypes = [CP, I32, I32, P, P, P, P, P, SP, P, GP, P, SZ, P]
         for f in ("gqa_resolve", "qkv_proj_normrope", "gqa_attn_core", "gqa_o_proj",
-                  "gqa_layer_forward"):
+                  "gqa_layer_forward", "gqa_layer_forward_train", "gqa_layer_backward"):
             getattr(L, f).restype = ctypes.c_int
         L.gqa_status_string.argtypes = [ctypes.c_int]
         L.gqa_status_string.restype = ctypes.c_char_p
@@ -324,8 +339,112 @@ def gqa_layer_forward(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *, k_ca
     return out, k_cache, v_cache
 
 
+class TrainSaved:
+    """Device buffers the training forward writes and the backward reads
+    (``gqa_saved`` of the C ABI): qkv [B, L, (Hq+2Hkv)d] fp32 before norm and
+    RoPE, q [B, Hq, L, d], k and v [B, Hkv, L, d] after norm and RoPE, o
+    [B, L, Hq*d] and lse [B, Hq, L] fp32."""
+
+    def __init__(self, cfg: GQAConfig, batch: int, q_len: int, device="cuda"):
+        torch = _torch()
+        hkv, d = _res(cfg)
+        dt = _dt(cfg)
+        B, L, hq = batch, q_len, cfg.num_heads
+        self.qkv = torch.empty((B, L, (hq + 2 * hkv) * d), dtype=torch.float32, device=device)
+        self.q = torch.empty((B, hq, L, d), dtype=dt, device=device)
+        self.k = torch.empty((B, hkv, L, d), dtype=dt, device=device)
+        self.v = torch.empty((B, hkv, L, d), dtype=dt, device=device)
+        self.o = torch.empty((B, L, hq * d), dtype=dt, device=device)
+        self.lse = torch.empty((B, hq, L), dtype=torch.float32, device=device)
+
+    def c(self) -> _CSaved:
+        return _CSaved(self.qkv.data_ptr(), self.q.data_ptr(), self.k.data_ptr(),
+                       self.v.data_ptr(), self.o.data_ptr(), self.lse.data_ptr())
+
+
+def gqa_layer_forward_train(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
+                            saved: TrainSaved = None, out=None, stream=None):
+    """The layer forward without a cache that keeps what the backward needs.
+    Returns (out [B, L, hidden], saved)."""
+    torch = _torch()
+    hkv, d = _res(cfg)
+    dt = _dt(cfg)
+    B, L, H = x.shape
+    _need(x, "x", dt, (B, L, cfg.hidden_size))
+    _need(w_qkv, "w_qkv", dt, ((cfg.num_heads + 2 * hkv) * d, H))
+    _need(w_o, "w_o", dt, (H, cfg.num_heads * d))
+    if cfg.qk_norm:
+        _need(q_norm_w, "q_norm_w", dt, (d,))
+        _need(k_norm_w, "k_norm_w", dt, (d,))
+    if saved is None:
+        saved = TrainSaved(cfg, B, L, x.device)
+    if out is None:
+        out = torch.empty((B, L, H), dtype=_out_dt(cfg), device=x.device)
+    _need(out, "out", _out_dt(cfg), (B, L, H))
+    cc, cs = cfg.c(), saved.c()
+    _check(lib().gqa_layer_forward_train(
+        ctypes.byref(cc), B, L, _ptr(x), _ptr(w_qkv),
+        _ptr(q_norm_w) if cfg.qk_norm else None, _ptr(k_norm_w) if cfg.qk_norm else None,
+        _ptr(w_o), ctypes.byref(cs), _ptr(out), None, 0, _stream(stream)))
+    return out, saved
+
+
+class BackwardWorkspace:
+    """A reusable workspace for ``gqa_layer_backward``."""
+
+    def __init__(self, cfg: GQAConfig, batch: int, q_len: int, device="cuda"):
+        self.nbytes = gqa_workspace_bytes(cfg, batch, q_len, q_len, WS_BACKWARD)
+        self.buf = _workspace(self.nbytes, device)
+
+
+def gqa_layer_backward(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, saved: TrainSaved,
+                       dout, *, grads: dict = None, workspace: BackwardWorkspace = None,
+                       stream=None):
+    """Gradients of the layer for the upstream gradient dout [B, L, hidden]
+    (cfg dtype).  Returns a dict: dx [B, L, hidden] (cfg dtype), dw_qkv,
+    dq_norm_w, dk_norm_w (None without QK-norm) and dw_o, all fp32."""
+    torch = _torch()
+    hkv, d = _res(cfg)
+    dt = _dt(cfg)
+    B, L, H = x.shape
+    _need(x, "x", dt, (B, L, cfg.hidden_size))
+    _need(dout, "dout", dt, (B, L, H))
+    nq = (cfg.num_heads + 2 * hkv) * d
+    _need(w_qkv, "w_qkv", dt, (nq, H))
+    _need(w_o, "w_o", dt, (H, cfg.num_heads * d))
+    if cfg.qk_norm:
+        _need(q_norm_w, "q_norm_w", dt, (d,))
+        _need(k_norm_w, "k_norm_w", dt, (d,))
+    if grads is None:
+        f32 = torch.float32
+        grads = {"dx": torch.empty((B, L, H), dtype=dt, device=x.device),
+                 "dw_qkv": torch.empty((nq, H), dtype=f32, device=x.device),
+                 "dq_norm_w": torch.empty((d,), dtype=f32, device=x.device) if cfg.qk_norm else None,
+                 "dk_norm_w": torch.empty((d,), dtype=f32, device=x.device) if cfg.qk_norm else None,
+                 "dw_o": torch.empty((H, cfg.num_heads * d), dtype=f32, device=x.device)}
+    _need(grads["dx"], "dx", dt, (B, L, H))
+    _need(grads["dw_qkv"], "dw_qkv", torch.float32, (nq, H))
+    _need(grads["dw_o"], "dw_o", torch.float32, (H, cfg.num_heads * d))
+    if cfg.qk_norm:
+        _need(grads["dq_norm_w"], "dq_norm_w", torch.float32, (d,))
+        _need(grads["dk_norm_w"], "dk_norm_w", torch.float32, (d,))
+    if workspace is None:
+        workspace = BackwardWorkspace(cfg, B, L, x.device)
+    cg = _CGrads(_ptr(grads["dx"]), _ptr(grads["dw_qkv"]),
+                 _ptr(grads["dq_norm_w"]) if cfg.qk_norm else None,
+                 _ptr(grads["dk_norm_w"]) if cfg.qk_norm else None, _ptr(grads["dw_o"]))
+    cc, cs = cfg.c(), saved.c()
+    _check(lib().gqa_layer_backward(
+        ctypes.byref(cc), B, L, _ptr(x), _ptr(w_qkv),
+        _ptr(q_norm_w) if cfg.qk_norm else None, _ptr(k_norm_w) if cfg.qk_norm else None,
+        _ptr(w_o), ctypes.byref(cs), _ptr(dout), ctypes.byref(cg), _ptr(workspace.buf),
+        workspace.nbytes, _stream(stream)))
+    return grads
+
+
 __all__ = [
     "GQAConfig", "GQAError", "LIB_PATH", "lib", "gqa_resolve", "gqa_workspace_bytes",
     "qkv_proj_normrope", "gqa_attn_core", "gqa_o_proj", "gqa_layer_forward",
-    "LayerWorkspace", "GQA_F32", "GQA_BF16",
+    "LayerWorkspace", "GQA_F32", "GQA_BF16", "TrainSaved", "gqa_layer_forward_train",
+    "BackwardWorkspace", "gqa_layer_backward",
 ]

@@ -105,16 +105,21 @@ __device__ __forceinline__ void wait_vmem() {
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
+// A batch of independent products (the plain epilogues) walks the members'
+// tiles one member after the other.
 struct TileOrder {
-  int ntn, ntm, total, per_xcd;
-  __device__ __forceinline__ TileOrder(int N, int M, int BN, int BM) {
+  int ntn, ntm, per_z, total, per_xcd;
+  __device__ __forceinline__ TileOrder(int N, int M, int BN, int BM, int batch) {
     ntn = (N + BN - 1) / BN;
     ntm = (M + BM - 1) / BM;
-    total = ntn * ntm;
+    per_z = ntn * ntm;
+    total = per_z * batch;
     per_xcd = (total + kXcds - 1) / kXcds;
   }
-  // position id of the order -> (feature tile, token tile)
-  __device__ __forceinline__ void at(int id, int& tn, int& tm) const {
+  // position id of the order -> (batch member, feature tile, token tile)
+  __device__ __forceinline__ void at(int id, int& z, int& tn, int& tm) const {
+    z = id / per_z;
+    id -= z * per_z;
     const int group = id / (kGroupM * ntn);
     const int first_m = group * kGroupM;
     const int gm = min(ntm - first_m, kGroupM);
@@ -170,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int N = a.N, M = a.M, K = a.K;
-  const TileOrder order(N, M, BN, BM);
+  const int batch = EPI == kEpiQKV ? 1 : max(a.batch, 1);
+  const TileOrder order(N, M, BN, BM, batch);
   const int xcd = (int)(blockIdx.x % kXcds);
   const int per_wg = (int)(gridDim.x / kXcds);  // workgroups on this XCD
   const int run_end = min((xcd + 1) * order.per_xcd, order.total);
@@ -199,12 +205,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       s.w = a.W; s.x = a.X; s.wbytes = 0; s.xbytes = 0; s.n0 = 0; s.m0 = 0;
       return s;
     }
-    int tn, tm;
-    order.at(tile, tn, tm);
+    int z, tn, tm;
+    order.at(tile, z, tn, tm);
     s.n0 = tn * BN;
     s.m0 = tm * BM;
-    s.w = a.W + (size_t)s.n0 * Kw;
-    s.x = a.X + (size_t)s.m0 * K;
+    s.w = a.W + (size_t)z * a.sW + (size_t)s.n0 * Kw;
+    s.x = a.X + (size_t)z * a.sX + (size_t)s.m0 * K;
     s.wbytes = rows_bytes(s.n0, N, Kw);
     s.xbytes = rows_bytes(s.m0, M, K);
     return s;
@@ -390,6 +396,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     auto put8 = [&](int row, int feat, u32x2 v) {
       stage8[(row * 16 + ((feat >> 3) ^ (row & 15))) * 2 + ((feat >> 2) & 1)] = v;
     };
+    // batch member of this tile: its output block
+    const size_t oz = EPI == kEpiQKV ? 0 : (size_t)(id / order.per_z) * a.sOut;
     if constexpr (EPI == kEpiPlainF32) {
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             if (n >= N) continue;
             floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
                          acc[f][t][4 * j + 3]};
-            *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + (size_t)m * N + n) = w;
+            *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + oz + (size_t)m * N + n) = w;
           }
       }
     } else if constexpr (EPI == kEpiPlain) {
@@ -429,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           const int row = 4 * i + (lane >> 4);
           const int m = m0 + wm * WM + 32 * t + row;
           const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
-          if (m < M && n < N) st16(static_cast<bf16*>(a.out) + (size_t)m * N + n, v);
+          if (m < M && n < N) st16(static_cast<bf16*>(a.out) + oz + (size_t)m * N + n, v);
         }
       }
     } else if (nw < N) {  // wave-uniform
@@ -749,9 +757,9 @@ namespace {
 // down to a multiple of the XCDs.  With fewer than kStages - 1 K stages a
 // load that runs ahead could reach two tiles further, so every workgroup
 // then gets exactly one tile.
-int gemm_workgroups(int N, int M, int K) {
+int gemm_workgroups(int N, int M, int K, int batch = 1) {
   constexpr int BN = 256, BM = 256;
-  const int tiles = gemm_tiles(N, M, BN, BM);
+  const int tiles = gemm_tiles(N, M, BN, BM) * batch;
   int grid = (tiles + kXcds - 1) / kXcds * kXcds;
   if ((K + kBK - 1) / kBK < kStages - 1) return grid;
   static int cus[64];
@@ -782,7 +790,7 @@ hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
 }
 
 hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream) {
-  const int grid = gemm_workgroups(args.N, args.M, args.K);
+  const int grid = gemm_workgroups(args.N, args.M, args.K, args.batch > 1 ? args.batch : 1);
   const bool kal = k_aligned(args);
   if (args.out_f32) {
     if (kal)

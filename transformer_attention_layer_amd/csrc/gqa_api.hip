@@ -296,9 +296,27 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   return check_launch(gqa::launch_normrope(n, st), "norm + rope");
 }
 
+// Prefill work split: a workgroup of 4 waves covers hpw query heads of one
+// KV group x pb blocks of 32 positions (hpw * pb = 4).
+gqa_status prefill_split(const Shape& s, int q_len, int* hpw, int* pb, int* n_hsub,
+                         int* n_qtiles) {
+  int h = 1;
+  if (s.G % 4 == 0) h = 4;
+  else if (s.G % 2 == 0) h = 2;
+  *hpw = h;
+  *pb = 4 / h;
+  *n_hsub = s.G / h;
+  *n_qtiles = (q_len + *pb * 32 - 1) / (*pb * 32);
+  if (*n_qtiles > 65535)
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "q_len %d needs more than 65535 query tiles", q_len);
+  return GQA_OK;
+}
+
+// lse (bf16 matrix-core path only): the prefill kernel also writes each
+// query row's log-sum-exp, whatever q_len is.
 gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, const void* q,
                     const void* kc, const void* vc, const int32_t* kv_base, int kv_add, int cap,
-                    void* o, bool o_split, void* ws, hipStream_t st) {
+                    void* o, bool o_split, void* ws, hipStream_t st, float* lse = nullptr) {
   const double scale = 1.0 / sqrt((double)s.d);
   if (!s.mfma) {  // fp32, or bf16 with a head_dim other than 64, 128, 256
     gqa::F32AttnArgs a{};
@@ -346,22 +364,16 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
     a.k8 = static_cast<const unsigned char*>(kc);
     a.v8 = static_cast<const unsigned char*>(vc);
   }
-  if (use_decode(s, q_len)) {
+  a.lse = lse;
+  if (!lse && use_decode(s, q_len)) {
     decode_split(s, batch, cap, &a.n_splits, &a.chunk);
     const size_t parts = (size_t)batch * s.Hkv * a.n_splits * 32;
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(parts * s.d * sizeof(float)));
     return check_launch(gqa::launch_attn_decode_bf16(a, st), "decode attention");
   }
-  int hpw = 1;
-  if (s.G % 4 == 0) hpw = 4;
-  else if (s.G % 2 == 0) hpw = 2;
-  a.hpw = hpw;
-  a.pb = 4 / hpw;
-  a.n_hsub = s.G / hpw;
-  a.n_qtiles = (q_len + a.pb * 32 - 1) / (a.pb * 32);
-  if (a.n_qtiles > 65535)
-    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "q_len %d needs more than 65535 query tiles", q_len);
+  gqa_status r = prefill_split(s, q_len, &a.hpw, &a.pb, &a.n_hsub, &a.n_qtiles);
+  if (r != GQA_OK) return r;
   return check_launch(gqa::launch_attn_prefill_bf16(a, st), "prefill attention");
 }
 
@@ -386,6 +398,118 @@ gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, co
   return check_launch(gqa::launch_gemm_f32(g, st), "o_proj (f32)");
 }
 
+// ---------------------------------------------------------------------------
+// Training (forward with saved activations, backward)
+// ---------------------------------------------------------------------------
+
+gqa_status check_train(const gqa_config& c, const Shape& s) {
+  if (!s.bf16) return fail(GQA_ERR_UNSUPPORTED_DTYPE, "the training entry points need GQA_BF16");
+  if (s.d != 64 && s.d != 128)
+    return fail(GQA_ERR_UNSUPPORTED_HEAD_DIM,
+                "Unsupported head_dim %d for training: the backward kernels take head_dim 64 "
+                "and 128", s.d);
+  if (c.o_split || s.kv_fp8)
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "the training entry points need o_split 0 and kv_fp8 0");
+  return GQA_OK;
+}
+
+// Split of the token axis for a weight-gradient GEMM with N x M outputs
+// (256 x 256 tiles): enough batch members that their tiles cover the 256
+// compute units, at least 512 tokens each, chunks of whole 64s.
+struct TokSplit {
+  int S, Rc;
+};
+TokSplit tok_split(long long T, int N, int M) {
+  const long long tiles = (long long)((N + 255) / 256) * ((M + 255) / 256);
+  long long S = (256 + tiles - 1) / tiles;
+  const long long max_s = T / 512 > 1 ? T / 512 : 1;
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  long long Rc = (T + S - 1) / S;
+  Rc = (Rc + 63) / 64 * 64;
+  TokSplit t;
+  t.Rc = (int)Rc;
+  t.S = (int)((T + Rc - 1) / Rc);
+  return t;
+}
+
+// Workspace of the backward: byte offsets of its buffers.
+struct BwdLayout {
+  TokSplit so, sq;  // splits of the dW_o and dW_qkv products
+  int gblocks;      // blocks of the norm/RoPE backward
+  size_t doutT, oT, dwo_part, woT, dO, D, dq, dk, dv, rope, gpart, dy, dyT, xT, dwq_part, wqT;
+  size_t total;
+};
+
+BwdLayout bwd_layout(const Shape& s, int batch, int L) {
+  BwdLayout b{};
+  const size_t T = (size_t)batch * L;
+  const size_t qw = (size_t)s.Hq * s.d, kvw = (size_t)s.Hkv * s.d;
+  b.so = tok_split((long long)T, s.H, (int)qw);
+  b.sq = tok_split((long long)T, s.n_qkv, s.H);
+  b.gblocks = (int)((T + gqa::kNormRopeBwdTokens - 1) / gqa::kNormRopeBwdTokens);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  b.doutT = take((size_t)b.so.S * b.so.Rc * s.H * 2);
+  b.oT = take((size_t)b.so.S * b.so.Rc * qw * 2);
+  b.dwo_part = take(b.so.S > 1 ? (size_t)b.so.S * s.H * qw * 4 : 0);
+  b.woT = take(qw * s.H * 2);
+  b.dO = take(T * qw * 2);
+  b.D = take(T * s.Hq * 4);
+  b.dq = take(T * qw * 4);
+  b.dk = take(T * kvw * 4);
+  b.dv = take(T * kvw * 4);
+  b.rope = take((size_t)L * (s.rot / 2) * 8);
+  b.gpart = take((size_t)b.gblocks * 2 * s.d * 4);
+  b.dy = take(T * s.n_qkv * 2);
+  b.dyT = take((size_t)b.sq.S * b.sq.Rc * s.n_qkv * 2);
+  b.xT = take((size_t)b.sq.S * b.sq.Rc * s.H * 2);
+  b.dwq_part = take(b.sq.S > 1 ? (size_t)b.sq.S * s.n_qkv * s.H * 4 : 0);
+  b.wqT = take((size_t)s.H * s.n_qkv * 2);
+  b.total = off;
+  return b;
+}
+
+// out (fp32 [M, N]) = sum over the token chunks of X_s W_s^T, with X and W
+// chunk-major ([S][M][Rc] and [S][N][Rc]); partial products go to `part`
+// and are summed when there is more than one chunk.
+gqa_status weight_grad(const __bf16* X, const __bf16* W, int M, int N, const TokSplit& t, float* part,
+                       float* out, hipStream_t st, const char* what) {
+  gqa::GemmArgs g{};
+  g.X = X;
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = t.Rc;
+  g.batch = t.S;
+  g.sX = (long long)M * t.Rc;
+  g.sW = (long long)N * t.Rc;
+  g.sOut = (long long)M * N;
+  g.out = t.S > 1 ? part : out;
+  g.out_f32 = 1;
+  gqa_status r = check_launch(gqa::launch_gemm_plain_bf16(g, st), what);
+  if (r != GQA_OK || t.S == 1) return r;
+  return check_launch(gqa::launch_sum_partials(part, t.S, (long long)M * N, out, st), what);
+}
+
+// out (cfg dtype [M, N]) = X [M, K] W^T with W given as [N, K]
+gqa_status plain_gemm(const __bf16* X, const __bf16* W, int M, int N, int K, void* out, int out_f32,
+                      hipStream_t st, const char* what) {
+  gqa::GemmArgs g{};
+  g.X = X;
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.out = out;
+  g.out_f32 = out_f32;
+  return check_launch(gqa::launch_gemm_plain_bf16(g, st), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -404,6 +528,8 @@ size_t gqa_workspace_bytes(const gqa_config* cfg, int32_t batch, int32_t q_len,
     case GQA_WS_ATTN: return ws_attn(s, batch, q_len, kv_capacity);
     case GQA_WS_LAYER: return ws_layer(s, batch, q_len, kv_capacity);
     case GQA_WS_OPROJ: return 0;
+    case GQA_WS_TRAIN_FORWARD: return 0;
+    case GQA_WS_BACKWARD: return bwd_layout(s, batch, q_len).total;
     default: return 0;
   }
 }
@@ -505,6 +631,194 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
                s.o_split, ws_a, st);
   if (r != GQA_OK) return r;
   r = run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st);
+  return r == GQA_OK ? ok() : r;
+}
+
+gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t q_len,
+                                   const void* x, const void* w_qkv, const void* q_norm_w,
+                                   const void* k_norm_w, const void* w_o, const gqa_saved* saved,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  gqa_config c;
+  Shape s;
+  gqa_status r = resolve(cfg, &c, &s);
+  if (r != GQA_OK) return r;
+  if ((r = check_train(c, s)) != GQA_OK) return r;
+  if ((r = check_common(s, batch, q_len, q_len)) != GQA_OK) return r;
+  if (batch == 0 || q_len == 0) return ok();
+  if (!x || !w_qkv || !w_o || !out || !saved)
+    return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, w_o, saved and out must be non-null");
+  if (!saved->qkv || !saved->q || !saved->k || !saved->v || !saved->o || !saved->lse)
+    return fail(GQA_ERR_INVALID_ARG, "every buffer of saved must be non-null");
+  if (c.qk_norm && (!q_norm_w || !k_norm_w))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
+  const int T = batch * q_len;
+  hipStream_t st = (hipStream_t)stream;
+  // fused projection in fp32 (kept), then norm + RoPE + head-major scatter
+  gqa::GemmArgs g{};
+  g.W = static_cast<const __bf16*>(w_qkv);
+  g.X = static_cast<const __bf16*>(x);
+  g.N = s.n_qkv;
+  g.M = T;
+  g.K = s.H;
+  g.out = saved->qkv;
+  g.out_f32 = 1;
+  r = use_skinny(s, T) ? check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection")
+                       : check_launch(gqa::launch_gemm_plain_bf16(g, st), "qkv projection");
+  if (r != GQA_OK) return r;
+  gqa::NormRopeArgs n{};
+  n.y = saved->qkv;
+  n.q_norm_w = q_norm_w;
+  n.k_norm_w = k_norm_w;
+  n.q = saved->q;
+  n.k_cache = saved->k;
+  n.v_cache = saved->v;
+  n.B = batch;
+  n.L = q_len;
+  n.Hq = s.Hq;
+  n.Hkv = s.Hkv;
+  n.d = s.d;
+  n.rot = s.rot;
+  n.cap = q_len;
+  n.qk_norm = c.qk_norm;
+  n.bf16 = 1;
+  n.eps = c.rms_eps;
+  n.theta = (double)c.rope_theta;
+  if ((r = check_launch(gqa::launch_normrope(n, st), "norm + rope")) != GQA_OK) return r;
+  r = run_attn(c, s, batch, q_len, saved->q, saved->k, saved->v, nullptr, q_len, q_len, saved->o,
+               false, nullptr, st, saved->lse);
+  if (r != GQA_OK) return r;
+  r = run_oproj(s, T, saved->o, false, w_o, out, st);
+  return r == GQA_OK ? ok() : r;
+}
+
+gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_len, const void* x,
+                              const void* w_qkv, const void* q_norm_w, const void* k_norm_w,
+                              const void* w_o, const gqa_saved* saved, const void* dout,
+                              const gqa_grads* grads, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  gqa_config c;
+  Shape s;
+  gqa_status r = resolve(cfg, &c, &s);
+  if (r != GQA_OK) return r;
+  if ((r = check_train(c, s)) != GQA_OK) return r;
+  if ((r = check_common(s, batch, q_len, q_len)) != GQA_OK) return r;
+  if (batch == 0 || q_len == 0) return ok();
+  if (!x || !w_qkv || !w_o || !saved || !dout || !grads)
+    return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, w_o, saved, dout and grads must be non-null");
+  if (!saved->qkv || !saved->q || !saved->k || !saved->v || !saved->o || !saved->lse)
+    return fail(GQA_ERR_INVALID_ARG, "every buffer of saved must be non-null");
+  if (!grads->dx || !grads->dw_qkv || !grads->dw_o)
+    return fail(GQA_ERR_INVALID_ARG, "grads->dx, dw_qkv and dw_o must be non-null");
+  if (c.qk_norm && (!q_norm_w || !k_norm_w || !grads->dq_norm_w || !grads->dk_norm_w))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight or its gradient is null");
+  const BwdLayout lay = bwd_layout(s, batch, q_len);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", lay.total,
+                workspace_bytes);
+  char* w = static_cast<char*>(workspace);
+  auto bfp = [&](size_t off) { return reinterpret_cast<__bf16*>(w + off); };
+  auto f32p = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  hipStream_t st = (hipStream_t)stream;
+  const int T = batch * q_len;
+  const int qw = s.Hq * s.d;
+  const __bf16* dout_b = static_cast<const __bf16*>(dout);
+  const __bf16* x_b = static_cast<const __bf16*>(x);
+
+  // o_proj: dW_o = dout^T o (token-chunked), dO = dout W_o
+  r = check_launch(gqa::launch_transpose_bf16(dout_b, T, s.H, lay.so.Rc, bfp(lay.doutT), st),
+                   "transpose dout");
+  if (r != GQA_OK) return r;
+  r = check_launch(gqa::launch_transpose_bf16(static_cast<const __bf16*>(saved->o), T, qw, lay.so.Rc,
+                                              bfp(lay.oT), st),
+                   "transpose o");
+  if (r != GQA_OK) return r;
+  r = weight_grad(bfp(lay.doutT), bfp(lay.oT), s.H, qw, lay.so, f32p(lay.dwo_part), grads->dw_o,
+                  st, "dW_o");
+  if (r != GQA_OK) return r;
+  r = check_launch(gqa::launch_transpose_bf16(static_cast<const __bf16*>(w_o), s.H, qw, s.H,
+                                              bfp(lay.woT), st),
+                   "transpose W_o");
+  if (r != GQA_OK) return r;
+  r = plain_gemm(dout_b, bfp(lay.woT), T, qw, s.H, bfp(lay.dO), 0, st, "dO");
+  if (r != GQA_OK) return r;
+
+  // attention: dq, dk, dv (fp32, head-major)
+  gqa::AttnBwdArgs a{};
+  a.d = s.d;
+  a.q = static_cast<const __bf16*>(saved->q);
+  a.k = static_cast<const __bf16*>(saved->k);
+  a.v = static_cast<const __bf16*>(saved->v);
+  a.o = static_cast<const __bf16*>(saved->o);
+  a.dO = bfp(lay.dO);
+  a.lse = saved->lse;
+  a.D = f32p(lay.D);
+  a.dq = f32p(lay.dq);
+  a.dk = f32p(lay.dk);
+  a.dv = f32p(lay.dv);
+  a.B = batch;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.L = q_len;
+  a.causal = c.causal;
+  const double scale = 1.0 / sqrt((double)s.d);
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  if ((r = prefill_split(s, q_len, &a.hpw, &a.pb, &a.n_hsub, &a.n_qtiles)) != GQA_OK) return r;
+  if ((r = check_launch(gqa::launch_attn_bwd_bf16(a, st), "attention backward")) != GQA_OK)
+    return r;
+
+  // RoPE and QK-norm: dy = gradient of the fused projection output
+  float2* table = reinterpret_cast<float2*>(w + lay.rope);
+  r = check_launch(gqa::launch_rope_table(table, nullptr, q_len, q_len, s.rot / 2,
+                                          (double)c.rope_theta, st),
+                   "rope table");
+  if (r != GQA_OK) return r;
+  gqa::NormRopeBwdArgs n{};
+  n.dq = a.dq;
+  n.dk = a.dk;
+  n.dv = a.dv;
+  n.y = saved->qkv;
+  n.q_norm_w = static_cast<const __bf16*>(q_norm_w);
+  n.k_norm_w = static_cast<const __bf16*>(k_norm_w);
+  n.rope = table;
+  n.dy = bfp(lay.dy);
+  n.dgamma_part = f32p(lay.gpart);
+  n.B = batch;
+  n.L = q_len;
+  n.Hq = s.Hq;
+  n.Hkv = s.Hkv;
+  n.d = s.d;
+  n.rot = s.rot;
+  n.qk_norm = c.qk_norm;
+  n.eps = c.rms_eps;
+  if ((r = check_launch(gqa::launch_normrope_bwd(n, st), "norm + rope backward")) != GQA_OK)
+    return r;
+  if (c.qk_norm) {
+    r = check_launch(gqa::launch_dgamma_reduce(f32p(lay.gpart), lay.gblocks, s.d,
+                                               grads->dq_norm_w, grads->dk_norm_w, st),
+                     "norm weight gradients");
+    if (r != GQA_OK) return r;
+  }
+
+  // fused projection: dW_qkv = dy^T x (token-chunked), dx = dy W_qkv
+  r = check_launch(gqa::launch_transpose_bf16(bfp(lay.dy), T, s.n_qkv, lay.sq.Rc, bfp(lay.dyT), st),
+                   "transpose dy");
+  if (r != GQA_OK) return r;
+  r = check_launch(gqa::launch_transpose_bf16(x_b, T, s.H, lay.sq.Rc, bfp(lay.xT), st),
+                   "transpose x");
+  if (r != GQA_OK) return r;
+  r = weight_grad(bfp(lay.dyT), bfp(lay.xT), s.n_qkv, s.H, lay.sq, f32p(lay.dwq_part),
+                  grads->dw_qkv, st, "dW_qkv");
+  if (r != GQA_OK) return r;
+  r = check_launch(gqa::launch_transpose_bf16(static_cast<const __bf16*>(w_qkv), s.n_qkv, s.H,
+                                              s.n_qkv, bfp(lay.wqT), st),
+                   "transpose W_qkv");
+  if (r != GQA_OK) return r;
+  r = plain_gemm(bfp(lay.dy), bfp(lay.wqT), T, s.H, s.n_qkv, grads->dx, 0, st, "dx");
   return r == GQA_OK ? ok() : r;
 }
 

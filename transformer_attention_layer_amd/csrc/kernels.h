@@ -15,6 +15,10 @@ struct GemmArgs {
   const __bf16* W;  // [N, K]
   const __bf16* X;  // [M, K]
   int N, M, K;
+  // plain epilogues only: `batch` independent products (0 counts as 1), member z
+  // at W + z sW, X + z sX, out + z sOut (elements)
+  int batch;
+  long long sW, sX, sOut;
   // plain epilogue: out[m, n], bf16 or (out_f32) fp32
   void* out;
   int out_f32;
@@ -52,6 +56,7 @@ struct AttnArgs {
   float* part_o;       // [B, Hkv, n_splits, 32, d]
   float2* part_ml;     // [B, Hkv, n_splits, 32] (running max in log2 units, sum)
   int n_splits, chunk;
+  float* lse;          // prefill, optional: [B, Hq, Lq] natural log of each row's softmax denominator
 };
 
 hipError_t launch_rope_table(float2* table, const int* start_pos, int rows, int L, int half,
@@ -60,6 +65,57 @@ hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream);
 
 hipError_t launch_attn_prefill_bf16(const AttnArgs& args, hipStream_t stream);
+
+// Attention backward (bf16 matrix cores, head_dim 64 or 128, no cache:
+// keys are the L tokens of each sequence).
+struct AttnBwdArgs {
+  int d;
+  const __bf16* q;   // [B, Hq, L, d] after norm and RoPE
+  const __bf16* k;   // [B, Hkv, L, d]
+  const __bf16* v;   // [B, Hkv, L, d]
+  const __bf16* o;   // [B, L, Hq * d] forward attention output
+  const __bf16* dO;  // [B, L, Hq * d] its gradient
+  const float* lse;  // [B, Hq, L] natural log of each row's softmax denominator
+  float* D;          // [B, Hq, L] rowsum(dO * o): written by the dQ kernel
+  float* dq;         // [B, Hq, L, d]
+  float* dk;         // [B, Hkv, L, d]
+  float* dv;         // [B, Hkv, L, d]
+  int B, Hq, Hkv, G, L, causal;
+  float scale;       // d^-0.5
+  float scale_log2;  // scale * log2(e)
+  int hpw, pb, n_qtiles, n_hsub;  // dQ kernel work split (as the forward prefill)
+};
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& args, hipStream_t stream);
+
+// Backward through QK-norm and RoPE: per (token, head of the fused
+// projection) the gradient of the projection output, bf16 [T, n_qkv], and
+// per-block partial sums of the norm-weight gradients.
+struct NormRopeBwdArgs {
+  const float* dq;  // [B, Hq, L, d]
+  const float* dk;  // [B, Hkv, L, d]
+  const float* dv;  // [B, Hkv, L, d]
+  const float* y;   // [T, n_qkv] projection output before norm and RoPE
+  const __bf16* q_norm_w;
+  const __bf16* k_norm_w;
+  const float2* rope;  // [L, rot / 2] (cos, sin) of position t
+  __bf16* dy;          // [T, n_qkv]
+  float* dgamma_part;  // [blocks][2][d]: q then k weight-gradient partial sums
+  int B, L, Hq, Hkv, d, rot, qk_norm;
+  float eps;
+};
+constexpr int kNormRopeBwdTokens = 16;  // tokens per block of the norm/RoPE backward
+hipError_t launch_normrope_bwd(const NormRopeBwdArgs& args, hipStream_t stream);
+// out[k][j] = sum over blocks of part[blk][k][j], k < 2, j < d (fp32)
+hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* dq_w, float* dk_w,
+                                hipStream_t stream);
+// bf16 transpose into row chunks: in [R, C] (row-major) -> out[s][C][Rc] for
+// s < ceil(R / Rc), out[s][c][r'] = in[s Rc + r'][c], zero where s Rc + r' >= R;
+// Rc % 8 == 0 and C % 8 == 0.
+hipError_t launch_transpose_bf16(const __bf16* in, int R, int C, int Rc, __bf16* out,
+                                 hipStream_t stream);
+// out[i] = sum_s part[s * n + i], fp32, n % 4 == 0
+hipError_t launch_sum_partials(const float* part, int S, long long n, float* out,
+                               hipStream_t stream);
 hipError_t launch_attn_decode_bf16(const AttnArgs& args, hipStream_t stream);
 
 // fp32 path (any even head_dim up to 256)
