@@ -51,6 +51,16 @@ def flops_of(w):
     return {"qkv": qkv, "attn": attn, "oproj": oproj, "total": qkv + attn + oproj}
 
 
+def bwd_flops_of(w):
+    """Algorithmic FLOPs of the layer backward: each projection's input and
+    weight gradients (two products the size of its forward), and the
+    attention's five products over the visible pairs (scores recomputed,
+    dP, dV, dQ, dK) where the forward has two."""
+    f = flops_of(w)
+    qkv, oproj, attn = 2.0 * f["qkv"], 2.0 * f["oproj"], 2.5 * f["attn"]
+    return {"qkv": qkv, "attn": attn, "oproj": oproj, "total": qkv + attn + oproj}
+
+
 def kv_bytes_of(w):
     """Bytes of K and V a decode step must read: every valid row of the
     cache including the appended one, for every sequence and KV head."""
@@ -161,6 +171,40 @@ def bench_prefill(w, steps, warmup, torch, T, GI):
             fn()
         part_ms[k] = _time_loop(fn, steps, torch)
     return ms, part_ms
+
+
+def bench_train(w, steps, warmup, torch, T, GI):
+    """The training pair on a prefill workload: gqa_layer_forward_train
+    (which also keeps q, k, v, o, the fp32 projection and the row
+    log-sum-exps) and gqa_layer_backward, each timed over `steps` calls."""
+    cfg = T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
+                      head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+                      qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True,
+                      rotary_dim=w.rotary_dim)
+    h = GI.device_layer_inputs(w)
+    dout = GI.device_upstream_grad(w)
+    out = torch.empty((w.batch, w.seq, w.hidden), dtype=torch.float32, device="cuda")
+    saved = T.TrainSaved(cfg, w.batch, w.seq)
+    ws = T.BackwardWorkspace(cfg, w.batch, w.seq)
+    args5 = (cfg, h["x"], h["w_qkv"], h["q_norm_w"], h["k_norm_w"], h["w_o"])
+
+    def fwd():
+        T.gqa_layer_forward_train(*args5, saved=saved, out=out)
+
+    fwd()
+    grads = T.gqa_layer_backward(*args5, saved, dout, workspace=ws)
+
+    def bwd():
+        T.gqa_layer_backward(*args5, saved, dout, grads=grads, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    fwd_ms = _time_loop(fwd, steps, torch)
+    bwd_ms = _time_loop(bwd, steps, torch)
+    del saved, ws, grads
+    torch.cuda.empty_cache()
+    return fwd_ms, bwd_ms
 
 
 def bench_decode(w, steps, warmup, torch, T, GI):
@@ -277,6 +321,8 @@ def main():
     ap.add_argument("--workload", default="prefill_h1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training forward + backward timing")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured GEMM / read references")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -336,6 +382,18 @@ def main():
                               "frac": round(gbs / PEAK_HBM_GBS, 4),
                               "traffic": stored_traffic(w.name, "attn_decode"),
                               "algorithmic_bytes": kvb, "avg_launch_ms": round(attn_ms, 5)}
+
+    if w.cache_len == 0 and not args.no_train and w.dtype == "bf16" and w.d in (64, 128) \
+            and not w.o_split:
+        fwd_ms, bwd_ms = bench_train(w, args.steps, args.warmup, torch, T, GI)
+        fb = bwd_flops_of(w)
+        ff = flops_of(w)
+        bt = fb["total"] / (bwd_ms * 1e-3) / 1e12
+        result["training"] = {
+            "forward_train_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+            "backward_tflops": round(bt, 2), "backward_frac_of_peak": round(bt / peak, 4),
+            "step_tflops": round((ff["total"] + fb["total"]) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
+            "backward_algorithmic_flop": fb["total"]}
 
     if w.cache_len == 0 and not args.no_decode:
         dec = {}

@@ -223,9 +223,11 @@ def test_training_entry_points_validate_before_launch(backward):
         "GQA_ERR_UNSUPPORTED_SHAPE"
     assert name(_raw_train(cfg(), 2, 16, null_saved=True, backward=backward)) == \
         "GQA_ERR_INVALID_ARG"
-    if backward:
-        assert name(_raw_train(cfg(), 2, 16, ws_bytes=64, backward=True)) == \
-            "GQA_ERR_WORKSPACE_TOO_SMALL"
+    # the vectorised norm/RoPE passes turn 4 features per lane: rotary width % 8
+    assert name(_raw_train(cfg(rotary_dim=36), 2, 16, backward=backward)) == \
+        "GQA_ERR_UNSUPPORTED_SHAPE"
+    assert name(_raw_train(cfg(), 2, 16, ws_bytes=64, backward=backward)) == \
+        "GQA_ERR_WORKSPACE_TOO_SMALL"
 
 
 def test_backward_workspace_covers_its_buffers():
@@ -238,5 +240,6 @@ def test_backward_workspace_covers_its_buffers():
     n = T.gqa_workspace_bytes(c, B, L, L, T.WS_BACKWARD)
     floor = T_ * qw * 2 + T_ * nq * 2 + T_ * (qw + 2 * kvw) * 4 + T_ * (H + qw + nq + H) * 2
     assert n >= floor
-    assert T.gqa_workspace_bytes(c, B, L, L, T.WS_TRAIN_FORWARD) == 0
+    # the training forward's RoPE table: L rows of d/2 (cos, sin) pairs
+    assert T.gqa_workspace_bytes(c, B, L, L, T.WS_TRAIN_FORWARD) == L * 64 * 8
     assert T.gqa_workspace_bytes(cfg(dtype="f32"), B, L, L, T.WS_BACKWARD) > 0  # sized, then rejected

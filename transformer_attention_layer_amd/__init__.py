@@ -363,9 +363,11 @@ class TrainSaved:
 
 
 def gqa_layer_forward_train(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
-                            saved: TrainSaved = None, out=None, stream=None):
+                            saved: TrainSaved = None, out=None, workspace=None, stream=None):
     """The layer forward without a cache that keeps what the backward needs.
-    Returns (out [B, L, hidden], saved)."""
+    ``workspace``: a uint8 device tensor of gqa_workspace_bytes(...,
+    WS_TRAIN_FORWARD) bytes (allocated when omitted).  Returns
+    (out [B, L, hidden], saved)."""
     torch = _torch()
     hkv, d = _res(cfg)
     dt = _dt(cfg)
@@ -381,11 +383,14 @@ def gqa_layer_forward_train(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *
     if out is None:
         out = torch.empty((B, L, H), dtype=_out_dt(cfg), device=x.device)
     _need(out, "out", _out_dt(cfg), (B, L, H))
+    if workspace is None:
+        workspace = _workspace(gqa_workspace_bytes(cfg, B, L, L, WS_TRAIN_FORWARD), x.device)
     cc, cs = cfg.c(), saved.c()
     _check(lib().gqa_layer_forward_train(
         ctypes.byref(cc), B, L, _ptr(x), _ptr(w_qkv),
         _ptr(q_norm_w) if cfg.qk_norm else None, _ptr(k_norm_w) if cfg.qk_norm else None,
-        _ptr(w_o), ctypes.byref(cs), _ptr(out), None, 0, _stream(stream)))
+        _ptr(w_o), ctypes.byref(cs), _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return out, saved
 
 

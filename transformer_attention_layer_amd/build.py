@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libgqa.so")
 SOURCES = ["gqa_api.hip", "gemm_bf16.hip", "attn_bf16.hip", "attn_bwd.hip", "bwd_kernels.hip",
-           "f32_kernels.hip"]
+           "normrope_rows.hip", "f32_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

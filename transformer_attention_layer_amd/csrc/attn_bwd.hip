@@ -257,7 +257,10 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   float lse2 = INFINITY;
   if (row_valid) {
     lse2 = lse_log2(a.lse[qrow]);
-    if (hh == 0) a.D[qrow] = drow;
+    if (hh == 0) {
+      a.D[qrow] = drow;
+      a.lse2[qrow] = lse2;
+    }
   }
 
   floatx16 dq[G::NB];
@@ -320,47 +323,53 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
 // One 64-query tile of one query head for the dK/dV kernel.  Lane = key
 // (l % 32); register r of a 32-query block holds query 8 (r / 4) + 4 hh +
-// r % 4.
+// r % 4.  sl / sD hold the tile's 64 row log-sum-exps (log2 units) and D.
+// Both 32-query blocks always run: a block with no visible pair is masked
+// to p = 0 (it only occurs on the diagonal tile).
 template <int KD>
 __device__ __forceinline__ void dkv_tile(floatx16 (&dk)[Geo<KD>::NB], floatx16 (&dv)[Geo<KD>::NB],
                                          const u32x4 (&kf)[Geo<KD>::NC],
                                          const u32x4 (&vf)[Geo<KD>::NC], const lds_u32x4* sq,
-                                         const lds_u32x4* sd, const SwzOffsets<KD>& so,
-                                         const float* lse_row, const float* d_row, int q0,
+                                         const lds_u32x4* sd, const lds_float* sl,
+                                         const lds_float* sD, const SwzOffsets<KD>& so, int q0,
                                          int kw0, int key, int L, bool causal, float c_log2,
                                          int hh) {
   using G = Geo<KD>;
-  constexpr int TQ = kBwdTQ;
-  u32x4 pf[TQ / 16], dsf[TQ / 16];
-  bool live[TQ / 32];
+  constexpr int TQ = kBwdTQ, QB = TQ / 32;
+  floatx16 s[QB], dp[QB];
   const floatx16 z = {};
+  // the QB score and QB dP accumulation chains are interleaved
 #pragma unroll
-  for (int qb = 0; qb < TQ / 32; ++qb) {
+  for (int c = 0; c < G::NC; ++c) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      s[qb] = mfma32x32x16(sq[qb * 32 * G::NCH + so.row[c]], kf[c], c == 0 ? z : s[qb]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      dp[qb] = mfma32x32x16(sd[qb * 32 * G::NCH + so.row[c]], vf[c], c == 0 ? z : dp[qb]);
+  }
+  u32x4 pf[TQ / 16], dsf[TQ / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
     const int qb0 = q0 + 32 * qb;
-    // wave-uniform: some query of the block sees some key of the wave
-    live[qb] = qb0 < L && (!causal || qb0 + 31 >= kw0);
-    if (!live[qb]) continue;
-    floatx16 s = z, dp = z;
-#pragma unroll
-    for (int c = 0; c < G::NC; ++c) s = mfma32x32x16(sq[qb * 32 * G::NCH + so.row[c]], kf[c], s);
-#pragma unroll
-    for (int c = 0; c < G::NC; ++c) dp = mfma32x32x16(sd[qb * 32 * G::NCH + so.row[c]], vf[c], dp);
-    const bool masked = (causal && qb0 < kw0 + 31) || qb0 + 32 > L;
+    const bool masked = (causal && qb0 < kw0 + 31) || qb0 + 32 > L;  // wave-uniform
     float pv[16], dsv[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const floatx4 l4 = *reinterpret_cast<const lds_floatx4*>(sl + 32 * qb + 8 * i + 4 * hh);
+      const floatx4 d4 = *reinterpret_cast<const lds_floatx4*>(sD + 32 * qb + 8 * i + 4 * hh);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * i + e;
-        const int q = qb0 + 8 * i + 4 * hh + e;
-        const bool qv = q < L;
-        const float l2 = qv ? lse_log2(lse_row[q]) : INFINITY;
-        const float dd = qv ? d_row[q] : 0.f;
-        float p = fast_exp2(__builtin_fmaf(s[r], c_log2, -l2));
-        if (masked && (!qv || (causal && q < key))) p = 0.f;
+        float p = fast_exp2(__builtin_fmaf(s[qb][r], c_log2, -l4[e]));
+        if (masked) {
+          const int q = qb0 + 8 * i + 4 * hh + e;
+          if (q >= L || (causal && q < key)) p = 0.f;
+        }
         pv[r] = p;
-        dsv[r] = p * (dp[r] - dd);
+        dsv[r] = p * (dp[qb][r] - d4[e]);
       }
+    }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       float p8[8], d8[8];
@@ -374,14 +383,12 @@ __device__ __forceinline__ void dkv_tile(floatx16 (&dk)[Geo<KD>::NB], floatx16 (
     }
   }
 #pragma unroll
-  for (int g = 0; g < TQ / 16; ++g) {
-    if (!live[g >> 1]) continue;
+  for (int g = 0; g < TQ / 16; ++g)
 #pragma unroll
     for (int d = 0; d < G::NB; ++d) {
       dv[d] = mfma32x32x16(tr_frag<KD>(sd, so, g, d), pf[g], dv[d]);
       dk[d] = mfma32x32x16(tr_frag<KD>(sq, so, g, d), dsf[g], dk[d]);
     }
-  }
 }
 
 template <int KD>
@@ -391,8 +398,11 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   using Tile = RowTile<KD, TQ, 1>;
   __shared__ u32x4 sq0[TQ * G::NCH], sq1[TQ * G::NCH];
   __shared__ u32x4 sd0[TQ * G::NCH], sd1[TQ * G::NCH];
+  __shared__ float sl0[TQ], sl1[TQ], sD0[TQ], sD1[TQ];
   lds_u32x4* const sq[2] = {(lds_u32x4*)sq0, (lds_u32x4*)sq1};
   lds_u32x4* const sd[2] = {(lds_u32x4*)sd0, (lds_u32x4*)sd1};
+  lds_float* const sl[2] = {(lds_float*)sl0, (lds_float*)sl1};
+  lds_float* const sD[2] = {(lds_float*)sD0, (lds_float*)sD1};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -440,24 +450,32 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
 
   auto head_of = [&](int it) { return kvh * a.G + it / per_head; };
   auto q0_of = [&](int it) { return (qt0 + it % per_head) * TQ; };
-  auto load = [&](int it, lds_u32x4* dq_, lds_u32x4* dd_) {
+  // a tile's Q and dO rows (every wave a share), and its 64 lse2 and D
+  // values (one 4-byte load per lane, waves 0 and 1); rows past L read 0
+  auto load = [&](int it, lds_u32x4* dq_, lds_u32x4* dd_, lds_float* dl_, lds_float* dD_) {
     const int hq = head_of(it), q0 = q0_of(it);
     plan_q.load(rows_rsrc<KD>(a.q + (((size_t)b * a.Hq + hq) * L + q0) * KD, L - q0, G::RB), dq_);
     plan_d.load(rows_rsrc<KD>(a.dO + (((size_t)b * L + q0) * a.Hq + hq) * KD, L - q0, dstride),
                 dd_);
+    const size_t lrow = ((size_t)b * a.Hq + hq) * L + q0;
+    if (wave < 2) {
+      const float* src = wave == 0 ? a.lse2 + lrow : a.D + lrow;
+      lds_float* dst = wave == 0 ? dl_ : dD_;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, (long long)(L - q0) * 4),
+                                               (__attribute__((address_space(3))) void*)dst, 4,
+                                               (unsigned)lane * 4, 0, 0, 0);
+    }
   };
 
-  if (n_it > 0) load(0, sq[0], sd[0]);
+  if (n_it > 0) load(0, sq[0], sd[0], sl[0], sD[0]);
   __syncthreads();
   auto step = [&](auto bufc, int it) {
     constexpr int B = decltype(bufc)::value;
-    if (it + 1 < n_it) load(it + 1, sq[B ^ 1], sd[B ^ 1]);
-    const int hq = head_of(it), q0 = q0_of(it);
-    if (kw0 < L && (!a.causal || q0 + TQ - 1 >= kw0)) {
-      const size_t lrow = ((size_t)b * a.Hq + hq) * L;
-      dkv_tile<KD>(dk, dv, kf, vf, sq[B], sd[B], so, a.lse + lrow, a.D + lrow, q0, kw0, key, L,
+    if (it + 1 < n_it) load(it + 1, sq[B ^ 1], sd[B ^ 1], sl[B ^ 1], sD[B ^ 1]);
+    const int q0 = q0_of(it);
+    if (kw0 < L && (!a.causal || q0 + TQ - 1 >= kw0))
+      dkv_tile<KD>(dk, dv, kf, vf, sq[B], sd[B], sl[B], sD[B], so, q0, kw0, key, L,
                    a.causal != 0, a.scale_log2, hh);
-    }
     __syncthreads();
   };
   for (int it = 0; it < n_it; it += 2) {

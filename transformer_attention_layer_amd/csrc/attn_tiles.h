@@ -13,6 +13,8 @@ namespace {
 // generic-to-LDS conversion (and its null check) is left for the compiler.
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) const floatx4 lds_floatx4;
 
 // Geometry of a K or V tile row for head size KD: KD bf16 = NCH 16-byte
 // chunks; one 64-lane load instruction (64 x 16 B) fills RPI rows.

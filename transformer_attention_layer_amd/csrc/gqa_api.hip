@@ -180,11 +180,22 @@ gqa_status check_fp8_attn(const Shape& s, int q_len) {
   return GQA_OK;
 }
 
+// The vectorised bf16 norm/RoPE pass (head_dim 64, 128, 256; rotary width
+// a multiple of 8) after the fp32 projection; FP8 caches take the general
+// pass, which also encodes.
+bool use_rows_normrope(const Shape& s) {
+  return s.bf16 && !s.kv_fp8 && gqa::normrope_rows_ok(s.d, s.rot);
+}
+
+size_t rope_table_bytes(const Shape& s, size_t rows) {
+  return align_up(rows * (s.rot / 2) * sizeof(float) * 2);
+}
+
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
-  if (use_fused_qkv(s, (long long)T))
-    return align_up(T * (s.rot / 2) * sizeof(float) * 2);  // rope table, T rows max
-  return align_up(T * (size_t)s.n_qkv * sizeof(float));   // fp32 projection output
+  if (use_fused_qkv(s, (long long)T)) return rope_table_bytes(s, T);  // T rows max
+  const size_t y = align_up(T * (size_t)s.n_qkv * sizeof(float));    // fp32 projection output
+  return use_rows_normrope(s) ? y + rope_table_bytes(s, T) : y;
 }
 
 size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
@@ -271,6 +282,34 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     r = check_launch(gqa::launch_gemm_f32(g, st), "qkv projection (f32)");
   }
   if (r != GQA_OK) return r;
+  if (use_rows_normrope(s)) {
+    float2* table =
+        reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up((size_t)T * s.n_qkv * sizeof(float)));
+    const int rows = start_pos ? T : q_len;
+    r = check_launch(
+        gqa::launch_rope_table(table, start_pos, rows, q_len, s.rot / 2, (double)c.rope_theta, st),
+        "rope table");
+    if (r != GQA_OK) return r;
+    gqa::NormRopeRowsArgs n{};
+    n.y = y;
+    n.q_norm_w = static_cast<const __bf16*>(qn);
+    n.k_norm_w = static_cast<const __bf16*>(kn);
+    n.rope = table;
+    n.start_pos = start_pos;
+    n.q = static_cast<__bf16*>(q);
+    n.k_cache = static_cast<__bf16*>(kc);
+    n.v_cache = static_cast<__bf16*>(vc);
+    n.B = batch;
+    n.L = q_len;
+    n.Hq = s.Hq;
+    n.Hkv = s.Hkv;
+    n.d = s.d;
+    n.rot = s.rot;
+    n.cap = cap;
+    n.qk_norm = c.qk_norm;
+    n.eps = c.rms_eps;
+    return check_launch(gqa::launch_normrope_fwd_rows(n, st), "norm + rope");
+  }
   gqa::NormRopeArgs n{};
   n.y = y;
   n.q_norm_w = qn;
@@ -410,6 +449,10 @@ gqa_status check_train(const gqa_config& c, const Shape& s) {
                 "and 128", s.d);
   if (c.o_split || s.kv_fp8)
     return fail(GQA_ERR_UNSUPPORTED_SHAPE, "the training entry points need o_split 0 and kv_fp8 0");
+  if (!gqa::normrope_rows_ok(s.d, s.rot))
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE,
+                "the training entry points need a rotary width that is a multiple of 8 (got %d)",
+                s.rot);
   return GQA_OK;
 }
 
@@ -437,7 +480,7 @@ TokSplit tok_split(long long T, int N, int M) {
 struct BwdLayout {
   TokSplit so, sq;  // splits of the dW_o and dW_qkv products
   int gblocks;      // blocks of the norm/RoPE backward
-  size_t doutT, oT, dwo_part, woT, dO, D, dq, dk, dv, rope, gpart, dy, dyT, xT, dwq_part, wqT;
+  size_t doutT, oT, dwo_part, woT, dO, D, lse2, dq, dk, dv, rope, gpart, dy, dyT, xT, dwq_part, wqT;
   size_t total;
 };
 
@@ -447,7 +490,7 @@ BwdLayout bwd_layout(const Shape& s, int batch, int L) {
   const size_t qw = (size_t)s.Hq * s.d, kvw = (size_t)s.Hkv * s.d;
   b.so = tok_split((long long)T, s.H, (int)qw);
   b.sq = tok_split((long long)T, s.n_qkv, s.H);
-  b.gblocks = (int)((T + gqa::kNormRopeBwdTokens - 1) / gqa::kNormRopeBwdTokens);
+  b.gblocks = gqa::normrope_bwd_blocks(batch, L, s.Hq + 2 * s.Hkv, s.d);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -460,6 +503,7 @@ BwdLayout bwd_layout(const Shape& s, int batch, int L) {
   b.woT = take(qw * s.H * 2);
   b.dO = take(T * qw * 2);
   b.D = take(T * s.Hq * 4);
+  b.lse2 = take(T * s.Hq * 4);
   b.dq = take(T * qw * 4);
   b.dk = take(T * kvw * 4);
   b.dv = take(T * kvw * 4);
@@ -528,7 +572,7 @@ size_t gqa_workspace_bytes(const gqa_config* cfg, int32_t batch, int32_t q_len,
     case GQA_WS_ATTN: return ws_attn(s, batch, q_len, kv_capacity);
     case GQA_WS_LAYER: return ws_layer(s, batch, q_len, kv_capacity);
     case GQA_WS_OPROJ: return 0;
-    case GQA_WS_TRAIN_FORWARD: return 0;
+    case GQA_WS_TRAIN_FORWARD: return rope_table_bytes(s, (size_t)q_len);
     case GQA_WS_BACKWARD: return bwd_layout(s, batch, q_len).total;
     default: return 0;
   }
@@ -639,8 +683,6 @@ gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t
                                    const void* k_norm_w, const void* w_o, const gqa_saved* saved,
                                    void* out, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   gqa_config c;
   Shape s;
   gqa_status r = resolve(cfg, &c, &s);
@@ -654,6 +696,10 @@ gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t
     return fail(GQA_ERR_INVALID_ARG, "every buffer of saved must be non-null");
   if (c.qk_norm && (!q_norm_w || !k_norm_w))
     return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
+  const size_t need = rope_table_bytes(s, (size_t)q_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace_bytes);
   const int T = batch * q_len;
   hipStream_t st = (hipStream_t)stream;
   // fused projection in fp32 (kept), then norm + RoPE + head-major scatter
@@ -668,13 +714,19 @@ gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t
   r = use_skinny(s, T) ? check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection")
                        : check_launch(gqa::launch_gemm_plain_bf16(g, st), "qkv projection");
   if (r != GQA_OK) return r;
-  gqa::NormRopeArgs n{};
+  float2* table = static_cast<float2*>(workspace);
+  r = check_launch(
+      gqa::launch_rope_table(table, nullptr, q_len, q_len, s.rot / 2, (double)c.rope_theta, st),
+      "rope table");
+  if (r != GQA_OK) return r;
+  gqa::NormRopeRowsArgs n{};
   n.y = saved->qkv;
-  n.q_norm_w = q_norm_w;
-  n.k_norm_w = k_norm_w;
-  n.q = saved->q;
-  n.k_cache = saved->k;
-  n.v_cache = saved->v;
+  n.q_norm_w = static_cast<const __bf16*>(q_norm_w);
+  n.k_norm_w = static_cast<const __bf16*>(k_norm_w);
+  n.rope = table;
+  n.q = static_cast<__bf16*>(saved->q);
+  n.k_cache = static_cast<__bf16*>(saved->k);
+  n.v_cache = static_cast<__bf16*>(saved->v);
   n.B = batch;
   n.L = q_len;
   n.Hq = s.Hq;
@@ -683,10 +735,8 @@ gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t
   n.rot = s.rot;
   n.cap = q_len;
   n.qk_norm = c.qk_norm;
-  n.bf16 = 1;
   n.eps = c.rms_eps;
-  n.theta = (double)c.rope_theta;
-  if ((r = check_launch(gqa::launch_normrope(n, st), "norm + rope")) != GQA_OK) return r;
+  if ((r = check_launch(gqa::launch_normrope_fwd_rows(n, st), "norm + rope")) != GQA_OK) return r;
   r = run_attn(c, s, batch, q_len, saved->q, saved->k, saved->v, nullptr, q_len, q_len, saved->o,
                false, nullptr, st, saved->lse);
   if (r != GQA_OK) return r;
@@ -755,6 +805,7 @@ gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_le
   a.dO = bfp(lay.dO);
   a.lse = saved->lse;
   a.D = f32p(lay.D);
+  a.lse2 = f32p(lay.lse2);
   a.dq = f32p(lay.dq);
   a.dk = f32p(lay.dk);
   a.dv = f32p(lay.dv);

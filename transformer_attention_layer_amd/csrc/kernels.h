@@ -77,6 +77,7 @@ struct AttnBwdArgs {
   const __bf16* dO;  // [B, L, Hq * d] its gradient
   const float* lse;  // [B, Hq, L] natural log of each row's softmax denominator
   float* D;          // [B, Hq, L] rowsum(dO * o): written by the dQ kernel
+  float* lse2;       // [B, Hq, L] lse in log2 units (+inf: no visible key): written by the dQ kernel
   float* dq;         // [B, Hq, L, d]
   float* dk;         // [B, Hkv, L, d]
   float* dv;         // [B, Hkv, L, d]
@@ -87,9 +88,27 @@ struct AttnBwdArgs {
 };
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& args, hipStream_t stream);
 
-// Backward through QK-norm and RoPE: per (token, head of the fused
-// projection) the gradient of the projection output, bf16 [T, n_qkv], and
-// per-block partial sums of the norm-weight gradients.
+// QK-norm + RoPE per (token, head) row of an fp32 projection output with
+// bf16 outputs, head_dim 64, 128 or 256 and a rotary width that is a
+// multiple of 8 (normrope_rows_ok); cos / sin from a rope_table.
+struct NormRopeRowsArgs {
+  const float* y;  // [T, n_qkv]
+  const __bf16* q_norm_w;
+  const __bf16* k_norm_w;
+  const float2* rope;    // [rows, rot / 2]: rows = T (indexed by token row) with start_pos, else L
+  const int* start_pos;  // [B] or null
+  __bf16* q;             // [B, Hq, L, d]
+  __bf16* k_cache;       // [B, Hkv, cap, d]
+  __bf16* v_cache;
+  int B, L, Hq, Hkv, d, rot, cap, qk_norm;
+  float eps;
+};
+bool normrope_rows_ok(int d, int rot);
+hipError_t launch_normrope_fwd_rows(const NormRopeRowsArgs& args, hipStream_t stream);
+
+// Backward through QK-norm and RoPE (same shapes and limits): per (token,
+// head of the fused projection) the gradient of the projection output, bf16
+// [T, n_qkv], and per-block partial sums of the norm-weight gradients.
 struct NormRopeBwdArgs {
   const float* dq;  // [B, Hq, L, d]
   const float* dk;  // [B, Hkv, L, d]
@@ -99,11 +118,11 @@ struct NormRopeBwdArgs {
   const __bf16* k_norm_w;
   const float2* rope;  // [L, rot / 2] (cos, sin) of position t
   __bf16* dy;          // [T, n_qkv]
-  float* dgamma_part;  // [blocks][2][d]: q then k weight-gradient partial sums
+  float* dgamma_part;  // [normrope_bwd_blocks][2][d]: q then k weight-gradient partial sums
   int B, L, Hq, Hkv, d, rot, qk_norm;
   float eps;
 };
-constexpr int kNormRopeBwdTokens = 16;  // tokens per block of the norm/RoPE backward
+int normrope_bwd_blocks(int B, int L, int nh, int d);
 hipError_t launch_normrope_bwd(const NormRopeBwdArgs& args, hipStream_t stream);
 // out[k][j] = sum over blocks of part[blk][k][j], k < 2, j < d (fp32)
 hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* dq_w, float* dk_w,

@@ -1,0 +1,258 @@
+// Per-head QK-norm + RoPE of the fused projection output, forward and
+// backward, for bf16 outputs and head_dim 64, 128 or 256 on gfx950 (tutorial
+// "Multi-Head and Grouped-Query Attention (Full Layer)", section 4 steps 2-4;
+// section 3: the norm has dim = head_dim and works within each head).
+//
+// Layout: a row is one (token, head of the fused projection) pair of D
+// features; R = D / 4 lanes hold a row, 4 consecutive features per lane
+// (16-byte fp32 loads), so a wave holds 64 / R rows.  Row reductions are
+// shuffles within the lane group; the RoPE partner of feature e (e +- r/2)
+// is 4 features away per r/8 lanes in the same group (r % 8 == 0), fetched
+// by shuffle.  cos / sin come from a table [positions][r/2] built in double.
+//
+//   forward : out_e = rot(y_e * rs * w_e),   rs = (mean(y^2) + eps)^-1/2
+//   backward: dn = rot^T(g);  dy_e = rs (w_e dn_e - y_e rs^2 mean(w dn y));
+//             dw_e += dn_e y_e rs  (partial sums per block)
+// where rot turns pair (e, e + r/2) by [[c, -s], [s, c]] and passes
+// features r .. D-1 through.
+#include "common.h"
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kRowsNT = 256;
+constexpr int kRowsIter = 8;  // rows per lane group per block
+
+template <int R>
+GQA_DEV float group_sum(float v) {
+#pragma unroll
+  for (int o = R / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+GQA_DEV floatx4 ld_f4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+
+GQA_DEV floatx4 bf16x4_to_f4(u32x2 w) {
+  return floatx4{lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y)};
+}
+
+GQA_DEV u32x2 f4_to_bf16x4(floatx4 v) {
+  return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// Partner values of this lane's 4 features (feature e -> e + rh for e < rh,
+// e - rh for rh <= e < rot); lanes of other features get their own values.
+template <int R>
+GQA_DEV floatx4 partner4(floatx4 v, int sub, int rh4, int rot4) {
+  const int base = threadIdx.x & 63 & ~(R - 1);
+  int src = sub;
+  if (sub < rh4) src = sub + rh4;
+  else if (sub < rot4) src = sub - rh4;
+  floatx4 p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __shfl(v[i], base + src, 64);
+  return p;
+}
+
+// (cos, sin) of this lane's 4 features at table row `pos`
+GQA_DEV void cossin4(const float2* rope, int rh, int pos, int e0, floatx4& c, floatx4& s) {
+  const int j0 = e0 < rh ? e0 : e0 - rh;
+  const floatx4 a = ld_f4(reinterpret_cast<const float*>(rope + (size_t)pos * rh + j0));
+  const floatx4 b = ld_f4(reinterpret_cast<const float*>(rope + (size_t)pos * rh + j0 + 2));
+  c = floatx4{a[0], a[2], b[0], b[2]};
+  s = floatx4{a[1], a[3], b[1], b[3]};
+}
+
+template <int D>
+__global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRowsArgs a) {
+  constexpr int R = D / 4, RPW = 64 / R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % R, e0 = 4 * sub;
+  const int nh = a.Hq + 2 * a.Hkv;
+  const long long rows = (long long)a.B * a.L * nh;
+  const int rh = a.rot >> 1, rh4 = rh / 4, rot4 = a.rot / 4;
+  const size_t n_qkv = (size_t)nh * D;
+  const long long r0 = ((long long)blockIdx.x * kRowsIter * (kRowsNT / 64) + wave) * RPW + lane / R;
+#pragma unroll 2
+  for (int it = 0; it < kRowsIter; ++it) {
+    const long long r = r0 + (long long)it * (kRowsNT / 64) * RPW;
+    const bool live = r < rows;  // uniform within a lane group
+    const long long m = live ? r / nh : 0;
+    const int head = live ? (int)(r - m * nh) : 0;
+    const int b = (int)(m / a.L), tok = (int)(m - (long long)b * a.L);
+    int kind, h;
+    if (head < a.Hq) { kind = 0; h = head; }
+    else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
+    else { kind = 2; h = head - a.Hq - a.Hkv; }
+    floatx4 y = ld_f4(a.y + (size_t)m * n_qkv + (size_t)head * D + e0);
+    const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
+    if (kind != 2) {
+      if (a.qk_norm) {
+        const float ss = group_sum<R>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
+        const float rs = 1.0f / sqrtf(ss / (float)D + a.eps);
+        const floatx4 w = bf16x4_to_f4(ld8((kind == 0 ? a.q_norm_w : a.k_norm_w) + e0));
+        y = y * rs * w;
+      }
+      const floatx4 p = partner4<R>(y, sub, rh4, rot4);
+      if (e0 < a.rot) {
+        floatx4 c, s;
+        cossin4(a.rope, rh, a.start_pos ? (int)m : tok, e0, c, s);
+        y = e0 < rh ? y * c - p * s : y * c + p * s;
+      }
+    }
+    if (!live) continue;
+    bf16* dst;
+    if (kind == 0) {
+      dst = a.q + (((size_t)b * a.Hq + h) * a.L + tok) * D;
+    } else {
+      if (pos < 0 || pos >= a.cap) continue;
+      dst = (kind == 1 ? a.k_cache : a.v_cache) + (((size_t)b * a.Hkv + h) * a.cap + pos) * D;
+    }
+    st8(dst + e0, f4_to_bf16x4(y));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdArgs a) {
+  constexpr int R = D / 4, RPW = 64 / R;
+  __shared__ floatx4 red[kRowsNT / 64][RPW][2][R];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % R, e0 = 4 * sub, grp = lane / R;
+  const int nh = a.Hq + 2 * a.Hkv;
+  const long long rows = (long long)a.B * a.L * nh;
+  const int rh = a.rot >> 1, rh4 = rh / 4, rot4 = a.rot / 4;
+  const size_t n_qkv = (size_t)nh * D;
+  floatx4 gw[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  const long long r0 = ((long long)blockIdx.x * kRowsIter * (kRowsNT / 64) + wave) * RPW + grp;
+#pragma unroll 2
+  for (int it = 0; it < kRowsIter; ++it) {
+    const long long r = r0 + (long long)it * (kRowsNT / 64) * RPW;
+    const bool live = r < rows;
+    const long long m = live ? r / nh : 0;
+    const int head = live ? (int)(r - m * nh) : 0;
+    const int b = (int)(m / a.L), tok = (int)(m - (long long)b * a.L);
+    int kind, h;
+    if (head < a.Hq) { kind = 0; h = head; }
+    else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
+    else { kind = 2; h = head - a.Hq - a.Hkv; }
+    const float* g = kind == 0   ? a.dq + (((size_t)b * a.Hq + h) * a.L + tok) * D
+                     : kind == 1 ? a.dk + (((size_t)b * a.Hkv + h) * a.L + tok) * D
+                                 : a.dv + (((size_t)b * a.Hkv + h) * a.L + tok) * D;
+    floatx4 v = ld_f4(g + e0);
+    if (kind != 2) {
+      // RoPE backward: the transpose of the rotation
+      const floatx4 p = partner4<R>(v, sub, rh4, rot4);
+      if (e0 < a.rot) {
+        floatx4 c, s;
+        cossin4(a.rope, rh, tok, e0, c, s);
+        v = e0 < rh ? v * c + p * s : v * c - p * s;
+      }
+      if (a.qk_norm) {
+        const floatx4 y = ld_f4(a.y + (size_t)m * n_qkv + (size_t)head * D + e0);
+        const floatx4 w = bf16x4_to_f4(ld8((kind == 0 ? a.q_norm_w : a.k_norm_w) + e0));
+        const floatx4 wd = w * v;
+        const float ss = group_sum<R>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
+        const float c = group_sum<R>(wd[0] * y[0] + wd[1] * y[1] + wd[2] * y[2] + wd[3] * y[3]);
+        const float rs = 1.0f / sqrtf(ss / (float)D + a.eps);
+        const float k = rs * rs * c / (float)D;
+        if (live) gw[kind] += v * y * rs;
+        v = rs * (wd - y * k);
+      }
+    }
+    if (live) st8(a.dy + (size_t)m * n_qkv + (size_t)head * D + e0, f4_to_bf16x4(v));
+  }
+  if (!a.qk_norm) return;
+  // block partial sums of the two weight gradients
+  red[wave][grp][0][sub] = gw[0];
+  red[wave][grp][1][sub] = gw[1];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 2 * R; idx += kRowsNT) {
+    const int kk = idx / R, sb = idx - kk * R;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kRowsNT / 64; ++w)
+#pragma unroll
+      for (int gq = 0; gq < RPW; ++gq) acc += red[w][gq][kk][sb];
+    *reinterpret_cast<floatx4*>(a.dgamma_part + ((size_t)blockIdx.x * 2 + kk) * D + 4 * sb) = acc;
+  }
+}
+
+// Block (kk, chunk of 64 features): 16 slices of the partials per feature,
+// summed in a fixed order, then the slices.
+__global__ __launch_bounds__(1024) void dgamma_reduce_kernel(const float* __restrict__ part,
+                                                             int blocks, int d, float* dq_w,
+                                                             float* dk_w) {
+  __shared__ float red[16][64];
+  const int kk = blockIdx.y;
+  const int f = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int slice = threadIdx.x >> 6;
+  float s = 0.f;
+  if (f < d) {
+#pragma unroll 4
+    for (int i = slice; i < blocks; i += 16) s += part[((size_t)i * 2 + kk) * d + f];
+  }
+  red[slice][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (slice == 0 && f < d) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += red[i][threadIdx.x & 63];
+    (kk == 0 ? dq_w : dk_w)[f] = t;
+  }
+}
+
+template <int D>
+long long rows_blocks(long long rows) {
+  const long long per = (long long)kRowsIter * (kRowsNT / 64) * (64 / (D / 4));
+  return (rows + per - 1) / per;
+}
+
+}  // namespace
+
+bool normrope_rows_ok(int d, int rot) {
+  return (d == 64 || d == 128 || d == 256) && rot % 8 == 0 && rot > 0;
+}
+
+int normrope_bwd_blocks(int B, int L, int nh, int d) {
+  const long long rows = (long long)B * L * nh;
+  switch (d) {
+    case 64: return (int)rows_blocks<64>(rows);
+    case 128: return (int)rows_blocks<128>(rows);
+    case 256: return (int)rows_blocks<256>(rows);
+    default: return 0;
+  }
+}
+
+hipError_t launch_normrope_fwd_rows(const NormRopeRowsArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.L * (a.Hq + 2 * a.Hkv);
+  if (rows == 0) return hipSuccess;
+  if (!normrope_rows_ok(a.d, a.rot)) return hipErrorInvalidValue;
+  switch (a.d) {
+    case 64: normrope_fwd_rows_kernel<64><<<(unsigned)rows_blocks<64>(rows), kRowsNT, 0, stream>>>(a); break;
+    case 128: normrope_fwd_rows_kernel<128><<<(unsigned)rows_blocks<128>(rows), kRowsNT, 0, stream>>>(a); break;
+    default: normrope_fwd_rows_kernel<256><<<(unsigned)rows_blocks<256>(rows), kRowsNT, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_normrope_bwd(const NormRopeBwdArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.L * (a.Hq + 2 * a.Hkv);
+  if (rows == 0) return hipSuccess;
+  if (!normrope_rows_ok(a.d, a.rot)) return hipErrorInvalidValue;
+  switch (a.d) {
+    case 64: normrope_bwd_rows_kernel<64><<<(unsigned)rows_blocks<64>(rows), kRowsNT, 0, stream>>>(a); break;
+    case 128: normrope_bwd_rows_kernel<128><<<(unsigned)rows_blocks<128>(rows), kRowsNT, 0, stream>>>(a); break;
+    default: normrope_bwd_rows_kernel<256><<<(unsigned)rows_blocks<256>(rows), kRowsNT, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* dq_w, float* dk_w,
+                                hipStream_t stream) {
+  dim3 grid((d + 63) / 64, 2);
+  dgamma_reduce_kernel<<<grid, 1024, 0, stream>>>(part, blocks, d, dq_w, dk_w);
+  return hipGetLastError();
+}
+
+}  // namespace gqa
