@@ -86,9 +86,11 @@ def kernel_of_part(w, part: str) -> str:
     return KERNEL_OF_PART[part]
 
 
-SOURCES_OF_KERNEL = {"qkv_gemm": "gemm_bf16.hip", "oproj_gemm": "gemm_bf16.hip",
-                     "attn_prefill": "attn_bf16.hip", "attn_decode": "attn_bf16.hip",
-                     "qkv_gemm_normrope": "gemm_bf16.hip", "attn_vec": "f32_kernels.hip"}
+SOURCES_OF_KERNEL = {"qkv_gemm": ("gemm_bf16.hip",), "oproj_gemm": ("gemm_bf16.hip",),
+                     "attn_prefill": ("attn_bf16.hip", "attn_tiles.h"),
+                     "attn_decode": ("attn_bf16.hip", "attn_tiles.h"),
+                     "qkv_gemm_normrope": ("gemm_bf16.hip", "normrope_rows.hip"),
+                     "attn_vec": ("f32_kernels.hip",)}
 # MI355X fp32 vector peak as published (it counts packed-fp32 issue; plain
 # FMAs, which these kernels use, reach half of it)
 PEAK_F32_VALU_TFLOPS = 157.3
@@ -100,7 +102,7 @@ def kernel_source_sha(kernel: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "transformer_attention_layer_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("common.h", "kernels.h", SOURCES_OF_KERNEL[kernel]):
+    for f in ("common.h", "kernels.h", *SOURCES_OF_KERNEL[kernel]):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
