@@ -25,8 +25,8 @@
 //        group and every query tile that can see them; dV^T += dO^T P and
 //        dK^T += Q^T dS take P and dS from registers, dO^T and Q^T from
 //        transposing LDS reads of the staged tiles.
-// Tiles sit in LDS with the K swizzle; they are read both as MFMA rows and
-// transposed.
+// Tiles sit in LDS with a swizzle under which both their row reads and their
+// transposing reads are free of bank conflicts.
 #include <type_traits>
 
 #include "common.h"
@@ -41,7 +41,7 @@ constexpr int kBwdTK = 64;       // keys per LDS tile (dQ)
 constexpr int kBwdTQ = 64;       // queries per LDS tile (dK/dV)
 constexpr int kBwdKeysWG = 128;  // keys per dK/dV workgroup, 32 per wave
 
-// Fragment offsets into a tile stored with the K swizzle (Geo::kslot).
+// Fragment offsets into a tile stored with the both-way swizzle (Geo::bslot).
 //   row[c]: 16-byte slot of the row fragment for feature step c (row l32,
 //           chunk 2c + hh: features 16c + 8hh .. +7), MFMA A operand over
 //           features.
@@ -63,19 +63,19 @@ __device__ __forceinline__ void swz_offsets(SwzOffsets<KD>& o, int lane) {
   using G = Geo<KD>;
   const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c) o.row[c] = G::kslot(l32, 2 * c + hh);
+  for (int c = 0; c < G::NC; ++c) o.row[c] = G::bslot(l32, 2 * c + hh);
   const int Gq = lane >> 4, j = lane & 15;
   const int r0 = 4 * (Gq >> 1) + (j >> 2);
 #pragma unroll
   for (int d = 0; d < G::NB; ++d) {
     const int feat = 32 * d + 16 * (Gq & 1) + 4 * (j & 3);
-    o.tr0[d] = G::kslot(r0, feat >> 3) * 16 + (feat & 7) * 2;
-    o.tr1[d] = G::kslot(r0 + 8, feat >> 3) * 16 + (feat & 7) * 2;
+    o.tr0[d] = G::bslot(r0, feat >> 3) * 16 + (feat & 7) * 2;
+    o.tr1[d] = G::bslot(r0 + 8, feat >> 3) * 16 + (feat & 7) * 2;
   }
 }
 
 // Loads of a tile of ROWS rows x KD bf16 straight into LDS (buffer_load ...
-// lds) with the K swizzle; consecutive rows are `stride` bytes apart in
+// lds) with the both-way swizzle; consecutive rows are `stride` bytes apart in
 // global memory.  One instruction fills 64 consecutive slots; lane i writes
 // slot i and so loads the chunk the swizzle puts there.  Rows past the
 // descriptor's range read as zero.  USER tells the kernels' instantiations
@@ -94,7 +94,7 @@ struct RowTile {
     for (int j = 0; j < JW; ++j) {
       const int row = (wave * JW + j) * G::RPI + lane / G::NCH;
       const int p = lane % G::NCH;
-      off[j] = (unsigned)(row * stride + ((p ^ G::kswz(row)) << 4));
+      off[j] = (unsigned)(row * stride + ((p ^ G::bswz(row)) << 4));
     }
     slot0 = wave * JW * 64;
   }
@@ -126,6 +126,14 @@ __device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
   return acc;
 }
 
+// s_waitcnt with the vector-memory counter at N (0..63): all but this
+// wave's N most recent vector memory operations (here: LDS DMA) are done.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // log-sum-exp of a row in log2 units of the scaled score; a row with no
 // visible key (-inf) gets +inf, so that every p of it is 0.
 __device__ __forceinline__ float lse_log2(float lse) {
@@ -142,7 +150,7 @@ __device__ __forceinline__ u32x4 pack8(const float (&v)[8]) {
 }
 
 // A operand over 16 rows of row group g for feature block d, from a tile
-// with the K swizzle: rows become the MFMA's K index in the order the score
+// with the both-way swizzle: rows become the MFMA's K index in the order the score
 // registers hold them (4 hh + 0..3, then 8 + 4 hh + 0..3).
 template <int KD>
 __device__ __forceinline__ u32x4 tr_frag(const lds_u32x4* tile, const SwzOffsets<KD>& so, int g,
@@ -167,21 +175,42 @@ __device__ __forceinline__ void dq_tile(floatx16 (&dq)[Geo<KD>::NB],
                                         int kend_row, bool masked, float c_log2, float lse2,
                                         float drow, int hh) {
   using G = Geo<KD>;
-  constexpr int KB = TK / 32;
+  constexpr int KB = TK / 32, NG = TK / 16;
   floatx16 s[KB], dp[KB];
   const floatx16 z = {};
+  // S^T = K Q^T and dP^T = V dO^T over the feature steps; each step's row
+  // fragments are read while the previous step's MFMAs run
+  u32x4 fa[2][2 * KB];  // [buffer][K rows of block kb | V rows of block kb]
+  auto read_rows = [&](int c, u32x4(&f)[2 * KB]) {
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c)
+    for (int kb = 0; kb < KB; ++kb) {
+      f[kb] = sk[kb * 32 * G::NCH + so.row[c]];
+      f[KB + kb] = sv[kb * 32 * G::NCH + so.row[c]];
+    }
+  };
+  read_rows(0, fa[0]);
+#pragma unroll
+  for (int c = 0; c < G::NC; ++c) {
+    if (c + 1 < G::NC) read_rows(c + 1, fa[(c + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      s[kb] = mfma32x32x16(sk[kb * 32 * G::NCH + so.row[c]], qf[c], c == 0 ? z : s[kb]);
-#pragma unroll
-  for (int c = 0; c < G::NC; ++c)
+      s[kb] = mfma32x32x16(fa[c & 1][kb], qf[c], c == 0 ? z : s[kb]);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      dp[kb] = mfma32x32x16(sv[kb * 32 * G::NCH + so.row[c]], df[c], c == 0 ? z : dp[kb]);
+      dp[kb] = mfma32x32x16(fa[c & 1][KB + kb], df[c], c == 0 ? z : dp[kb]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  u32x4 fb[2][G::NB];  // K^T fragments of one 16-key group
+  auto read_tr = [&](int g, u32x4(&f)[G::NB]) {
 #pragma unroll
-  for (int g = 0; g < TK / 16; ++g) {
+    for (int d = 0; d < G::NB; ++d) f[d] = tr_frag<KD>(sk, so, g, d);
+  };
+  read_tr(0, fb[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 dsf[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
     const int kb = g >> 1, rb = 8 * (g & 1);
     float ds[8];
 #pragma unroll
@@ -194,9 +223,17 @@ __device__ __forceinline__ void dq_tile(floatx16 (&dq)[Geo<KD>::NB],
       }
       ds[e] = p * (dp[kb][r] - drow);
     }
-    const u32x4 dsf = pack8(ds);
+    dsf[g] = pack8(ds);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // dQ^T += K^T dS^T per 16-key group, the next group's K^T read meanwhile
 #pragma unroll
-    for (int d = 0; d < G::NB; ++d) dq[d] = mfma32x32x16(tr_frag<KD>(sk, so, g, d), dsf, dq[d]);
+  for (int g = 0; g < NG; ++g) {
+    if (g + 1 < NG) read_tr(g + 1, fb[(g + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < G::NB; ++d) dq[d] = mfma32x32x16(fb[g & 1][d], dsf[g], dq[d]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -335,20 +372,45 @@ __device__ __forceinline__ void dkv_tile(floatx16 (&dk)[Geo<KD>::NB], floatx16 (
                                          int kw0, int key, int L, bool causal, float c_log2,
                                          int hh) {
   using G = Geo<KD>;
-  constexpr int TQ = kBwdTQ, QB = TQ / 32;
+  constexpr int TQ = kBwdTQ, QB = TQ / 32, NG = TQ / 16;
   floatx16 s[QB], dp[QB];
   const floatx16 z = {};
-  // the QB score and QB dP accumulation chains are interleaved
+  // S = Q K^T and dP = dO V^T over the feature steps; each step's row
+  // fragments are read while the previous step's MFMAs run
+  u32x4 fa[2][2 * QB];  // [buffer][Q rows of block qb | dO rows of block qb]
+  auto read_rows = [&](int c, u32x4(&f)[2 * QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f[qb] = sq[qb * 32 * G::NCH + so.row[c]];
+      f[QB + qb] = sd[qb * 32 * G::NCH + so.row[c]];
+    }
+  };
+  read_rows(0, fa[0]);
 #pragma unroll
   for (int c = 0; c < G::NC; ++c) {
+    if (c + 1 < G::NC) read_rows(c + 1, fa[(c + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      s[qb] = mfma32x32x16(sq[qb * 32 * G::NCH + so.row[c]], kf[c], c == 0 ? z : s[qb]);
+      s[qb] = mfma32x32x16(fa[c & 1][qb], kf[c], c == 0 ? z : s[qb]);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-      dp[qb] = mfma32x32x16(sd[qb * 32 * G::NCH + so.row[c]], vf[c], c == 0 ? z : dp[qb]);
+      dp[qb] = mfma32x32x16(fa[c & 1][QB + qb], vf[c], c == 0 ? z : dp[qb]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  u32x4 pf[TQ / 16], dsf[TQ / 16];
+  // the first row group's transposed fragments (dO^T, Q^T) go out now and
+  // land while the softmax terms are formed
+  u32x4 fb[2][2 * G::NB];  // [buffer][dO^T of block d | Q^T of block d]
+  auto read_tr = [&](int g, u32x4(&f)[2 * G::NB]) {
+#pragma unroll
+    for (int d = 0; d < G::NB; ++d) {
+      f[d] = tr_frag<KD>(sd, so, g, d);
+      f[G::NB + d] = tr_frag<KD>(sq, so, g, d);
+    }
+  };
+  read_tr(0, fb[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 pf[NG], dsf[NG];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qb0 = q0 + 32 * qb;
@@ -382,13 +444,20 @@ __device__ __forceinline__ void dkv_tile(floatx16 (&dk)[Geo<KD>::NB], floatx16 (
       dsf[2 * qb + h2] = pack8(d8);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // dV^T += dO^T P and dK^T += Q^T dS per 16-query group; the next group's
+  // fragments are read while the current group's MFMAs run
 #pragma unroll
-  for (int g = 0; g < TQ / 16; ++g)
+  for (int g = 0; g < NG; ++g) {
+    if (g + 1 < NG) read_tr(g + 1, fb[(g + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < G::NB; ++d) {
-      dv[d] = mfma32x32x16(tr_frag<KD>(sd, so, g, d), pf[g], dv[d]);
-      dk[d] = mfma32x32x16(tr_frag<KD>(sq, so, g, d), dsf[g], dk[d]);
+      dv[d] = mfma32x32x16(fb[g & 1][d], pf[g], dv[d]);
+      dk[d] = mfma32x32x16(fb[g & 1][G::NB + d], dsf[g], dk[d]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <int KD>
@@ -396,20 +465,28 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   using G = Geo<KD>;
   constexpr int TQ = kBwdTQ;
   using Tile = RowTile<KD, TQ, 1>;
-  __shared__ u32x4 sq0[TQ * G::NCH], sq1[TQ * G::NCH];
-  __shared__ u32x4 sd0[TQ * G::NCH], sd1[TQ * G::NCH];
-  __shared__ float sl0[TQ], sl1[TQ], sD0[TQ], sD1[TQ];
-  lds_u32x4* const sq[2] = {(lds_u32x4*)sq0, (lds_u32x4*)sq1};
-  lds_u32x4* const sd[2] = {(lds_u32x4*)sd0, (lds_u32x4*)sd1};
-  lds_float* const sl[2] = {(lds_float*)sl0, (lds_float*)sl1};
-  lds_float* const sD[2] = {(lds_float*)sD0, (lds_float*)sD1};
+  // a ring of 3 tile slots: tile it + 2 loads while tile it is used
+  __shared__ u32x4 sq0[TQ * G::NCH], sq1[TQ * G::NCH], sq2[TQ * G::NCH];
+  __shared__ u32x4 sd0[TQ * G::NCH], sd1[TQ * G::NCH], sd2[TQ * G::NCH];
+  __shared__ float sl0[TQ], sl1[TQ], sl2[TQ], sD0[TQ], sD1[TQ], sD2[TQ];
+  lds_u32x4* const sq[3] = {(lds_u32x4*)sq0, (lds_u32x4*)sq1, (lds_u32x4*)sq2};
+  lds_u32x4* const sd[3] = {(lds_u32x4*)sd0, (lds_u32x4*)sd1, (lds_u32x4*)sd2};
+  lds_float* const sl[3] = {(lds_float*)sl0, (lds_float*)sl1, (lds_float*)sl2};
+  lds_float* const sD[3] = {(lds_float*)sD0, (lds_float*)sD1, (lds_float*)sD2};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int kblk = blockIdx.x;  // low key blocks see the most queries: launched first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order: workgroup i runs on XCD i % 8; the key blocks of one
+  // (sequence, KV head) all go to the same XCD, so that they share its L2
+  // for the query tiles they all read (in the same, descending order)
   const int L = a.L;
+  const int nkb = (L + kBwdKeysWG - 1) / kBwdKeysWG;
+  const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
+  const int grp = xcd + 8 * (slot / nkb);  // (sequence, KV head) pair
+  const int kblk = slot - (slot / nkb) * nkb;
+  if (grp >= a.B * a.Hkv) return;  // padding of the grid to a multiple of 8 groups
+  const int b = grp / a.Hkv, kvh = grp - b * a.Hkv;
   const int kwg0 = kblk * kBwdKeysWG;
   const int kw0 = kwg0 + wave * 32;
   const int key = kw0 + l32;
@@ -449,7 +526,7 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   swz_offsets<KD>(so, lane);
 
   auto head_of = [&](int it) { return kvh * a.G + it / per_head; };
-  auto q0_of = [&](int it) { return (qt0 + it % per_head) * TQ; };
+  auto q0_of = [&](int it) { return (nqt - 1 - it % per_head) * TQ; };
   // a tile's Q and dO rows (every wave a share), and its 64 lse2 and D
   // values (one 4-byte load per lane, waves 0 and 1); rows past L read 0
   auto load = [&](int it, lds_u32x4* dq_, lds_u32x4* dd_, lds_float* dl_, lds_float* dD_) {
@@ -468,19 +545,32 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   };
 
   if (n_it > 0) load(0, sq[0], sd[0], sl[0], sD[0]);
-  __syncthreads();
-  auto step = [&](auto bufc, int it) {
-    constexpr int B = decltype(bufc)::value;
-    if (it + 1 < n_it) load(it + 1, sq[B ^ 1], sd[B ^ 1], sl[B ^ 1], sD[B ^ 1]);
+  if (n_it > 1) load(1, sq[1], sd[1], sl[1], sD[1]);
+  // Per tile: wait for this wave's loads of tile it (those of tile it + 1
+  // may stay in flight; loads complete in order), barrier (every wave's
+  // share landed, and every wave is done with tile it - 1), then load tile
+  // it + 2 into the slot of tile it - 1.  Slots are compile-time constants.
+  auto step = [&](auto slotc, int it) {
+    constexpr int S = decltype(slotc)::value;
+    if (it + 1 < n_it) {
+      if (wave < 2) wait_vm<2 * Tile::JW + 1>();
+      else wait_vm<2 * Tile::JW>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int N2 = (S + 2) % 3;
+    if (it + 2 < n_it) load(it + 2, sq[N2], sd[N2], sl[N2], sD[N2]);
     const int q0 = q0_of(it);
     if (kw0 < L && (!a.causal || q0 + TQ - 1 >= kw0))
-      dkv_tile<KD>(dk, dv, kf, vf, sq[B], sd[B], sl[B], sD[B], so, q0, kw0, key, L,
+      dkv_tile<KD>(dk, dv, kf, vf, sq[S], sd[S], sl[S], sD[S], so, q0, kw0, key, L,
                    a.causal != 0, a.scale_log2, hh);
-    __syncthreads();
   };
-  for (int it = 0; it < n_it; it += 2) {
+  for (int it = 0; it < n_it; it += 3) {
     step(std::integral_constant<int, 0>{}, it);
     if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 < n_it) step(std::integral_constant<int, 2>{}, it + 2);
   }
 
   if (!key_valid) return;
@@ -505,8 +595,9 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t stream) {
   attn_bwd_dq_kernel<KD><<<g1, kBwdNT, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2((a.L + kBwdKeysWG - 1) / kBwdKeysWG, a.Hkv, a.B);
-  attn_bwd_dkv_kernel<KD><<<g2, kBwdNT, 0, stream>>>(a);
+  const int nkb = (a.L + kBwdKeysWG - 1) / kBwdKeysWG;
+  const int groups = (a.B * a.Hkv + 7) / 8 * 8;  // the grid maps 8 groups at a time
+  attn_bwd_dkv_kernel<KD><<<groups * nkb, kBwdNT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -43,6 +43,22 @@ struct Geo {
   __device__ static __forceinline__ int vswz(int row) {
     return KD == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
   }
+  // Tiles read both as MFMA rows and transposed (the backward kernels): a
+  // row fragment read wants the 16 rows of a 16-row run on 16 distinct
+  // 16-byte bank slots, a transposing read by 32 lanes wants 4 aligned rows
+  // x 4 aligned chunks on 16 distinct slots.  With 256-byte rows, slot =
+  // chunk ^ (4 (r % 4) + (r / 4) % 4) does both (a bijection over 16 rows
+  // whose bits 2-3 differ across 4 aligned rows); with 128-byte rows two
+  // rows share a bank window and the same holds for
+  // chunk ^ (4 ((r / 2) % 2) + (r / 4) % 4) within each row parity.
+  __device__ static __forceinline__ int bswz(int row) {
+    static_assert(KD == 64 || KD == 128, "both-way tiles: head_dim 64 or 128");
+    return KD == 64 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3))
+                    : (((row & 3) << 2) | ((row >> 2) & 3));
+  }
+  __device__ static __forceinline__ int bslot(int row, int chunk) {
+    return row * NCH + (chunk ^ bswz(row));
+  }
   __device__ static __forceinline__ int kslot(int row, int chunk) {
     return row * NCH + (chunk ^ kswz(row));
   }
