@@ -480,7 +480,7 @@ TokSplit tok_split(long long T, int N, int M) {
 struct BwdLayout {
   TokSplit so, sq;  // splits of the dW_o and dW_qkv products
   int gblocks;      // blocks of the norm/RoPE backward
-  size_t doutT, oT, dwo_part, woT, dO, D, lse2, dq, dk, dv, rope, gpart, dy, dyT, xT, dwq_part, wqT;
+  size_t doutT, oT, dwo_part, woT, dO, D, lse2, dq, dk, dv, rope, gpart, gstage, dy, dyT, xT, dwq_part, wqT;
   size_t total;
 };
 
@@ -509,6 +509,7 @@ BwdLayout bwd_layout(const Shape& s, int batch, int L) {
   b.dv = take(T * kvw * 4);
   b.rope = take((size_t)L * (s.rot / 2) * 8);
   b.gpart = take((size_t)b.gblocks * 2 * s.d * 4);
+  b.gstage = take(gqa::dgamma_stage_floats(s.d) * 4);
   b.dy = take(T * s.n_qkv * 2);
   b.dyT = take((size_t)b.sq.S * b.sq.Rc * s.n_qkv * 2);
   b.xT = take((size_t)b.sq.S * b.sq.Rc * s.H * 2);
@@ -850,7 +851,8 @@ gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_le
     return r;
   if (c.qk_norm) {
     r = check_launch(gqa::launch_dgamma_reduce(f32p(lay.gpart), lay.gblocks, s.d,
-                                               grads->dq_norm_w, grads->dk_norm_w, st),
+                                               f32p(lay.gstage), grads->dq_norm_w,
+                                               grads->dk_norm_w, st),
                      "norm weight gradients");
     if (r != GQA_OK) return r;
   }

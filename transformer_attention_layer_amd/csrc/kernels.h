@@ -124,9 +124,12 @@ struct NormRopeBwdArgs {
 };
 int normrope_bwd_blocks(int B, int L, int nh, int d);
 hipError_t launch_normrope_bwd(const NormRopeBwdArgs& args, hipStream_t stream);
-// out[k][j] = sum over blocks of part[blk][k][j], k < 2, j < d (fp32)
-hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* dq_w, float* dk_w,
-                                hipStream_t stream);
+// dq_w[j] = sum over blocks of part[blk][0][j], dk_w[j] likewise with
+// [blk][1][j] (fp32, fixed order); `stage` holds dgamma_stage_floats(d)
+// floats of scratch.
+size_t dgamma_stage_floats(int d);
+hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* stage, float* dq_w,
+                                float* dk_w, hipStream_t stream);
 // bf16 transpose into row chunks: in [R, C] (row-major) -> out[s][C][Rc] for
 // s < ceil(R / Rc), out[s][c][r'] = in[s Rc + r'][c], zero where s Rc + r' >= R;
 // Rc % 8 == 0 and C % 8 == 0.

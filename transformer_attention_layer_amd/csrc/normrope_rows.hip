@@ -178,27 +178,29 @@ __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdA
   }
 }
 
-// Block (kk, chunk of 64 features): 16 slices of the partials per feature,
-// summed in a fixed order, then the slices.
-__global__ __launch_bounds__(1024) void dgamma_reduce_kernel(const float* __restrict__ part,
-                                                             int blocks, int d, float* dq_w,
-                                                             float* dk_w) {
-  __shared__ float red[16][64];
-  const int kk = blockIdx.y;
-  const int f = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int slice = threadIdx.x >> 6;
-  float s = 0.f;
-  if (f < d) {
-#pragma unroll 4
-    for (int i = slice; i < blocks; i += 16) s += part[((size_t)i * 2 + kk) * d + f];
+// Sum of the per-block partials [blocks][2][d] in two fixed-order stages:
+// stage 1 block j sums partial rows j, j + S1, j + 2 S1, ... (one thread per
+// column of the 2 d columns) into stage[j][2][d]; stage 2 sums the S1 rows.
+constexpr int kReduceS1 = 256;
+
+__global__ __launch_bounds__(256) void dgamma_stage1_kernel(const float* __restrict__ part,
+                                                            int blocks, int d,
+                                                            float* __restrict__ stage) {
+  const int j = blockIdx.x;
+  for (int col = threadIdx.x; col < 2 * d; col += 256) {
+    float s = 0.f;
+    for (int i = j; i < blocks; i += kReduceS1) s += part[(size_t)i * 2 * d + col];
+    stage[(size_t)j * 2 * d + col] = s;
   }
-  red[slice][threadIdx.x & 63] = s;
-  __syncthreads();
-  if (slice == 0 && f < d) {
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) t += red[i][threadIdx.x & 63];
-    (kk == 0 ? dq_w : dk_w)[f] = t;
+}
+
+__global__ __launch_bounds__(256) void dgamma_stage2_kernel(const float* __restrict__ stage, int d,
+                                                            float* dq_w, float* dk_w) {
+  for (int col = threadIdx.x; col < 2 * d; col += 256) {
+    float s = 0.f;
+    for (int j = 0; j < kReduceS1; ++j) s += stage[(size_t)j * 2 * d + col];
+    if (col < d) dq_w[col] = s;
+    else dk_w[col - d] = s;
   }
 }
 
@@ -248,10 +250,14 @@ hipError_t launch_normrope_bwd(const NormRopeBwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* dq_w, float* dk_w,
-                                hipStream_t stream) {
-  dim3 grid((d + 63) / 64, 2);
-  dgamma_reduce_kernel<<<grid, 1024, 0, stream>>>(part, blocks, d, dq_w, dk_w);
+size_t dgamma_stage_floats(int d) { return (size_t)kReduceS1 * 2 * d; }
+
+hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* stage, float* dq_w,
+                                float* dk_w, hipStream_t stream) {
+  dgamma_stage1_kernel<<<kReduceS1, 256, 0, stream>>>(part, blocks, d, stage);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dgamma_stage2_kernel<<<1, 256, 0, stream>>>(stage, d, dq_w, dk_w);
   return hipGetLastError();
 }
 
