@@ -212,17 +212,21 @@ __device__ __forceinline__ void dq_tile(floatx16 (&dq)[Geo<KD>::NB],
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const int kb = g >> 1, rb = 8 * (g & 1);
-    float ds[8];
+    float p[8], ds[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = rb + e;
-      float p = fast_exp2(__builtin_fmaf(s[kb][r], c_log2, -lse2));
-      if (masked) {
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kb][rb + e], c_log2, -lse2));
+    if (masked) {
+      // a real branch: only the diagonal and tail tiles pay for the mask
+      asm volatile("");
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = rb + e;
         const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key >= kend_row) p = 0.f;
+        if (key >= kend_row) p[e] = 0.f;
       }
-      ds[e] = p * (dp[kb][r] - drow);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ds[e] = p[e] * (dp[kb][rb + e] - drow);
     dsf[g] = pack8(ds);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -416,22 +420,25 @@ __device__ __forceinline__ void dkv_tile(floatx16 (&dk)[Geo<KD>::NB], floatx16 (
     const int qb0 = q0 + 32 * qb;
     const bool masked = (causal && qb0 < kw0 + 31) || qb0 + 32 > L;  // wave-uniform
     float pv[16], dsv[16];
+    floatx4 d4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const floatx4 l4 = *reinterpret_cast<const lds_floatx4*>(sl + 32 * qb + 8 * i + 4 * hh);
-      const floatx4 d4 = *reinterpret_cast<const lds_floatx4*>(sD + 32 * qb + 8 * i + 4 * hh);
+      d4[i] = *reinterpret_cast<const lds_floatx4*>(sD + 32 * qb + 8 * i + 4 * hh);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * i + e;
-        float p = fast_exp2(__builtin_fmaf(s[qb][r], c_log2, -l4[e]));
-        if (masked) {
-          const int q = qb0 + 8 * i + 4 * hh + e;
-          if (q >= L || (causal && q < key)) p = 0.f;
-        }
-        pv[r] = p;
-        dsv[r] = p * (dp[qb][r] - d4[e]);
+      for (int e = 0; e < 4; ++e) pv[4 * i + e] = fast_exp2(__builtin_fmaf(s[qb][4 * i + e], c_log2, -l4[e]));
+    }
+    if (masked) {
+      // a real branch: only diagonal and tail tiles pay for the mask
+      asm volatile("");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = qb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (q >= L || (causal && q < key)) pv[r] = 0.f;
       }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsv[r] = pv[r] * (dp[qb][r] - d4[r >> 2][r & 3]);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       float p8[8], d8[8];
