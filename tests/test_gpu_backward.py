@@ -153,3 +153,48 @@ def test_backward_is_deterministic():
     for k in g1:
         if g1[k] is not None:
             assert torch.equal(g1[k], g2[k]), k
+
+
+def test_fullsize_directional_derivatives():
+    """At the bench's size and launch configuration (8 x 2048, 1024-wide,
+    16/8/128), where the float64 oracle is too slow: for each gradient g of a
+    parameter p, the central difference f(p + v) - f(p - v) of
+    f = sum(dout * forward) equals <g, (p + v) - (p - v)> to first order,
+    with v along g itself (a wrong scale, sign or pattern of g breaks it).
+    Step sizes: 0.5% of the parameter's RMS (2% for the 128-entry norm
+    weights, whose bf16 steps are coarse); the bounds cover the O(step^2)
+    truncation and the bf16 rounding noise of two forwards (measured 4e-8 to
+    1.1e-3, and 6e-3 / 1e-2 for the norm weights)."""
+    T = T_()
+    w = GI.WORKLOADS["prefill_h1024"]
+    announce(f"[backward] full size directional derivatives B={w.batch} L={w.seq}")
+    cfg = cfg_of(w)
+    h = GI.device_layer_inputs(w)
+    dout = GI.device_upstream_grad(w)
+    saved = T.TrainSaved(cfg, w.batch, w.seq)
+    out = torch.empty((w.batch, w.seq, w.hidden), dtype=torch.float32, device="cuda")
+
+    def f(p):
+        T.gqa_layer_forward_train(cfg, p["x"], p["w_qkv"], p["q_norm_w"], p["k_norm_w"], p["w_o"],
+                                  saved=saved, out=out)
+        return float((out.double() * dout.double()).sum())
+
+    f(h)
+    g = T.gqa_layer_backward(cfg, h["x"], h["w_qkv"], h["q_norm_w"], h["k_norm_w"], h["w_o"],
+                             saved, dout)
+    g = {k: v.clone() for k, v in g.items()}
+    for name, key, eps, tol in (("x", "dx", 0.005, 1e-2), ("w_qkv", "dw_qkv", 0.005, 1e-2),
+                                ("w_o", "dw_o", 0.005, 1e-2), ("q_norm_w", "dq_norm_w", 0.02, 5e-2),
+                                ("k_norm_w", "dk_norm_w", 0.02, 5e-2)):
+        p0 = h[name]
+        gr = g[key].double()
+        assert torch.isfinite(gr).all(), key
+        v = gr / gr.pow(2).mean().sqrt() * p0.double().pow(2).mean().sqrt() * eps
+        pp, pm = dict(h), dict(h)
+        pp[name] = (p0.double() + v).to(p0.dtype)
+        pm[name] = (p0.double() - v).to(p0.dtype)
+        pred = float((gr * (pp[name].double() - pm[name].double())).sum())
+        est = f(pp) - f(pm)
+        rel = abs(est - pred) / abs(pred)
+        print(f"  {key}: difference {est:.6e} vs <g, step> {pred:.6e}: rel {rel:.2e}", flush=True)
+        assert rel <= tol, (key, est, pred, rel)
