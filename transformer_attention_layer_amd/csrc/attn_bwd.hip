@@ -37,7 +37,7 @@ namespace gqa {
 namespace {
 
 constexpr int kBwdNT = 256;      // 4 waves
-constexpr int kBwdTK = 64;       // keys per LDS tile (dQ)
+constexpr int kBwdTK = 32;       // keys per LDS tile (dQ): small enough for 2 waves per SIMD
 constexpr int kBwdTQ = 64;       // queries per LDS tile (dK/dV)
 constexpr int kBwdKeysWG = 128;  // keys per dK/dV workgroup, 32 per wave
 
@@ -242,7 +242,7 @@ __device__ __forceinline__ void dq_tile(floatx16 (&dq)[Geo<KD>::NB],
 }
 
 template <int KD>
-__global__ __launch_bounds__(kBwdNT) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(kBwdNT, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   using G = Geo<KD>;
   constexpr int TK = kBwdTK;
   using Tile = RowTile<KD, TK, 0>;
