@@ -1,6 +1,7 @@
 /*
  * gqa.h -- C ABI of the MI355X (gfx950) library for the forward pass of a
- * grouped-query attention layer whose head_dim is set explicitly.
+ * grouped-query attention layer whose head_dim is set explicitly, and for
+ * its backward pass (gqa_layer_forward_train / gqa_layer_backward).
  *
  * The layer (tutorial "Multi-Head and Grouped-Query Attention (Full Layer)",
  * section 4, Attention.__call__ steps 1-7; GPT-NeoX issue "Support explicit
@@ -34,6 +35,8 @@
  *   runs a vector-unit attention (correct, much slower).  bf16 also needs num_heads*head_dim and
  *   (num_heads + 2*num_kv_heads)*head_dim to be multiples of 8, and o_split
  *   needs num_heads*head_dim to be a multiple of 32 (GQA_ERR_UNSUPPORTED_SHAPE).
+ * - The training pair takes GQA_BF16 with head_dim 64 or 128 and a rotary
+ *   width that is a multiple of 8; see its declarations below.
  */
 #ifndef GQA_H_
 #define GQA_H_
@@ -210,9 +213,10 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
  * passes; "Attention head partitions: keep each head's dependencies
  * intact": gradients of the shared KV parameters).  No cache: the keys of
  * sequence b are its own q_len tokens at positions 0 .. q_len - 1.
- * Both need cfg->dtype GQA_BF16, head_dim 64 or 128, o_split 0 and kv_fp8 0
- * (else GQA_ERR_UNSUPPORTED_DTYPE / _HEAD_DIM / _SHAPE).  All buffers are
- * device memory owned by the caller.
+ * Both need cfg->dtype GQA_BF16, head_dim 64 or 128, a rotary width that is
+ * a multiple of 8, o_split 0 and kv_fp8 0 (else GQA_ERR_UNSUPPORTED_DTYPE /
+ * _HEAD_DIM / _SHAPE).  All buffers are device memory owned by the caller;
+ * every check runs on the host before any launch.
  */
 typedef struct {
   float* qkv;  /* [batch, q_len, (Hq + 2*Hkv) * d]: the fused projection output
@@ -236,7 +240,8 @@ typedef struct {
 /*
  * The layer forward of gqa_layer_forward without a cache, writing every
  * buffer of *saved; out as there (fp32 when cfg->out_f32).  Needs
- * gqa_workspace_bytes(..., GQA_WS_TRAIN_FORWARD) bytes of workspace.
+ * gqa_workspace_bytes(..., GQA_WS_TRAIN_FORWARD) bytes of workspace (the
+ * RoPE table; GQA_ERR_WORKSPACE_TOO_SMALL otherwise).
  */
 gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t q_len,
                                    const void* x, const void* w_qkv,
