@@ -347,14 +347,15 @@ __global__ __launch_bounds__(kBwdNT, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
   if (!row_valid) return;
   // dQ^T: lane = query, register r of block d = feature 32 d + 8 (r / 4) + 4 hh + r % 4
-  float* dst = a.dq + qrow * KD;
+  bf16* dst = a.dq + qrow * KD;
 #pragma unroll
   for (int d = 0; d < G::NB; ++d)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const floatx4 w = {dq[d][4 * j] * a.scale, dq[d][4 * j + 1] * a.scale,
-                         dq[d][4 * j + 2] * a.scale, dq[d][4 * j + 3] * a.scale};
-      *reinterpret_cast<floatx4*>(dst + 32 * d + 8 * j + 4 * hh) = w;
+      u32x2 w;
+      w.x = pack_bf16x2(dq[d][4 * j] * a.scale, dq[d][4 * j + 1] * a.scale);
+      w.y = pack_bf16x2(dq[d][4 * j + 2] * a.scale, dq[d][4 * j + 3] * a.scale);
+      st8(dst + 32 * d + 8 * j + 4 * hh, w);
     }
 }
 
@@ -582,17 +583,19 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
 
   if (!key_valid) return;
   // dK^T, dV^T: lane = key, register r of block d = feature 32 d + 8 (r / 4) + 4 hh + r % 4
-  float* dkr = a.dk + krow * KD;
-  float* dvr = a.dv + krow * KD;
+  bf16* dkr = a.dk + krow * KD;
+  bf16* dvr = a.dv + krow * KD;
 #pragma unroll
   for (int d = 0; d < G::NB; ++d)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const floatx4 wk = {dk[d][4 * j] * a.scale, dk[d][4 * j + 1] * a.scale,
-                          dk[d][4 * j + 2] * a.scale, dk[d][4 * j + 3] * a.scale};
-      const floatx4 wv = {dv[d][4 * j], dv[d][4 * j + 1], dv[d][4 * j + 2], dv[d][4 * j + 3]};
-      *reinterpret_cast<floatx4*>(dkr + 32 * d + 8 * j + 4 * hh) = wk;
-      *reinterpret_cast<floatx4*>(dvr + 32 * d + 8 * j + 4 * hh) = wv;
+      u32x2 wk, wv;
+      wk.x = pack_bf16x2(dk[d][4 * j] * a.scale, dk[d][4 * j + 1] * a.scale);
+      wk.y = pack_bf16x2(dk[d][4 * j + 2] * a.scale, dk[d][4 * j + 3] * a.scale);
+      wv.x = pack_bf16x2(dv[d][4 * j], dv[d][4 * j + 1]);
+      wv.y = pack_bf16x2(dv[d][4 * j + 2], dv[d][4 * j + 3]);
+      st8(dkr + 32 * d + 8 * j + 4 * hh, wk);
+      st8(dvr + 32 * d + 8 * j + 4 * hh, wv);
     }
 }
 

@@ -514,9 +514,9 @@ BwdLayout bwd_layout(const Shape& s, int batch, int L) {
   b.dO = take(T * qw * 2);
   b.D = take(T * s.Hq * 4);
   b.lse2 = take(T * s.Hq * 4);
-  b.dq = take(T * qw * 4);
-  b.dk = take(T * kvw * 4);
-  b.dv = take(T * kvw * 4);
+  b.dq = take(T * qw * 2);
+  b.dk = take(T * kvw * 2);
+  b.dv = take(T * kvw * 2);
   b.rope = take((size_t)L * (s.rot / 2) * 8);
   b.gpart = take((size_t)b.gblocks * 2 * s.d * 4);
   b.gstage = take(gqa::dgamma_stage_floats(s.d) * 4);
@@ -806,7 +806,7 @@ gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_le
   r = plain_gemm(dout_b, bfp(lay.woT), T, qw, s.H, bfp(lay.dO), 0, st, "dO");
   if (r != GQA_OK) return r;
 
-  // attention: dq, dk, dv (fp32, head-major)
+  // attention: dq, dk, dv (bf16, head-major)
   gqa::AttnBwdArgs a{};
   a.d = s.d;
   a.q = static_cast<const __bf16*>(saved->q);
@@ -817,9 +817,9 @@ gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_le
   a.lse = saved->lse;
   a.D = f32p(lay.D);
   a.lse2 = f32p(lay.lse2);
-  a.dq = f32p(lay.dq);
-  a.dk = f32p(lay.dk);
-  a.dv = f32p(lay.dv);
+  a.dq = bfp(lay.dq);
+  a.dk = bfp(lay.dk);
+  a.dv = bfp(lay.dv);
   a.B = batch;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;

@@ -78,9 +78,9 @@ struct AttnBwdArgs {
   const float* lse;  // [B, Hq, L] natural log of each row's softmax denominator
   float* D;          // [B, Hq, L] rowsum(dO * o): written by the dQ kernel
   float* lse2;       // [B, Hq, L] lse in log2 units (+inf: no visible key): written by the dQ kernel
-  float* dq;         // [B, Hq, L, d]
-  float* dk;         // [B, Hkv, L, d]
-  float* dv;         // [B, Hkv, L, d]
+  __bf16* dq;        // [B, Hq, L, d]
+  __bf16* dk;        // [B, Hkv, L, d]
+  __bf16* dv;        // [B, Hkv, L, d]
   int B, Hq, Hkv, G, L, causal;
   float scale;       // d^-0.5
   float scale_log2;  // scale * log2(e)
@@ -110,10 +110,10 @@ hipError_t launch_normrope_fwd_rows(const NormRopeRowsArgs& args, hipStream_t st
 // head of the fused projection) the gradient of the projection output, bf16
 // [T, n_qkv], and per-block partial sums of the norm-weight gradients.
 struct NormRopeBwdArgs {
-  const float* dq;  // [B, Hq, L, d]
-  const float* dk;  // [B, Hkv, L, d]
-  const float* dv;  // [B, Hkv, L, d]
-  const float* y;   // [T, n_qkv] projection output before norm and RoPE
+  const __bf16* dq;  // [B, Hq, L, d]
+  const __bf16* dk;  // [B, Hkv, L, d]
+  const __bf16* dv;  // [B, Hkv, L, d]
+  const float* y;    // [T, n_qkv] projection output before norm and RoPE
   const __bf16* q_norm_w;
   const __bf16* k_norm_w;
   const float2* rope;  // [L, rot / 2] (cos, sin) of position t

@@ -136,10 +136,10 @@ __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdA
     if (head < a.Hq) { kind = 0; h = head; }
     else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
     else { kind = 2; h = head - a.Hq - a.Hkv; }
-    const float* g = kind == 0   ? a.dq + (((size_t)b * a.Hq + h) * a.L + tok) * D
-                     : kind == 1 ? a.dk + (((size_t)b * a.Hkv + h) * a.L + tok) * D
-                                 : a.dv + (((size_t)b * a.Hkv + h) * a.L + tok) * D;
-    floatx4 v = ld_f4(g + e0);
+    const bf16* g = kind == 0   ? a.dq + (((size_t)b * a.Hq + h) * a.L + tok) * D
+                    : kind == 1 ? a.dk + (((size_t)b * a.Hkv + h) * a.L + tok) * D
+                                : a.dv + (((size_t)b * a.Hkv + h) * a.L + tok) * D;
+    floatx4 v = bf16x4_to_f4(ld8(g + e0));
     if (kind != 2) {
       // RoPE backward: the transpose of the rotation
       const floatx4 p = partner4<R>(v, sub, rh4, rot4);
