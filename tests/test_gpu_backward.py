@@ -57,8 +57,8 @@ def check_grad(got, ref, what):
 
 BASE = GI.WORKLOADS["prefill_h1024"]
 
-# (name, workload): several key/query tiles with ragged tails, GQA groups 2
-# and 4, MQA, head_dim 64 and 128, no mask, no QK-norm, partial rotary.
+# (name, workload): several key/query tiles with ragged tails, GQA groups 2,
+# 3 and 4, MQA, head_dim 64 and 128, no mask, no QK-norm, partial rotary.
 CASES = [
     ("h1024_gqa2_L300", BASE.with_(batch=2, seq=300)),
     ("h1024_gqa2_L1", BASE.with_(batch=3, seq=1)),
@@ -68,6 +68,9 @@ CASES = [
                                                batch=1, causal=False, seed=12)),
     ("h512_d64_nonorm_rot32_L97", BASE.with_(hidden=512, hq=4, hkv=4, head_dim=64, seq=97,
                                              batch=2, qk_norm=False, rotary_dim=32, seed=13)),
+    # an odd group (3 query heads per KV head: one head per wave in dQ)
+    ("h768_gqa3_d64_L190", BASE.with_(hidden=768, hq=12, hkv=4, head_dim=64, seq=190,
+                                      batch=2, seed=14)),
 ]
 
 
