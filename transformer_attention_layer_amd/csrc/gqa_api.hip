@@ -500,7 +500,7 @@ BwdLayout bwd_layout(const Shape& s, int batch, int L) {
   const size_t qw = (size_t)s.Hq * s.d, kvw = (size_t)s.Hkv * s.d;
   b.so = tok_split((long long)T, s.H, (int)qw);
   b.sq = tok_split((long long)T, s.n_qkv, s.H);
-  b.gblocks = gqa::normrope_bwd_blocks(batch, L, s.Hq + 2 * s.Hkv, s.d);
+  b.gblocks = gqa::normrope_bwd_blocks((long long)T, b.sq.Rc, s.Hq + 2 * s.Hkv);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -848,6 +848,8 @@ gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_le
   n.k_norm_w = static_cast<const __bf16*>(k_norm_w);
   n.rope = table;
   n.dy = bfp(lay.dy);
+  n.dyT = bfp(lay.dyT);
+  n.Rc = lay.sq.Rc;
   n.dgamma_part = f32p(lay.gpart);
   n.B = batch;
   n.L = q_len;
@@ -867,10 +869,8 @@ gqa_status gqa_layer_backward(const gqa_config* cfg, int32_t batch, int32_t q_le
     if (r != GQA_OK) return r;
   }
 
-  // fused projection: dW_qkv = dy^T x (token-chunked), dx = dy W_qkv
-  r = check_launch(gqa::launch_transpose_bf16(bfp(lay.dy), T, s.n_qkv, lay.sq.Rc, bfp(lay.dyT), st),
-                   "transpose dy");
-  if (r != GQA_OK) return r;
+  // fused projection: dW_qkv = dy^T x (token-chunked; dy^T came from the
+  // norm/RoPE backward), dx = dy W_qkv
   r = check_launch(gqa::launch_transpose_bf16(x_b, T, s.H, lay.sq.Rc, bfp(lay.xT), st),
                    "transpose x");
   if (r != GQA_OK) return r;

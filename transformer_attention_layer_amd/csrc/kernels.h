@@ -118,11 +118,13 @@ struct NormRopeBwdArgs {
   const __bf16* k_norm_w;
   const float2* rope;  // [L, rot / 2] (cos, sin) of position t
   __bf16* dy;          // [T, n_qkv]
+  __bf16* dyT;         // token chunks [ceil(T / Rc)][n_qkv][Rc] of dy^T, zero past T
+  int Rc;              // tokens per chunk, a multiple of 64
   float* dgamma_part;  // [normrope_bwd_blocks][2][d]: q then k weight-gradient partial sums
   int B, L, Hq, Hkv, d, rot, qk_norm;
   float eps;
 };
-int normrope_bwd_blocks(int B, int L, int nh, int d);
+int normrope_bwd_blocks(long long T, int Rc, int nh);
 hipError_t launch_normrope_bwd(const NormRopeBwdArgs& args, hipStream_t stream);
 // dq_w[j] = sum over blocks of part[blk][0][j], dk_w[j] likewise with
 // [blk][1][j] (fp32, fixed order); `stage` holds dgamma_stage_floats(d)

@@ -113,29 +113,38 @@ __global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRows
   }
 }
 
+// Backward: a block takes one head of the fused projection (the grid's y)
+// over kBwdTokens consecutive tokens (x).  Each row's gradient goes to dy
+// [T, n_qkv] (token-major, for dx = dy W_qkv) and, through an LDS tile, to
+// dyT (token chunks [s][n_qkv][Rc], for dW_qkv = dy^T x): the tile's
+// kBwdTokens tokens lie in one chunk (Rc is a multiple of 64), so every
+// feature's run of tokens is written in one piece.
+constexpr int kBwdTokens = 64;
+
 template <int D>
 __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdArgs a) {
   constexpr int R = D / 4, RPW = 64 / R;
-  __shared__ floatx4 red[kRowsNT / 64][RPW][2][R];
+  constexpr int PASSES = kBwdTokens / (kRowsNT / 64) / RPW;  // rows per lane group
+  static_assert(PASSES * RPW * (kRowsNT / 64) == kBwdTokens, "a block covers kBwdTokens tokens");
+  __shared__ floatx4 red[kRowsNT / 64][RPW][R];
+  __shared__ u32x2 tile[kBwdTokens][R];  // bf16 dy of the block's tokens
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % R, e0 = 4 * sub, grp = lane / R;
-  const int nh = a.Hq + 2 * a.Hkv;
-  const long long rows = (long long)a.B * a.L * nh;
+  const int head = blockIdx.y;
+  const int kind = head < a.Hq ? 0 : head < a.Hq + a.Hkv ? 1 : 2;  // block-uniform
+  const int h = kind == 0 ? head : kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
+  const long long T = (long long)a.B * a.L;
+  const long long m0 = (long long)blockIdx.x * kBwdTokens;
   const int rh = a.rot >> 1, rh4 = rh / 4, rot4 = a.rot / 4;
-  const size_t n_qkv = (size_t)nh * D;
-  floatx4 gw[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-  const long long r0 = ((long long)blockIdx.x * kRowsIter * (kRowsNT / 64) + wave) * RPW + grp;
+  const size_t n_qkv = (size_t)(a.Hq + 2 * a.Hkv) * D;
+  floatx4 gw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
-  for (int it = 0; it < kRowsIter; ++it) {
-    const long long r = r0 + (long long)it * (kRowsNT / 64) * RPW;
-    const bool live = r < rows;
-    const long long m = live ? r / nh : 0;
-    const int head = live ? (int)(r - m * nh) : 0;
-    const int b = (int)(m / a.L), tok = (int)(m - (long long)b * a.L);
-    int kind, h;
-    if (head < a.Hq) { kind = 0; h = head; }
-    else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
-    else { kind = 2; h = head - a.Hq - a.Hkv; }
+  for (int it = 0; it < PASSES; ++it) {
+    const int t = (it * (kRowsNT / 64) + wave) * RPW + grp;  // token within the block
+    const long long m = m0 + t;
+    const bool live = m < T;  // uniform within a lane group
+    const long long mm = live ? m : 0;
+    const int b = (int)(mm / a.L), tok = (int)(mm - (long long)b * a.L);
     const bf16* g = kind == 0   ? a.dq + (((size_t)b * a.Hq + h) * a.L + tok) * D
                     : kind == 1 ? a.dk + (((size_t)b * a.Hkv + h) * a.L + tok) * D
                                 : a.dv + (((size_t)b * a.Hkv + h) * a.L + tok) * D;
@@ -149,32 +158,50 @@ __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdA
         v = e0 < rh ? v * c + p * s : v * c - p * s;
       }
       if (a.qk_norm) {
-        const floatx4 y = ld_f4(a.y + (size_t)m * n_qkv + (size_t)head * D + e0);
+        const floatx4 y = ld_f4(a.y + (size_t)mm * n_qkv + (size_t)head * D + e0);
         const floatx4 w = bf16x4_to_f4(ld8((kind == 0 ? a.q_norm_w : a.k_norm_w) + e0));
         const floatx4 wd = w * v;
         const float ss = group_sum<R>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
         const float c = group_sum<R>(wd[0] * y[0] + wd[1] * y[1] + wd[2] * y[2] + wd[3] * y[3]);
         const float rs = 1.0f / sqrtf(ss / (float)D + a.eps);
         const float k = rs * rs * c / (float)D;
-        if (live) gw[kind] += v * y * rs;
+        if (live) gw += v * y * rs;
         v = rs * (wd - y * k);
       }
     }
-    if (live) st8(a.dy + (size_t)m * n_qkv + (size_t)head * D + e0, f4_to_bf16x4(v));
+    const u32x2 packed = f4_to_bf16x4(v);
+    tile[t][sub] = live ? packed : u32x2{0u, 0u};  // tokens past T: zeros in dyT's padding
+    if (live) st8(a.dy + (size_t)m * n_qkv + (size_t)head * D + e0, packed);
+  }
+  // the transposed copy: feature f's kBwdTokens tokens, 16 bytes per thread
+  const int s_chunk = (int)(m0 / a.Rc);
+  const long long t0 = m0 - (long long)s_chunk * a.Rc;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < D * (kBwdTokens / 8); idx += kRowsNT) {
+    const int f = idx / (kBwdTokens / 8), tg = (idx - f * (kBwdTokens / 8)) * 8;
+    const unsigned short* col = reinterpret_cast<const unsigned short*>(&tile[0][0]) + f;
+    constexpr int RS = R * 4;  // ushorts per tile row
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned)col[(tg + 2 * i) * RS] | ((unsigned)col[(tg + 2 * i + 1) * RS] << 16);
+    st16(a.dyT + ((size_t)s_chunk * n_qkv + (size_t)head * D + f) * a.Rc + t0 + tg, w);
   }
   if (!a.qk_norm) return;
-  // block partial sums of the two weight gradients
-  red[wave][grp][0][sub] = gw[0];
-  red[wave][grp][1][sub] = gw[1];
+  // block partial sums of this head kind's weight gradient (the other kind: 0)
+  red[wave][grp][sub] = gw;
   __syncthreads();
   for (int idx = threadIdx.x; idx < 2 * R; idx += kRowsNT) {
     const int kk = idx / R, sb = idx - kk * R;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (kk == kind) {
 #pragma unroll
-    for (int w = 0; w < kRowsNT / 64; ++w)
+      for (int w = 0; w < kRowsNT / 64; ++w)
 #pragma unroll
-      for (int gq = 0; gq < RPW; ++gq) acc += red[w][gq][kk][sb];
-    *reinterpret_cast<floatx4*>(a.dgamma_part + ((size_t)blockIdx.x * 2 + kk) * D + 4 * sb) = acc;
+        for (int gq = 0; gq < RPW; ++gq) acc += red[w][gq][sb];
+    }
+    const size_t blk = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    *reinterpret_cast<floatx4*>(a.dgamma_part + (blk * 2 + kk) * D + 4 * sb) = acc;
   }
 }
 
@@ -216,14 +243,14 @@ bool normrope_rows_ok(int d, int rot) {
   return (d == 64 || d == 128 || d == 256) && rot % 8 == 0 && rot > 0;
 }
 
-int normrope_bwd_blocks(int B, int L, int nh, int d) {
-  const long long rows = (long long)B * L * nh;
-  switch (d) {
-    case 64: return (int)rows_blocks<64>(rows);
-    case 128: return (int)rows_blocks<128>(rows);
-    case 256: return (int)rows_blocks<256>(rows);
-    default: return 0;
-  }
+// The grid covers every token chunk in full (tiles past T write zeros into
+// dyT's padding, which the weight-gradient GEMM reads).
+long long normrope_bwd_tiles(long long T, int Rc) {
+  return (T + Rc - 1) / Rc * Rc / kBwdTokens;
+}
+
+int normrope_bwd_blocks(long long T, int Rc, int nh) {
+  return (int)(normrope_bwd_tiles(T, Rc) * nh);
 }
 
 hipError_t launch_normrope_fwd_rows(const NormRopeRowsArgs& a, hipStream_t stream) {
@@ -239,13 +266,16 @@ hipError_t launch_normrope_fwd_rows(const NormRopeRowsArgs& a, hipStream_t strea
 }
 
 hipError_t launch_normrope_bwd(const NormRopeBwdArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.B * a.L * (a.Hq + 2 * a.Hkv);
-  if (rows == 0) return hipSuccess;
-  if (!normrope_rows_ok(a.d, a.rot)) return hipErrorInvalidValue;
+  const long long T = (long long)a.B * a.L;
+  if (T == 0) return hipSuccess;
+  if (!normrope_rows_ok(a.d, a.rot) || a.Rc % kBwdTokens != 0) return hipErrorInvalidValue;
+  const long long gx = normrope_bwd_tiles(T, a.Rc);
+  if (gx > 0x7fffffffLL || a.Hq + 2 * a.Hkv > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)gx, a.Hq + 2 * a.Hkv);
   switch (a.d) {
-    case 64: normrope_bwd_rows_kernel<64><<<(unsigned)rows_blocks<64>(rows), kRowsNT, 0, stream>>>(a); break;
-    case 128: normrope_bwd_rows_kernel<128><<<(unsigned)rows_blocks<128>(rows), kRowsNT, 0, stream>>>(a); break;
-    default: normrope_bwd_rows_kernel<256><<<(unsigned)rows_blocks<256>(rows), kRowsNT, 0, stream>>>(a); break;
+    case 64: normrope_bwd_rows_kernel<64><<<grid, kRowsNT, 0, stream>>>(a); break;
+    case 128: normrope_bwd_rows_kernel<128><<<grid, kRowsNT, 0, stream>>>(a); break;
+    default: normrope_bwd_rows_kernel<256><<<grid, kRowsNT, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }
