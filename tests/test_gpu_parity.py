@@ -40,6 +40,11 @@ SMALL = {
     "wide_h5120": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=260),
     "decode_h2560_gqa": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000),
     "decode_h2560_mqa": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777),
+    # key splits merged by the decode combine: 5 (an odd count, so the
+    # combine's lane groups take different numbers of splits) and 69 (more
+    # than one 64-split chunk of weights)
+    "decode_gqa_5_splits": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=5000),
+    "decode_mqa_69_splits": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=1, cache_len=70000),
     # bf16 head sizes other than 128 (separate norm/RoPE pass, vector-unit attention)
     "bf16_d64": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=150, hq=8, hkv=2, head_dim=64),
     "bf16_d256": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=130, hq=4, hkv=2, head_dim=256),

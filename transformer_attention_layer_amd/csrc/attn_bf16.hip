@@ -527,64 +527,62 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_fp8_kernel(AttnArgs a) 
 }
 
 // Merge of the decode splits: one workgroup per (query row, KV head,
-// sequence); lane s first holds split s for the maxima and sums, then lane
-// e accumulates features e, e + 64, ... of every split's partial output.
+// sequence).  Lane s first holds split s for the maxima and sums.  For the
+// outputs the wave is cut into 256 / KD groups of KD / 4 lanes; group g
+// adds splits g, g + 256 / KD, ... with one 16-byte load of four features
+// per lane and split (several splits' loads in flight at once), and the
+// groups' sums are added across lanes at the end.
 template <int KD>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
-  constexpr int FPL = (KD + 63) / 64;  // features per lane
-  __shared__ float wsh[64];
+  constexpr int LPR = KD / 4;    // lanes per row of KD features
+  constexpr int SPL = 64 / LPR;  // splits read per load step
   const int lane = threadIdx.x;
+  const int sg = lane / LPR, e4 = lane % LPR;
   const int row = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int head_local = row / a.Lq;
   const int tq = row - head_local * a.Lq;
   const int hq = kvh * a.G + head_local;
-  const size_t base = (((size_t)b * a.Hkv + kvh) * a.n_splits) * 32 + row;
+  const int ns = a.n_splits;
+  const size_t base = (((size_t)b * a.Hkv + kvh) * ns) * 32 + row;
   float mmax = -INFINITY;
-  for (int s = lane; s < a.n_splits; s += 64) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
+  for (int s = lane; s < ns; s += 64) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
 #pragma unroll
   for (int x = 32; x > 0; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x, 64));
   const float muse = mmax == -INFINITY ? 0.f : mmax;
+  __shared__ float wsh[64];
   float lsum = 0.f;
-  float o[FPL];
-#pragma unroll
-  for (int f = 0; f < FPL; ++f) o[f] = 0.f;
-  const float* po = a.part_o + base * KD;
-  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
-    const int s = s0 + lane;
+  floatx4 o = {0.f, 0.f, 0.f, 0.f};
+  const float* po = a.part_o + base * KD + 4 * e4;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
     float w = 0.f;
-    if (s < a.n_splits) {
-      const float2 ml = a.part_ml[base + (size_t)s * 32];
+    if (s0 + lane < ns) {
+      const float2 ml = a.part_ml[base + (size_t)(s0 + lane) * 32];
       w = fast_exp2(ml.x - muse);
       lsum += w * ml.y;
     }
-    __syncthreads();  // previous chunk's weights are consumed
+    __syncthreads();  // the previous chunk's weights are consumed
     wsh[lane] = w;
     __syncthreads();
-    const int n = min(64, a.n_splits - s0);
-    for (int i = 0; i < n; ++i) {
+    const int n = min(64, ns - s0);
+#pragma unroll 4
+    for (int i = sg; i < n; i += SPL) {
       const float wi = wsh[i];
-      const float* pr = po + (size_t)(s0 + i) * 32 * KD;
-#pragma unroll
-      for (int f = 0; f < FPL; ++f) {
-        const int e = lane + 64 * f;
-        if (e < KD) o[f] += wi * pr[e];
-      }
+      const floatx4 v = *reinterpret_cast<const floatx4*>(po + (size_t)(s0 + i) * 32 * KD);
+      o += wi * v;
     }
   }
 #pragma unroll
   for (int x = 32; x > 0; x >>= 1) lsum += __shfl_xor(lsum, x, 64);
+#pragma unroll
+  for (int x = LPR; x < 64; x <<= 1)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] += __shfl_xor(o[c], x, 64);
+  if (sg != 0) return;
   const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
   const size_t width = (size_t)a.Hq * KD;
   bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
-#pragma unroll
-  for (int f = 0; f < FPL; ++f) {
-    const int e = lane + 64 * f;
-    if (e >= KD) continue;
-    const float h = o[f] * inv;
-    const bf16 hb = (bf16)h;
-    orow[e] = hb;
-    if (a.o_split) orow[width + e] = (bf16)(h - (float)hb);
-  }
+  const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  store_o4(orow + 4 * e4, width, v, a.o_split);
 }
 
 template <int KD>

@@ -147,20 +147,23 @@ bool use_decode(const Shape& s, int q_len) { return s.mfma && s.G * q_len <= 32;
 // Splits of at least kDecodeMinChunk keys: shorter ones make the partial
 // results (32 rows x 128 floats per split) a sizeable share of the traffic.
 // About 4096 waves in all (4 per SIMD of an MI355X) by default.  With few
-// (sequence, KV head) streams, one round of kDecodeRound waves (one per
-// SIMD: the decode kernels run one wave per SIMD) with longer chunks is
-// faster, as long as it still gives each stream 8 or more splits.
-// Measured on 32768-token caches: MQA (64 streams) 5.04 TB/s with 33 splits
-// of 1024 keys (3 rounds, the last 64 waves), 4.9 with 32, 5.29 with 16
-// (one round); GQA (512 streams) 6.05 with 8 splits, 5.94 with 2.
+// (sequence, KV head) streams, one round of waves with longer chunks is
+// faster, as long as it still gives each stream 8 or more splits: 512 waves
+// (two per CU) over a bf16 cache, 1024 over an FP8 cache, whose kernel
+// spends more time per tile in each wave.  Measured on 32768-token caches:
+// MQA (64 streams) 5.40-5.55 TB/s with 8 splits, 5.23-5.33 with 16, 4.5
+// with 6; GQA (512 streams) 6.05 with 8 splits, 5.94 with 2; MQA over an
+// FP8 cache 4.45 TB/s with 16 splits, 2.98 with 8.
 constexpr int kDecodeMinChunk = 1024;
-constexpr long long kDecodeRound = 1024;
+constexpr long long kDecodeRoundBf16 = 512;
+constexpr long long kDecodeRoundFp8 = 1024;
 void decode_split(const Shape& s, int batch, int cap, int* n_splits, int* chunk) {
   const long long streams = (long long)batch * s.Hkv;
   long long want = (4096 + streams - 1) / (streams > 0 ? streams : 1);
   long long max_splits = (cap + kDecodeMinChunk - 1) / kDecodeMinChunk;
   if (want > max_splits) want = max_splits;
-  const long long one_round = kDecodeRound / (streams > 0 ? streams : 1);
+  const long long round = s.kv_fp8 ? kDecodeRoundFp8 : kDecodeRoundBf16;
+  const long long one_round = round / (streams > 0 ? streams : 1);
   if (one_round >= 8 && one_round < want) want = one_round;
   if (want < 1) want = 1;
   int ch = (int)((cap + want - 1) / want);
