@@ -490,6 +490,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           }
         };
         const int mr = mb + l32;
+        if (a.y_raw && mr < M) {  // a.y_raw is wave-uniform
+          float* yr = a.y_raw + (size_t)mr * N + nw + 4 * hh;
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
+                                 acc[f][t][4 * j + 3]};
+              *reinterpret_cast<floatx4*>(yr + 32 * f + 8 * j) = w;
+            }
+        }
         int rb, rtok;
         locate(l32, rb, rtok);
         const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;

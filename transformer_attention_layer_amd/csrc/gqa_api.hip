@@ -242,9 +242,11 @@ gqa_status check_common(const Shape& s, int batch, int q_len, int cap) {
   return GQA_OK;
 }
 
+// y_raw (fused path only): also keep the fp32 projection before norm and RoPE.
 gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, const void* x,
                    const void* w_qkv, const void* qn, const void* kn, const int32_t* start_pos,
-                   void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st) {
+                   void* q, void* kc, void* vc, int cap, void* ws, hipStream_t st,
+                   float* y_raw = nullptr) {
   const int T = batch * q_len;
   if (use_fused_qkv(s, T)) {
     float2* table = reinterpret_cast<float2*>(ws);
@@ -273,6 +275,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     g.qk_norm = c.qk_norm;
     g.rot = s.rot;
     g.eps = c.rms_eps;
+    g.y_raw = y_raw;
     return check_launch(gqa::launch_gemm_qkv_bf16(g, st), "qkv projection");
   }
   float* y = reinterpret_cast<float*>(ws);
@@ -716,6 +719,18 @@ gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t
                 workspace_bytes);
   const int T = batch * q_len;
   hipStream_t st = (hipStream_t)stream;
+  if (use_fused_qkv(s, T)) {
+    // projection with the norm + RoPE epilogue, which also keeps the fp32
+    // projection for the backward
+    r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, nullptr, saved->q, saved->k,
+                saved->v, q_len, workspace, st, saved->qkv);
+    if (r != GQA_OK) return r;
+    r = run_attn(c, s, batch, q_len, saved->q, saved->k, saved->v, nullptr, q_len, q_len,
+                 saved->o, false, nullptr, st, saved->lse);
+    if (r != GQA_OK) return r;
+    r = run_oproj(s, T, saved->o, false, w_o, out, st);
+    return r == GQA_OK ? ok() : r;
+  }
   // fused projection in fp32 (kept), then norm + RoPE + head-major scatter
   gqa::GemmArgs g{};
   g.W = static_cast<const __bf16*>(w_qkv);

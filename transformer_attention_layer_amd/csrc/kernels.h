@@ -34,6 +34,7 @@ struct GemmArgs {
   int L, Hq, Hkv, cap, qk_norm;
   int rot;                // rotary width: 128 (full) or 64 (first half of each head)
   float eps;
+  float* y_raw;           // optional: [M, N] fp32 projection before norm and RoPE
 };
 
 struct AttnArgs {
