@@ -191,6 +191,25 @@ def test_product_path_has_no_oracle_dependency():
                 assert "import oracle" not in txt and "from oracle" not in txt, f
 
 
+def test_missing_library_fails_loudly():
+    """Without the built library the binding raises at its first call
+    instead of falling back to anything else."""
+    import subprocess
+    import sys
+    code = ("import transformer_attention_layer_amd as T\n"
+            "try:\n"
+            "    T.lib()\n"
+            "except ImportError as e:\n"
+            "    print('raised', 'missing' in str(e))\n"
+            "else:\n"
+            "    print('loaded')\n")
+    env = dict(os.environ, GQA_LIB=os.path.join(ROOT, "no_such_dir", "libgqa.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "raised True", r.stdout
+
+
 def _raw_train(c, batch, q_len, saved_ptr=1, ws_bytes=1 << 40, backward=False, null_saved=False):
     L = T.lib()
     cc = c.c()
