@@ -22,7 +22,7 @@ namespace gqa {
 namespace {
 
 constexpr int kRowsNT = 256;
-constexpr int kRowsIter = 8;  // rows per lane group per block
+constexpr int kRowsIter = 8;  // most rows per lane group per block
 
 template <int R>
 GQA_DEV float group_sum(float v) {
@@ -64,23 +64,26 @@ GQA_DEV void cossin4(const float2* rope, int rh, int pos, int e0, floatx4& c, fl
   s = floatx4{a[1], a[3], b[1], b[3]};
 }
 
+// Rows are numbered below 2^31 (the launch checks), so the row -> (token,
+// head) and token -> (sequence, position) splits are 32-bit divisions.
 template <int D>
-__global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRowsArgs a) {
+__global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRowsArgs a, int iters) {
   constexpr int R = D / 4, RPW = 64 / R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % R, e0 = 4 * sub;
   const int nh = a.Hq + 2 * a.Hkv;
-  const long long rows = (long long)a.B * a.L * nh;
+  const unsigned rows = (unsigned)a.B * (unsigned)a.L * (unsigned)nh;
   const int rh = a.rot >> 1, rh4 = rh / 4, rot4 = a.rot / 4;
   const size_t n_qkv = (size_t)nh * D;
-  const long long r0 = ((long long)blockIdx.x * kRowsIter * (kRowsNT / 64) + wave) * RPW + lane / R;
+  const unsigned r0 = ((blockIdx.x * (unsigned)iters) * (kRowsNT / 64) + wave) * RPW + lane / R;
 #pragma unroll 2
-  for (int it = 0; it < kRowsIter; ++it) {
-    const long long r = r0 + (long long)it * (kRowsNT / 64) * RPW;
+  for (int it = 0; it < iters; ++it) {
+    const unsigned r = r0 + (unsigned)it * (kRowsNT / 64) * RPW;
     const bool live = r < rows;  // uniform within a lane group
-    const long long m = live ? r / nh : 0;
-    const int head = live ? (int)(r - m * nh) : 0;
-    const int b = (int)(m / a.L), tok = (int)(m - (long long)b * a.L);
+    const unsigned m = live ? r / (unsigned)nh : 0u;
+    const int head = live ? (int)(r - m * (unsigned)nh) : 0;
+    const unsigned bu = m / (unsigned)a.L;
+    const int b = (int)bu, tok = (int)(m - bu * (unsigned)a.L);
     int kind, h;
     if (head < a.Hq) { kind = 0; h = head; }
     else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
@@ -144,7 +147,8 @@ __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdA
     const long long m = m0 + t;
     const bool live = m < T;  // uniform within a lane group
     const long long mm = live ? m : 0;
-    const int b = (int)(mm / a.L), tok = (int)(mm - (long long)b * a.L);
+    const unsigned bu = (unsigned)mm / (unsigned)a.L;  // T < 2^31 (the launch checks)
+    const int b = (int)bu, tok = (int)((unsigned)mm - bu * (unsigned)a.L);
     const bf16* g = kind == 0   ? a.dq + (((size_t)b * a.Hq + h) * a.L + tok) * D
                     : kind == 1 ? a.dk + (((size_t)b * a.Hkv + h) * a.L + tok) * D
                                 : a.dv + (((size_t)b * a.Hkv + h) * a.L + tok) * D;
@@ -231,10 +235,26 @@ __global__ __launch_bounds__(256) void dgamma_stage2_kernel(const float* __restr
   }
 }
 
+// Rows per lane group and block: kRowsIter for large row counts, fewer
+// when that would leave fewer than about 1024 blocks (a decode step has a
+// few thousand rows, which then spread over many CUs instead of queueing in
+// a few lane groups).
 template <int D>
-long long rows_blocks(long long rows) {
-  const long long per = (long long)kRowsIter * (kRowsNT / 64) * (64 / (D / 4));
-  return (rows + per - 1) / per;
+int rows_iters(long long rows) {
+  const long long per_iter = (long long)(kRowsNT / 64) * (64 / (D / 4));
+  long long it = rows / (per_iter * 1024);
+  if (it > kRowsIter) it = kRowsIter;
+  if (it < 1) it = 1;
+  return (int)it;
+}
+
+template <int D>
+hipError_t launch_rows(const NormRopeRowsArgs& a, long long rows, hipStream_t stream) {
+  const int iters = rows_iters<D>(rows);
+  const long long per = (long long)iters * (kRowsNT / 64) * (64 / (D / 4));
+  const long long blocks = (rows + per - 1) / per;
+  normrope_fwd_rows_kernel<D><<<(unsigned)blocks, kRowsNT, 0, stream>>>(a, iters);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -256,19 +276,19 @@ int normrope_bwd_blocks(long long T, int Rc, int nh) {
 hipError_t launch_normrope_fwd_rows(const NormRopeRowsArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.L * (a.Hq + 2 * a.Hkv);
   if (rows == 0) return hipSuccess;
-  if (!normrope_rows_ok(a.d, a.rot)) return hipErrorInvalidValue;
+  if (!normrope_rows_ok(a.d, a.rot) || rows > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (a.d) {
-    case 64: normrope_fwd_rows_kernel<64><<<(unsigned)rows_blocks<64>(rows), kRowsNT, 0, stream>>>(a); break;
-    case 128: normrope_fwd_rows_kernel<128><<<(unsigned)rows_blocks<128>(rows), kRowsNT, 0, stream>>>(a); break;
-    default: normrope_fwd_rows_kernel<256><<<(unsigned)rows_blocks<256>(rows), kRowsNT, 0, stream>>>(a); break;
+    case 64: return launch_rows<64>(a, rows, stream);
+    case 128: return launch_rows<128>(a, rows, stream);
+    default: return launch_rows<256>(a, rows, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_normrope_bwd(const NormRopeBwdArgs& a, hipStream_t stream) {
   const long long T = (long long)a.B * a.L;
   if (T == 0) return hipSuccess;
-  if (!normrope_rows_ok(a.d, a.rot) || a.Rc % kBwdTokens != 0) return hipErrorInvalidValue;
+  if (!normrope_rows_ok(a.d, a.rot) || a.Rc % kBwdTokens != 0 || T > 0x7fffffffLL)
+    return hipErrorInvalidValue;
   const long long gx = normrope_bwd_tiles(T, a.Rc);
   if (gx > 0x7fffffffLL || a.Hq + 2 * a.Hkv > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)gx, a.Hq + 2 * a.Hkv);
