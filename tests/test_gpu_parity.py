@@ -154,10 +154,12 @@ def test_prefill_variants(variant):
 @pytest.mark.parametrize("tokens", [1, 17, 64, 65, 200, 256])
 def test_few_token_projection_path(tokens):
     """Up to 256 tokens take the weight-streaming projections (32-feature
-    tiles, K split over 8 waves) and a separate norm + RoPE pass; ragged
-    token and feature counts, with and without QK-norm and the hi+lo split."""
+    tiles, K split over 8 waves, and for narrow outputs over workgroups too)
+    and a separate norm + RoPE pass; ragged token and feature counts, with
+    and without QK-norm and the hi+lo split (also with a 1024-wide o_proj,
+    whose K is split over workgroups)."""
     for base, kw in (("prefill_h1024", {}), ("wide_h5120", {"hq": 40, "hkv": 8}),
-                     ("quotient_h4096", {})):
+                     ("quotient_h4096", {}), ("prefill_h1024", {"o_split": True})):
         w = GI.WORKLOADS[base].with_(batch=1, seq=tokens, **kw)
         announce(f"[few tokens] {base} {kw} T={tokens} o_split={w.o_split}")
         h = GI.host_layer_inputs(w)

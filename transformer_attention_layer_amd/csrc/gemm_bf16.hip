@@ -689,10 +689,14 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs
   const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W + (size_t)f0 * Kw, (long long)(N - f0) * Kw * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + (size_t)m0 * K, (long long)(M - m0) * K * 2);
+  // this workgroup's share of K (split z of gridDim.z), then each wave's
   const int ksteps = (K + 15) / 16;
-  const int per = (ksteps + kSkinnyWaves - 1) / kSkinnyWaves;
-  const int kb = wave * per * 16;
-  const int ke = min(K, kb + per * 16);
+  const int zsteps = (ksteps + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int zb = (int)blockIdx.z * zsteps;
+  const int ze = min(ksteps, zb + zsteps);
+  const int per = (max(ze - zb, 0) + kSkinnyWaves - 1) / kSkinnyWaves;
+  const int kb = (zb + wave * per) * 16;
+  const int ke = min(min(K, ze * 16), kb + per * 16);
   constexpr unsigned kOob = 0x80000000u;
 
   floatx16 acc0 = {}, acc1 = {};
@@ -723,6 +727,9 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs
     acc0 += red[w][0][lane];
     acc1 += red[w][1][lane];
   }
+  // split z's partial product goes to part[z]
+  const bool partial = gridDim.z > 1;
+  float* const pz = partial ? a.part + (size_t)blockIdx.z * M * N : nullptr;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const floatx16& c = t == 0 ? acc0 : acc1;
@@ -732,7 +739,10 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs
     for (int j = 0; j < 4; ++j) {
       const int n = f0 + 8 * j + 4 * hh;
       if (n >= N) continue;
-      if (a.out_f32) {
+      if (partial) {
+        floatx4 w = {c[4 * j + 0], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]};
+        *reinterpret_cast<floatx4*>(pz + (size_t)m * N + n) = w;
+      } else if (a.out_f32) {
         floatx4 w = {c[4 * j + 0], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]};
         *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + (size_t)m * N + n) = w;
       } else {
@@ -745,11 +755,49 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs
   }
 }
 
+// out = sum over the splits of part[z] (four elements per thread), fp32 or
+// bf16 (N % 4 == 0)
+__global__ __launch_bounds__(256) void skinny_sum_kernel(const float* __restrict__ part, int S,
+                                                         long long n4, void* out, int out_f32) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  floatx4 acc = reinterpret_cast<const floatx4*>(part)[i];
+  for (int z = 1; z < S; ++z) acc += reinterpret_cast<const floatx4*>(part + (size_t)z * n4 * 4)[i];
+  if (out_f32) {
+    reinterpret_cast<floatx4*>(out)[i] = acc;
+  } else {
+    u32x2 w;
+    w.x = pack_bf16x2(acc[0], acc[1]);
+    w.y = pack_bf16x2(acc[2], acc[3]);
+    reinterpret_cast<u32x2*>(out)[i] = w;
+  }
+}
+
 }  // namespace
 
+// Only when the features alone leave more than half of the CUs idle: a
+// decode step's o_proj (2560 features: 80 workgroups) went from 58 to 30 us
+// (+4 us for the sum) with 4 splits, while its QKV projection (4352
+// features: 136 workgroups) did not gain from 2.
+int skinny_ksplit(int N, int K) {
+  const int wgs = (N + 31) / 32;
+  if (wgs >= 128) return 1;
+  int ks = (256 + wgs - 1) / wgs;
+  const int max_ks = (K + 15) / 16 / kSkinnyWaves;  // at least one K step per wave
+  if (ks > max_ks) ks = max_ks;
+  if (ks > 8) ks = 8;
+  return ks < 1 ? 1 : ks;
+}
+
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
-  dim3 grid((args.N + 31) / 32, (args.M + 63) / 64);
+  const int ks = args.part && args.ksplit > 1 ? args.ksplit : 1;
+  dim3 grid((args.N + 31) / 32, (args.M + 63) / 64, ks);
   gemm_skinny_kernel<<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  const long long n4 = (long long)args.M * args.N / 4;
+  skinny_sum_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, stream>>>(args.part, ks, n4, args.out,
+                                                                       args.out_f32);
   return hipGetLastError();
 }
 

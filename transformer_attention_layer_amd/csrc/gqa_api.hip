@@ -204,11 +204,33 @@ size_t rope_table_bytes(const Shape& s, size_t rows) {
   return align_up(rows * (s.rot / 2) * sizeof(float) * 2);
 }
 
+// Partial products of the few-token projections when their K is split
+// over workgroups: the QKV projection's, and the layer's o_proj's, which
+// reuse the same bytes once the projection has been normalised.
+size_t skinny_part_bytes(const Shape& s, size_t T) {
+  if (!use_skinny(s, (long long)T)) return 0;
+  size_t b = 0;
+  if (s.n_qkv % 4 == 0)
+    b = (size_t)gqa::skinny_ksplit(s.n_qkv, s.H) * T * s.n_qkv * sizeof(float);
+  const int ko = s.Hq * s.d * (s.o_split ? 2 : 1);
+  if (s.H % 4 == 0) {
+    const size_t o = (size_t)gqa::skinny_ksplit(s.H, ko) * T * s.H * sizeof(float);
+    if (o > b) b = o;
+  }
+  return align_up(b);
+}
+
+// Offset of those partial products in the projection's workspace: after
+// the fp32 projection and the RoPE table.
+size_t skinny_part_offset(const Shape& s, size_t T) {
+  const size_t y = align_up(T * (size_t)s.n_qkv * sizeof(float));  // fp32 projection output
+  return use_rows_normrope(s) ? y + align_up(rope_table_bytes(s, T)) : y;
+}
+
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
   if (use_fused_qkv(s, (long long)T)) return rope_table_bytes(s, T);  // T rows max
-  const size_t y = align_up(T * (size_t)s.n_qkv * sizeof(float));    // fp32 projection output
-  return use_rows_normrope(s) ? y + rope_table_bytes(s, T) : y;
+  return skinny_part_offset(s, T) + skinny_part_bytes(s, T);
 }
 
 size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
@@ -289,6 +311,10 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     g.K = s.H;
     g.out = y;
     g.out_f32 = 1;
+    if (use_skinny(s, T) && s.n_qkv % 4 == 0) {
+      g.ksplit = gqa::skinny_ksplit(s.n_qkv, s.H);
+      g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + skinny_part_offset(s, (size_t)T));
+    }
     r = use_skinny(s, T)
             ? check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection (few tokens)")
             : check_launch(gqa::launch_gemm_plain_bf16(g, st), "qkv projection");
@@ -432,8 +458,9 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   return check_launch(gqa::launch_attn_prefill_bf16(a, st), "prefill attention");
 }
 
+// part (few tokens, optional): skinny_part_bytes of scratch for a K split.
 gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, const void* w_o,
-                     void* out, hipStream_t st) {
+                     void* out, hipStream_t st, void* part = nullptr) {
   if (s.bf16) {
     gqa::GemmArgs g{};
     g.W = static_cast<const __bf16*>(w_o);
@@ -444,8 +471,13 @@ gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, co
     g.w_kmod = o_split ? s.Hq * s.d : 0;
     g.out = out;
     g.out_f32 = s.out_f32;
-    if (use_skinny(s, tokens))
+    if (use_skinny(s, tokens)) {
+      if (part && s.H % 4 == 0) {
+        g.ksplit = gqa::skinny_ksplit(s.H, g.K);
+        g.part = static_cast<float*>(part);
+      }
       return check_launch(gqa::launch_gemm_skinny_bf16(g, st), "o_proj (few tokens)");
+    }
     return check_launch(gqa::launch_gemm_plain_bf16(g, st), "o_proj");
   }
   gqa::F32Args g{static_cast<const float*>(o), static_cast<const float*>(w_o),
@@ -691,7 +723,10 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
   r = run_attn(c, s, batch, q_len, qbuf, k_cache, v_cache, cache_len, q_len, kv_capacity, obuf,
                s.o_split, ws_a, st);
   if (r != GQA_OK) return r;
-  r = run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st);
+  // few tokens: the projection's workspace, free again, holds o_proj's partial products
+  r = run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st,
+                use_fused_qkv(s, (long long)T) ? nullptr
+                                                : static_cast<char*>(ws_q) + skinny_part_offset(s, T));
   return r == GQA_OK ? ok() : r;
 }
 

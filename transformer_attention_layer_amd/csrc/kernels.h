@@ -35,7 +35,13 @@ struct GemmArgs {
   int rot;                // rotary width: 128 (full) or 64 (first half of each head)
   float eps;
   float* y_raw;           // optional: [M, N] fp32 projection before norm and RoPE
+  // few-token GEMM only: K split over ksplit workgroups (<= 1: none), whose
+  // fp32 partial products go to part [ksplit][M][N] and are then summed into out
+  int ksplit;
+  float* part;
 };
+// K splits for the few-token GEMM that bring its workgroups to about one per CU
+int skinny_ksplit(int N, int K);
 
 struct AttnArgs {
   int d;            // head_dim: 64, 128 or 256
