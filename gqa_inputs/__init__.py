@@ -95,9 +95,14 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns
     float32 holding exactly representable bf16 values."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return r.astype(np.uint32).view(np.float32).reshape(a.shape)
+    u = a.view(np.uint32)
+    # bits + 0x7FFF + (lowest kept bit), truncated: in 32-bit lanes, in place
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u
+    r &= 0xFFFF0000
+    return r.view(np.float32).reshape(a.shape)
 
 
 def _finish(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -18,8 +18,8 @@ def _lib_or_skip():
     return T.lib()
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "gqa.h")).read()
+def _declared_functions(header="gqa.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                        src, flags=re.M)
@@ -39,6 +39,30 @@ def test_library_exports_every_declared_symbol():
     for n in _declared_functions():
         assert hasattr(L, n), n
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_every_header_has_its_library():
+    """Each header under include/ belongs to one built library."""
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include"))
+                  if f.endswith(".h")) == ["gqa.h", "gqa_peaks.h"]
+
+
+def test_peaks_library_exports_and_checks_arguments():
+    """The measurement microkernels' library exports what include/gqa_peaks.h
+    declares, and rejects bad arguments on the host (nothing launched)."""
+    from transformer_attention_layer_amd import peaks as P
+    if not os.path.exists(P.PEAKS_LIB_PATH):
+        pytest.skip("libgqa_peaks.so not built")
+    L = P.lib()
+    names = _declared_functions("gqa_peaks.h")
+    assert names == ["gqa_peak_mfma_bf16", "gqa_peak_stream_read"]
+    for n in names:
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+    assert L.gqa_peak_mfma_bf16(0, 10, 16, None) == 1          # no workgroups
+    assert L.gqa_peak_mfma_bf16(4, 10, None, None) == 1        # no sink
+    assert L.gqa_peak_stream_read(None, 32768, 4, 16, None) == 1
+    assert L.gqa_peak_stream_read(256, 1000, 4, 16, None) == 1  # size not a multiple of 32768
+    assert L.gqa_peak_stream_read(8, 32768, 4, 16, None) == 1   # misaligned
 
 
 def cfg(**kw):

@@ -201,3 +201,32 @@ def test_fullsize_directional_derivatives():
         rel = abs(est - pred) / abs(pred)
         print(f"  {key}: difference {est:.6e} vs <g, step> {pred:.6e}: rel {rel:.2e}", flush=True)
         assert rel <= tol, (key, est, pred, rel)
+
+
+def test_backward_persistent_gemm_shapes():
+    """A shape whose backward GEMMs walk more than one 256 x 256 tile per
+    workgroup (dx 4096 x 5120: 320 tiles; dO 4096 x 4096; dW_qkv 6144 x
+    5120 over 4096 tokens: 480 tiles, one token chunk; dW_o 5120 x 4096: 320
+    tiles), element by element against the oracle's chain rule in float32;
+    a second backward call is bitwise identical."""
+    w = BASE.with_(batch=16, seq=256, hidden=5120, hq=32, hkv=8, seed=15)
+    announce(f"[backward] persistent GEMM shapes B={w.batch} L={w.seq} H={w.hidden} "
+             f"{w.hq}/{w.hkv}/{w.d}")
+    T = T_()
+    res = resolved(w)
+    h, dout, out, saved, grads = _run(w)
+    g2 = T.gqa_layer_backward(cfg_of(w), *[GI.to_device({k: h[k]}, w)[k] for k in
+                                           ("x", "w_qkv", "q_norm_w", "k_norm_w", "w_o")],
+                              saved, torch.from_numpy(dout).cuda().to(torch.bfloat16))
+    torch.cuda.synchronize()
+    for k in grads:
+        if grads[k] is not None:
+            assert torch.equal(grads[k], g2[k]), k
+    g = O.layer_backward(res, h["x"], h["w_qkv"], h["q_norm_w"], h["k_norm_w"], h["w_o"], dout,
+                         rope_theta=w.rope_theta, rms_eps=w.rms_eps, qk_norm=w.qk_norm,
+                         causal=w.causal, dtype=np.float32)
+    check_grad(to_np(grads["dw_o"]), g["dw_o"], "dW_o")
+    check_grad(to_np(grads["dw_qkv"]), g["dw_qkv"], "dW_qkv")
+    check_grad(to_np(grads["dx"]), g["dx"], "dx")
+    check_grad(to_np(grads["dq_norm_w"]), g["dq_norm_w"], "dq_norm_w")
+    check_grad(to_np(grads["dk_norm_w"]), g["dk_norm_w"], "dk_norm_w")

@@ -1,9 +1,10 @@
-"""Compile the HIP sources of the GQA layer into ``libgqa.so`` (gfx950).
+"""Compile the HIP sources of the GQA layer into ``libgqa.so`` (gfx950), and
+the measurement microkernels into ``libgqa_peaks.so``.
 
 Run ``python -m transformer_attention_layer_amd.build`` or call ``build()``.
 Every source is compiled with hipcc for gfx950 only; packed fp32 VALU forms
-are disabled (``-packed-fp32-ops``), and the objects are linked into one
-shared library next to this file.
+are disabled (``-packed-fp32-ops``), and the objects are linked into shared
+libraries next to this file.
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libgqa.so")
 SOURCES = ["gqa_api.hip", "gemm_bf16.hip", "attn_bf16.hip", "attn_bwd.hip", "bwd_kernels.hip",
            "normrope_rows.hip", "f32_kernels.hip"]
+PEAKS_LIB = os.path.join(HERE, "libgqa_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -37,19 +40,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libgqa.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link ``libgqa.so`` and ``libgqa_peaks.so``;
+    returns the layer library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 
