@@ -374,8 +374,8 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   }
 
   const float lt = sum_xor32(st.l);
-  if (!row_valid) return;  // only the group's real rows are merged
-  const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * 32 + l32;
+  if (!row_valid) return;  // only the group's real rows are kept and merged
+  const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * rows + l32;
   if (hh == 0) a.part_ml[pidx] = make_float2(st.m, lt);
   float* po = a.part_o + pidx * KD;
 #pragma unroll
@@ -513,8 +513,8 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_fp8_kernel(AttnArgs a) 
   }
 
   const float lt = sum_xor32(st.l);
-  if (!row_valid) return;  // only the group's real rows are merged
-  const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * 32 + l32;
+  if (!row_valid) return;  // only the group's real rows are kept and merged
+  const size_t pidx = (((size_t)b * a.Hkv + kvh) * a.n_splits + split) * rows + l32;
   if (hh == 0) a.part_ml[pidx] = make_float2(st.m, lt);
   float* po = a.part_o + pidx * KD;
 #pragma unroll
@@ -543,9 +543,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const int tq = row - head_local * a.Lq;
   const int hq = kvh * a.G + head_local;
   const int ns = a.n_splits;
-  const size_t base = (((size_t)b * a.Hkv + kvh) * ns) * 32 + row;
+  const int rows = a.G * a.Lq;  // partial rows per split
+  const size_t base = (((size_t)b * a.Hkv + kvh) * ns) * rows + row;
   float mmax = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * 32].x);
+  for (int s = lane; s < ns; s += 64) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * rows].x);
 #pragma unroll
   for (int x = 32; x > 0; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x, 64));
   const float muse = mmax == -INFINITY ? 0.f : mmax;
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   for (int s0 = 0; s0 < ns; s0 += 64) {
     float w = 0.f;
     if (s0 + lane < ns) {
-      const float2 ml = a.part_ml[base + (size_t)(s0 + lane) * 32];
+      const float2 ml = a.part_ml[base + (size_t)(s0 + lane) * rows];
       w = fast_exp2(ml.x - muse);
       lsum += w * ml.y;
     }
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll 4
     for (int i = sg; i < n; i += SPL) {
       const float wi = wsh[i];
-      const floatx4 v = *reinterpret_cast<const floatx4*>(po + (size_t)(s0 + i) * 32 * KD);
+      const floatx4 v = *reinterpret_cast<const floatx4*>(po + (size_t)(s0 + i) * rows * KD);
       o += wi * v;
     }
   }

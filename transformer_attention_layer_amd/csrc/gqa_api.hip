@@ -145,7 +145,8 @@ size_t esize(const Shape& s) { return s.bf16 ? 2 : 4; }
 bool use_decode(const Shape& s, int q_len) { return s.mfma && s.G * q_len <= 32; }
 
 // Splits of at least kDecodeMinChunk keys: shorter ones make the partial
-// results (32 rows x 128 floats per split) a sizeable share of the traffic.
+// results (G * q_len rows x head_dim floats per split) a sizeable share of
+// the traffic.
 // About 4096 waves in all (4 per SIMD of an MI355X) by default.  With few
 // (sequence, KV head) streams, one round of waves with longer chunks is
 // faster, as long as it still gives each stream 8 or more splits: 512 waves
@@ -237,7 +238,7 @@ size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
   if (!use_decode(s, q_len)) return 0;
   int ns, ch;
   decode_split(s, batch, cap, &ns, &ch);
-  const size_t parts = (size_t)batch * s.Hkv * ns * 32;
+  const size_t parts = (size_t)batch * s.Hkv * ns * s.G * q_len;  // the group's real rows
   return align_up(parts * s.d * sizeof(float)) + align_up(parts * 2 * sizeof(float));
 }
 
@@ -448,7 +449,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   a.lse = lse;
   if (!lse && use_decode(s, q_len)) {
     decode_split(s, batch, cap, &a.n_splits, &a.chunk);
-    const size_t parts = (size_t)batch * s.Hkv * a.n_splits * 32;
+    const size_t parts = (size_t)batch * s.Hkv * a.n_splits * s.G * q_len;
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(parts * s.d * sizeof(float)));
     return check_launch(gqa::launch_attn_decode_bf16(a, st), "decode attention");

@@ -60,8 +60,8 @@ struct AttnArgs {
   // prefill work split
   int hpw, pb, n_qtiles, n_hsub;
   // split-KV decode
-  float* part_o;       // [B, Hkv, n_splits, 32, d]
-  float2* part_ml;     // [B, Hkv, n_splits, 32] (running max in log2 units, sum)
+  float* part_o;       // [B, Hkv, n_splits, G * Lq, d]
+  float2* part_ml;     // [B, Hkv, n_splits, G * Lq] (running max in log2 units, sum)
   int n_splits, chunk;
   float* lse;          // prefill, optional: [B, Hq, Lq] natural log of each row's softmax denominator
 };
