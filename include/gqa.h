@@ -17,7 +17,9 @@
  * - All tensor arguments are DEVICE pointers owned by the caller; the
  *   library never allocates or frees device memory.  Scratch space comes
  *   from the caller's `workspace` (size from gqa_workspace_bytes, at least
- *   256-byte aligned).  Inputs are read-only; outputs must not alias inputs.
+ *   256-byte aligned), except for gqa_layer_forward_noalloc, which uses a
+ *   static device array of the library's own.  Inputs are read-only;
+ *   outputs must not alias inputs.
  * - One element type per call, cfg->dtype: GQA_BF16 (bf16 storage, fp32
  *   accumulation and fp32 norm/RoPE/softmax) or GQA_F32.
  * - All tensors are dense row-major with the shapes given below.  Rows of x,
@@ -206,6 +208,27 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
                              int32_t kv_capacity, const int32_t* cache_len,
                              void* out, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * gqa_layer_forward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments, outputs and errors as
+ * gqa_layer_forward, and the same kernels, but the workspace is the
+ * library's own static device array of 32 MiB (one per GPU, held until the
+ * process ends).  The call allocates and frees nothing.  A call that needs
+ * more than 32 MiB of workspace (gqa_workspace_bytes(..., GQA_WS_LAYER))
+ * returns GQA_ERR_WORKSPACE_TOO_SMALL and launches nothing; a decode step
+ * of 64 sequences against 32K-token caches needs about 14 MiB.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, or two threads) race and give undefined results.  The array
+ * keeps what the last call left; nothing in it needs to start at zero.
+ */
+gqa_status gqa_layer_forward_noalloc(const gqa_config* cfg, int32_t batch, int32_t q_len,
+                                     const void* x, const void* w_qkv,
+                                     const void* q_norm_w, const void* k_norm_w,
+                                     const void* w_o, void* k_cache, void* v_cache,
+                                     int32_t kv_capacity, const int32_t* cache_len,
+                                     void* out, void* stream);
 
 /*
  * Training: a forward that keeps what the backward reads, and the backward

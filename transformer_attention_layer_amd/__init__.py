@@ -8,7 +8,7 @@ raises at the first call, and there is no fallback path.
 
 Entry points carry the names of the C ABI in ``include/gqa.h``:
 ``qkv_proj_normrope``, ``gqa_attn_core``, ``gqa_o_proj``,
-``gqa_layer_forward``, the training pair ``gqa_layer_forward_train`` and
+``gqa_layer_forward`` (and ``gqa_layer_forward_noalloc``), the training pair ``gqa_layer_forward_train`` and
 ``gqa_layer_backward``, plus ``gqa_resolve`` and ``gqa_workspace_bytes``.
 """
 from __future__ import annotations
@@ -115,11 +115,13 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_core.argtypes = [CP, I32, I32, P, P, P, P, I32, P, P, SZ, P]
         L.gqa_o_proj.argtypes = [CP, I32, P, P, P, P]
         L.gqa_layer_forward.argtypes = [CP, I32, I32, P, P, P, P, P, P, P, I32, P, P, P, SZ, P]
+        L.gqa_layer_forward_noalloc.argtypes = [CP, I32, I32, P, P, P, P, P, P, P, I32, P, P, P]
         SP, GP = ctypes.POINTER(_CSaved), ctypes.POINTER(_CGrads)
         L.gqa_layer_forward_train.argtypes = [CP, I32, I32, P, P, P, P, P, SP, P, P, SZ, P]
         L.gqa_layer_backward.argtypes = [CP, I32, I32, P, P, P, P, P, SP, P, GP, P, SZ, P]
         for f in ("gqa_resolve", "qkv_proj_normrope", "gqa_attn_core", "gqa_o_proj",
-                  "gqa_layer_forward", "gqa_layer_forward_train", "gqa_layer_backward"):
+                  "gqa_layer_forward", "gqa_layer_forward_noalloc", "gqa_layer_forward_train",
+                  "gqa_layer_backward"):
             getattr(L, f).restype = ctypes.c_int
         L.gqa_status_string.argtypes = [ctypes.c_int]
         L.gqa_status_string.restype = ctypes.c_char_p
@@ -339,6 +341,43 @@ def gqa_layer_forward(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *, k_ca
     return out, k_cache, v_cache
 
 
+def gqa_layer_forward_noalloc(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, *, k_cache,
+                              v_cache, cache_len=None, out=None, stream=None):
+    """``gqa_layer_forward`` without a workspace argument: the library's own
+    static scratch memory (one per GPU, shared by every call on that GPU;
+    calls that overlap on one GPU race) serves as the workspace, and the C
+    call allocates nothing.  The caches are required; ``out`` is allocated
+    here when not given.  Raises GQAError (GQA_ERR_WORKSPACE_TOO_SMALL) when
+    the call needs more scratch than the library holds.  Returns
+    (out, k_cache, v_cache)."""
+    torch = _torch()
+    hkv, d = _res(cfg)
+    dt = _dt(cfg)
+    B, L, H = x.shape
+    _need(x, "x", dt, (B, L, cfg.hidden_size))
+    _need(w_qkv, "w_qkv", dt, ((cfg.num_heads + 2 * hkv) * d, H))
+    _need(w_o, "w_o", dt, (H, cfg.num_heads * d))
+    if cfg.qk_norm:
+        _need(q_norm_w, "q_norm_w", dt, (d,))
+        _need(k_norm_w, "k_norm_w", dt, (d,))
+    cdt = _cache_dt(cfg)
+    if k_cache is None or v_cache is None:
+        raise ValueError("k_cache and v_cache are required")
+    cap = k_cache.shape[2]
+    _need(k_cache, "k_cache", cdt, (B, hkv, cap, d))
+    _need(v_cache, "v_cache", cdt, (B, hkv, cap, d))
+    cl = _i32(cache_len, "cache_len", B)
+    if out is None:
+        out = torch.empty((B, L, H), dtype=_out_dt(cfg), device=x.device)
+    _need(out, "out", _out_dt(cfg), (B, L, H))
+    cc = cfg.c()
+    _check(lib().gqa_layer_forward_noalloc(
+        ctypes.byref(cc), B, L, _ptr(x), _ptr(w_qkv),
+        _ptr(q_norm_w) if cfg.qk_norm else None, _ptr(k_norm_w) if cfg.qk_norm else None,
+        _ptr(w_o), _ptr(k_cache), _ptr(v_cache), cap, _ptr(cl), _ptr(out), _stream(stream)))
+    return out, k_cache, v_cache
+
+
 class TrainSaved:
     """Device buffers the training forward writes and the backward reads
     (``gqa_saved`` of the C ABI): qkv [B, L, (Hq+2Hkv)d] fp32 before norm and
@@ -450,6 +489,7 @@ def gqa_layer_backward(cfg: GQAConfig, x, w_qkv, q_norm_w, k_norm_w, w_o, saved:
 __all__ = [
     "GQAConfig", "GQAError", "LIB_PATH", "lib", "gqa_resolve", "gqa_workspace_bytes",
     "qkv_proj_normrope", "gqa_attn_core", "gqa_o_proj", "gqa_layer_forward",
+    "gqa_layer_forward_noalloc",
     "LayerWorkspace", "GQA_F32", "GQA_BF16", "TrainSaved", "gqa_layer_forward_train",
     "BackwardWorkspace", "gqa_layer_backward",
 ]

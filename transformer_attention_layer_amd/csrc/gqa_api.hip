@@ -13,8 +13,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gqa.h"
 #include "kernels.h"
+
+// Scratch memory of gqa_layer_forward_noalloc (see scratch_of_current_device).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -604,6 +610,57 @@ gqa_status plain_gemm(const __bf16* X, const __bf16* W, int M, int N, int K, voi
   return check_launch(gqa::launch_gemm_plain_bf16(g, st), what);
 }
 
+// The checks every layer forward makes on the host before any launch.
+gqa_status check_layer_call(const gqa_config* cfg, int batch, int q_len, const void* x,
+                            const void* w_qkv, const void* q_norm_w, const void* k_norm_w,
+                            const void* w_o, const void* k_cache, const void* v_cache,
+                            int kv_capacity, const void* out, gqa_config* c, Shape* s) {
+  gqa_status r = resolve(cfg, c, s);
+  if (r != GQA_OK) return r;
+  if ((r = check_common(*s, batch, q_len, kv_capacity)) != GQA_OK) return r;
+  if (batch == 0 || q_len == 0) return ok();
+  if (!x || !w_qkv || !w_o || !k_cache || !v_cache || !out)
+    return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, w_o, k_cache, v_cache and out must be non-null");
+  if (c->qk_norm && (!q_norm_w || !k_norm_w))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
+  return check_fp8_attn(*s, q_len);
+}
+
+// The layer's kernels in order (workspace of ws_layer bytes, already checked).
+gqa_status run_layer(const gqa_config& c, const Shape& s, int batch, int q_len, const void* x,
+                     const void* w_qkv, const void* q_norm_w, const void* k_norm_w,
+                     const void* w_o, void* k_cache, void* v_cache, int kv_capacity,
+                     const int32_t* cache_len, void* out, void* workspace, hipStream_t st);
+
+// Scratch of gqa_layer_forward_noalloc: a static device array, one copy per
+// GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is taken once per
+// device with hipGetSymbolAddress (device current) and used from then on.
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+gqa_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GQA_ERR_UNSUPPORTED_SHAPE, "device %d: the static scratch covers devices 0..%d",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -695,19 +752,50 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
                              size_t workspace_bytes, void* stream) {
   gqa_config c;
   Shape s;
-  gqa_status r = resolve(cfg, &c, &s);
-  if (r != GQA_OK) return r;
-  if ((r = check_common(s, batch, q_len, kv_capacity)) != GQA_OK) return r;
-  if (batch == 0 || q_len == 0) return ok();
-  if (!x || !w_qkv || !w_o || !k_cache || !v_cache || !out)
-    return fail(GQA_ERR_INVALID_ARG, "x, w_qkv, w_o, k_cache, v_cache and out must be non-null");
-  if (c.qk_norm && (!q_norm_w || !k_norm_w))
-    return fail(GQA_ERR_INVALID_ARG, "qk_norm is on but a norm weight is null");
-  if ((r = check_fp8_attn(s, q_len)) != GQA_OK) return r;
+  gqa_status r = check_layer_call(cfg, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, w_o, k_cache,
+                                  v_cache, kv_capacity, out, &c, &s);
+  if (r != GQA_OK || batch == 0 || q_len == 0) return r;
   const size_t need = ws_layer(s, batch, q_len, kv_capacity);
   if (!workspace || workspace_bytes < need)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace_bytes);
+  r = run_layer(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, w_o, k_cache, v_cache,
+                kv_capacity, cache_len, out, workspace, (hipStream_t)stream);
+  return r == GQA_OK ? ok() : r;
+}
+
+gqa_status gqa_layer_forward_noalloc(const gqa_config* cfg, int32_t batch, int32_t q_len,
+                                     const void* x, const void* w_qkv, const void* q_norm_w,
+                                     const void* k_norm_w, const void* w_o, void* k_cache,
+                                     void* v_cache, int32_t kv_capacity, const int32_t* cache_len,
+                                     void* out, void* stream) {
+  gqa_config c;
+  Shape s;
+  gqa_status r = check_layer_call(cfg, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, w_o, k_cache,
+                                  v_cache, kv_capacity, out, &c, &s);
+  if (r != GQA_OK || batch == 0 || q_len == 0) return r;
+  const size_t need = ws_layer(s, batch, q_len, kv_capacity);
+  if (need > kScratchBytes)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL,
+                "gqa_layer_forward_noalloc: this call needs %zu bytes of scratch, more than the "
+                "library's static %zu (use gqa_layer_forward with a workspace)",
+                need, (size_t)kScratchBytes);
+  void* scr = nullptr;
+  if ((r = scratch_of_current_device(&scr)) != GQA_OK) return r;
+  r = run_layer(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, w_o, k_cache, v_cache,
+                kv_capacity, cache_len, out, scr, (hipStream_t)stream);
+  return r == GQA_OK ? ok() : r;
+}
+
+}  // extern "C"
+
+namespace {
+
+gqa_status run_layer(const gqa_config& c, const Shape& s, int batch, int q_len, const void* x,
+                     const void* w_qkv, const void* q_norm_w, const void* k_norm_w,
+                     const void* w_o, void* k_cache, void* v_cache, int kv_capacity,
+                     const int32_t* cache_len, void* out, void* workspace, hipStream_t st) {
+  gqa_status r;
   const size_t T = (size_t)batch * q_len;
   char* w = static_cast<char*>(workspace);
   void* ws_q = w;
@@ -717,7 +805,6 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
   void* obuf = w;
   w += align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1));
   void* ws_a = w;
-  hipStream_t st = (hipStream_t)stream;
   r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, cache_len, qbuf, k_cache, v_cache,
               kv_capacity, ws_q, st);
   if (r != GQA_OK) return r;
@@ -725,11 +812,15 @@ gqa_status gqa_layer_forward(const gqa_config* cfg, int32_t batch, int32_t q_len
                s.o_split, ws_a, st);
   if (r != GQA_OK) return r;
   // few tokens: the projection's workspace, free again, holds o_proj's partial products
-  r = run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st,
-                use_fused_qkv(s, (long long)T) ? nullptr
-                                                : static_cast<char*>(ws_q) + skinny_part_offset(s, T));
-  return r == GQA_OK ? ok() : r;
+  return run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st,
+                   use_fused_qkv(s, (long long)T)
+                       ? nullptr
+                       : static_cast<char*>(ws_q) + skinny_part_offset(s, T));
 }
+
+}  // namespace
+
+extern "C" {
 
 gqa_status gqa_layer_forward_train(const gqa_config* cfg, int32_t batch, int32_t q_len,
                                    const void* x, const void* w_qkv, const void* q_norm_w,
