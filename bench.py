@@ -156,16 +156,17 @@ def layer_cfg(T, w, **kw):
     return T.GQAConfig(hidden_size=w.hidden, num_heads=w.hq, num_kv_heads=w.hkv,
                        head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
                        qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=True,
-                       o_split=w.o_split, rotary_dim=w.rotary_dim, **kw)
+                       o_split=w.o_split, o_fp16=w.o_fp16, rotary_dim=w.rotary_dim, **kw)
 
 
 def bench_prefill(w, steps, warmup, torch, T, GI):
     """Layer step time, and the time of each entry point (the QKV one is one
     kernel plus its small RoPE table build; attention and o_proj one kernel
     each) on the same stream and inputs.  The layer's own o_proj reads the
-    attention output in its carrier format; the standalone o_proj reads one
-    bf16 value per element, so with a hi + lo carrier the layer's o_proj
-    time is the layer step minus the QKV and attention entry points."""
+    attention output in its carrier format (fp16, or a bf16 hi + lo pair);
+    the standalone o_proj reads one bf16 value per element, so the layer's
+    o_proj time (with its W_o conversion, for fp16) is reported as the layer
+    step minus the QKV and attention entry points."""
     cfg = layer_cfg(T, w)
     h = GI.device_layer_inputs(w)
     d = w.d
@@ -309,7 +310,7 @@ def measured_peaks(torch):
     """What this machine delivers to the library's own microkernels
     (libgqa_peaks.so): a bf16 MFMA-only loop (4 waves per workgroup, 1024
     workgroups, 8 independent 32x32x16 MFMAs per trip) and a streaming read
-    of 4 GiB (16-byte loads, each byte once).  Each is the best of 5 timed
+    of 4 GiB (16-byte nontemporal loads, each byte once, 8192 workgroups).  Each is the best of 5 timed
     calls after 2 untimed ones, timed with HIP events on the launch stream."""
     from transformer_attention_layer_amd import peaks as P
 
@@ -331,7 +332,7 @@ def measured_peaks(torch):
     flop = 4.0 * wg * iters * P.MFMA_FLOP_PER_WAVE_ITER
     mfma_ms = best_ms(lambda: P.mfma_bf16(wg, iters, sink))
     buf = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
-    rwg = 256 * 8
+    rwg = 8192  # the fastest of 1024 .. 16384 workgroups on an MI355X
     rsink = torch.empty(rwg * 256, dtype=torch.int32, device="cuda")
     read_ms = best_ms(lambda: P.stream_read(buf, rwg, rsink))
     del buf, sink, rsink
@@ -511,7 +512,7 @@ def main():
             "num_heads": w.hq, "num_kv_heads": w.hkv, "head_dim": w.d,
             "head_dim_explicit": w.head_dim is not None, "qk_norm": w.qk_norm,
             "rope_theta": w.rope_theta, "causal": w.causal, "cache_len": w.cache_len,
-            "out_dtype": "f32", "o_split": w.o_split,
+            "out_dtype": "f32", "o_split": w.o_split, "o_fp16": w.o_fp16,
             "kv_cache": "fp8_e4m3" if w.kv_fp8 else w.dtype}
     print(f"[bench] {w.name}", file=sys.stderr, flush=True)
     if w.cache_len == 0:

@@ -37,13 +37,17 @@ class Workload:
     seed: int
     causal: bool = True
     cache_len: int = 0       # decode: tokens already in the cache
-    # Launch option of the layer for this workload: carry the attention
-    # output into o_proj as a bf16 hi + lo pair.  On for the layers whose
-    # o_proj reduces over Hq*d >= 4096 values, where the bf16 rounding of
-    # the attention output alone moves outputs by ~1e-2.
+    # Launch options of the layer for this workload: how the attention output
+    # reaches o_proj.  For the layers whose o_proj reduces over Hq*d >= 4096
+    # values, where the bf16 rounding of the attention output alone moves
+    # outputs by ~1e-2, it is carried either as fp16 (prefill: one fp16
+    # o_proj pass over W_o converted to fp16) or as a bf16 hi + lo pair
+    # (decode: a few tokens, where reading W_o twice costs less than
+    # converting it).
     o_split: bool = False
     rotary_dim: Optional[int] = None  # partial rotary width; None = head_dim
     kv_fp8: bool = False      # K/V caches hold FP8 (E4M3) codes, scales 1
+    o_fp16: bool = False
 
     @property
     def d(self) -> int:
@@ -66,9 +70,9 @@ WORKLOADS = {
     "prefill_h1024": Workload("prefill_h1024", 8, 2048, 1024, 16, 8, 128, True,
                               1e6, 1e-6, "bf16", 1),
     "quotient_h4096": Workload("quotient_h4096", 4, 8192, 4096, 32, 8, None,
-                               False, 5e5, 1e-6, "bf16", 2, o_split=True),
+                               False, 5e5, 1e-6, "bf16", 2, o_fp16=True),
     "wide_h5120": Workload("wide_h5120", 2, 16384, 5120, 64, 8, 128, True, 1e6,
-                           1e-6, "bf16", 3, o_split=True),
+                           1e-6, "bf16", 3, o_fp16=True),
     "decode_h2560_gqa": Workload("decode_h2560_gqa", 64, 1, 2560, 32, 8, 128,
                                  True, 1e6, 1e-6, "bf16", 4, cache_len=32768,
                                  o_split=True),

@@ -121,6 +121,18 @@ typedef struct {
                             0: the caches hold `dtype` values. */
   float k_scale;         /* kv_fp8 only: per-tensor scales, 0 = 1.0; positive */
   float v_scale;         /* and finite, else GQA_ERR_INVALID_ARG */
+  int32_t o_fp16;        /* bf16 only (ignored for GQA_F32), gqa_layer_forward
+                            and gqa_layer_forward_noalloc only.  1: the
+                            attention output reaches o_proj as fp16 (11
+                            significant bits, rounded to nearest even) and
+                            o_proj runs on the fp16 matrix cores with W_o
+                            converted to fp16 (exactly, for weights from 2^-17
+                            to 65504 in magnitude) in the workspace: one
+                            o_proj pass instead of o_split's two.  Values past
+                            65504 in magnitude (o or W_o) become infinities, so
+                            the output turns non-finite rather than wrong.
+                            Cannot be combined with o_split
+                            (GQA_ERR_INVALID_ARG). */
 } gqa_config;
 
 /* Host only (no device needed): copy *in to *out with num_kv_heads and

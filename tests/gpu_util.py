@@ -39,7 +39,7 @@ def announce(msg: str):
     sys.stdout.flush()
 
 
-def cfg_of(w: GI.Workload, out_f32: bool = True, o_split=None):
+def cfg_of(w: GI.Workload, out_f32: bool = True, o_split=None, o_fp16=None):
     """The binding's config for a workload, with the workload's own launch
     options.  Parity runs take the o_proj output in fp32 (the accumulator):
     a bf16 output is that value rounded once more, checked bit-exactly in
@@ -49,6 +49,7 @@ def cfg_of(w: GI.Workload, out_f32: bool = True, o_split=None):
                        head_dim=w.head_dim, rope_theta=w.rope_theta, rms_eps=w.rms_eps,
                        qk_norm=w.qk_norm, causal=w.causal, dtype=w.dtype, out_f32=out_f32,
                        o_split=w.o_split if o_split is None else o_split,
+                       o_fp16=w.o_fp16 if o_fp16 is None else o_fp16,
                        rotary_dim=w.rotary_dim)
 
 

@@ -103,6 +103,8 @@ def test_resolve_explicit_and_quotient():
     # the hi | lo split reads W_o twice in 32-wide K stages: 3*88 % 32 != 0
     (dict(num_heads=3, num_kv_heads=3, head_dim=88, o_split=True), "GQA_ERR_UNSUPPORTED_SHAPE"),
     (dict(hidden_size=0), "GQA_ERR_INVALID_ARG"),
+    # two carriers of the attention output at once
+    (dict(o_split=True, o_fp16=True), "GQA_ERR_INVALID_ARG"),
     (dict(rotary_dim=63), "GQA_ERR_INVALID_ARG"),
     (dict(rotary_dim=130), "GQA_ERR_INVALID_ARG"),
     (dict(rope_theta=0.0), "GQA_ERR_INVALID_ARG"),
@@ -286,3 +288,18 @@ def test_backward_workspace_covers_its_buffers():
     # the training forward's RoPE table: L rows of d/2 (cos, sin) pairs
     assert T.gqa_workspace_bytes(c, B, L, L, T.WS_TRAIN_FORWARD) == L * 64 * 8
     assert T.gqa_workspace_bytes(cfg(dtype="f32"), B, L, L, T.WS_BACKWARD) > 0  # sized, then rejected
+
+
+def test_o_fp16_flag_and_workspace():
+    """o_fp16 takes 0 or 1, and the layer workspace grows by W_o as fp16
+    (hidden x Hq*d x 2 bytes, 256-byte aligned)."""
+    _lib_or_skip()
+    cc = cfg().c()
+    cc.o_fp16 = 2
+    out = T._CConfig()
+    assert T.STATUS_NAMES[T.lib().gqa_resolve(ctypes.byref(cc), ctypes.byref(out))] == \
+        "GQA_ERR_INVALID_ARG"
+    assert T.gqa_resolve(cfg(o_fp16=True))["o_fp16"] == 1
+    a = T.gqa_workspace_bytes(cfg(), 2, 300, 300, T.WS_LAYER)
+    b = T.gqa_workspace_bytes(cfg(o_fp16=True), 2, 300, 300, T.WS_LAYER)
+    assert b - a == 1024 * 16 * 128 * 2

@@ -49,7 +49,7 @@ SMALL = {
     "bf16_d64": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=150, hq=8, hkv=2, head_dim=64),
     "bf16_d256": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=130, hq=4, hkv=2, head_dim=256),
     "bf16_d80_quotient": GI.WORKLOADS["quotient_h4096"].with_(batch=1, seq=90, hidden=640, hq=8,
-                                                             hkv=4),
+                                                             hkv=4, o_fp16=False, o_split=True),
     "bf16_d64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=300, hq=8, hkv=4,
                                                               head_dim=64),
     # partial rotary: 64 of 128 in the fused epilogue, 48 of 128 through the
@@ -59,6 +59,18 @@ SMALL = {
     "rot32_of_64": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=90, hq=8, hkv=2, head_dim=64,
                                                        rotary_dim=32),
     "rot64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=500, rotary_dim=64),
+    # the fp16 carrier of the attention output on every attention kernel:
+    # prefill, the decode merge, the vector-unit path, few-token o_proj
+    "o_fp16_d256": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=130, hq=4, hkv=2,
+                                                       head_dim=256, o_fp16=True),
+    "o_fp16_d80": GI.WORKLOADS["quotient_h4096"].with_(batch=1, seq=90, hidden=640, hq=8, hkv=4),
+    # the bf16 hi + lo carrier on the prefill path (o_proj reads W_o twice along K)
+    "o_split_prefill": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=260, o_fp16=False,
+                                                        o_split=True),
+    "o_fp16_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000,
+                                                            o_split=False, o_fp16=True),
+    "o_fp16_mqa_decode": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777,
+                                                                o_split=False, o_fp16=True),
 }
 
 
@@ -159,7 +171,8 @@ def test_few_token_projection_path(tokens):
     and without QK-norm and the hi+lo split (also with a 1024-wide o_proj,
     whose K is split over workgroups)."""
     for base, kw in (("prefill_h1024", {}), ("wide_h5120", {"hq": 40, "hkv": 8}),
-                     ("quotient_h4096", {}), ("prefill_h1024", {"o_split": True})):
+                     ("quotient_h4096", {}), ("prefill_h1024", {"o_split": True}),
+                     ("quotient_h4096", {"o_fp16": False, "o_split": True})):
         w = GI.WORKLOADS[base].with_(batch=1, seq=tokens, **kw)
         announce(f"[few tokens] {base} {kw} T={tokens} o_split={w.o_split}")
         h = GI.host_layer_inputs(w)

@@ -51,7 +51,7 @@ class _CConfig(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("out_f32", ctypes.c_int32),
                 ("o_split", ctypes.c_int32), ("rotary_dim", ctypes.c_int32),
                 ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("o_fp16", ctypes.c_int32)]
 
 
 class _CSaved(ctypes.Structure):
@@ -84,6 +84,7 @@ class GQAConfig:
     kv_fp8: bool = False    # K/V caches hold FP8 (E4M3) codes as torch.uint8
     k_scale: float = 1.0    # kv_fp8: an entry stands for value(code) * scale
     v_scale: float = 1.0
+    o_fp16: bool = False    # layer forward: attention output as fp16, o_proj on fp16 MFMA
 
     def c(self) -> _CConfig:
         return _CConfig(self.hidden_size, self.num_heads, self.num_kv_heads or 0,
@@ -91,7 +92,8 @@ class GQAConfig:
                         int(bool(self.qk_norm)), int(bool(self.causal)),
                         GQA_BF16 if self.dtype == "bf16" else GQA_F32, int(bool(self.out_f32)),
                         int(bool(self.o_split)), int(self.rotary_dim or 0),
-                        int(bool(self.kv_fp8)), float(self.k_scale), float(self.v_scale))
+                        int(bool(self.kv_fp8)), float(self.k_scale), float(self.v_scale),
+                        int(bool(self.o_fp16)))
 
 
 _lib = None

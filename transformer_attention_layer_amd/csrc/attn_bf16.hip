@@ -181,10 +181,18 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[Geo<KD>::NC], const bf16* qro
   }
 }
 
-// Four consecutive output features as bf16; with `split` also the rounding
-// residual (value - bf16(value)) as bf16, `width` elements further on.
-__device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)[4], int split) {
+// Four consecutive output features as bf16 (or, with `f16`, as fp16); with
+// `split` also the rounding residual (value - bf16(value)) as bf16, `width`
+// elements further on.
+__device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)[4], int split,
+                                        int f16) {
   u32x2 w;
+  if (f16) {
+    w.x = pack_f16x2(v[0], v[1]);
+    w.y = pack_f16x2(v[2], v[3]);
+    st8(p, w);
+    return;
+  }
   w.x = pack_bf16x2(v[0], v[1]);
   w.y = pack_bf16x2(v[2], v[3]);
   st8(p, w);
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = st.o[d][4 * j + i] * inv;
-      store_o4(orow + 32 * d + 8 * j + 4 * hh, width, v, a.o_split);
+      store_o4(orow + 32 * d + 8 * j + 4 * hh, width, v, a.o_split, a.o_f16);
     }
 }
 
@@ -583,7 +591,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const size_t width = (size_t)a.Hq * KD;
   bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
   const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-  store_o4(orow + 4 * e4, width, v, a.o_split);
+  store_o4(orow + 4 * e4, width, v, a.o_split, a.o_f16);
 }
 
 template <int KD>

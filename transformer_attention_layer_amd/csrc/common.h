@@ -89,6 +89,21 @@ GQA_DEV floatx16 mfma32x32x16(u32x4 a, u32x4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// The same product on the fp16 matrix cores: A and B hold fp16 values.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+GQA_DEV floatx16 mfma32x32x16_f16(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even float -> fp16 bits (two values packed, low first);
+// one v_cvt_pk_f16_f32.  Magnitudes past 65504 become infinities.
+GQA_DEV unsigned int pack_f16x2(float lo, float hi) {
+  const floatx2 f = {lo, hi};
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f, halfx2));
+}
+
 GQA_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
 // Combine v across lanes l and l ^ 32 with v_permlane32_swap (a VALU

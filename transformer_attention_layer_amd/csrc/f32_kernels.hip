@@ -139,7 +139,7 @@ __global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
 // T is the element type of q, the caches and o (float, or bf16 for head
 // sizes the bf16 matrix-core kernels do not cover); with bf16 and o_split
 // the output is the bf16 value followed, Hq * d further on, by its rounding
-// residual.
+// residual; with bf16 and o_f16 it is the fp16 value.
 template <typename T>
 __global__ __launch_bounds__(64) void attn_vec_kernel(F32AttnArgs a) {
   const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -189,6 +189,12 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(F32AttnArgs a) {
     const int e = lane + 64 * u;
     if (e >= d) continue;
     const float val = ov[u] * inv;
+    if constexpr (sizeof(T) == 2) {
+      if (a.o_f16) {  // fp16 bits in the 16-bit slot
+        reinterpret_cast<_Float16*>(o)[e] = (_Float16)val;
+        continue;
+      }
+    }
     const T hi = (T)val;
     o[e] = hi;
     if (a.o_split) o[width + e] = (T)(val - (float)hi);

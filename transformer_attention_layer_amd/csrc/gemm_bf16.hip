@@ -153,8 +153,13 @@ __device__ __forceinline__ int rows_bytes(int row0, int nrows, int ld) {
 // makes the next tile's first stage visible.  Compared with one workgroup
 // per tile, the next tile's prologue and the workgroup launch are off the
 // critical path, which pays at short K (a few stages per tile).
-template <int BN, int BM, int EPI, bool KALIGN>
+//
+// F16 (plain epilogues only): W and X hold fp16 values and the products run
+// on the fp16 matrix cores; everything else (staging, order, epilogue) is
+// the same, since the loads move bytes.
+template <int BN, int BM, int EPI, bool KALIGN, bool F16 = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
+  static_assert(!F16 || EPI != kEpiQKV, "the QKV epilogue takes bf16 operands");
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FB = WN / 32, TB = WM / 32;
   static_assert(WN == 128, "the epilogues stage 128 features per wave");
@@ -325,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < FB * TB; ++i) {
         const int f = i / TB, t = i % TB;
-        acc[f][t] = mfma32x32x16(fa[sub][f], fb[sub][t], acc[f][t]);
+        acc[f][t] = F16 ? mfma32x32x16_f16(fa[sub][f], fb[sub][t], acc[f][t])
+                        : mfma32x32x16(fa[sub][f], fb[sub][t], acc[f][t]);
         if (i < 8) {
           // next substep's fragments in the order its MFMAs use them
           if (reads) {
@@ -678,6 +684,7 @@ __global__ void rope_table_kernel(float2* __restrict__ table, const int* __restr
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyUnroll = 4;
 
+template <bool F16>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs a) {
   __shared__ floatx16 red[kSkinnyWaves - 1][2][64];
   const int lane = threadIdx.x & 63;
@@ -706,8 +713,8 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs
     const u32x4 fa = buf_ld16(rw, kwc < Kw ? (unsigned)((l32 * Kw + kwc) * 2) : kOob);
     const u32x4 fb0 = buf_ld16(rx, kxc < K ? (unsigned)((l32 * K + kxc) * 2) : kOob);
     const u32x4 fb1 = buf_ld16(rx, kxc < K ? (unsigned)(((32 + l32) * K + kxc) * 2) : kOob);
-    acc0 = mfma32x32x16(fa, fb0, acc0);
-    acc1 = mfma32x32x16(fa, fb1, acc1);
+    acc0 = F16 ? mfma32x32x16_f16(fa, fb0, acc0) : mfma32x32x16(fa, fb0, acc0);
+    acc1 = F16 ? mfma32x32x16_f16(fa, fb1, acc1) : mfma32x32x16(fa, fb1, acc1);
   };
   int k = kb;
   for (; k + 16 * kSkinnyUnroll <= ke; k += 16 * kSkinnyUnroll) {
@@ -773,7 +780,31 @@ __global__ __launch_bounds__(256) void skinny_sum_kernel(const float* __restrict
   }
 }
 
+// bf16 -> fp16, eight values per thread (16-byte loads and stores); bf16 to
+// fp32 is exact, fp32 to fp16 rounds to nearest even.
+__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const u32x4* __restrict__ in,
+                                                           u32x4* __restrict__ out, long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 v = in[i];
+  u32x4 r;
+  r.x = pack_f16x2(lo_bf16(v.x), hi_bf16(v.x));
+  r.y = pack_f16x2(lo_bf16(v.y), hi_bf16(v.y));
+  r.z = pack_f16x2(lo_bf16(v.z), hi_bf16(v.z));
+  r.w = pack_f16x2(lo_bf16(v.w), hi_bf16(v.w));
+  out[i] = r;
+}
+
 }  // namespace
+
+hipError_t launch_cvt_bf16_f16(const __bf16* in, void* out, long long n, hipStream_t stream) {
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const long long n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  cvt_bf16_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(
+      reinterpret_cast<const u32x4*>(in), static_cast<u32x4*>(out), n8);
+  return hipGetLastError();
+}
 
 // Only when the features alone leave more than half of the CUs idle: a
 // decode step's o_proj (2560 features: 80 workgroups) went from 58 to 30 us
@@ -792,7 +823,10 @@ int skinny_ksplit(int N, int K) {
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
   const int ks = args.part && args.ksplit > 1 ? args.ksplit : 1;
   dim3 grid((args.N + 31) / 32, (args.M + 63) / 64, ks);
-  gemm_skinny_kernel<<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+  if (args.f16)
+    gemm_skinny_kernel<true><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+  else
+    gemm_skinny_kernel<false><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const long long n4 = (long long)args.M * args.N / 4;
@@ -851,6 +885,20 @@ hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
 hipError_t launch_gemm_plain_bf16(const GemmArgs& args, hipStream_t stream) {
   const int grid = gemm_workgroups(args.N, args.M, args.K, args.batch > 1 ? args.batch : 1);
   const bool kal = k_aligned(args);
+  if (args.f16) {  // the output projection of an fp16-carried attention output
+    if (args.out_f32) {
+      if (kal)
+        gemm_bf16_kernel<256, 256, kEpiPlainF32, true, true><<<grid, kThreads, 0, stream>>>(args);
+      else
+        gemm_bf16_kernel<256, 256, kEpiPlainF32, false, true><<<grid, kThreads, 0, stream>>>(args);
+    } else {
+      if (kal)
+        gemm_bf16_kernel<256, 256, kEpiPlain, true, true><<<grid, kThreads, 0, stream>>>(args);
+      else
+        gemm_bf16_kernel<256, 256, kEpiPlain, false, true><<<grid, kThreads, 0, stream>>>(args);
+    }
+    return hipGetLastError();
+  }
   if (args.out_f32) {
     if (kal)
       gemm_bf16_kernel<256, 256, kEpiPlainF32, true><<<grid, kThreads, 0, stream>>>(args);

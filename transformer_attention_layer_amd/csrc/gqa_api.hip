@@ -50,6 +50,7 @@ struct Shape {
   bool fused;    // mfma, and the rotary width (128 or 64) fits the fused QKV epilogue
   bool out_f32;  // o_proj output in fp32
   bool o_split;  // layer forward: attention output as a bf16 hi + lo pair
+  bool o_f16;    // layer forward: attention output as fp16, o_proj on the fp16 matrix cores
   bool kv_fp8;   // caches hold E4M3 codes
   float k_scale, v_scale;
 };
@@ -118,8 +119,11 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
   if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
     return fail(GQA_ERR_INVALID_ARG, "rms_eps must be >= 0 and finite");
   if ((c.qk_norm != 0 && c.qk_norm != 1) || (c.causal != 0 && c.causal != 1) ||
-      (c.out_f32 != 0 && c.out_f32 != 1) || (c.o_split != 0 && c.o_split != 1))
-    return fail(GQA_ERR_INVALID_ARG, "qk_norm, causal, out_f32 and o_split must be 0 or 1");
+      (c.out_f32 != 0 && c.out_f32 != 1) || (c.o_split != 0 && c.o_split != 1) ||
+      (c.o_fp16 != 0 && c.o_fp16 != 1))
+    return fail(GQA_ERR_INVALID_ARG, "qk_norm, causal, out_f32, o_split and o_fp16 must be 0 or 1");
+  if (c.o_split && c.o_fp16)
+    return fail(GQA_ERR_INVALID_ARG, "o_split and o_fp16 are two carriers of the same value: set one");
   // every kernel indexes heads and widths in 32-bit
   const long long n_qkv = (long long)(c.num_heads + 2LL * c.num_kv_heads) * c.head_dim;
   if (n_qkv > (1LL << 30) || (long long)c.num_heads * c.head_dim > (1LL << 30))
@@ -138,6 +142,7 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->fused = sh->bf16 && c.head_dim == 128 && (c.rotary_dim == 128 || c.rotary_dim == 64);
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
     sh->o_split = c.o_split && c.dtype == GQA_BF16;
+    sh->o_f16 = c.o_fp16 && c.dtype == GQA_BF16;
     sh->kv_fp8 = c.kv_fp8 != 0;
     sh->k_scale = c.kv_fp8 ? c.k_scale : 1.f;
     sh->v_scale = c.kv_fp8 ? c.v_scale : 1.f;
@@ -248,11 +253,16 @@ size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
   return align_up(parts * s.d * sizeof(float)) + align_up(parts * 2 * sizeof(float));
 }
 
+// W_o converted to fp16 for an fp16-carried attention output
+size_t wo16_bytes(const Shape& s) {
+  return s.o_f16 ? align_up((size_t)s.H * s.Hq * s.d * 2) : 0;
+}
+
 size_t ws_layer(const Shape& s, int batch, int q_len, int cap) {
   const size_t T = (size_t)batch * q_len;
   return ws_qkv(s, batch, q_len) + align_up(T * s.Hq * s.d * esize(s)) /* q */ +
          align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1)) /* attention output */ +
-         ws_attn(s, batch, q_len, cap);
+         ws_attn(s, batch, q_len, cap) + wo16_bytes(s);
 }
 
 gqa_status check_launch(hipError_t e, const char* what) {
@@ -404,7 +414,8 @@ gqa_status prefill_split(const Shape& s, int q_len, int* hpw, int* pb, int* n_hs
 // query row's log-sum-exp, whatever q_len is.
 gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, const void* q,
                     const void* kc, const void* vc, const int32_t* kv_base, int kv_add, int cap,
-                    void* o, bool o_split, void* ws, hipStream_t st, float* lse = nullptr) {
+                    void* o, bool o_split, void* ws, hipStream_t st, float* lse = nullptr,
+                    bool o_f16 = false) {
   const double scale = 1.0 / sqrt((double)s.d);
   if (!s.mfma) {  // fp32, or bf16 with a head_dim other than 64, 128, 256
     gqa::F32AttnArgs a{};
@@ -414,6 +425,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
     a.o = o;
     a.bf16 = s.bf16;
     a.o_split = o_split && s.bf16;
+    a.o_f16 = o_f16 && s.bf16;
     a.kv_base = kv_base;
     a.kv_add = kv_add;
     a.B = batch;
@@ -433,6 +445,7 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   a.v = static_cast<const __bf16*>(vc);
   a.o = static_cast<__bf16*>(o);
   a.o_split = o_split;
+  a.o_f16 = o_f16;
   a.kv_base = kv_base;
   a.kv_add = kv_add;
   a.B = batch;
@@ -466,11 +479,14 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
 }
 
 // part (few tokens, optional): skinny_part_bytes of scratch for a K split.
+// w_o16 (optional): W_o as fp16, for an attention output o held as fp16.
 gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, const void* w_o,
-                     void* out, hipStream_t st, void* part = nullptr) {
+                     void* out, hipStream_t st, void* part = nullptr,
+                     const void* w_o16 = nullptr) {
   if (s.bf16) {
     gqa::GemmArgs g{};
-    g.W = static_cast<const __bf16*>(w_o);
+    g.W = static_cast<const __bf16*>(w_o16 ? w_o16 : w_o);
+    g.f16 = w_o16 ? 1 : 0;
     g.X = static_cast<const __bf16*>(o);
     g.N = s.H;
     g.M = tokens;
@@ -805,17 +821,26 @@ gqa_status run_layer(const gqa_config& c, const Shape& s, int batch, int q_len, 
   void* obuf = w;
   w += align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1));
   void* ws_a = w;
+  w += ws_attn(s, batch, q_len, kv_capacity);
+  void* wo16 = s.o_f16 ? w : nullptr;
   r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, cache_len, qbuf, k_cache, v_cache,
               kv_capacity, ws_q, st);
   if (r != GQA_OK) return r;
   r = run_attn(c, s, batch, q_len, qbuf, k_cache, v_cache, cache_len, q_len, kv_capacity, obuf,
-               s.o_split, ws_a, st);
+               s.o_split, ws_a, st, nullptr, s.o_f16);
   if (r != GQA_OK) return r;
+  if (wo16) {
+    r = check_launch(gqa::launch_cvt_bf16_f16(static_cast<const __bf16*>(w_o), wo16,
+                                              (long long)s.H * s.Hq * s.d, st),
+                     "W_o to fp16");
+    if (r != GQA_OK) return r;
+  }
   // few tokens: the projection's workspace, free again, holds o_proj's partial products
   return run_oproj(s, (int)T, obuf, s.o_split, w_o, out, st,
                    use_fused_qkv(s, (long long)T)
                        ? nullptr
-                       : static_cast<char*>(ws_q) + skinny_part_offset(s, T));
+                       : static_cast<char*>(ws_q) + skinny_part_offset(s, T),
+                   wo16);
 }
 
 }  // namespace

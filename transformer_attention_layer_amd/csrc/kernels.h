@@ -23,6 +23,7 @@ struct GemmArgs {
   void* out;
   int out_f32;
   int w_kmod;       // > 0: W column k % w_kmod (W read twice along K for a hi | lo X)
+  int f16;          // plain epilogues and few-token GEMM: W and X hold fp16 values
   // QKV epilogue (head_dim 128)
   __bf16* q;        // [B, Hq, L, 128]
   __bf16* k_cache;  // [B, Hkv, cap, 128]
@@ -53,6 +54,7 @@ struct AttnArgs {
   float v_scale;            // multiplies the output (FP8 V scale; 1 otherwise)
   __bf16* o;        // [B, Lq, Hq * d], or [B, Lq, 2, Hq * d] (hi | lo) when o_split
   int o_split;
+  int o_f16;        // o holds fp16 values (rounded to nearest even) instead of bf16
   const int* kv_base;  // kv_len[b] = (kv_base ? kv_base[b] : 0) + kv_add, clamped to [0, cap]
   int kv_add;
   int B, Hq, Hkv, G, Lq, cap, causal;
@@ -178,9 +180,12 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream);
 struct F32AttnArgs {
   const void* q; const void* k; const void* v; void* o;
   const int* kv_base; int kv_add;
-  int B, Hq, Hkv, Lq, cap, d, causal, bf16, o_split;
+  int B, Hq, Hkv, Lq, cap, d, causal, bf16, o_split, o_f16;
   float scale;
 };
+
+// out[i] = fp16(in[i]) (bf16 -> fp16, round to nearest even; n % 8 == 0)
+hipError_t launch_cvt_bf16_f16(const __bf16* in, void* out, long long n, hipStream_t stream);
 hipError_t launch_attn_vec(const F32AttnArgs& args, hipStream_t stream);
 
 }  // namespace gqa
