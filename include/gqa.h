@@ -95,10 +95,11 @@ typedef struct {
                             its rounding stays out of the output; costs one more
                             o_proj pass.  0: one bf16 value, the tutorial's cast
                             of the attention result to the input dtype. */
-  int32_t rotary_dim;    /* r, 0 = head_dim.  Partial rotary (GPT-NeoX issue
-                            "Scaling and RoPE": RoPE at the effective head_dim
-                            "subject to the existing rotary_pct behavior"):
-                            the first r entries of each q and k head rotate as
+  int32_t rotary_dim;    /* r, 0 = head_dim.  Partial rotary (GPT-NeoX issue,
+                            "Scaling and RoPE": RoPE is built at the effective
+                            head_dim and keeps the rotary_pct option, which the
+                            page does not define; read here as follows): the
+                            first r entries of each q and k head rotate as
                             a width-r rotate-half RoPE (entry i < r/2 pairs with
                             i + r/2, angle pos * theta^(-2i/r)); entries r ..
                             head_dim-1 pass through.  Must be even and at most

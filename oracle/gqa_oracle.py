@@ -10,17 +10,20 @@ What it computes, step by step, follows the sources below; each function
 names the passage it implements.
 
 * "Tutorial 07: Multi-Head and Grouped-Query Attention (Full Layer)",
-  section 4 (the ``Attention.__call__`` code, steps 1 to 7) for the order of
-  the steps: project, per-head QK-norm, RoPE on q and k, grouped attention in
-  float, flatten to the query width, output projection.  Section 3 says the
-  norm has dim = head_dim and runs per head.
+  sections 3 and 4 for what the layer computes: q, k, v projections, a
+  per-head RMSNorm of q and k (dim = head_dim), RoPE on q and k, attention
+  in float, and the output projection.
+* "Attention head partitions: keep each head's dependencies intact" for the
+  grouping: attention is computed per KV head, with the query heads it
+  serves stacked against its keys and values.
 * GPT-NeoX issue "Support explicit attention head_dim independent of
   hidden_size / num_attention_heads", sections "Proposed configuration
   behavior", "Proposed implementation", "Fused QKV projection", "Attention
   output flattening", "Output projection" and "Scaling and RoPE" for the
   shapes, the quotient fallback, the divisibility rules and the scale.
 * "num_heads Is Not a Capacity Knob", section "Why the cost does not move",
-  for the weight and multiply-accumulate counts.
+  for the weight and multiply-accumulate counts, and for the output
+  projection as a sum of each head's output through its own slice of W_O.
 
 Readings where the pages are silent (each also listed in the design doc):
 
@@ -40,8 +43,8 @@ Readings where the pages are silent (each also listed in the design doc):
    sees keys at positions <= its own (bottom-right causal alignment); new
    k and v are appended before attending.
 8. The layer returns the o_proj output; the residual add is the caller's.
-9. Partial rotary (the NeoX issue's "existing rotary_pct behavior", not
-   defined on the pages): with rotary_dim r < d, only the first r entries of
+9. Partial rotary (the NeoX issue keeps its rotary_pct option for RoPE at
+   the effective head_dim but does not define it): with rotary_dim r < d, only the first r entries of
    each head rotate, as a rotate-half RoPE of width r (entry i < r/2 pairs
    with i + r/2 and turns by ``p * theta**(-2i/r)``); entries r .. d-1 pass
    through.  r = d is reading 3.
@@ -194,6 +197,14 @@ def split_heads(y: np.ndarray, res: Resolved):
     return q, k, v
 
 
+def weight_blocks(w_qkv: np.ndarray, res: Resolved):
+    """The fused weight's row blocks W_q [Hq*d, H], W_k [Hkv*d, H] and W_v
+    [Hkv*d, H] (GPT-NeoX issue, "Fused QKV projection": its output width is
+    the query width plus twice the KV width; reading 4: rows Q | K | V)."""
+    qw, kw = res.q_width, res.kv_width
+    return w_qkv[:qw], w_qkv[qw:qw + kw], w_qkv[qw + kw:qw + 2 * kw]
+
+
 def rms_norm_heads(v: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     """Per-head RMSNorm over the last axis (tutorial section 3: the norm has
     dim = head_dim and works within each head)."""
@@ -211,7 +222,7 @@ def apply_rope(v: np.ndarray, positions: np.ndarray, theta: float,
                rotary_dim: Optional[int] = None) -> np.ndarray:
     """Rotate-half RoPE of v [B, L, heads, d] at integer positions [B, L]
     (tutorial section 4, step 3; GPT-NeoX issue "Scaling and RoPE": built at
-    the effective head_dim, subject to rotary_pct).  ``rotary_dim`` r (None =
+    the effective head_dim, with the rotary_pct option kept).  ``rotary_dim`` r (None =
     d) rotates the first r entries as a width-r RoPE and passes the rest
     (reading 9)."""
     d = v.shape[-1]
@@ -229,8 +240,12 @@ def grouped_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                       q_pos: np.ndarray, kv_len: np.ndarray, scale: float,
                       causal: bool = True) -> np.ndarray:
     """softmax(q k^T * scale) v with each KV head serving Hq/Hkv query heads
-    (tutorial section 4, step 6; "Attention head partitions ...": the
-    head-to-KV-group map).
+    (tutorial section 4, step 6; "Attention head partitions ...": a KV head
+    and the group of query heads it serves form one unit).
+
+    Computed per KV group: the group's G query heads are stacked into one
+    [G*Lq, d] block of query rows, scored against that KV head's keys, and
+    each row's softmax weights average its values.
 
     q [B, Hq, Lq, d]; k, v [B, Hkv, S, d] with S >= kv_len[b]; q_pos [B, Lq]
     holds each query's position.  Query i of batch b sees keys j < kv_len[b],
@@ -243,18 +258,18 @@ def grouped_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     out = np.zeros((bsz, hq, lq, v.shape[-1]), dtype=q.dtype)
     for b in range(bsz):
         n = int(kv_len[b])
-        key_idx = np.arange(n)
         visible = np.ones((lq, n), dtype=bool)
         if causal:
-            visible = key_idx[None, :] <= q_pos[b][:, None]
-        for h in range(hq):
-            g = h // group
-            s = np.matmul(q[b, h], k[b, g, :n].T) * q.dtype.type(scale)
-            s = np.where(visible, s, -np.inf)
-            m = np.max(s, axis=-1, keepdims=True)
-            p = np.exp(s - m)
+            visible = np.arange(n)[None, :] <= q_pos[b][:, None]
+        rows_visible = np.tile(visible, (group, 1))           # [G*Lq, n]
+        for g in range(hkv):
+            heads = slice(g * group, (g + 1) * group)          # the query heads of KV head g
+            qg = q[b, heads].reshape(group * lq, d)
+            s = np.matmul(qg, k[b, g, :n].T) * q.dtype.type(scale)
+            s = np.where(rows_visible, s, -np.inf)
+            p = np.exp(s - np.max(s, axis=-1, keepdims=True))
             p = p / np.sum(p, axis=-1, keepdims=True)
-            out[b, h] = np.matmul(p, v[b, g, :n])
+            out[b, heads] = np.matmul(p, v[b, g, :n]).reshape(group, lq, -1)
     return out
 
 
@@ -263,6 +278,20 @@ def merge_heads(o: np.ndarray) -> np.ndarray:
     flattening": flatten to the query width, not the residual width)."""
     b, h, l, d = o.shape
     return o.transpose(0, 2, 1, 3).reshape(b, l, h * d)
+
+
+def project_heads_out(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """o_proj of per-head outputs o [B, Hq, L, d]: the sum over heads of each
+    head's output times its own d columns of W_o [hidden, Hq*d] ("num_heads
+    Is Not a Capacity Knob", "Why the cost does not move": the heads'
+    outputs, concatenated, meet W_O, i.e. each head contributes through its
+    slice; GPT-NeoX issue, "Output projection": W_o maps the query width
+    back to hidden).  Returns [B, L, hidden]."""
+    d = o.shape[-1]
+    out = np.zeros(o.shape[:1] + o.shape[2:3] + (w_o.shape[0],), dtype=o.dtype)
+    for h in range(o.shape[1]):
+        out += project(o[:, h], w_o[:, h * d:(h + 1) * d])
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -324,11 +353,16 @@ def quantize_e4m3(x) -> np.ndarray:
 
 def qkv_normrope(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, positions,
                  rope_theta, rms_eps, qk_norm=True, rope=True, rotary_dim=None):
-    """Steps 1 to 4 of the tutorial's ``Attention.__call__``: project, QK-norm,
-    RoPE, transpose to head-major.  Returns q [B, Hq, L, d] and k, v
-    [B, Hkv, L, d] (k after norm and RoPE, v raw)."""
-    y = project(x, w_qkv)
-    q, k, v = split_heads(y, res)
+    """q, k, v of the layer (tutorial section 4, steps 1-4): each is x times
+    its own row block of the fused weight, split into heads; q and k are
+    normalised per head (QK-norm) and rotated at their positions (RoPE).
+    Returns q [B, Hq, L, d] and k, v [B, Hkv, L, d] (k after norm and RoPE,
+    v raw)."""
+    b, l, _ = x.shape
+    wq, wk, wv = weight_blocks(w_qkv, res)
+    q = project(x, wq).reshape(b, l, res.hq, res.d)
+    k = project(x, wk).reshape(b, l, res.hkv, res.d)
+    v = project(x, wv).reshape(b, l, res.hkv, res.d)
     if qk_norm:
         q = rms_norm_heads(q, q_norm_w, rms_eps)
         k = rms_norm_heads(k, k_norm_w, rms_eps)
@@ -347,7 +381,9 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
                   rotary_dim: Optional[int] = None, kv_fp8: bool = False,
                   k_scale: float = 1.0, v_scale: float = 1.0,
                   dtype=np.float64):
-    """The layer forward (tutorial section 4, steps 1 to 7).
+    """The layer forward (tutorial section 4, steps 1 to 7): q, k, v, the
+    cache update, grouped attention, and the output projection summed over
+    heads.
 
     x [B, L, hidden]; w_qkv [(Hq+2Hkv)d, hidden]; w_o [hidden, Hq*d].
     Without a cache, positions are 0..L-1.  With ``k_cache``/``v_cache``
@@ -410,7 +446,7 @@ def layer_forward(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, *,
         kv_len = start + seq
         k_out, v_out = kk, vv
     o = grouped_attention(q, kk, vv, positions, kv_len, res.scale, causal)
-    out = project(merge_heads(o), w_o)
+    out = project_heads_out(o, w_o)
     return out, k_out, v_out
 
 
@@ -435,9 +471,9 @@ def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
     for b, items in by_b.items():
         tmax = max(t for _, t in items)
         xb = np.asarray(x[b:b + 1, :tmax + 1], dtype=dtype)
-        y_prefix = project(xb, np.asarray(w_qkv[res.q_width:], dtype=dtype))
-        k = y_prefix[..., :res.kv_width].reshape(1, tmax + 1, res.hkv, res.d)
-        v = y_prefix[..., res.kv_width:].reshape(1, tmax + 1, res.hkv, res.d)
+        wq, wk, wv = weight_blocks(np.asarray(w_qkv, dtype=dtype), res)
+        k = project(xb, wk).reshape(1, tmax + 1, res.hkv, res.d)
+        v = project(xb, wv).reshape(1, tmax + 1, res.hkv, res.d)
         pos_all = np.arange(tmax + 1, dtype=np.int64)[None, :]
         if qk_norm:
             k = rms_norm_heads(k, np.asarray(k_norm_w, dtype=dtype), rms_eps)
@@ -447,14 +483,13 @@ def layer_forward_rows(res: Resolved, x, w_qkv, q_norm_w, k_norm_w, w_o, rows,
         v = v.transpose(0, 2, 1, 3)
         ts = np.array([t for _, t in items], dtype=np.int64)
         xq = np.asarray(x[b:b + 1, ts], dtype=dtype)
-        q = project(xq, np.asarray(w_qkv[:res.q_width], dtype=dtype))
-        q = q.reshape(1, len(ts), res.hq, res.d)
+        q = project(xq, wq).reshape(1, len(ts), res.hq, res.d)
         if qk_norm:
             q = rms_norm_heads(q, np.asarray(q_norm_w, dtype=dtype), rms_eps)
         q = apply_rope(q, ts[None, :], rope_theta, **kw).transpose(0, 2, 1, 3)
         o = grouped_attention(q, k, v, ts[None, :],
                               np.array([tmax + 1]), res.scale, True)
-        o_rows = project(merge_heads(o), np.asarray(w_o, dtype=dtype))[0]
+        o_rows = project_heads_out(o, np.asarray(w_o, dtype=dtype))[0]
         for j, (i, _) in enumerate(items):
             out[i] = o_rows[j]
     return out

@@ -15,6 +15,7 @@ _orig = {name: getattr(O, name) for name in (
     "resolve_config", "attention_param_count", "macs_per_token", "project",
     "split_heads", "rms_norm_heads", "rope_inv_freq", "apply_rope",
     "grouped_attention", "merge_heads", "qkv_normrope", "e4m3_value", "quantize_e4m3",
+    "weight_blocks", "project_heads_out",
     "project_backward", "rms_norm_heads_backward", "apply_rope_backward",
     "grouped_attention_backward")}
 
@@ -78,6 +79,19 @@ def _split_kv_swapped(y, res):
     if k.shape == v.shape:
         return q, v, k
     return q, k, v
+
+
+def _blocks_k_v_swapped(w_qkv, res):
+    """The fused weight's K and V row blocks taken in the wrong order."""
+    wq, wk, wv = _orig["weight_blocks"](w_qkv, res)
+    return wq, wv, wk
+
+
+def _heads_out_slices_shifted(o, w_o):
+    """Head h multiplied by the W_o columns of head h + 1 (cyclically)."""
+    d, hq = o.shape[-1], o.shape[1]
+    w = np.concatenate([w_o[:, d:], w_o[:, :d]], axis=1) if hq > 1 else w_o
+    return _orig["project_heads_out"](o, w)
 
 
 def _resolve_always_quotient(hidden_size, num_heads, num_kv_heads=None,
@@ -202,6 +216,8 @@ MUTATIONS = {
     "flatten_without_transpose": (
         "merge_heads", lambda o: o.reshape(o.shape[0], o.shape[2], -1)),
     "k_v_swapped": ("split_heads", _split_kv_swapped),
+    "k_v_weight_blocks_swapped": ("weight_blocks", _blocks_k_v_swapped),
+    "o_proj_head_slices_shifted": ("project_heads_out", _heads_out_slices_shifted),
     "projection_transposed_operand": (
         "project", lambda x, w: np.matmul(x, w.T) if w.shape[0] != w.shape[1]
         else np.matmul(x, w)),
