@@ -21,8 +21,10 @@ namespace gqa {
 
 namespace {
 
-constexpr int kBK = 32;          // K elements per LDS stage
-constexpr int kStages = 4;       // LDS ring: loads run kStages - 1 stages ahead
+constexpr int kBK = 64;          // K elements per LDS stage: one 128-byte line per row
+constexpr int kStages = 2;       // loads run kStages stages ahead
+constexpr int kWSlots = 3;       // LDS ring slots of W stages
+constexpr int kXSlots = 2;       // LDS ring slots of X stages
 constexpr int kCPR = kBK / 8;    // 16-byte chunks per LDS row
 constexpr int kThreads = 256;    // 4 waves, 2 x 2 over the C^T tile
 
@@ -40,45 +42,55 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 // One operand's share of a K stage, staged straight from global memory into
 // LDS (buffer_load ... lds, no register staging).  One instruction fills 64
-// consecutive 16-byte LDS slots = kRowsPerDma rows; lane i writes slot i, so
-// it loads the global chunk that the swizzle places there.  A wave issues
-// kInstr of them per stage; the per-lane byte offsets at K = 0 are computed
-// once, and chunks at or past column `kcols` read as zero.
+// consecutive 16-byte LDS slots = kRowsPerDma rows, each one whole 128-byte
+// line of the operand (half lines cost the address unit and L2 one request
+// per 64 bytes); lane i writes slot i, so it loads the global chunk that the
+// swizzle places there.  A wave issues kInstr of them per stage; the
+// per-lane byte offsets at K = 0 are computed once, and chunks at or past
+// column `kcols` read as zero.
 constexpr int kRowsPerDma = 64 / kCPR;
-static_assert(kRowsPerDma % (kRPW * kCPR) == 0, "one swizzle term per lane for all instructions");
+// the swizzle term of a lane alternates between even and odd instructions
+static_assert(2 * kRowsPerDma == kRPW * kCPR, "two swizzle terms per lane");
 
 template <int ROWS>
 struct DmaPlan {
   static constexpr int kInstr = ROWS / kRowsPerDma / (kThreads / 64);
+  static_assert(kInstr % 2 == 0, "instruction parity fixes the swizzle term");
   unsigned voff[kInstr];  // byte offset of this lane's chunk at K = 0
-  int kc;                 // K offset (elements) of this lane's chunk
+  int kc[2];              // K offset (elements) of this lane's chunk: even, odd instructions
   int slot0;              // first LDS slot of this wave's rows
 
   __device__ __forceinline__ void init(int ld, int wave, int lane) {
     const int r_in = lane / kCPR;
-    // the swizzle term depends on row / kRPW, which is the same for every
-    // instruction of the wave (rows advance in multiples of kRowsPerDma,
-    // a multiple of kRPW * kCPR)
-    const int c = (lane % kCPR) ^ ((r_in / kRPW) & (kCPR - 1));
+    // row = (wave kInstr + j) kRowsPerDma + r_in, so (row / kRPW) % kCPR
+    // depends on the lane and on the parity of j only
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      kc[p] = ((lane % kCPR) ^ (((p * kRowsPerDma + r_in) / kRPW) & (kCPR - 1))) * 8;
 #pragma unroll
     for (int j = 0; j < kInstr; ++j) {
       const int row = (wave * kInstr + j) * kRowsPerDma + r_in;
-      voff[j] = (unsigned)((row * ld + c * 8) * 2);
+      voff[j] = (unsigned)((row * ld + kc[j & 1]) * 2);
     }
-    kc = c * 8;
     slot0 = wave * kInstr * kRowsPerDma * kCPR;
   }
 
-  // instruction j of the stage whose K offset is k0, into `stage` (the
-  // operand's first slot in that LDS stage).  kalign (the row length is a
-  // multiple of kBK, so no stage has a K tail; a compile-time constant at
-  // every call): the descriptor is already based at the stage's K offset,
-  // and the per-lane offset alone decides whether the row exists.
-  // Otherwise chunks at or past column `kcols` are redirected out of range.
+  // instruction j of the stage whose K offset (along X) is k0, into `stage`
+  // (the operand's first slot in that LDS stage).  kalign (the row lengths
+  // are multiples of kBK, so no stage has a K tail; a compile-time constant
+  // at every call): the descriptor is already based at the stage's K
+  // offset, and the per-lane offset alone decides whether the row exists.
+  // Otherwise each chunk finds its own column: X column k reads operand
+  // column k - wrap once k >= wrap (wrap > 0: W read twice for X = [hi |
+  // lo]), and chunks at or past column `kcols` are redirected out of range.
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, u32x4* stage, int j, int k0,
-                                        int kcols, bool kalign) const {
-    const unsigned v = kalign ? voff[j]
-                              : k0 + kc < kcols ? voff[j] + (unsigned)(k0 * 2) : 0x80000000u;
+                                        int kcols, int wrap, bool kalign) const {
+    unsigned v = voff[j];
+    if (!kalign) {
+      const int kk = k0 + kc[j & 1];
+      const int kw = wrap > 0 && kk >= wrap ? kk - wrap : kk;
+      v = kw < kcols ? v + (unsigned)((kw - kc[j & 1]) * 2) : 0x80000000u;
+    }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(stage + slot0 + j * kRowsPerDma * kCPR), 16,
         v, 0, 0, 0);
@@ -92,6 +104,11 @@ template <int N, bool LDS = false>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LDS ? 0 : 15) << 8));
+}
+
+// s_waitcnt for all of this wave's LDS reads
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 // Output tiles and their order.  The tile order walks groups of kGroupM
@@ -143,14 +160,15 @@ __device__ __forceinline__ int rows_bytes(int row0, int nrows, int ld) {
 }
 
 // A persistent workgroup computes its tiles one after the other through one
-// continuous LDS pipeline: its K stages are numbered across tiles, the ring
-// slot of stage s is s % kStages, and the loads that run kStages - 1 stages
-// ahead cross into the next tile during the last trips of the current one,
-// so the next tile's first two stages are in LDS when the current tile's
-// epilogue starts (the third is loaded right after it).  The epilogue
-// stages its output through LDS rows past the ring (32 tokens x 128
-// features per wave at a time) and needs no barrier; a barrier after it
-// makes the next tile's first stage visible.  Compared with one workgroup
+// continuous LDS pipeline: its K stages are numbered across tiles, W of
+// stage s sits in ring slot s % 3 and X in slot s % 2 (160 KB), and the
+// loads that run two stages ahead cross into the next tile during the last
+// trips of the current one, so the next tile's first stage (and the W half
+// of its second) is in LDS when the current tile's epilogue starts; the
+// rest of its second stage is loaded right after it.  The epilogue stages
+// its output through the X slot of the tile's last stage (32 tokens x 128
+// features per wave at a time) after one barrier; a barrier after it makes
+// the next tile's first stage visible.  Compared with one workgroup
 // per tile, the next tile's prologue and the workgroup launch are off the
 // critical path, which pays at short K (a few stages per tile).
 //
@@ -163,15 +181,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FB = WN / 32, TB = WM / 32;
   static_assert(WN == 128, "the epilogues stage 128 features per wave");
-  static_assert(kBK == 32 && kStages == 4, "the pipeline below is written for 2 substeps x 4 stages");
+  static_assert(kBK == 64 && kStages == 2 && kWSlots == 3 && kXSlots == 2,
+                "the pipeline below is written for 4 substeps, W 3 and X 2 stages deep");
   static_assert(FB == 4 && TB == 4, "16 MFMAs per substep");
-  // One LDS array: the K-stage ring, then the epilogue's staging rows (per
-  // wave 32 rows x 256 B).  A second __shared__ array would give the
-  // compiler alias scopes under which it waits for every LDS DMA in flight
-  // before each fragment read; the waits below already order them.
-  constexpr int kStageSlots = (BN + BM) * kCPR;
-  __shared__ u32x4 lds[kStages * kStageSlots + (kThreads / 64) * 32 * 16];
-  auto ring = [&](int slot) { return &lds[slot * kStageSlots]; };
+  // One LDS array: the W ring, then the X ring.  A second __shared__ array
+  // would give the compiler alias scopes under which it waits for every
+  // LDS DMA in flight before each fragment read; the waits below already
+  // order them.
+  constexpr int kWStage = BN * kCPR, kXStage = BM * kCPR;  // 16-byte slots per stage
+  static_assert((kThreads / 64) * 32 * 16 <= kXStage, "the epilogue stages through an X slot");
+  __shared__ u32x4 lds[kWSlots * kWStage + kXSlots * kXStage];
+  auto wring = [&](unsigned slot) { return &lds[slot * kWStage]; };
+  auto xring = [&](unsigned slot) { return &lds[kWSlots * kWStage + slot * kXStage]; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,8 +217,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   pw.init(Kw, wave, lane);
   px.init(K, wave, lane);
   constexpr int kLw = DmaPlan<BN>::kInstr, kLx = DmaPlan<BM>::kInstr;
-  static_assert(kLw == 4 && kLx == 4, "one load per two MFMAs in each substep's second half");
-  // K offset into W of a tile's stage kt (K <= 2 Kw: X = [hi | lo] reads W at most twice)
+  static_assert(kLw == 8 && kLx == 8, "one load per MFMA in a stage's last substep");
+  const int wrap = a.w_kmod > 0 ? Kw : 0;
+  // K offset into W of a tile's stage kt when K is aligned (K <= 2 Kw: X =
+  // [hi | lo] reads W at most twice, and Kw is a multiple of kBK)
   auto w_k0 = [&](int kt) { const int k0 = kt * kBK; return k0 >= Kw ? k0 - Kw : k0; };
 
   // Operand rows of the current tile (cur) and of this workgroup's next
@@ -223,20 +246,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   Src cur = src_of(id);
   Src nxt = src_of(id + per_wg);
 
-  // The loads of stage kt of a tile into ring slot `slot`: two buffer
-  // descriptors (rebased to the stage's K offset when K is aligned) and 8
-  // instructions, issued one at a time (half 0 = W, 1 = X).
+  // The loads of stage kt of a tile into W ring slot ws and X ring slot xs:
+  // two buffer descriptors (rebased to the stage's K offset when K is
+  // aligned) and 8 + 8 instructions, issued one at a time (half 0 = W, 1 =
+  // X).
   struct StageLoad {
     __amdgpu_buffer_rsrc_t w, x;
-    u32x4* dst;
-    int kw, kx;
+    u32x4 *dw, *dx;
+    int kx;
   };
-  auto stage_load = [&](const Src& s, int slot, int kt) {
+  auto stage_load = [&](const Src& s, int kt, unsigned ws, unsigned xs) {
     StageLoad l;
-    l.dst = ring(slot);
-    l.kw = w_k0(kt);
+    l.dw = wring(ws);
+    l.dx = xring(xs);
     l.kx = kt * kBK;
-    const int ow = KALIGN ? l.kw : 0, ox = KALIGN ? l.kx : 0;
+    const int ow = KALIGN ? w_k0(kt) : 0, ox = KALIGN ? l.kx : 0;
     l.w = __builtin_amdgcn_make_buffer_rsrc((void*)(s.w + ow), 0, max(s.wbytes - 2 * ow, 0),
                                             0x00020000);
     l.x = __builtin_amdgcn_make_buffer_rsrc((void*)(s.x + ox), 0, max(s.xbytes - 2 * ox, 0),
@@ -244,103 +268,104 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     return l;
   };
   auto issue = [&](const StageLoad& l, int j, int half) {
-    if (half == 0) pw.issue(l.w, l.dst, j, l.kw, Kw, KALIGN);
-    else px.issue(l.x, l.dst + BN * kCPR, j, l.kx, K, KALIGN);
-  };
-  auto load = [&](const Src& s, int slot, int kt, int j, int half) {
-    issue(stage_load(s, slot, kt), j, half);
+    if (half == 0) pw.issue(l.w, l.dw, j, l.kx, Kw, wrap, KALIGN);
+    else px.issue(l.x, l.dx, j, l.kx, K, 0, KALIGN);
   };
 
   // LDS offsets (16-byte slots) of this lane's fragments: row-major
-  // fragments of W (features) and X (tokens), chunk = 2 * substep + hh
-  int oa[2][FB], ob[2][TB];
+  // fragments of W (features) and X (tokens), chunk = 2 * substep + hh.
+  // Every fragment row is l32 plus a multiple of 16, so the swizzle term is
+  // l32's and one base per substep serves all fragments.
+  static_assert(WN % 16 == 0 && WM % 16 == 0 && BN % 16 == 0, "fragment rows keep l32's swizzle");
+  int cs[4];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-    for (int f = 0; f < FB; ++f) oa[sub][f] = swz(wn * WN + 32 * f + l32, 2 * sub + hh);
-#pragma unroll
-    for (int t = 0; t < TB; ++t) ob[sub][t] = BN * kCPR + swz(wm * WM + 32 * t + l32, 2 * sub + hh);
-  }
+  for (int sub = 0; sub < 4; ++sub) cs[sub] = swz(l32, 2 * sub + hh);
+  // offsets within a W slot and within an X slot
+  auto offa = [&](int sub, int f) { return cs[sub] + (wn * WN + 32 * f) * kCPR; };
+  auto offb = [&](int sub, int t) { return cs[sub] + (wm * WM + 32 * t) * kCPR; };
 
-  // Prologue: the first tile's stages 0 .. kStages - 2 (or, for K of fewer
-  // stages, whatever follows them) in flight, stage 0 landed and visible.
+  // Prologue: the first tile's stages 0 and 1 (or, for a one-stage K,
+  // whatever follows stage 0) in flight, stage 0 landed and visible.
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p) {
+  for (int p = 0; p < kStages; ++p) {
     const bool in_cur = p < nk;
+    const StageLoad l = stage_load(in_cur ? cur : nxt, in_cur ? p : p - nk, p, p);
 #pragma unroll
-    for (int j = 0; j < kLw; ++j) load(in_cur ? cur : nxt, p, in_cur ? p : p - nk, j, 0);
+    for (int j = 0; j < kLw; ++j) issue(l, j, 0);
 #pragma unroll
-    for (int j = 0; j < kLx; ++j) load(in_cur ? cur : nxt, p, in_cur ? p : p - nk, j, 1);
+    for (int j = 0; j < kLx; ++j) issue(l, j, 1);
   }
-  wait_vmem<2 * (kLw + kLx)>();
+  wait_vmem<kLw + kLx>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
   u32x4 fa[2][FB], fb[2][TB];
   {
-    const u32x4* st = ring(0);
+    const u32x4* sw = wring(0);
+    const u32x4* sx = xring(0);
 #pragma unroll
-    for (int f = 0; f < FB; ++f) fa[0][f] = st[oa[0][f]];
+    for (int f = 0; f < FB; ++f) fa[0][f] = sw[offa(0, f)];
 #pragma unroll
-    for (int t = 0; t < TB; ++t) fb[0][t] = st[ob[0][t]];
+    for (int t = 0; t < TB; ++t) fb[0][t] = sx[offb(0, t)];
   }
 
-  // One K stage (two 16-wide substeps) per trip; g is the stage's number
+  // One K stage (four 16-wide substeps) per trip; g is the stage's number
   // in this workgroup's sequence and kt its index in the current tile.
   // Each substep issues its 16 MFMAs interleaved with the 8 LDS reads of
-  // the next substep's fragments (first half) and 4 of the loads of stage
-  // g + 3 (second half), so that no wave stalls for long on a queue of
-  // loads.  Stage g + 3 goes to the ring slot of stage g - 1.  Every wave's
-  // reads of that slot had completed (s_waitcnt lgkmcnt(0)) before it
-  // reached the barrier in the middle of trip g - 1 (or, for a tile's last
-  // trip, the barrier after its epilogue), which in turn makes stage g
-  // visible.  Stage g + 3 is stage kt + 3 of this tile or, past its end, a
-  // stage of the next one.  A tile's last trip (NEXT false) issues no loads,
-  // reads no fragments in its second substep and has no barrier in the
-  // middle: its stage g + 3 (the next tile's stage 2) is loaded, and the
-  // next tile's first fragments are read, after the epilogue.  Loads
-  // complete in order, so a load the epilogue itself issues then waits
-  // only for stages issued a trip or more earlier.
+  // the next substep's fragments (first half).  The loads of stage g + 2
+  // go to the slots of stages g - 1 (W) and g (X): W's, free since the
+  // previous trip's barrier, in the second halves of the first two
+  // substeps (one load per two MFMAs), X's in the last substep.  Before the
+  // last substep every wave waits for stage g + 1 (only the W half of
+  // stage g + 2 may still be in flight) and meets the others at a barrier:
+  // stage g + 1 is then visible, and every wave's reads of stage g are done
+  // (its last substep's fragments were read during the third), so the last
+  // substep reloads stage g's X slot while it reads the first fragments of
+  // stage g + 1.  Stage g + 2 is stage kt + 2 of this tile or, past its
+  // end, a stage of the next one.  A tile's last trip (NEXT false) loads
+  // W of stage g + 2 (the next tile's stage 1) but no X, reads no
+  // fragments in its last substep and has no barrier there: X of the next
+  // tile's stage 1 is loaded, and the next tile's first fragments are read,
+  // after the epilogue.
   floatx16 acc[FB][TB];
-  unsigned g = 0;  // unsigned: the ring slot g % kStages is a mask
-  // A trip loads stage kt + kofs of tile rl (kofs = 3 with this tile,
-  // 3 - nk with the next one); a tile's last trip (NEXT false) loads
-  // nothing.
+  unsigned g = 0;  // unsigned: the X slot g % 2 is a mask
+  // A trip loads stage kt + kofs of tile rl (kofs = 2 with this tile,
+  // 2 - nk with the next one).
   auto trip = [&](int kt, const Src& rl, int kofs, auto NEXT) {
-    const int sl = (int)((g + kStages - 1) % kStages);
-    const StageLoad ld = stage_load(rl, sl, kt + kofs);
-    const u32x4* st = ring((int)(g % kStages));
-    const u32x4* st1 = ring((int)((g + 1) % kStages));
+    const unsigned w0 = g % kWSlots, w1 = (g + 1) % kWSlots, w2 = (g + 2) % kWSlots;
+    const u32x4* sw = wring(w0);
+    const u32x4* sx = xring(g % kXSlots);
+    const u32x4* sw1 = wring(w1);
+    const u32x4* sx1 = xring((g + 1) % kXSlots);
+    const StageLoad ld = stage_load(rl, kt + kofs, w2, g % kXSlots);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (sub == 1) {
+    for (int sub = 0; sub < 4; ++sub) {
+      if (sub == 3) {
         if constexpr (NEXT) {
-          // stage g + 1 landed: stage g + 2 (8 loads) and the first half of
-          // stage g + 3 (4 loads) may still be in flight; this wave's reads
-          // of stage g are done
-          wait_vmem<kLw + kLx + kLw, true>();
+          wait_vmem<kLw, true>();
           __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool reads = sub == 0 || NEXT;
-      const u32x4* rs = sub == 0 ? st : st1;
-      const int(&ra)[FB] = oa[sub ^ 1];
-      const int(&rb)[TB] = ob[sub ^ 1];
+      const bool reads = sub < 3 || NEXT;
+      const u32x4* rw = sub < 3 ? sw : sw1;
+      const u32x4* rx = sub < 3 ? sx : sx1;
+      const int ns = (sub + 1) & 3;  // the substep whose fragments are read
+      const int cb = sub & 1, nb = cb ^ 1;
 #pragma unroll
       for (int i = 0; i < FB * TB; ++i) {
         const int f = i / TB, t = i % TB;
-        acc[f][t] = F16 ? mfma32x32x16_f16(fa[sub][f], fb[sub][t], acc[f][t])
-                        : mfma32x32x16(fa[sub][f], fb[sub][t], acc[f][t]);
-        if (i < 8) {
+        acc[f][t] = F16 ? mfma32x32x16_f16(fa[cb][f], fb[cb][t], acc[f][t])
+                        : mfma32x32x16(fa[cb][f], fb[cb][t], acc[f][t]);
+        if (i < 8 && reads) {
           // next substep's fragments in the order its MFMAs use them
-          if (reads) {
-            if (i == 0) fa[sub ^ 1][0] = rs[ra[0]];
-            else if (i <= 4) fb[sub ^ 1][i - 1] = rs[rb[i - 1]];
-            else fa[sub ^ 1][i - 4] = rs[ra[i - 4]];
-          }
-        } else if ((i & 1) == 0) {
-          if constexpr (NEXT) issue(ld, (i - 8) / 2, sub);
+          if (i == 0) fa[nb][0] = rw[offa(ns, 0)];
+          else if (i <= 4) fb[nb][i - 1] = rx[offb(ns, i - 1)];
+          else fa[nb][i - 4] = rw[offa(ns, i - 4)];
+        }
+        if (sub < 2 && i >= 8 && (i & 1) == 0) issue(ld, 4 * sub + (i - 8) / 2, 0);
+        if constexpr (NEXT) {
+          if (sub == 3 && i >= 8) issue(ld, i - 8, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -362,12 +387,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     const int nw = n0 + wn * WN;  // first feature of this wave
 
     {
-      // from trip nk - 3 on, the loads run into the next tile (one uniform
-      // branch per trip; the descriptors change once per tile)
-      Src rl = cur;
-      int kofs = kStages - 1;
+      // from trip nk - 2 on, the loads run into the next tile (one uniform
+      // branch per trip; the descriptors change once per tile).  A
+      // one-stage K has one tile per workgroup: its last trip loads zeros.
+      Src rl = nk < kStages ? nxt : cur;
+      int kofs = nk < kStages ? 0 : kStages;
       for (int kt = 0; kt < nk - 1; ++kt) {
-        if (kt == nk - kStages + 1) {
+        if (kt == nk - kStages) {
           // a real branch, not selects executed on every trip
           asm volatile("");
           rl = nxt;
@@ -377,6 +403,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       }
       trip(nk - 1, rl, kofs, False());
     }
+    // every wave's reads of the last stage done: its X slot stages the output
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 
     // The accumulators of token blocks t0 .. TB - 1 stay in the
     // matrix-core registers until block t0's epilogue starts: the compiler
@@ -390,7 +420,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           if (t >= t0) asm volatile("" : "+a"(acc[f][t]));
     };
 
-    u32x4* const stage = &lds[kStages * kStageSlots + wave * 32 * 16];  // 32 rows x 16 chunks
+    // 32 rows x 16 chunks per wave, in the X slot of the last stage (g - 1)
+    u32x4* const stage = xring((g + 1) % kXSlots) + wave * 32 * 16;
     // lane-derived epilogue addresses are computed here, not kept live
     // (and spilled) across the K loop
     int lane = tid & 63;
@@ -627,31 +658,32 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
 
-    // every load and store of this wave done (the next tile's stages 0
-    // and 1 landed), on the way out of the loop too
+    // every load and store of this wave done (the next tile's stage 0
+    // landed), on the way out of the loop too
     wait_vmem<0, true>();
     id += per_wg;
     if (id >= run_end) break;
     cur = nxt;
     nxt = src_of(id + per_wg);
-    // stage 0 of the next tile (ring slot g % kStages) visible; every
-    // wave's reads of the last stage are done
+    // stage 0 of the next tile visible; every wave's staging is done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // the next tile's stage 2 (held back by the last trip) into the slot
-    // of the last trip's stage; the stage index is opaque so that its load
-    // offsets are not hoisted out of the tile loop
-    int k2 = kStages - 2;
-    asm volatile("" : "+s"(k2));
+    // X of the next tile's stage 1 (held back by the last trip) into the X
+    // slot that staged the output; the stage index is opaque so that its
+    // load offsets are not hoisted out of the tile loop
+    int k1 = kStages - 1;
+    asm volatile("" : "+s"(k1));
+    {
+      const StageLoad l = stage_load(cur, k1, (g + 1) % kWSlots, (g + 1) % kXSlots);
 #pragma unroll
-    for (int j = 0; j < kLw; ++j) load(cur, (int)((g + kStages - 2) % kStages), k2, j, 0);
+      for (int j = 0; j < kLx; ++j) issue(l, j, 1);
+    }
+    const u32x4* sw = wring(g % kWSlots);
+    const u32x4* sx = xring(g % kXSlots);
 #pragma unroll
-    for (int j = 0; j < kLx; ++j) load(cur, (int)((g + kStages - 2) % kStages), k2, j, 1);
-    const u32x4* st = ring((int)(g % kStages));
+    for (int f = 0; f < FB; ++f) fa[0][f] = sw[offa(0, f)];
 #pragma unroll
-    for (int f = 0; f < FB; ++f) fa[0][f] = st[oa[0][f]];
-#pragma unroll
-    for (int t = 0; t < TB; ++t) fb[0][t] = st[ob[0][t]];
+    for (int t = 0; t < TB; ++t) fb[0][t] = sx[offb(0, t)];
   }
 }
 
@@ -847,14 +879,14 @@ namespace {
 
 // Workgroups of the large GEMMs: one per tile (padded to a multiple of the
 // XCDs), at most one per compute unit (each holds 160 KB of LDS), rounded
-// down to a multiple of the XCDs.  With fewer than kStages - 1 K stages a
-// load that runs ahead could reach two tiles further, so every workgroup
-// then gets exactly one tile.
+// down to a multiple of the XCDs.  With fewer than kStages K stages a load
+// that runs ahead could reach two tiles further, so every workgroup then
+// gets exactly one tile.
 int gemm_workgroups(int N, int M, int K, int batch = 1) {
   constexpr int BN = 256, BM = 256;
   const int tiles = gemm_tiles(N, M, BN, BM) * batch;
   int grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  if ((K + kBK - 1) / kBK < kStages - 1) return grid;
+  if ((K + kBK - 1) / kBK < kStages) return grid;
   static int cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return grid;
