@@ -171,6 +171,20 @@ def test_workspace_sizes():
     assert T.gqa_workspace_bytes(cfg(num_kv_heads=5), 1, 1, 1, T.WS_LAYER) == 0
 
 
+def test_workspace_sizes_of_empty_and_few_token_calls():
+    """Sizing an empty call (no batch, or no new tokens) is host arithmetic
+    only and must not divide by the zero token count; a few-token call's
+    projection workspace holds at least its fp32 output."""
+    _lib_or_skip()
+    dec = cfg(hidden_size=2560, num_heads=32, num_kv_heads=1)
+    for kind in (T.WS_QKV, T.WS_ATTN, T.WS_LAYER):
+        for batch, q_len in ((0, 1), (4, 0), (0, 0)):
+            assert T.gqa_workspace_bytes(dec, batch, q_len, 64, kind) >= 0
+    n_qkv = (32 + 2) * 128
+    for tokens in (1, 64, 256):
+        assert T.gqa_workspace_bytes(dec, tokens, 1, 64, T.WS_QKV) >= tokens * n_qkv * 4
+
+
 def _raw_call_layer(c, batch, q_len, cap, ptr=1, ws_bytes=1 << 40):
     L = T.lib()
     cc = c.c()

@@ -794,6 +794,124 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs
   }
 }
 
+// The few-token GEMM for K (and a hi|lo X's W width) a multiple of 64: a
+// workgroup computes 64 features x 64 tokens over its share of K.  Its
+// stages of 64 K (whole 128-byte lines of 64 W rows and 64 X rows, 16 KB)
+// are loaded straight into a ring of kSkR LDS slots, kSkR - 2 stages ahead
+// of the products, so a workgroup keeps about 48 KB of loads in flight and
+// the weights stream at close to the memory's rate; each wave owns one
+// 32 x 32 block of the output (4 MFMAs per stage).  Stage i's slot is
+// reloaded with stage i + kSkR - 1 right after the barrier that opens
+// stage i + 1: every wave has read it by then.
+constexpr int kSkR = 5;
+constexpr int kSkStage = 2 * 64 * 8;  // 16-byte slots per stage (W rows, then X rows)
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  // s_waitcnt needs an immediate: n (0 .. N) in steps of 4 loads per stage
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmem<N>();
+      return;
+    }
+    wait_vmem_upto<N - 4>(n);
+  } else {
+    wait_vmem<0>();
+  }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs a) {
+  __shared__ u32x4 lds[kSkR * kSkStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int N = a.N, M = a.M, K = a.K;
+  const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
+  const int f0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  // this workgroup's stages [s0, s0 + n) of the K/64 stages
+  const int nst = K / 64;
+  const int zs = (nst + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int s0 = (int)blockIdx.z * zs;
+  const int n = max(min(nst, s0 + zs) - s0, 0);
+
+  // Loads: waves 0-1 move W rows, waves 2-3 X rows, 32 rows per wave in 4
+  // instructions of 8 whole rows each, into the swizzled slots the
+  // fragment reads expect (chunk c of row r at c ^ ((r / 2) % 8)).
+  const int op = wave >> 1;
+  const int rbase = 32 * (wave & 1);
+  const int ld = op ? K : Kw;
+  const long long opbytes = op ? (long long)(M - m0) * K * 2 : (long long)(N - f0) * Kw * 2;
+  const __bf16* opbase = op ? a.X + (size_t)m0 * K : a.W + (size_t)f0 * Kw;
+  unsigned voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = rbase + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    voff[j] = (unsigned)((row * ld + c * 8) * 2);
+  }
+  auto issue_stage = [&](int i) {
+    const int k0 = (s0 + i) * 64;
+    const int kc = op ? k0 : (k0 >= Kw ? k0 - Kw : k0);  // W is read twice for X = [hi | lo]
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(opbase + kc, opbytes - 2LL * kc);
+    u32x4* dst = &lds[(i % kSkR) * kSkStage + op * 512 + rbase * 8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(r, dst + 64 * j, voff[j]);
+  };
+
+  // fragments: wave = (feature block fb, token block tb)
+  const int fb = wave & 1, tb = wave >> 1;
+  int oa[4], ob[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int c = (2 * st + hh) ^ ((l32 >> 1) & 7);  // rows 32 fb + l32 and 32 tb + l32 share it
+    oa[st] = (32 * fb + l32) * 8 + c;
+    ob[st] = 512 + (32 * tb + l32) * 8 + c;
+  }
+
+  const int pro = min(n, kSkR);
+  for (int i = 0; i < pro; ++i) issue_stage(i);
+  floatx16 acc = {};
+  for (int i = 0; i < n; ++i) {
+    // stage i landed: only the stages issued after it may be in flight
+    // (up to kSkR - 1 of them, 4 loads each)
+    const int issued = i == 0 ? pro : min(n, i + kSkR - 1);
+    wait_vmem_upto<4 * (kSkR - 1)>(4 * (issued - i - 1));
+    __builtin_amdgcn_s_barrier();
+    // every wave is past its reads of stage i - 1: reload that slot
+    if (i >= 1 && i + kSkR - 1 < n) issue_stage(i + kSkR - 1);
+    const u32x4* sl = &lds[(i % kSkR) * kSkStage];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 fa = sl[oa[st]], fbv = sl[ob[st]];
+      acc = F16 ? mfma32x32x16_f16(fa, fbv, acc) : mfma32x32x16(fa, fbv, acc);
+    }
+    wait_lds();
+  }
+
+  const bool partial = gridDim.z > 1;
+  float* const pz = partial ? a.part + (size_t)blockIdx.z * M * N : nullptr;
+  const int m = m0 + 32 * tb + l32;
+  if (m >= M) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int nn = f0 + 32 * fb + 8 * j + 4 * hh;
+    if (nn >= N) continue;
+    if (partial) {
+      floatx4 w = {acc[4 * j + 0], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+      *reinterpret_cast<floatx4*>(pz + (size_t)m * N + nn) = w;
+    } else if (a.out_f32) {
+      floatx4 w = {acc[4 * j + 0], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+      *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + (size_t)m * N + nn) = w;
+    } else {
+      u32x2 w;
+      w.x = pack_bf16x2(acc[4 * j + 0], acc[4 * j + 1]);
+      w.y = pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3]);
+      st8(static_cast<bf16*>(a.out) + (size_t)m * N + nn, w);
+    }
+  }
+}
+
 // out = sum over the splits of part[z] (four elements per thread), fp32 or
 // bf16 (N % 4 == 0)
 __global__ __launch_bounds__(256) void skinny_sum_kernel(const float* __restrict__ part, int S,
@@ -838,11 +956,22 @@ hipError_t launch_cvt_bf16_f16(const __bf16* in, void* out, long long n, hipStre
   return hipGetLastError();
 }
 
-// Only when the features alone leave more than half of the CUs idle: a
-// decode step's o_proj (2560 features: 80 workgroups) went from 58 to 30 us
-// (+4 us for the sum) with 4 splits, while its QKV projection (4352
-// features: 136 workgroups) did not gain from 2.
-int skinny_ksplit(int N, int K) {
+// The 64-aligned kernel: K splits that bring the workgroups (64 x 64
+// output blocks) to about two per CU, each with at least two K stages of
+// 64.  Otherwise (the general kernel, 32 features per workgroup) only when
+// the features alone leave more than half of the CUs idle: a decode step's
+// o_proj (2560 features: 80 workgroups) went from 58 to 30 us (+4 us for
+// the sum) with 4 splits, while its QKV projection (4352 features: 136
+// workgroups) did not gain from 2.
+int skinny_ksplit(int N, int K, int M) {
+  if (K % 64 == 0) {
+    const int wgs = max(1, ((N + 63) / 64) * ((M + 63) / 64));  // M = 0: an empty call
+    int ks = (512 + wgs - 1) / wgs;
+    const int max_ks = K / 64 / 2;
+    if (ks > max_ks) ks = max_ks;
+    if (ks > 16) ks = 16;
+    return ks < 1 ? 1 : ks;
+  }
   const int wgs = (N + 31) / 32;
   if (wgs >= 128) return 1;
   int ks = (256 + wgs - 1) / wgs;
@@ -854,11 +983,19 @@ int skinny_ksplit(int N, int K) {
 
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
   const int ks = args.part && args.ksplit > 1 ? args.ksplit : 1;
-  dim3 grid((args.N + 31) / 32, (args.M + 63) / 64, ks);
-  if (args.f16)
-    gemm_skinny_kernel<true><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
-  else
-    gemm_skinny_kernel<false><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+  if (args.K % 64 == 0 && (args.w_kmod <= 0 || args.w_kmod % 64 == 0)) {
+    dim3 grid((args.N + 63) / 64, (args.M + 63) / 64, ks);
+    if (args.f16)
+      gemm_skinny_lds_kernel<true><<<grid, 256, 0, stream>>>(args);
+    else
+      gemm_skinny_lds_kernel<false><<<grid, 256, 0, stream>>>(args);
+  } else {
+    dim3 grid((args.N + 31) / 32, (args.M + 63) / 64, ks);
+    if (args.f16)
+      gemm_skinny_kernel<true><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+    else
+      gemm_skinny_kernel<false><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const long long n4 = (long long)args.M * args.N / 4;

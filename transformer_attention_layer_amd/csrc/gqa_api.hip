@@ -223,10 +223,10 @@ size_t skinny_part_bytes(const Shape& s, size_t T) {
   if (!use_skinny(s, (long long)T)) return 0;
   size_t b = 0;
   if (s.n_qkv % 4 == 0)
-    b = (size_t)gqa::skinny_ksplit(s.n_qkv, s.H) * T * s.n_qkv * sizeof(float);
+    b = (size_t)gqa::skinny_ksplit(s.n_qkv, s.H, (int)T) * T * s.n_qkv * sizeof(float);
   const int ko = s.Hq * s.d * (s.o_split ? 2 : 1);
   if (s.H % 4 == 0) {
-    const size_t o = (size_t)gqa::skinny_ksplit(s.H, ko) * T * s.H * sizeof(float);
+    const size_t o = (size_t)gqa::skinny_ksplit(s.H, ko, (int)T) * T * s.H * sizeof(float);
     if (o > b) b = o;
   }
   return align_up(b);
@@ -329,7 +329,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     g.out = y;
     g.out_f32 = 1;
     if (use_skinny(s, T) && s.n_qkv % 4 == 0) {
-      g.ksplit = gqa::skinny_ksplit(s.n_qkv, s.H);
+      g.ksplit = gqa::skinny_ksplit(s.n_qkv, s.H, T);
       g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + skinny_part_offset(s, (size_t)T));
     }
     r = use_skinny(s, T)
@@ -496,7 +496,7 @@ gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, co
     g.out_f32 = s.out_f32;
     if (use_skinny(s, tokens)) {
       if (part && s.H % 4 == 0) {
-        g.ksplit = gqa::skinny_ksplit(s.H, g.K);
+        g.ksplit = gqa::skinny_ksplit(s.H, g.K, tokens);
         g.part = static_cast<float*>(part);
       }
       return check_launch(gqa::launch_gemm_skinny_bf16(g, st), "o_proj (few tokens)");

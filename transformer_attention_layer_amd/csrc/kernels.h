@@ -41,8 +41,9 @@ struct GemmArgs {
   int ksplit;
   float* part;
 };
-// K splits for the few-token GEMM that bring its workgroups to about one per CU
-int skinny_ksplit(int N, int K);
+// K splits for the few-token GEMM of M tokens that bring its workgroups to
+// about one or two per CU
+int skinny_ksplit(int N, int K, int M);
 
 struct AttnArgs {
   int d;            // head_dim: 64, 128 or 256
