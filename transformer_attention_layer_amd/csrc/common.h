@@ -16,6 +16,18 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // 0.5 * log2(e) etc. are formed on the host; log2(e) here for exp2-based softmax.
 #define GQA_LOG2E 1.4426950408889634f
 
+// (cos, sin) of position pos at rotary frequency i of `half` (the rotary
+// width is 2 half): angle pos * theta^(-2 i / (2 half)), in double, rounded
+// to float once.  One definition for the RoPE table and for the kernels that
+// evaluate it in place, so both give the same values.
+GQA_DEV float2 rope_cos_sin(long pos, int i, int half, double theta) {
+  const double inv = pow(theta, -2.0 * (double)i / (double)(2 * half));
+  const double ang = (double)pos * inv;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  return make_float2((float)cs, (float)sn);
+}
+
 GQA_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 GQA_DEV u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 GQA_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -701,11 +701,7 @@ __global__ void rope_table_kernel(float2* __restrict__ table, const int* __restr
   } else {
     pos = row;
   }
-  const double inv = pow(theta, -2.0 * (double)i / (double)(2 * half));
-  const double ang = (double)pos * inv;
-  double s, c;
-  sincos(ang, &s, &c);
-  table[idx] = make_float2((float)c, (float)s);
+  table[idx] = rope_cos_sin(pos, i, half, theta);
 }
 
 // Few-token projection (decode): weight streaming.  A workgroup computes a
@@ -957,8 +953,9 @@ hipError_t launch_cvt_bf16_f16(const __bf16* in, void* out, long long n, hipStre
 }
 
 // The 64-aligned kernel: K splits that bring the workgroups (64 x 64
-// output blocks) to about two per CU, each with at least two K stages of
-// 64.  Otherwise (the general kernel, 32 features per workgroup) only when
+// output blocks) to at most two per CU (one round: a few workgroups past
+// that would double the time), each with at least two K stages of 64, and
+// no split left short or empty.  Otherwise (the general kernel, 32 features per workgroup) only when
 // the features alone leave more than half of the CUs idle: a decode step's
 // o_proj (2560 features: 80 workgroups) went from 58 to 30 us (+4 us for
 // the sum) with 4 splits, while its QKV projection (4352 features: 136
@@ -966,11 +963,13 @@ hipError_t launch_cvt_bf16_f16(const __bf16* in, void* out, long long n, hipStre
 int skinny_ksplit(int N, int K, int M) {
   if (K % 64 == 0) {
     const int wgs = max(1, ((N + 63) / 64) * ((M + 63) / 64));  // M = 0: an empty call
-    int ks = (512 + wgs - 1) / wgs;
-    const int max_ks = K / 64 / 2;
-    if (ks > max_ks) ks = max_ks;
+    const int nst = K / 64;
+    int ks = 512 / wgs;
+    if (ks > nst / 2) ks = nst / 2;
     if (ks > 16) ks = 16;
-    return ks < 1 ? 1 : ks;
+    if (ks <= 1) return 1;
+    const int per = (nst + ks - 1) / ks;  // stages per split
+    return (nst + per - 1) / per;
   }
   const int wgs = (N + 31) / 32;
   if (wgs >= 128) return 1;
@@ -997,7 +996,7 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
       gemm_skinny_kernel<false><<<grid, 64 * kSkinnyWaves, 0, stream>>>(args);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ks == 1) return e;
+  if (e != hipSuccess || ks == 1 || args.keep_parts) return e;
   const long long n4 = (long long)args.M * args.N / 4;
   skinny_sum_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, stream>>>(args.part, ks, n4, args.out,
                                                                        args.out_f32);

@@ -331,6 +331,8 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     if (use_skinny(s, T) && s.n_qkv % 4 == 0) {
       g.ksplit = gqa::skinny_ksplit(s.n_qkv, s.H, T);
       g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + skinny_part_offset(s, (size_t)T));
+      // the norm + RoPE pass sums the partial products itself
+      g.keep_parts = use_rows_normrope(s) ? 1 : 0;
     }
     r = use_skinny(s, T)
             ? check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection (few tokens)")
@@ -342,18 +344,30 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   }
   if (r != GQA_OK) return r;
   if (use_rows_normrope(s)) {
+    gqa::NormRopeRowsArgs n{};
+    // few tokens: the angles are evaluated in place (no table launch)
+    const bool few = use_skinny(s, T);
     float2* table =
         reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up((size_t)T * s.n_qkv * sizeof(float)));
-    const int rows = start_pos ? T : q_len;
-    r = check_launch(
-        gqa::launch_rope_table(table, start_pos, rows, q_len, s.rot / 2, (double)c.rope_theta, st),
-        "rope table");
-    if (r != GQA_OK) return r;
-    gqa::NormRopeRowsArgs n{};
+    if (!few) {
+      const int rows = start_pos ? T : q_len;
+      r = check_launch(
+          gqa::launch_rope_table(table, start_pos, rows, q_len, s.rot / 2, (double)c.rope_theta, st),
+          "rope table");
+      if (r != GQA_OK) return r;
+    }
     n.y = y;
+    if (few && s.bf16 && s.n_qkv % 4 == 0) {
+      const int ks = gqa::skinny_ksplit(s.n_qkv, s.H, T);
+      if (ks > 1) {
+        n.part = reinterpret_cast<const float*>(static_cast<char*>(ws) + skinny_part_offset(s, (size_t)T));
+        n.parts = ks;
+      }
+    }
+    n.theta = (double)c.rope_theta;
     n.q_norm_w = static_cast<const __bf16*>(qn);
     n.k_norm_w = static_cast<const __bf16*>(kn);
-    n.rope = table;
+    n.rope = few ? nullptr : table;
     n.start_pos = start_pos;
     n.q = static_cast<__bf16*>(q);
     n.k_cache = static_cast<__bf16*>(kc);

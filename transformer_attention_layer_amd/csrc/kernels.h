@@ -40,6 +40,7 @@ struct GemmArgs {
   // fp32 partial products go to part [ksplit][M][N] and are then summed into out
   int ksplit;
   float* part;
+  int keep_parts;  // ksplit > 1: leave the partial products for the consumer to sum
 };
 // K splits for the few-token GEMM of M tokens that bring its workgroups to
 // about one or two per CU
@@ -102,10 +103,14 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& args, hipStream_t stream);
 // bf16 outputs, head_dim 64, 128 or 256 and a rotary width that is a
 // multiple of 8 (normrope_rows_ok); cos / sin from a rope_table.
 struct NormRopeRowsArgs {
-  const float* y;  // [T, n_qkv]
+  const float* y;     // [T, n_qkv]
+  const float* part;  // or, when set, `parts` partial products [parts][T][n_qkv] summed in order
+  int parts;
   const __bf16* q_norm_w;
   const __bf16* k_norm_w;
-  const float2* rope;    // [rows, rot / 2]: rows = T (indexed by token row) with start_pos, else L
+  const float2* rope;    // [rows, rot / 2]: rows = T (indexed by token row) with start_pos, else L;
+                         // null: evaluated in place from each row's position and theta
+  double theta;
   const int* start_pos;  // [B] or null
   __bf16* q;             // [B, Hq, L, d]
   __bf16* k_cache;       // [B, Hkv, cap, d]

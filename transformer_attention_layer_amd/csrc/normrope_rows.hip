@@ -88,7 +88,25 @@ __global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRows
     if (head < a.Hq) { kind = 0; h = head; }
     else if (head < a.Hq + a.Hkv) { kind = 1; h = head - a.Hq; }
     else { kind = 2; h = head - a.Hq - a.Hkv; }
-    floatx4 y = ld_f4(a.y + (size_t)m * n_qkv + (size_t)head * D + e0);
+    floatx4 y;
+    if (a.part) {
+      // the split K's partial products, summed in split order; the loads
+      // of four splits go out together
+      const size_t o = (size_t)m * n_qkv + (size_t)head * D + e0;
+      const size_t plane = (size_t)a.B * a.L * n_qkv;
+      y = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int z0 = 0; z0 < a.parts; z0 += 4) {
+        floatx4 pz[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pz[i] = z0 + i < a.parts ? ld_f4(a.part + (size_t)(z0 + i) * plane + o) : floatx4{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (z0 + i < a.parts) y = z0 + i == 0 ? pz[i] : y + pz[i];
+      }
+    } else {
+      y = ld_f4(a.y + (size_t)m * n_qkv + (size_t)head * D + e0);
+    }
     const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
     if (kind != 2) {
       if (a.qk_norm) {
@@ -100,7 +118,27 @@ __global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRows
       const floatx4 p = partner4<R>(y, sub, rh4, rot4);
       if (e0 < a.rot) {
         floatx4 c, s;
-        cossin4(a.rope, rh, a.start_pos ? (int)m : tok, e0, c, s);
+        if (a.rope) {
+          cossin4(a.rope, rh, a.start_pos ? (int)m : tok, e0, c, s);
+        } else {
+          // lanes of the first half evaluate the angles; their partners
+          // (features + rh) take the same values
+          if (e0 < rh) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float2 cs = rope_cos_sin(pos, e0 + j, rh, a.theta);
+              c[j] = cs.x;
+              s[j] = cs.y;
+            }
+          }
+          const int base = threadIdx.x & 63 & ~(R - 1);
+          const int src = base + (e0 < rh ? sub : sub - rh4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            c[j] = __shfl(c[j], src, 64);
+            s[j] = __shfl(s[j], src, 64);
+          }
+        }
         y = e0 < rh ? y * c - p * s : y * c + p * s;
       }
     }
