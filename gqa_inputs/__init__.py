@@ -75,16 +75,16 @@ WORKLOADS = {
                            1e-6, "bf16", 3, o_fp16=True),
     "decode_h2560_gqa": Workload("decode_h2560_gqa", 64, 1, 2560, 32, 8, 128,
                                  True, 1e6, 1e-6, "bf16", 4, cache_len=32768,
-                                 o_split=True),
+                                 o_fp16=True),
     "decode_h2560_mqa": Workload("decode_h2560_mqa", 64, 1, 2560, 32, 1, 128,
                                  True, 1e6, 1e-6, "bf16", 4, cache_len=32768,
-                                 o_split=True),
+                                 o_fp16=True),
     # The decode workloads with FP8 (E4M3) K/V caches: half the cache bytes.
     "decode_h2560_gqa_fp8": Workload("decode_h2560_gqa_fp8", 64, 1, 2560, 32, 8, 128, True,
-                                     1e6, 1e-6, "bf16", 4, cache_len=32768, o_split=True,
+                                     1e6, 1e-6, "bf16", 4, cache_len=32768, o_fp16=True,
                                      kv_fp8=True),
     "decode_h2560_mqa_fp8": Workload("decode_h2560_mqa_fp8", 64, 1, 2560, 32, 1, 128, True,
-                                     1e6, 1e-6, "bf16", 4, cache_len=32768, o_split=True,
+                                     1e6, 1e-6, "bf16", 4, cache_len=32768, o_fp16=True,
                                      kv_fp8=True),
     # The explicit head_dim the pages cite for Gemma 3 (hidden 640, four
     # query heads, head_dim 256 rather than 160); one KV head.  Runs the

@@ -60,17 +60,20 @@ SMALL = {
                                                        rotary_dim=32),
     "rot64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=500, rotary_dim=64),
     # the fp16 carrier of the attention output on every attention kernel:
-    # prefill, the decode merge, the vector-unit path, few-token o_proj
+    # prefill, the decode merge (the decode workloads), the vector-unit path
     "o_fp16_d256": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=130, hq=4, hkv=2,
                                                        head_dim=256, o_fp16=True),
     "o_fp16_d80": GI.WORKLOADS["quotient_h4096"].with_(batch=1, seq=90, hidden=640, hq=8, hkv=4),
     # the bf16 hi + lo carrier on the prefill path (o_proj reads W_o twice along K)
     "o_split_prefill": GI.WORKLOADS["wide_h5120"].with_(batch=1, seq=260, o_fp16=False,
                                                         o_split=True),
-    "o_fp16_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000,
-                                                            o_split=False, o_fp16=True),
-    "o_fp16_mqa_decode": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777,
-                                                                o_split=False, o_fp16=True),
+    # ... and on the decode path (few-token o_proj over [hi | lo]); the
+    # decode workloads themselves carry o as fp16, with W_o rounded to fp16
+    # inside the few-token product
+    "o_split_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, cache_len=1000,
+                                                             o_split=True, o_fp16=False),
+    "o_split_mqa_decode": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, cache_len=777,
+                                                                 o_split=True, o_fp16=False),
 }
 
 

@@ -816,8 +816,9 @@ __device__ __forceinline__ void wait_vmem_upto(int n) {
   }
 }
 
-template <bool F16>
+template <bool F16, bool WCVT = false>
 __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs a) {
+  static_assert(!WCVT || F16, "W is rounded to fp16 for the fp16 products");
   __shared__ u32x4 lds[kSkR * kSkStage];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -879,7 +880,14 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs a) {
     const u32x4* sl = &lds[(i % kSkR) * kSkStage];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const u32x4 fa = sl[oa[st]], fbv = sl[ob[st]];
+      u32x4 fa = sl[oa[st]];
+      const u32x4 fbv = sl[ob[st]];
+      if constexpr (WCVT) {
+        fa.x = pack_f16x2(lo_bf16(fa.x), hi_bf16(fa.x));
+        fa.y = pack_f16x2(lo_bf16(fa.y), hi_bf16(fa.y));
+        fa.z = pack_f16x2(lo_bf16(fa.z), hi_bf16(fa.z));
+        fa.w = pack_f16x2(lo_bf16(fa.w), hi_bf16(fa.w));
+      }
       acc = F16 ? mfma32x32x16_f16(fa, fbv, acc) : mfma32x32x16(fa, fbv, acc);
     }
     wait_lds();
@@ -980,11 +988,17 @@ int skinny_ksplit(int N, int K, int M) {
   return ks < 1 ? 1 : ks;
 }
 
+bool skinny_lds_ok(int K, int w_kmod) { return K % 64 == 0 && (w_kmod <= 0 || w_kmod % 64 == 0); }
+
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
   const int ks = args.part && args.ksplit > 1 ? args.ksplit : 1;
-  if (args.K % 64 == 0 && (args.w_kmod <= 0 || args.w_kmod % 64 == 0)) {
+  if (args.w_bf16_to_f16 && (!args.f16 || !skinny_lds_ok(args.K, args.w_kmod)))
+    return hipErrorInvalidValue;
+  if (skinny_lds_ok(args.K, args.w_kmod)) {
     dim3 grid((args.N + 63) / 64, (args.M + 63) / 64, ks);
-    if (args.f16)
+    if (args.w_bf16_to_f16)
+      gemm_skinny_lds_kernel<true, true><<<grid, 256, 0, stream>>>(args);
+    else if (args.f16)
       gemm_skinny_lds_kernel<true><<<grid, 256, 0, stream>>>(args);
     else
       gemm_skinny_lds_kernel<false><<<grid, 256, 0, stream>>>(args);

@@ -494,13 +494,16 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
 
 // part (few tokens, optional): skinny_part_bytes of scratch for a K split.
 // w_o16 (optional): W_o as fp16, for an attention output o held as fp16.
+// w_cvt (few tokens, o as fp16, skinny_lds_ok): W_o stays bf16 and is
+// rounded to fp16 inside the product.
 gqa_status run_oproj(const Shape& s, int tokens, const void* o, bool o_split, const void* w_o,
                      void* out, hipStream_t st, void* part = nullptr,
-                     const void* w_o16 = nullptr) {
+                     const void* w_o16 = nullptr, bool w_cvt = false) {
   if (s.bf16) {
     gqa::GemmArgs g{};
     g.W = static_cast<const __bf16*>(w_o16 ? w_o16 : w_o);
-    g.f16 = w_o16 ? 1 : 0;
+    g.f16 = w_o16 || w_cvt ? 1 : 0;
+    g.w_bf16_to_f16 = w_cvt ? 1 : 0;
     g.X = static_cast<const __bf16*>(o);
     g.N = s.H;
     g.M = tokens;
@@ -836,7 +839,10 @@ gqa_status run_layer(const gqa_config& c, const Shape& s, int batch, int q_len, 
   w += align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1));
   void* ws_a = w;
   w += ws_attn(s, batch, q_len, kv_capacity);
-  void* wo16 = s.o_f16 ? w : nullptr;
+  // o as fp16: W_o as fp16 too, converted once per call, or (few tokens)
+  // rounded inside the product
+  const bool w_cvt = s.o_f16 && use_skinny(s, T) && gqa::skinny_lds_ok(s.Hq * s.d, 0);
+  void* wo16 = s.o_f16 && !w_cvt ? w : nullptr;
   r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, cache_len, qbuf, k_cache, v_cache,
               kv_capacity, ws_q, st);
   if (r != GQA_OK) return r;
@@ -854,7 +860,7 @@ gqa_status run_layer(const gqa_config& c, const Shape& s, int batch, int q_len, 
                    use_fused_qkv(s, (long long)T)
                        ? nullptr
                        : static_cast<char*>(ws_q) + skinny_part_offset(s, T),
-                   wo16);
+                   wo16, w_cvt);
 }
 
 }  // namespace

@@ -41,10 +41,16 @@ struct GemmArgs {
   int ksplit;
   float* part;
   int keep_parts;  // ksplit > 1: leave the partial products for the consumer to sum
+  // few-token GEMM with f16 set and skinny_lds_ok: W holds bf16, rounded to
+  // fp16 as its fragments are read (the same rounding as launch_cvt_bf16_f16)
+  int w_bf16_to_f16;
 };
 // K splits for the few-token GEMM of M tokens that bring its workgroups to
 // about one or two per CU
 int skinny_ksplit(int N, int K, int M);
+// the few-token GEMM's LDS-streamed kernel applies (K and a hi | lo X's W
+// width multiples of 64)
+bool skinny_lds_ok(int K, int w_kmod);
 
 struct AttnArgs {
   int d;            // head_dim: 64, 128 or 256
