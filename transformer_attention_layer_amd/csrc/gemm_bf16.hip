@@ -688,12 +688,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // cos/sin of position * theta^(-2i/d) for i < d/2, angles in double.
-__global__ void rope_table_kernel(float2* __restrict__ table, const int* __restrict__ start_pos,
-                                  int rows, int L, int half, double theta) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * half) return;
-  const int row = idx / half;
-  const int i = idx - row * half;
+// Entry idx of the RoPE table: row `row` is token row - b L of sequence b
+// (position start_pos[b] + that token), or position row without start_pos.
+__device__ __forceinline__ void rope_entry(float2* table, const int* start_pos, int rows, int L,
+                                           int half, double theta, long idx) {
+  if (idx >= (long)rows * half) return;
+  const int row = (int)(idx / half);
+  const int i = (int)(idx - (long)row * half);
   long pos;
   if (start_pos) {
     const int b = row / L;
@@ -702,6 +703,11 @@ __global__ void rope_table_kernel(float2* __restrict__ table, const int* __restr
     pos = row;
   }
   table[idx] = rope_cos_sin(pos, i, half, theta);
+}
+
+__global__ void rope_table_kernel(float2* __restrict__ table, const int* __restrict__ start_pos,
+                                  int rows, int L, int half, double theta) {
+  rope_entry(table, start_pos, rows, L, half, theta, (long)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // Few-token projection (decode): weight streaming.  A workgroup computes a
@@ -868,6 +874,13 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs a) {
 
   const int pro = min(n, kSkR);
   for (int i = 0; i < pro; ++i) issue_stage(i);
+  if (a.rope_table) {
+    const long nthreads = (long)gridDim.x * gridDim.y * gridDim.z * 256;
+    const long gid = (((long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 256 +
+                     threadIdx.x;
+    for (long e = gid; e < (long)a.rope_rows * a.rope_half; e += nthreads)
+      rope_entry(a.rope_table, a.rope_start_pos, a.rope_rows, a.rope_L, a.rope_half, a.rope_theta, e);
+  }
   floatx16 acc = {};
   for (int i = 0; i < n; ++i) {
     // stage i landed: only the stages issued after it may be in flight
@@ -994,6 +1007,7 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& args, hipStream_t stream) {
   const int ks = args.part && args.ksplit > 1 ? args.ksplit : 1;
   if (args.w_bf16_to_f16 && (!args.f16 || !skinny_lds_ok(args.K, args.w_kmod)))
     return hipErrorInvalidValue;
+  if (args.rope_table && !skinny_lds_ok(args.K, args.w_kmod)) return hipErrorInvalidValue;
   if (skinny_lds_ok(args.K, args.w_kmod)) {
     dim3 grid((args.N + 63) / 64, (args.M + 63) / 64, ks);
     if (args.w_bf16_to_f16)

@@ -239,6 +239,12 @@ size_t skinny_part_offset(const Shape& s, size_t T) {
   return use_rows_normrope(s) ? y + align_up(rope_table_bytes(s, T)) : y;
 }
 
+// The RoPE table of the separate norm/RoPE pass: after the fp32 projection.
+float2* rope_table_at(const Shape& s, void* ws, size_t T) {
+  return reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                   align_up(T * (size_t)s.n_qkv * sizeof(float)));
+}
+
 size_t ws_qkv(const Shape& s, int batch, int q_len) {
   const size_t T = (size_t)batch * q_len;
   if (use_fused_qkv(s, (long long)T)) return rope_table_bytes(s, T);  // T rows max
@@ -334,6 +340,15 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
       // the norm + RoPE pass sums the partial products itself
       g.keep_parts = use_rows_normrope(s) ? 1 : 0;
     }
+    if (use_skinny(s, T) && use_rows_normrope(s) && gqa::skinny_lds_ok(s.H, 0)) {
+      // the projection also fills the RoPE table (no launch of its own)
+      g.rope_table = rope_table_at(s, ws, (size_t)T);
+      g.rope_start_pos = start_pos;
+      g.rope_rows = start_pos ? T : q_len;
+      g.rope_L = q_len;
+      g.rope_half = s.rot / 2;
+      g.rope_theta = (double)c.rope_theta;
+    }
     r = use_skinny(s, T)
             ? check_launch(gqa::launch_gemm_skinny_bf16(g, st), "qkv projection (few tokens)")
             : check_launch(gqa::launch_gemm_plain_bf16(g, st), "qkv projection");
@@ -345,11 +360,9 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
   if (r != GQA_OK) return r;
   if (use_rows_normrope(s)) {
     gqa::NormRopeRowsArgs n{};
-    // few tokens: the angles are evaluated in place (no table launch)
     const bool few = use_skinny(s, T);
-    float2* table =
-        reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up((size_t)T * s.n_qkv * sizeof(float)));
-    if (!few) {
+    float2* table = rope_table_at(s, ws, (size_t)T);
+    if (!(few && gqa::skinny_lds_ok(s.H, 0))) {
       const int rows = start_pos ? T : q_len;
       r = check_launch(
           gqa::launch_rope_table(table, start_pos, rows, q_len, s.rot / 2, (double)c.rope_theta, st),
@@ -357,17 +370,16 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
       if (r != GQA_OK) return r;
     }
     n.y = y;
-    if (few && s.bf16 && s.n_qkv % 4 == 0) {
+    if (few && s.n_qkv % 4 == 0) {
       const int ks = gqa::skinny_ksplit(s.n_qkv, s.H, T);
       if (ks > 1) {
         n.part = reinterpret_cast<const float*>(static_cast<char*>(ws) + skinny_part_offset(s, (size_t)T));
         n.parts = ks;
       }
     }
-    n.theta = (double)c.rope_theta;
     n.q_norm_w = static_cast<const __bf16*>(qn);
     n.k_norm_w = static_cast<const __bf16*>(kn);
-    n.rope = few ? nullptr : table;
+    n.rope = table;
     n.start_pos = start_pos;
     n.q = static_cast<__bf16*>(q);
     n.k_cache = static_cast<__bf16*>(kc);

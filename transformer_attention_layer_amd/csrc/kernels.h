@@ -44,6 +44,13 @@ struct GemmArgs {
   // few-token GEMM with f16 set and skinny_lds_ok: W holds bf16, rounded to
   // fp16 as its fragments are read (the same rounding as launch_cvt_bf16_f16)
   int w_bf16_to_f16;
+  // few-token GEMM with skinny_lds_ok, optional: also fill the RoPE table
+  // [rope_rows, rope_half] as launch_rope_table would (its workgroups'
+  // first threads, while their first loads are in flight)
+  float2* rope_table;
+  const int* rope_start_pos;
+  int rope_rows, rope_L, rope_half;
+  double rope_theta;
 };
 // K splits for the few-token GEMM of M tokens that bring its workgroups to
 // about one or two per CU
@@ -114,9 +121,7 @@ struct NormRopeRowsArgs {
   int parts;
   const __bf16* q_norm_w;
   const __bf16* k_norm_w;
-  const float2* rope;    // [rows, rot / 2]: rows = T (indexed by token row) with start_pos, else L;
-                         // null: evaluated in place from each row's position and theta
-  double theta;
+  const float2* rope;    // [rows, rot / 2]: rows = T (indexed by token row) with start_pos, else L
   const int* start_pos;  // [B] or null
   __bf16* q;             // [B, Hq, L, d]
   __bf16* k_cache;       // [B, Hkv, cap, d]

@@ -118,27 +118,7 @@ __global__ __launch_bounds__(kRowsNT) void normrope_fwd_rows_kernel(NormRopeRows
       const floatx4 p = partner4<R>(y, sub, rh4, rot4);
       if (e0 < a.rot) {
         floatx4 c, s;
-        if (a.rope) {
-          cossin4(a.rope, rh, a.start_pos ? (int)m : tok, e0, c, s);
-        } else {
-          // lanes of the first half evaluate the angles; their partners
-          // (features + rh) take the same values
-          if (e0 < rh) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float2 cs = rope_cos_sin(pos, e0 + j, rh, a.theta);
-              c[j] = cs.x;
-              s[j] = cs.y;
-            }
-          }
-          const int base = threadIdx.x & 63 & ~(R - 1);
-          const int src = base + (e0 < rh ? sub : sub - rh4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            c[j] = __shfl(c[j], src, 64);
-            s[j] = __shfl(s[j], src, 64);
-          }
-        }
+        cossin4(a.rope, rh, a.start_pos ? (int)m : tok, e0, c, s);
         y = e0 < rh ? y * c - p * s : y * c + p * s;
       }
     }
