@@ -52,6 +52,17 @@ SMALL = {
                                                              hkv=4, o_fp16=False, o_split=True),
     "bf16_d64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=300, hq=8, hkv=4,
                                                               head_dim=64),
+    # the QKV projection's own norm/RoPE epilogue for head_dim 64 and 256
+    # (more than 256 tokens): 256 with and without a cache to continue,
+    # 64 with rotary 32 and with an odd head count (the last wave of
+    # features holds one head)
+    "bf16_d256_fused": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=150, hq=4, hkv=2,
+                                                           head_dim=256),
+    "gemma_d256_chunk": GI.WORKLOADS["gemma_h640_d256"].with_(batch=2, seq=200, cache_len=100),
+    "rot32_of_64_fused": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=150, hq=8, hkv=2,
+                                                             head_dim=64, rotary_dim=32),
+    "bf16_d64_odd_heads": GI.WORKLOADS["prefill_h1024"].with_(batch=1, seq=300, hq=3, hkv=1,
+                                                              head_dim=64),
     # partial rotary: 64 of 128 in the fused epilogue, 48 of 128 through the
     # separate norm/RoPE pass, 32 of 64 on the fallback path, 64 of 128 decode
     "rot64_of_128": GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=170, rotary_dim=64),
@@ -168,11 +179,11 @@ def test_prefill_variants(variant):
 
 @pytest.mark.parametrize("tokens", [1, 17, 64, 65, 200, 256])
 def test_few_token_projection_path(tokens):
-    """Up to 256 tokens take the weight-streaming projections (32-feature
-    tiles, K split over 8 waves, and for narrow outputs over workgroups too)
-    and a separate norm + RoPE pass; ragged token and feature counts, with
-    and without QK-norm and the hi+lo split (also with a 1024-wide o_proj,
-    whose K is split over workgroups)."""
+    """Up to 256 tokens take the weight-streaming projections (K split over
+    workgroups, 64-feature blocks streamed through LDS when K is a multiple
+    of 64, else 32-feature tiles) and a separate norm + RoPE pass; ragged
+    token and feature counts, with and without QK-norm and the hi+lo split
+    (also with a 1024-wide o_proj)."""
     for base, kw in (("prefill_h1024", {}), ("wide_h5120", {"hq": 40, "hkv": 8}),
                      ("quotient_h4096", {}), ("prefill_h1024", {"o_split": True}),
                      ("quotient_h4096", {"o_fp16": False, "o_split": True})):

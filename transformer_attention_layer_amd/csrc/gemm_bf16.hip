@@ -60,7 +60,9 @@ struct DmaPlan {
   int kc[2];              // K offset (elements) of this lane's chunk: even, odd instructions
   int slot0;              // first LDS slot of this wave's rows
 
-  __device__ __forceinline__ void init(int ld, int wave, int lane) {
+  // swap12: LDS rows 64..127 take operand rows 128..191 and the other
+  // way round (a head_dim-256 head's RoPE partners then sit in one wave)
+  __device__ __forceinline__ void init(int ld, int wave, int lane, bool swap12 = false) {
     const int r_in = lane / kCPR;
     // row = (wave kInstr + j) kRowsPerDma + r_in, so (row / kRPW) % kCPR
     // depends on the lane and on the parity of j only
@@ -69,7 +71,9 @@ struct DmaPlan {
       kc[p] = ((lane % kCPR) ^ (((p * kRowsPerDma + r_in) / kRPW) & (kCPR - 1))) * 8;
 #pragma unroll
     for (int j = 0; j < kInstr; ++j) {
-      const int row = (wave * kInstr + j) * kRowsPerDma + r_in;
+      int row = (wave * kInstr + j) * kRowsPerDma + r_in;
+      if (swap12 && (row >> 6) == 1) row += 64;
+      else if (swap12 && (row >> 6) == 2) row -= 64;
       voff[j] = (unsigned)((row * ld + kc[j & 1]) * 2);
     }
     slot0 = wave * kInstr * kRowsPerDma * kCPR;
@@ -177,7 +181,7 @@ __device__ __forceinline__ int rows_bytes(int row0, int nrows, int ld) {
 // the same, since the loads move bytes.
 template <int BN, int BM, int EPI, bool KALIGN, bool F16 = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
-  static_assert(!F16 || EPI != kEpiQKV, "the QKV epilogue takes bf16 operands");
+  static_assert(!F16 || !is_qkv_epi(EPI), "the QKV epilogues take bf16 operands");
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FB = WN / 32, TB = WM / 32;
   static_assert(WN == 128, "the epilogues stage 128 features per wave");
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int N = a.N, M = a.M, K = a.K;
-  const int batch = EPI == kEpiQKV ? 1 : max(a.batch, 1);
+  const int batch = is_qkv_epi(EPI) ? 1 : max(a.batch, 1);
   const TileOrder order(N, M, BN, BM, batch);
   const int xcd = (int)(blockIdx.x % kXcds);
   const int per_wg = (int)(gridDim.x / kXcds);  // workgroups on this XCD
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int Kw = a.w_kmod > 0 ? a.w_kmod : K;
   DmaPlan<BN> pw;
   DmaPlan<BM> px;
-  pw.init(Kw, wave, lane);
+  pw.init(Kw, wave, lane, EPI == kEpiQKV256);
   px.init(K, wave, lane);
   constexpr int kLw = DmaPlan<BN>::kInstr, kLx = DmaPlan<BM>::kInstr;
   static_assert(kLw == 8 && kLx == 8, "one load per MFMA in a stage's last substep");
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       stage8[(row * 16 + ((feat >> 3) ^ (row & 15))) * 2 + ((feat >> 2) & 1)] = v;
     };
     // batch member of this tile: its output block
-    const size_t oz = EPI == kEpiQKV ? 0 : (size_t)(id / order.per_z) * a.sOut;
+    const size_t oz = is_qkv_epi(EPI) ? 0 : (size_t)(id / order.per_z) * a.sOut;
     if constexpr (EPI == kEpiPlainF32) {
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
@@ -475,6 +479,327 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           const int m = m0 + wm * WM + 32 * t + row;
           const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
           if (m < M && n < N) st16(static_cast<bf16*>(a.out) + oz + (size_t)m * N + n, v);
+        }
+      }
+    } else if constexpr (EPI == kEpiQKV64) {
+      // ---- QKV epilogue, head_dim 64: two heads per wave ----
+      // As for head_dim 128 (below), with each 64-feature half of the wave
+      // (blocks 0-1 and 2-3) a head of its own: its norm sums the lane's two
+      // blocks, and RoPE pairs block 0 with block 1 (rot 64) or, for rot 32,
+      // the first two 8-feature steps of block 0 with its last two (block 1
+      // passes through).  Past the last head (an odd head count) the second
+      // half is skipped.
+      if (nw < N) {  // wave-uniform
+        const int Hq = a.Hq, Hkv = a.Hkv;
+        int kind[2], hid[2];
+        bool live[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int head = (nw >> 6) + hb;
+          live[hb] = nw + 64 * hb < N;
+          if (head < Hq) { kind[hb] = 0; hid[hb] = head; }
+          else if (head < Hq + Hkv) { kind[hb] = 1; hid[hb] = head - Hq; }
+          else { kind[hb] = 2; hid[hb] = head - Hq - Hkv; }
+        }
+        // norm weights of this lane's features 32 fl + 8 j + 4 hh + (0..3) of head hb
+        u32x2 wpk[2][2][4];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int fl = 0; fl < 2; ++fl)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+              const bool dn = live[hb] && kind[hb] != 2 && a.qk_norm;
+              wpk[hb][fl][j] =
+                  dn ? ld8((kind[hb] == 0 ? a.q_norm_w : a.k_norm_w) + 32 * fl + 8 * j + 4 * hh) : one;
+            }
+        const int half = a.rot >> 1;
+        const int L = a.L;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          pin_from(t);
+          const int mb = m0 + wm * WM + 32 * t;
+          const int b0 = mb / L;
+          const int tok0 = mb - b0 * L;
+          const bool long_seq = L >= 32;
+          auto locate = [&](int r, int& b, int& tok) {  // row mb + r, 0 <= r < 32
+            if (long_seq) {
+              tok = tok0 + r;
+              b = b0;
+              if (tok >= L) { tok -= L; ++b; }
+            } else {
+              b = (mb + r) / L;
+              tok = mb + r - b * L;
+            }
+          };
+          const int mr = mb + l32;
+          if (a.y_raw && mr < M) {
+            float* yr = a.y_raw + (size_t)mr * N + nw + 4 * hh;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                if (!live[f >> 1]) continue;
+                const floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1],
+                                   acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]};
+                *reinterpret_cast<floatx4*>(yr + 32 * f + 8 * j) = w;
+              }
+          }
+          int rb, rtok;
+          locate(l32, rb, rtok);
+          const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            if (!live[hb]) continue;  // wave-uniform
+            const int f0 = 2 * hb;
+            float inv = 1.0f;
+            if (kind[hb] != 2 && a.qk_norm) {
+              float ss = 0.f;
+#pragma unroll
+              for (int f = f0; f < f0 + 2; ++f)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
+              ss = sum_xor32(ss);
+              inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 64.0f) + a.eps);
+            }
+            // x of feature 32 fl + 8 j + 4 hh + e of head hb, normalised
+            auto xn = [&](int fl, int j, int e) {
+              const u32x2 w = wpk[hb][fl][j];
+              const float g = (e & 1) ? hi_bf16(e < 2 ? w.x : w.y) : lo_bf16(e < 2 ? w.x : w.y);
+              return acc[f0 + fl][t][4 * j + e] * inv * g;
+            };
+            auto put4 = [&](int feat, const float (&y)[4]) {
+              u32x2 o;
+              o.x = pack_bf16x2(y[0], y[1]);
+              o.y = pack_bf16x2(y[2], y[3]);
+              put8(l32, 64 * hb + feat, o);
+            };
+            if (kind[hb] == 2) {
+#pragma unroll
+              for (int fl = 0; fl < 2; ++fl)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float y[4] = {acc[f0 + fl][t][4 * j + 0], acc[f0 + fl][t][4 * j + 1],
+                                      acc[f0 + fl][t][4 * j + 2], acc[f0 + fl][t][4 * j + 3]};
+                  put4(32 * fl + 8 * j + 4 * hh, y);
+                }
+            } else {
+              // feature i < rot/2 pairs with i + rot/2: (block 0, step j) with
+              // (block 1, step j) for rot 64, with (block 0, step j + 2) for
+              // rot 32 (every index a constant)
+              auto pair = [&](int j, int fl2, int j2) {
+                const int i0 = 8 * j + 4 * hh;
+                const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
+                const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
+                const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
+                const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+                float y1[4], y2[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float x1 = xn(0, j, e), x2 = xn(fl2, j2, e);
+                  y1[e] = x1 * cc[e] - x2 * sn[e];
+                  y2[e] = x2 * cc[e] + x1 * sn[e];
+                }
+                put4(i0, y1);
+                put4(i0 + 32 * fl2 + 8 * (j2 - j), y2);
+              };
+              if (half == 32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pair(j, 1, j);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) pair(j, 0, j + 2);
+              }
+              if (half == 16) {  // block 1 is past the rotary width: norm only
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float y[4] = {xn(1, j, 0), xn(1, j, 1), xn(1, j, 2), xn(1, j, 3)};
+                  put4(32 + 8 * j + 4 * hh, y);
+                }
+              }
+            }
+          }
+          int sp0 = 0, sp1 = 0;
+          if (a.start_pos && long_seq) {
+            sp0 = a.start_pos[b0];
+            if ((b0 + 1) * L < M) sp1 = a.start_pos[b0 + 1];
+          }
+          // lane l moves chunk l % 16 of row 4 i + l / 16: chunks 0-7 are head
+          // 0's row, 8-15 head 1's
+          const int c = lane & 15;
+          const int hb = c >> 3;
+          const int kd = hb ? kind[1] : kind[0];
+          const int h = hb ? hid[1] : hid[0];
+          const bool lv = hb ? live[1] : live[0];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            const int m = mb + row;
+            const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
+            if (m >= M || !lv) continue;
+            int b, tok;
+            locate(row, b, tok);
+            bf16* dst;
+            if (kd == 0) {
+              dst = a.q + (((size_t)b * Hq + h) * L + tok) * 64;
+            } else {
+              const int base = !a.start_pos ? 0 : long_seq ? (b == b0 ? sp0 : sp1) : a.start_pos[b];
+              const int pos = base + tok;
+              if (pos < 0 || pos >= a.cap) continue;
+              dst = (kd == 1 ? a.k_cache : a.v_cache) + (((size_t)b * Hkv + h) * a.cap + pos) * 64;
+            }
+            st16(dst + 8 * (c & 7), v);
+          }
+        }
+      }
+    } else if constexpr (EPI == kEpiQKV256) {
+      // ---- QKV epilogue, head_dim 256 (full rotary): a tile is one head ----
+      // W's rows were loaded with 64-row blocks 1 and 2 swapped, so wave wn
+      // holds features 64 wn + (0..63) in blocks 0-1 and 128 + 64 wn + (0..63)
+      // in blocks 2-3: every RoPE pair (i, i + 128) sits in one lane, block f
+      // with f + 2, as for head_dim 128.  Only the norm's sum of squares
+      // spans the two waves of a pair (wn = 0, 1 over the same tokens): per
+      // 32-token block each wave posts its partial sum in LDS (two slots,
+      // alternating by block) and reads its partner's after one barrier.
+      // The slots are in the W ring slot of the tile's last stage, which no
+      // load writes before the next tile's first trip; the head is the same
+      // for the whole workgroup, so every wave runs the same barriers.
+      float* const xss = reinterpret_cast<float*>(wring((g + 2) % kWSlots));
+      const int Hq = a.Hq, Hkv = a.Hkv;
+      const int head = n0 >> 8;
+      int kind, h;
+      if (head < Hq) { kind = 0; h = head; }
+      else if (head < Hq + Hkv) { kind = 1; h = head - Hq; }
+      else { kind = 2; h = head - Hq - Hkv; }
+      const bool do_norm = kind != 2 && a.qk_norm;
+      // head feature of this wave's feature fl (0..127)
+      auto feat = [&](int fl) { return fl < 64 ? 64 * wn + fl : 64 + 64 * wn + fl; };
+      u32x2 wpk[4][4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+          wpk[f][j] = do_norm ? ld8((kind == 0 ? a.q_norm_w : a.k_norm_w) + feat(32 * f + 8 * j + 4 * hh))
+                              : one;
+        }
+      const int L = a.L;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        pin_from(t);
+        const int mb = m0 + wm * WM + 32 * t;
+        const int b0 = mb / L;
+        const int tok0 = mb - b0 * L;
+        const bool long_seq = L >= 32;
+        auto locate = [&](int r, int& b, int& tok) {  // row mb + r, 0 <= r < 32
+          if (long_seq) {
+            tok = tok0 + r;
+            b = b0;
+            if (tok >= L) { tok -= L; ++b; }
+          } else {
+            b = (mb + r) / L;
+            tok = mb + r - b * L;
+          }
+        };
+        const int mr = mb + l32;
+        if (a.y_raw && mr < M) {
+          float* yr = a.y_raw + (size_t)mr * N + n0 + 4 * hh;
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
+                                 acc[f][t][4 * j + 3]};
+              *reinterpret_cast<floatx4*>(yr + feat(32 * f + 8 * j)) = w;
+            }
+        }
+        int rb, rtok;
+        locate(l32, rb, rtok);
+        const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * 128;
+        float inv = 1.0f;
+        if (do_norm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
+          ss = sum_xor32(ss);
+          float* slot = xss + (t & 1) * 256;
+          slot[wave * 64 + lane] = ss;
+          wait_lds();
+          __builtin_amdgcn_s_barrier();
+          ss += slot[(wave ^ 1) * 64 + lane];
+          inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 256.0f) + a.eps);
+        }
+        auto put4 = [&](int fl, const float (&y)[4]) {
+          u32x2 o;
+          o.x = pack_bf16x2(y[0], y[1]);
+          o.y = pack_bf16x2(y[2], y[3]);
+          put8(l32, fl, o);
+        };
+        if (kind == 2) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y[4] = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
+                                  acc[f][t][4 * j + 3]};
+              put4(32 * f + 8 * j + 4 * hh, y);
+            }
+        } else {
+          // block f (head features 64 wn + i, i < 64) with block f + 2 (the
+          // same + 128); rotary frequency 64 wn + i
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i0 = 32 * f + 8 * j + 4 * hh;
+              const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + 64 * wn + i0);
+              const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + 64 * wn + i0 + 2);
+              const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
+              const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+              const u32x2 w1 = wpk[f][j], w2 = wpk[f + 2][j];
+              const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
+              const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
+              float y1[4], y2[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x1 = acc[f][t][4 * j + e] * inv * g1[e];
+                const float x2 = acc[f + 2][t][4 * j + e] * inv * g2[e];
+                y1[e] = x1 * cc[e] - x2 * sn[e];
+                y2[e] = x2 * cc[e] + x1 * sn[e];
+              }
+              put4(i0, y1);
+              put4(i0 + 64, y2);
+            }
+        }
+        int sp0 = 0, sp1 = 0;
+        if (kind != 0 && a.start_pos && long_seq) {
+          sp0 = a.start_pos[b0];
+          if ((b0 + 1) * L < M) sp1 = a.start_pos[b0 + 1];
+        }
+        // chunk l % 16 of row 4 i + l / 16: the wave's features 8 c .. 8 c + 7
+        const int c = lane & 15;
+        const int fo = feat(8 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const int m = mb + row;
+          const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
+          if (m >= M) continue;
+          int b, tok;
+          locate(row, b, tok);
+          bf16* dst;
+          if (kind == 0) {
+            dst = a.q + (((size_t)b * Hq + h) * L + tok) * 256;
+          } else {
+            const int base = !a.start_pos ? 0 : long_seq ? (b == b0 ? sp0 : sp1) : a.start_pos[b];
+            const int pos = base + tok;
+            if (pos < 0 || pos >= a.cap) continue;
+            dst = (kind == 1 ? a.k_cache : a.v_cache) + (((size_t)b * Hkv + h) * a.cap + pos) * 256;
+          }
+          st16(dst + fo, v);
         }
       }
     } else if (nw < N) {  // wave-uniform
@@ -1069,12 +1394,33 @@ bool k_aligned(const GemmArgs& a) {
 
 }  // namespace
 
+template <int EPI>
+void launch_qkv(const GemmArgs& args, int grid, hipStream_t stream) {
+  if (k_aligned(args))
+    gemm_bf16_kernel<256, 256, EPI, true><<<grid, kThreads, 0, stream>>>(args);
+  else
+    gemm_bf16_kernel<256, 256, EPI, false><<<grid, kThreads, 0, stream>>>(args);
+}
+
 hipError_t launch_gemm_qkv_bf16(const GemmArgs& args, hipStream_t stream) {
   const int grid = gemm_workgroups(args.N, args.M, args.K);
-  if (k_aligned(args))
-    gemm_bf16_kernel<256, 256, kEpiQKV, true><<<grid, kThreads, 0, stream>>>(args);
-  else
-    gemm_bf16_kernel<256, 256, kEpiQKV, false><<<grid, kThreads, 0, stream>>>(args);
+  switch (args.hd) {
+    case 0:
+    case 128:
+      if (args.rot != 128 && args.rot != 64) return hipErrorInvalidValue;
+      launch_qkv<kEpiQKV>(args, grid, stream);
+      break;
+    case 64:
+      if (args.rot != 64 && args.rot != 32) return hipErrorInvalidValue;
+      launch_qkv<kEpiQKV64>(args, grid, stream);
+      break;
+    case 256:
+      if (args.rot != 256) return hipErrorInvalidValue;
+      launch_qkv<kEpiQKV256>(args, grid, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

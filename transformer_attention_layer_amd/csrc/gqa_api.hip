@@ -139,7 +139,9 @@ gqa_status resolve(const gqa_config* in, gqa_config* out, Shape* sh) {
     sh->bf16 = c.dtype == GQA_BF16;
     sh->mfma = sh->bf16 && (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256);
     sh->rot = c.rotary_dim;
-    sh->fused = sh->bf16 && c.head_dim == 128 && (c.rotary_dim == 128 || c.rotary_dim == 64);
+    sh->fused = sh->bf16 && ((c.head_dim == 128 && (c.rotary_dim == 128 || c.rotary_dim == 64)) ||
+                             (c.head_dim == 64 && (c.rotary_dim == 64 || c.rotary_dim == 32)) ||
+                             (c.head_dim == 256 && c.rotary_dim == 256));
     sh->out_f32 = c.out_f32 || c.dtype == GQA_F32;
     sh->o_split = c.o_split && c.dtype == GQA_BF16;
     sh->o_f16 = c.o_fp16 && c.dtype == GQA_BF16;
@@ -319,6 +321,7 @@ gqa_status run_qkv(const gqa_config& c, const Shape& s, int batch, int q_len, co
     g.cap = cap;
     g.qk_norm = c.qk_norm;
     g.rot = s.rot;
+    g.hd = s.d;
     g.eps = c.rms_eps;
     g.y_raw = y_raw;
     return check_launch(gqa::launch_gemm_qkv_bf16(g, st), "qkv projection");

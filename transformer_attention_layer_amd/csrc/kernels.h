@@ -8,7 +8,10 @@
 
 namespace gqa {
 
-enum { kEpiPlain = 0, kEpiQKV = 1, kEpiPlainF32 = 2 };  // GEMM epilogue kinds
+// GEMM epilogue kinds: plain (bf16 or fp32 out), and the QKV projection's
+// norm + RoPE + head-major scatter for head_dim 128, 64 and 256
+enum { kEpiPlain = 0, kEpiQKV = 1, kEpiPlainF32 = 2, kEpiQKV64 = 3, kEpiQKV256 = 4 };
+constexpr bool is_qkv_epi(int e) { return e == kEpiQKV || e == kEpiQKV64 || e == kEpiQKV256; }
 
 // C^T[n, m] = sum_k W[n, k] X[m, k]  (bf16 in, fp32 accumulate)
 struct GemmArgs {
@@ -33,7 +36,8 @@ struct GemmArgs {
   const float2* rope;     // [rows, rot / 2] (cos, sin); rows = T if start_pos else L
   const int* start_pos;   // [B] or null
   int L, Hq, Hkv, cap, qk_norm;
-  int rot;                // rotary width: 128 (full) or 64 (first half of each head)
+  int rot;                // rotary width: head_dim 128: 128 or 64; 64: 64 or 32; 256: 256
+  int hd;                 // head_dim of the QKV epilogue: 128 (0 counts as 128), 64 or 256
   float eps;
   float* y_raw;           // optional: [M, N] fp32 projection before norm and RoPE
   // few-token GEMM only: K split over ksplit workgroups (<= 1: none), whose
