@@ -303,34 +303,38 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  u32x4 fa[2][FB], fb[2][TB];
+  u32x4 fa[4][FB], fb[4][TB];
   {
     const u32x4* sw = wring(0);
     const u32x4* sx = xring(0);
 #pragma unroll
-    for (int f = 0; f < FB; ++f) fa[0][f] = sw[offa(0, f)];
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-    for (int t = 0; t < TB; ++t) fb[0][t] = sx[offb(0, t)];
+      for (int f = 0; f < FB; ++f) fa[u][f] = sw[offa(u, f)];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) fb[u][t] = sx[offb(u, t)];
+    }
   }
 
   // One K stage (four 16-wide substeps) per trip; g is the stage's number
   // in this workgroup's sequence and kt its index in the current tile.
   // Each substep issues its 16 MFMAs interleaved with the 8 LDS reads of
-  // the next substep's fragments (first half).  The loads of stage g + 2
-  // go to the slots of stages g - 1 (W) and g (X): W's, free since the
-  // previous trip's barrier, in the second halves of the first two
-  // substeps (one load per two MFMAs), X's in the last substep.  Before the
-  // last substep every wave waits for stage g + 1 (only the W half of
-  // stage g + 2 may still be in flight) and meets the others at a barrier:
-  // stage g + 1 is then visible, and every wave's reads of stage g are done
-  // (its last substep's fragments were read during the third), so the last
-  // substep reloads stage g's X slot while it reads the first fragments of
-  // stage g + 1.  Stage g + 2 is stage kt + 2 of this tile or, past its
-  // end, a stage of the next one.  A tile's last trip (NEXT false) loads
-  // W of stage g + 2 (the next tile's stage 1) but no X, reads no
-  // fragments in its last substep and has no barrier there: X of the next
-  // tile's stage 1 is loaded, and the next tile's first fragments are read,
-  // after the epilogue.
+  // the fragments of the substep after next (first half), into one of four
+  // register sets, so a read has a whole substep to return.  The loads of
+  // stage g + 2 go to the slots of stages g - 1 (W) and g (X): W's, free
+  // since the previous trip's barrier, in the second halves of the first
+  // two substeps (one load per two MFMAs), X's in the second halves of the
+  // last two.  Before the third substep every wave waits for stage g + 1
+  // (only the W half of stage g + 2 may still be in flight) and meets the
+  // others at a barrier: stage g + 1 is then visible, and every wave's
+  // reads of stage g are done (the last two substeps' fragments were read
+  // during the first two), so the last two substeps reload stage g's X
+  // slot while they read the first fragments of stage g + 1.  Stage g + 2
+  // is stage kt + 2 of this tile or, past its end, a stage of the next
+  // one.  A tile's last trip (NEXT false) loads W of stage g + 2 (the next
+  // tile's stage 1) but no X, reads no fragments in its last two substeps
+  // and has no barrier: X of the next tile's stage 1 is loaded, and the
+  // next tile's first fragments are read, after the epilogue.
   floatx16 acc[FB][TB];
   unsigned g = 0;  // unsigned: the X slot g % 2 is a mask
   // A trip loads stage kt + kofs of tile rl (kofs = 2 with this tile,
@@ -344,18 +348,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     const StageLoad ld = stage_load(rl, kt + kofs, w2, g % kXSlots);
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      if (sub == 3) {
+      if (sub == 2) {
         if constexpr (NEXT) {
           wait_vmem<kLw, true>();
           __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool reads = sub < 3 || NEXT;
-      const u32x4* rw = sub < 3 ? sw : sw1;
-      const u32x4* rx = sub < 3 ? sx : sx1;
-      const int ns = (sub + 1) & 3;  // the substep whose fragments are read
-      const int cb = sub & 1, nb = cb ^ 1;
+      const bool reads = sub < 2 || NEXT;
+      const u32x4* rw = sub < 2 ? sw : sw1;
+      const u32x4* rx = sub < 2 ? sx : sx1;
+      const int ns = (sub + 2) & 3;  // the substep whose fragments are read
+      const int cb = sub, nb = ns;
 #pragma unroll
       for (int i = 0; i < FB * TB; ++i) {
         const int f = i / TB, t = i % TB;
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         }
         if (sub < 2 && i >= 8 && (i & 1) == 0) issue(ld, 4 * sub + (i - 8) / 2, 0);
         if constexpr (NEXT) {
-          if (sub == 3 && i >= 8) issue(ld, i - 8, 1);
+          if (sub >= 2 && i >= 8 && (i & 1) == 0) issue(ld, 4 * (sub - 2) + (i - 8) / 2, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1006,9 +1010,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     const u32x4* sw = wring(g % kWSlots);
     const u32x4* sx = xring(g % kXSlots);
 #pragma unroll
-    for (int f = 0; f < FB; ++f) fa[0][f] = sw[offa(0, f)];
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-    for (int t = 0; t < TB; ++t) fb[0][t] = sx[offb(0, t)];
+      for (int f = 0; f < FB; ++f) fa[u][f] = sw[offa(u, f)];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) fb[u][t] = sx[offb(u, t)];
+    }
   }
 }
 
