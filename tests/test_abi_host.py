@@ -306,7 +306,8 @@ def test_backward_workspace_covers_its_buffers():
 
 def test_o_fp16_flag_and_workspace():
     """o_fp16 takes 0 or 1, and the layer workspace grows by W_o as fp16
-    (hidden x Hq*d x 2 bytes, 256-byte aligned)."""
+    (hidden x Hq*d x 2 bytes, 256-byte aligned), except for few tokens,
+    whose o_proj rounds W_o inside the product."""
     _lib_or_skip()
     cc = cfg().c()
     cc.o_fp16 = 2
@@ -317,3 +318,6 @@ def test_o_fp16_flag_and_workspace():
     a = T.gqa_workspace_bytes(cfg(), 2, 300, 300, T.WS_LAYER)
     b = T.gqa_workspace_bytes(cfg(o_fp16=True), 2, 300, 300, T.WS_LAYER)
     assert b - a == 1024 * 16 * 128 * 2
+    a = T.gqa_workspace_bytes(cfg(), 64, 1, 300, T.WS_LAYER)
+    b = T.gqa_workspace_bytes(cfg(o_fp16=True), 64, 1, 300, T.WS_LAYER)
+    assert b == a

@@ -261,16 +261,22 @@ size_t ws_attn(const Shape& s, int batch, int q_len, int cap) {
   return align_up(parts * s.d * sizeof(float)) + align_up(parts * 2 * sizeof(float));
 }
 
+// o_proj of an fp16-carried attention output rounds W_o to fp16 inside the
+// product for few tokens; otherwise it reads a converted copy.
+bool oproj_rounds_w(const Shape& s, long long tokens) {
+  return s.o_f16 && use_skinny(s, tokens) && gqa::skinny_lds_ok(s.Hq * s.d, 0);
+}
+
 // W_o converted to fp16 for an fp16-carried attention output
-size_t wo16_bytes(const Shape& s) {
-  return s.o_f16 ? align_up((size_t)s.H * s.Hq * s.d * 2) : 0;
+size_t wo16_bytes(const Shape& s, long long tokens) {
+  return s.o_f16 && !oproj_rounds_w(s, tokens) ? align_up((size_t)s.H * s.Hq * s.d * 2) : 0;
 }
 
 size_t ws_layer(const Shape& s, int batch, int q_len, int cap) {
   const size_t T = (size_t)batch * q_len;
   return ws_qkv(s, batch, q_len) + align_up(T * s.Hq * s.d * esize(s)) /* q */ +
          align_up(T * s.Hq * s.d * esize(s) * (s.o_split ? 2 : 1)) /* attention output */ +
-         ws_attn(s, batch, q_len, cap) + wo16_bytes(s);
+         ws_attn(s, batch, q_len, cap) + wo16_bytes(s, (long long)T);
 }
 
 gqa_status check_launch(hipError_t e, const char* what) {
@@ -856,7 +862,7 @@ gqa_status run_layer(const gqa_config& c, const Shape& s, int batch, int q_len, 
   w += ws_attn(s, batch, q_len, kv_capacity);
   // o as fp16: W_o as fp16 too, converted once per call, or (few tokens)
   // rounded inside the product
-  const bool w_cvt = s.o_f16 && use_skinny(s, T) && gqa::skinny_lds_ok(s.Hq * s.d, 0);
+  const bool w_cvt = oproj_rounds_w(s, (long long)T);
   void* wo16 = s.o_f16 && !w_cvt ? w : nullptr;
   r = run_qkv(c, s, batch, q_len, x, w_qkv, q_norm_w, k_norm_w, cache_len, qbuf, k_cache, v_cache,
               kv_capacity, ws_q, st);
