@@ -204,13 +204,18 @@ __device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)
   }
 }
 
-// Prefill tile sizes: 64 keys (32 for head_dim 256, whose fragments would
-// not fit the registers of two waves per SIMD otherwise).
+// Prefill tile sizes and occupancy: head_dim 128 takes 32-key tiles, whose
+// registers (168) and LDS (32 KB) let three workgroups share a CU, so three
+// waves per SIMD hide each other's softmax and LDS latency (2% faster than
+// 64-key tiles at two waves per SIMD, which in turn beat 32-key tiles at
+// two); head_dim 64 keeps 64-key tiles (three waves per SIMD already);
+// head_dim 256 takes 32 keys at one wave per SIMD (its fragments would not
+// fit otherwise).
 template <int KD>
 struct PrefillCfg {
-  static constexpr int TK = KD == 256 ? 32 : 64;
+  static constexpr int TK = KD == 64 ? 64 : 32;
   static constexpr int NT = 256;
-  static constexpr int MIN_BLOCKS = KD == 256 ? 1 : 2;
+  static constexpr int MIN_BLOCKS = KD == 256 ? 1 : KD == 128 ? 3 : 2;
 };
 
 template <int KD>
