@@ -109,6 +109,18 @@ GQA_DEV floatx16 mfma32x32x16_f16(u32x4 a, u32x4 b, floatx16 c) {
                                                 __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
 }
 
+// D = A(16x32) * B(32x16) + C on the bf16 matrix cores (gfx950).  Lane l
+// supplies row l%16 of A and column l%16 of B, eight K-values each (the
+// same eight for A and B: K-group l/16); lane l, register r of D is row
+// 4*(l/16) + r, column l%16.
+GQA_DEV floatx4 mfma16x16x32(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+GQA_DEV floatx4 mfma16x16x32_f16(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+
 // Round-to-nearest-even float -> fp16 bits (two values packed, low first);
 // one v_cvt_pk_f16_f32.  Magnitudes past 65504 become infinities.
 GQA_DEV unsigned int pack_f16x2(float lo, float hi) {
@@ -126,6 +138,14 @@ GQA_DEV float max_xor32(float v) {
   const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
                                                   __builtin_bit_cast(unsigned, v), false, false);
   return fmaxf(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
+}
+// The same over lanes l and l ^ 16 with v_permlane16_swap, which swaps the
+// odd 16-lane rows of its first operand with the even rows of its second:
+// swap(v, v) returns rows (0, 0, 2, 2) of v and rows (1, 1, 3, 3).
+GQA_DEV float sum_xor16(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_bit_cast(float, (unsigned)q[0]) + __builtin_bit_cast(float, (unsigned)q[1]);
 }
 GQA_DEV float sum_xor32(float v) {
   const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),

@@ -8,10 +8,14 @@
 //
 // Both compute a tile of C^T: rows are output features n (rows of the weight
 // W [N, K]), columns are tokens m (rows of the activation X [M, K]); both
-// operands are K-contiguous.  With this orientation one lane of the MFMA
-// accumulator holds, for one token, 64 of the 128 features of a head and the
-// other 64 sit in lane l^32: the per-head RMS needs one cross-lane exchange,
-// and the RoPE partners (feature i and i + 64) sit in the same lane.
+// operands are K-contiguous.  The products run as 16x16x32 MFMAs (the
+// 32x32x16 form does the same work per cycle but draws more power, and
+// under the board's power limit the clock drops: about 4% slower here).
+// With this orientation one lane of the accumulators holds, for one token,
+// 32 of the 128 features of a head (4 consecutive features of each 16-row
+// block) and the other 96 sit in lanes l ^ 16, l ^ 32 and l ^ 48: the
+// per-head RMS needs two cross-lane exchanges, and the RoPE partners
+// (feature i and i + 64) sit in the same lane.
 #include <type_traits>
 
 #include "common.h"
@@ -183,11 +187,11 @@ template <int BN, int BM, int EPI, bool KALIGN, bool F16 = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(!F16 || !is_qkv_epi(EPI), "the QKV epilogues take bf16 operands");
   constexpr int WN = BN / 2, WM = BM / 2;
-  constexpr int FB = WN / 32, TB = WM / 32;
+  constexpr int FB = WN / 16, TB = WM / 16;
   static_assert(WN == 128, "the epilogues stage 128 features per wave");
   static_assert(kBK == 64 && kStages == 2 && kWSlots == 3 && kXSlots == 2,
-                "the pipeline below is written for 4 substeps, W 3 and X 2 stages deep");
-  static_assert(FB == 4 && TB == 4, "16 MFMAs per substep");
+                "the pipeline below is written for 2 steps, W 3 and X 2 stages deep");
+  static_assert(FB == 8 && TB == 8, "64 MFMAs per step");
   // One LDS array: the W ring, then the X ring.  A second __shared__ array
   // would give the compiler alias scopes under which it waits for every
   // LDS DMA in flight before each fragment read; the waits below already
@@ -202,8 +206,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const int l32 = lane & 31, hh = lane >> 5;
-
+  const int l16 = lane & 15, q4 = lane >> 4;
   const int N = a.N, M = a.M, K = a.K;
   const int batch = is_qkv_epi(EPI) ? 1 : max(a.batch, 1);
   const TileOrder order(N, M, BN, BM, batch);
@@ -277,16 +280,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   };
 
   // LDS offsets (16-byte slots) of this lane's fragments: row-major
-  // fragments of W (features) and X (tokens), chunk = 2 * substep + hh.
-  // Every fragment row is l32 plus a multiple of 16, so the swizzle term is
-  // l32's and one base per substep serves all fragments.
-  static_assert(WN % 16 == 0 && WM % 16 == 0 && BN % 16 == 0, "fragment rows keep l32's swizzle");
-  int cs[4];
+  // fragments of W (features) and X (tokens), row l16 of a 16-row block,
+  // chunk 4 s + q4 for the K step s (0, 1) of a stage.  Every fragment row
+  // is l16 plus a multiple of 16, so the swizzle term is l16's and one base
+  // per step serves all fragments.
+  static_assert(WN % 16 == 0 && WM % 16 == 0 && BN % 16 == 0, "fragment rows keep l16's swizzle");
+  int cs[2];
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub) cs[sub] = swz(l32, 2 * sub + hh);
+  for (int s = 0; s < 2; ++s) cs[s] = swz(l16, 4 * s + q4);
   // offsets within a W slot and within an X slot
-  auto offa = [&](int sub, int f) { return cs[sub] + (wn * WN + 32 * f) * kCPR; };
-  auto offb = [&](int sub, int t) { return cs[sub] + (wm * WM + 32 * t) * kCPR; };
+  auto offa = [&](int s, int f) { return cs[s] + (wn * WN + 16 * f) * kCPR; };
+  auto offb = [&](int s, int t) { return cs[s] + (wm * WM + 16 * t) * kCPR; };
 
   // Prologue: the first tile's stages 0 and 1 (or, for a one-stage K,
   // whatever follows stage 0) in flight, stage 0 landed and visible.
@@ -303,39 +307,37 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  u32x4 fa[4][FB], fb[4][TB];
+  // fragments of K step 0 of the first stage
+  u32x4 fa[2][FB], fb[2][TB];
   {
     const u32x4* sw = wring(0);
     const u32x4* sx = xring(0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int f = 0; f < FB; ++f) fa[0][f] = sw[offa(0, f)];
 #pragma unroll
-      for (int f = 0; f < FB; ++f) fa[u][f] = sw[offa(u, f)];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) fb[u][t] = sx[offb(u, t)];
-    }
+    for (int t = 0; t < TB; ++t) fb[0][t] = sx[offb(0, t)];
   }
 
-  // One K stage (four 16-wide substeps) per trip; g is the stage's number
-  // in this workgroup's sequence and kt its index in the current tile.
-  // Each substep issues its 16 MFMAs interleaved with the 8 LDS reads of
-  // the fragments of the substep after next (first half), into one of four
-  // register sets, so a read has a whole substep to return.  The loads of
-  // stage g + 2 go to the slots of stages g - 1 (W) and g (X): W's, free
-  // since the previous trip's barrier, in the second halves of the first
-  // two substeps (one load per two MFMAs), X's in the second halves of the
-  // last two.  Before the third substep every wave waits for stage g + 1
-  // (only the W half of stage g + 2 may still be in flight) and meets the
-  // others at a barrier: stage g + 1 is then visible, and every wave's
-  // reads of stage g are done (the last two substeps' fragments were read
-  // during the first two), so the last two substeps reload stage g's X
-  // slot while they read the first fragments of stage g + 1.  Stage g + 2
-  // is stage kt + 2 of this tile or, past its end, a stage of the next
-  // one.  A tile's last trip (NEXT false) loads W of stage g + 2 (the next
-  // tile's stage 1) but no X, reads no fragments in its last two substeps
-  // and has no barrier: X of the next tile's stage 1 is loaded, and the
-  // next tile's first fragments are read, after the epilogue.
-  floatx16 acc[FB][TB];
+  // One K stage (two 32-wide steps of 64 MFMAs) per trip; g is the stage's
+  // number in this workgroup's sequence and kt its index in the current
+  // tile.  The fragments of each step are read during the step before,
+  // into the other of two register sets, one read per two MFMAs in the
+  // first half of the step, so a read has at least half a step to return.
+  // The loads of stage g + 2 go to the slots of stages g - 1 (W) and g (X):
+  // W's, free since the previous trip's barrier, one per four MFMAs in the
+  // second half of the first step, X's likewise in the second step.  Before
+  // the second step every wave waits for stage g + 1 (only the W half of
+  // stage g + 2 may still be in flight) and meets the others at a barrier:
+  // stage g + 1 is then visible, and every wave's reads of stage g are done
+  // (the second step's fragments were read during the first), so the
+  // second step reloads stage g's X slot while it reads the first fragments
+  // of stage g + 1.  Stage g + 2 is stage kt + 2 of this tile or, past its
+  // end, a stage of the next one.  A tile's last trip (NEXT false) loads W
+  // of stage g + 2 (the next tile's stage 1) but no X, reads no fragments
+  // in its second step and has no barrier: X of the next tile's stage 1 is
+  // loaded, and the next tile's first fragments are read, after the
+  // epilogue.
+  floatx4 acc[FB][TB];
   unsigned g = 0;  // unsigned: the X slot g % 2 is a mask
   // A trip loads stage kt + kofs of tile rl (kofs = 2 with this tile,
   // 2 - nk with the next one).
@@ -347,33 +349,34 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     const u32x4* sx1 = xring((g + 1) % kXSlots);
     const StageLoad ld = stage_load(rl, kt + kofs, w2, g % kXSlots);
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      if (sub == 2) {
+    for (int step = 0; step < 2; ++step) {
+      if (step == 1) {
         if constexpr (NEXT) {
           wait_vmem<kLw, true>();
           __builtin_amdgcn_s_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool reads = sub < 2 || NEXT;
-      const u32x4* rw = sub < 2 ? sw : sw1;
-      const u32x4* rx = sub < 2 ? sx : sx1;
-      const int ns = (sub + 2) & 3;  // the substep whose fragments are read
-      const int cb = sub, nb = ns;
+      const bool reads = step == 0 || NEXT;
+      const u32x4* rw = step == 0 ? sw : sw1;
+      const u32x4* rx = step == 0 ? sx : sx1;
+      const int ns = step ^ 1;  // the K step whose fragments are read
+      const int cb = step, nb = ns;
 #pragma unroll
       for (int i = 0; i < FB * TB; ++i) {
         const int f = i / TB, t = i % TB;
-        acc[f][t] = F16 ? mfma32x32x16_f16(fa[cb][f], fb[cb][t], acc[f][t])
-                        : mfma32x32x16(fa[cb][f], fb[cb][t], acc[f][t]);
-        if (i < 8 && reads) {
-          // next substep's fragments in the order its MFMAs use them
-          if (i == 0) fa[nb][0] = rw[offa(ns, 0)];
-          else if (i <= 4) fb[nb][i - 1] = rx[offb(ns, i - 1)];
-          else fa[nb][i - 4] = rw[offa(ns, i - 4)];
+        acc[f][t] = F16 ? mfma16x16x32_f16(fa[cb][f], fb[cb][t], acc[f][t])
+                        : mfma16x16x32(fa[cb][f], fb[cb][t], acc[f][t]);
+        if (i < 32 && (i & 1) == 0 && reads) {
+          // next step's fragments in the order its MFMAs use them
+          const int r = i / 2;
+          if (r == 0) fa[nb][0] = rw[offa(ns, 0)];
+          else if (r <= TB) fb[nb][r - 1] = rx[offb(ns, r - 1)];
+          else fa[nb][r - TB] = rw[offa(ns, r - TB)];
         }
-        if (sub < 2 && i >= 8 && (i & 1) == 0) issue(ld, 4 * sub + (i - 8) / 2, 0);
+        if (step == 0 && i >= 32 && (i & 3) == 0) issue(ld, (i - 32) / 4, 0);
         if constexpr (NEXT) {
-          if (sub >= 2 && i >= 8 && (i & 1) == 0) issue(ld, 4 * (sub - 2) + (i - 8) / 2, 1);
+          if (step == 1 && i >= 32 && (i & 3) == 0) issue(ld, (i - 32) / 4, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < TB; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[f][t][r] = 0.f;
+        for (int r = 0; r < 4; ++r) acc[f][t][r] = 0.f;
 
     const int n0 = cur.n0, m0 = cur.m0;
     const int nw = n0 + wn * WN;  // first feature of this wave
@@ -428,18 +431,27 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           if (t >= t0) asm volatile("" : "+a"(acc[f][t]));
     };
 
-    // 32 rows x 16 chunks per wave, in the X slot of the last stage (g - 1)
+    // The output goes out in chunks of 32 tokens, token blocks 2 p and
+    // 2 p + 1: lane l holds rows l16 and 16 + l16 of the chunk, each with
+    // the wave's features 16 f + 4 q4 + (0..3), f = 0..7.  A chunk is staged
+    // as 32 rows x 16 chunks per wave in the X slot of the last stage (g - 1).
     u32x4* const stage = xring((g + 1) % kXSlots) + wave * 32 * 16;
     // lane-derived epilogue addresses are computed here, not kept live
     // (and spilled) across the K loop
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
-    const int l32 = lane & 31, hh = lane >> 5;
+    const int l16 = lane & 15, q4 = lane >> 4;
     u32x2* const stage8 = reinterpret_cast<u32x2*>(stage);
     // 4 features at feat (a multiple of 4) of row `row`; chunk c of row r
     // sits at slot c ^ (r & 15)
     auto put8 = [&](int row, int feat, u32x2 v) {
       stage8[(row * 16 + ((feat >> 3) ^ (row & 15))) * 2 + ((feat >> 2) & 1)] = v;
+    };
+    auto pack4 = [](const floatx4& v) {
+      u32x2 w;
+      w.x = pack_bf16x2(v[0], v[1]);
+      w.y = pack_bf16x2(v[2], v[3]);
+      return w;
     };
     // batch member of this tile: its output block
     const size_t oz = is_qkv_epi(EPI) ? 0 : (size_t)(id / order.per_z) * a.sOut;
@@ -447,40 +459,31 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
         pin_from(t);
-        const int m = m0 + wm * WM + 32 * t + l32;
+        const int m = m0 + wm * WM + 16 * t + l16;
         if (m >= M) continue;
 #pragma unroll
-        for (int f = 0; f < FB; ++f)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = nw + 32 * f + 8 * j + 4 * hh;
-            if (n >= N) continue;
-            floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
-                         acc[f][t][4 * j + 3]};
-            *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + oz + (size_t)m * N + n) = w;
-          }
+        for (int f = 0; f < FB; ++f) {
+          const int n = nw + 16 * f + 4 * q4;
+          if (n >= N) continue;
+          *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + oz + (size_t)m * N + n) = acc[f][t];
+        }
       }
     } else if constexpr (EPI == kEpiPlain) {
-      // per 32-token block: rows of 128 bf16 features per token in LDS,
+      // per 32-token chunk: rows of 128 bf16 features per token in LDS,
       // then stored 16 bytes per lane, 4 whole rows per instruction
 #pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        pin_from(t);
+      for (int p = 0; p < TB / 2; ++p) {
+        pin_from(2 * p);
 #pragma unroll
-        for (int f = 0; f < FB; ++f)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            u32x2 w;
-            w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
-            w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
-            put8(l32, 32 * f + 8 * j + 4 * hh, w);
-          }
+          for (int f = 0; f < FB; ++f) put8(16 * tt + l16, 16 * f + 4 * q4, pack4(acc[f][2 * p + tt]));
         const int c = lane & 15;
         const int n = nw + 8 * c;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int row = 4 * i + (lane >> 4);
-          const int m = m0 + wm * WM + 32 * t + row;
+          const int m = m0 + wm * WM + 32 * p + row;
           const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
           if (m < M && n < N) st16(static_cast<bf16*>(a.out) + oz + (size_t)m * N + n, v);
         }
@@ -488,11 +491,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     } else if constexpr (EPI == kEpiQKV64) {
       // ---- QKV epilogue, head_dim 64: two heads per wave ----
       // As for head_dim 128 (below), with each 64-feature half of the wave
-      // (blocks 0-1 and 2-3) a head of its own: its norm sums the lane's two
-      // blocks, and RoPE pairs block 0 with block 1 (rot 64) or, for rot 32,
-      // the first two 8-feature steps of block 0 with its last two (block 1
-      // passes through).  Past the last head (an odd head count) the second
-      // half is skipped.
+      // (blocks 0-3 and 4-7) a head of its own: its norm sums the lane's four
+      // blocks of the head over the token's four lanes, and RoPE pairs block
+      // f with f + 2 (rot 64) or, for rot 32, block 0 with block 1 (blocks 2
+      // and 3 pass through).  Past the last head (an odd head count) the
+      // second half is skipped.
       if (nw < N) {  // wave-uniform
         const int Hq = a.Hq, Hkv = a.Hkv;
         int kind[2], hid[2];
@@ -505,25 +508,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           else if (head < Hq + Hkv) { kind[hb] = 1; hid[hb] = head - Hq; }
           else { kind[hb] = 2; hid[hb] = head - Hq - Hkv; }
         }
-        // norm weights of this lane's features 32 fl + 8 j + 4 hh + (0..3) of head hb
-        u32x2 wpk[2][2][4];
+        // norm weights of this lane's features 16 (f % 4) + 4 q4 + (0..3) of head f / 4
+        u32x2 wpk[FB];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int fl = 0; fl < 2; ++fl)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
-              const bool dn = live[hb] && kind[hb] != 2 && a.qk_norm;
-              wpk[hb][fl][j] =
-                  dn ? ld8((kind[hb] == 0 ? a.q_norm_w : a.k_norm_w) + 32 * fl + 8 * j + 4 * hh) : one;
-            }
+        for (int f = 0; f < FB; ++f) {
+          const int hb = f >> 2;
+          const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+          const bool dn = live[hb] && kind[hb] != 2 && a.qk_norm;
+          wpk[f] = dn ? ld8((kind[hb] == 0 ? a.q_norm_w : a.k_norm_w) + 16 * (f & 3) + 4 * q4) : one;
+        }
         const int half = a.rot >> 1;
         const int L = a.L;
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-          pin_from(t);
-          const int mb = m0 + wm * WM + 32 * t;
+        for (int p = 0; p < TB / 2; ++p) {
+          pin_from(2 * p);
+          const int mb = m0 + wm * WM + 32 * p;
           const int b0 = mb / L;
           const int tok0 = mb - b0 * L;
           const bool long_seq = L >= 32;
@@ -537,89 +536,76 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
               tok = mb + r - b * L;
             }
           };
-          const int mr = mb + l32;
-          if (a.y_raw && mr < M) {
-            float* yr = a.y_raw + (size_t)mr * N + nw + 4 * hh;
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+          for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * p + tt;
+            const int row = 16 * tt + l16;
+            const int mr = mb + row;
+            if (a.y_raw && mr < M) {
+              float* yr = a.y_raw + (size_t)mr * N + nw + 4 * q4;
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                if (!live[f >> 1]) continue;
-                const floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1],
-                                   acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]};
-                *reinterpret_cast<floatx4*>(yr + 32 * f + 8 * j) = w;
+              for (int f = 0; f < FB; ++f) {
+                if (!live[f >> 2]) continue;
+                *reinterpret_cast<floatx4*>(yr + 16 * f) = acc[f][t];
               }
-          }
-          int rb, rtok;
-          locate(l32, rb, rtok);
-          const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            if (!live[hb]) continue;  // wave-uniform
-            const int f0 = 2 * hb;
-            float inv = 1.0f;
-            if (kind[hb] != 2 && a.qk_norm) {
-              float ss = 0.f;
-#pragma unroll
-              for (int f = f0; f < f0 + 2; ++f)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
-              ss = sum_xor32(ss);
-              inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 64.0f) + a.eps);
             }
-            // x of feature 32 fl + 8 j + 4 hh + e of head hb, normalised
-            auto xn = [&](int fl, int j, int e) {
-              const u32x2 w = wpk[hb][fl][j];
-              const float g = (e & 1) ? hi_bf16(e < 2 ? w.x : w.y) : lo_bf16(e < 2 ? w.x : w.y);
-              return acc[f0 + fl][t][4 * j + e] * inv * g;
-            };
-            auto put4 = [&](int feat, const float (&y)[4]) {
-              u32x2 o;
-              o.x = pack_bf16x2(y[0], y[1]);
-              o.y = pack_bf16x2(y[2], y[3]);
-              put8(l32, 64 * hb + feat, o);
-            };
-            if (kind[hb] == 2) {
+            int rb, rtok;
+            locate(row, rb, rtok);
+            const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
 #pragma unroll
-              for (int fl = 0; fl < 2; ++fl)
+            for (int hb = 0; hb < 2; ++hb) {
+              if (!live[hb]) continue;  // wave-uniform
+              const int f0 = 4 * hb;
+              float inv = 1.0f;
+              if (kind[hb] != 2 && a.qk_norm) {
+                float ss = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const float y[4] = {acc[f0 + fl][t][4 * j + 0], acc[f0 + fl][t][4 * j + 1],
-                                      acc[f0 + fl][t][4 * j + 2], acc[f0 + fl][t][4 * j + 3]};
-                  put4(32 * fl + 8 * j + 4 * hh, y);
-                }
-            } else {
-              // feature i < rot/2 pairs with i + rot/2: (block 0, step j) with
-              // (block 1, step j) for rot 64, with (block 0, step j + 2) for
-              // rot 32 (every index a constant)
-              auto pair = [&](int j, int fl2, int j2) {
-                const int i0 = 8 * j + 4 * hh;
-                const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
-                const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
-                const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
-                const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-                float y1[4], y2[4];
+                for (int f = f0; f < f0 + 4; ++f)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float x1 = xn(0, j, e), x2 = xn(fl2, j2, e);
-                  y1[e] = x1 * cc[e] - x2 * sn[e];
-                  y2[e] = x2 * cc[e] + x1 * sn[e];
-                }
-                put4(i0, y1);
-                put4(i0 + 32 * fl2 + 8 * (j2 - j), y2);
-              };
-              if (half == 32) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pair(j, 1, j);
-              } else {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) pair(j, 0, j + 2);
+                  for (int r = 0; r < 4; ++r) ss += acc[f][t][r] * acc[f][t][r];
+                ss = sum_xor32(sum_xor16(ss));
+                inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 64.0f) + a.eps);
               }
-              if (half == 16) {  // block 1 is past the rotary width: norm only
+              // x of feature 16 fl + 4 q4 + e of head hb, normalised
+              auto xn = [&](int fl, int e) {
+                const u32x2 w = wpk[f0 + fl];
+                const float gg = (e & 1) ? hi_bf16(e < 2 ? w.x : w.y) : lo_bf16(e < 2 ? w.x : w.y);
+                return acc[f0 + fl][t][e] * inv * gg;
+              };
+              auto put4 = [&](int feat, const floatx4& y) { put8(row, 64 * hb + feat, pack4(y)); };
+              if (kind[hb] == 2) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const float y[4] = {xn(1, j, 0), xn(1, j, 1), xn(1, j, 2), xn(1, j, 3)};
-                  put4(32 + 8 * j + 4 * hh, y);
+                for (int fl = 0; fl < 4; ++fl) put4(16 * fl + 4 * q4, acc[f0 + fl][t]);
+              } else {
+                // feature i < rot/2 pairs with i + rot/2: block fl with fl + 2
+                // for rot 64, block 0 with block 1 for rot 32 (every index a
+                // constant)
+                auto pair = [&](int fl, int fl2) {
+                  const int i0 = 16 * fl + 4 * q4;
+                  const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + i0);
+                  const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
+                  const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
+                  const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+                  floatx4 y1, y2;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const float x1 = xn(fl, e), x2 = xn(fl2, e);
+                    y1[e] = x1 * cc[e] - x2 * sn[e];
+                    y2[e] = x2 * cc[e] + x1 * sn[e];
+                  }
+                  put4(i0, y1);
+                  put4(16 * fl2 + 4 * q4, y2);
+                };
+                if (half == 32) {
+                  pair(0, 2);
+                  pair(1, 3);
+                } else {  // blocks 2 and 3 are past the rotary width: norm only
+                  pair(0, 1);
+#pragma unroll
+                  for (int fl = 2; fl < 4; ++fl) {
+                    const floatx4 y = {xn(fl, 0), xn(fl, 1), xn(fl, 2), xn(fl, 3)};
+                    put4(16 * fl + 4 * q4, y);
+                  }
                 }
               }
             }
@@ -660,15 +646,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     } else if constexpr (EPI == kEpiQKV256) {
       // ---- QKV epilogue, head_dim 256 (full rotary): a tile is one head ----
       // W's rows were loaded with 64-row blocks 1 and 2 swapped, so wave wn
-      // holds features 64 wn + (0..63) in blocks 0-1 and 128 + 64 wn + (0..63)
-      // in blocks 2-3: every RoPE pair (i, i + 128) sits in one lane, block f
-      // with f + 2, as for head_dim 128.  Only the norm's sum of squares
+      // holds features 64 wn + (0..63) in blocks 0-3 and 128 + 64 wn + (0..63)
+      // in blocks 4-7: every RoPE pair (i, i + 128) sits in one lane, block f
+      // with f + 4, as for head_dim 128.  Only the norm's sum of squares
       // spans the two waves of a pair (wn = 0, 1 over the same tokens): per
-      // 32-token block each wave posts its partial sum in LDS (two slots,
-      // alternating by block) and reads its partner's after one barrier.
-      // The slots are in the W ring slot of the tile's last stage, which no
-      // load writes before the next tile's first trip; the head is the same
-      // for the whole workgroup, so every wave runs the same barriers.
+      // 32-token chunk each wave posts its two partial sums per lane in LDS
+      // (two slots, alternating by chunk) and reads its partner's after one
+      // barrier.  The slots are in the W ring slot of the tile's last stage,
+      // which no load writes before the next tile's first trip; the head is
+      // the same for the whole workgroup, so every wave runs the same
+      // barriers.
       float* const xss = reinterpret_cast<float*>(wring((g + 2) % kWSlots));
       const int Hq = a.Hq, Hkv = a.Hkv;
       const int head = n0 >> 8;
@@ -679,20 +666,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       const bool do_norm = kind != 2 && a.qk_norm;
       // head feature of this wave's feature fl (0..127)
       auto feat = [&](int fl) { return fl < 64 ? 64 * wn + fl : 64 + 64 * wn + fl; };
-      u32x2 wpk[4][4];
+      u32x2 wpk[FB];
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
-          wpk[f][j] = do_norm ? ld8((kind == 0 ? a.q_norm_w : a.k_norm_w) + feat(32 * f + 8 * j + 4 * hh))
-                              : one;
-        }
+      for (int f = 0; f < FB; ++f) {
+        const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+        wpk[f] = do_norm ? ld8((kind == 0 ? a.q_norm_w : a.k_norm_w) + feat(16 * f + 4 * q4)) : one;
+      }
       const int L = a.L;
 #pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        pin_from(t);
-        const int mb = m0 + wm * WM + 32 * t;
+      for (int p = 0; p < TB / 2; ++p) {
+        pin_from(2 * p);
+        const int mb = m0 + wm * WM + 32 * p;
         const int b0 = mb / L;
         const int tok0 = mb - b0 * L;
         const bool long_seq = L >= 32;
@@ -706,76 +690,75 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             tok = mb + r - b * L;
           }
         };
-        const int mr = mb + l32;
-        if (a.y_raw && mr < M) {
-          float* yr = a.y_raw + (size_t)mr * N + n0 + 4 * hh;
+        const float2* cs[2];
+        float ss[2];
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = 2 * p + tt;
+          const int row = 16 * tt + l16;
+          const int mr = mb + row;
+          if (a.y_raw && mr < M) {
+            float* yr = a.y_raw + (size_t)mr * N + n0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
-                                 acc[f][t][4 * j + 3]};
-              *reinterpret_cast<floatx4*>(yr + feat(32 * f + 8 * j)) = w;
-            }
+            for (int f = 0; f < FB; ++f)
+              *reinterpret_cast<floatx4*>(yr + feat(16 * f + 4 * q4)) = acc[f][t];
+          }
+          int rb, rtok;
+          locate(row, rb, rtok);
+          cs[tt] = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * 128;
+          ss[tt] = 0.f;
+          if (do_norm) {
+#pragma unroll
+            for (int f = 0; f < FB; ++f)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) ss[tt] += acc[f][t][r] * acc[f][t][r];
+            ss[tt] = sum_xor32(sum_xor16(ss[tt]));
+          }
         }
-        int rb, rtok;
-        locate(l32, rb, rtok);
-        const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * 128;
-        float inv = 1.0f;
+        float inv[2] = {1.0f, 1.0f};
         if (do_norm) {
-          float ss = 0.f;
+          float* slot = xss + (p & 1) * 512;
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
-          ss = sum_xor32(ss);
-          float* slot = xss + (t & 1) * 256;
-          slot[wave * 64 + lane] = ss;
+          for (int tt = 0; tt < 2; ++tt) slot[(wave * 64 + lane) * 2 + tt] = ss[tt];
           wait_lds();
           __builtin_amdgcn_s_barrier();
-          ss += slot[(wave ^ 1) * 64 + lane];
-          inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 256.0f) + a.eps);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const float s = ss[tt] + slot[((wave ^ 1) * 64 + lane) * 2 + tt];
+            inv[tt] = 1.0f / __builtin_sqrtf(s * (1.0f / 256.0f) + a.eps);
+          }
         }
-        auto put4 = [&](int fl, const float (&y)[4]) {
-          u32x2 o;
-          o.x = pack_bf16x2(y[0], y[1]);
-          o.y = pack_bf16x2(y[2], y[3]);
-          put8(l32, fl, o);
-        };
         if (kind == 2) {
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float y[4] = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
-                                  acc[f][t][4 * j + 3]};
-              put4(32 * f + 8 * j + 4 * hh, y);
-            }
+            for (int f = 0; f < FB; ++f) put8(16 * tt + l16, 16 * f + 4 * q4, pack4(acc[f][2 * p + tt]));
         } else {
-          // block f (head features 64 wn + i, i < 64) with block f + 2 (the
+          // block f (head features 64 wn + i, i < 64) with block f + 4 (the
           // same + 128); rotary frequency 64 wn + i
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i0 = 32 * f + 8 * j + 4 * hh;
-              const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + 64 * wn + i0);
-              const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + 64 * wn + i0 + 2);
+            for (int f = 0; f < 4; ++f) {
+              const int t = 2 * p + tt;
+              const int i0 = 16 * f + 4 * q4;
+              const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs[tt] + 64 * wn + i0);
+              const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs[tt] + 64 * wn + i0 + 2);
               const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
               const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-              const u32x2 w1 = wpk[f][j], w2 = wpk[f + 2][j];
+              const u32x2 w1 = wpk[f], w2 = wpk[f + 4];
               const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
               const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
-              float y1[4], y2[4];
+              floatx4 y1, y2;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float x1 = acc[f][t][4 * j + e] * inv * g1[e];
-                const float x2 = acc[f + 2][t][4 * j + e] * inv * g2[e];
+                const float x1 = acc[f][t][e] * inv[tt] * g1[e];
+                const float x2 = acc[f + 4][t][e] * inv[tt] * g2[e];
                 y1[e] = x1 * cc[e] - x2 * sn[e];
                 y2[e] = x2 * cc[e] + x1 * sn[e];
               }
-              put4(i0, y1);
-              put4(i0 + 64, y2);
+              put8(16 * tt + l16, i0, pack4(y1));
+              put8(16 * tt + l16, i0 + 64, pack4(y2));
             }
         }
         int sp0 = 0, sp1 = 0;
@@ -808,12 +791,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       }
     } else if (nw < N) {  // wave-uniform
       // ---- QKV epilogue: one head of 128 features per wave ----
-      // Per 32-token block the lane's values are normalised and rotated in
-      // registers, written to LDS as rows of 128 bf16 per token and stored
+      // Per 32-token chunk a lane holds two tokens (rows l16 and 16 + l16)
+      // and, of each, the features 16 f + 4 q4 + (0..3), f = 0..7; the
+      // token's other 96 features sit in lanes l16 + 16 q, q != q4.  The
+      // values are normalised (a sum of squares over the lane's 32 values,
+      // then over the four lanes) and rotated in registers (feature i <
+      // rot/2 pairs with i + rot/2: block f with block f + rot/32, in the
+      // same lane), written to LDS as rows of 128 bf16 per token and stored
       // 16 bytes per lane, 4 whole rows per instruction (a head's rows are
-      // contiguous in q and in the caches).  Within a block, a lane handles
-      // four consecutive features i..i+3 together with their RoPE partners
-      // i+rot/2..i+rot/2+3, so only a few values are live at once.
+      // contiguous in q and in the caches).
       const int head = nw >> 7;
       const int Hq = a.Hq, Hkv = a.Hkv;
       int kind;  // 0 = q, 1 = k, 2 = v
@@ -823,25 +809,23 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       else { kind = 2; h = head - Hq - Hkv; }
       const bool do_norm = (kind != 2) && a.qk_norm;
       const bf16* wsrc = kind == 0 ? a.q_norm_w : a.k_norm_w;
-      // norm weights of this lane's features 32f + 8j + 4hh + (0..3), kept packed
-      u32x2 wpk[4][4];
+      // norm weights of this lane's features 16 f + 4 q4 + (0..3), kept packed
+      u32x2 wpk[FB];
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x2 z = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
-          wpk[f][j] = do_norm ? ld8(wsrc + 32 * f + 8 * j + 4 * hh) : z;
-        }
+      for (int f = 0; f < FB; ++f) {
+        const u32x2 one = {0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+        wpk[f] = do_norm ? ld8(wsrc + 16 * f + 4 * q4) : one;
+      }
       const int half = a.rot >> 1;
       const int L = a.L;
 #pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        pin_from(t);
-        // Token rows mb .. mb + 31 of this block: row m is token tok of
-        // sequence b (m = b L + tok).  One division per block (wave-uniform);
+      for (int p = 0; p < TB / 2; ++p) {
+        pin_from(2 * p);
+        // Token rows mb .. mb + 31 of this chunk: row m is token tok of
+        // sequence b (m = b L + tok).  One division per chunk (wave-uniform);
         // a row's (b, tok) follows by carrying over sequence ends, which
         // takes at most one step per row when L >= 32.
-        const int mb = m0 + wm * WM + 32 * t;
+        const int mb = m0 + wm * WM + 32 * p;
         const int b0 = mb / L;
         const int tok0 = mb - b0 * L;
         const bool long_seq = L >= 32;
@@ -855,114 +839,104 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             tok = mb + r - b * L;
           }
         };
-        const int mr = mb + l32;
-        if (a.y_raw && mr < M) {  // a.y_raw is wave-uniform
-          float* yr = a.y_raw + (size_t)mr * N + nw + 4 * hh;
+        // the lane's two rows: raw projection out, RoPE table rows, norm scales
+        const float2* cs[2];
+        float inv[2];
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = 2 * p + tt;
+          const int row = 16 * tt + l16;
+          const int mr = mb + row;
+          if (a.y_raw && mr < M) {  // a.y_raw is wave-uniform
+            float* yr = a.y_raw + (size_t)mr * N + nw + 4 * q4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const floatx4 w = {acc[f][t][4 * j + 0], acc[f][t][4 * j + 1], acc[f][t][4 * j + 2],
-                                 acc[f][t][4 * j + 3]};
-              *reinterpret_cast<floatx4*>(yr + 32 * f + 8 * j) = w;
-            }
-        }
-        int rb, rtok;
-        locate(l32, rb, rtok);
-        const float2* cs = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
-        float inv = 1.0f;
-        if (do_norm) {
-          float ss = 0.f;
+            for (int f = 0; f < FB; ++f) *reinterpret_cast<floatx4*>(yr + 16 * f) = acc[f][t];
+          }
+          int rb, rtok;
+          locate(row, rb, rtok);
+          cs[tt] = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
+          inv[tt] = 1.0f;
+          if (do_norm) {
+            float ss = 0.f;
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < FB; ++f)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ss += acc[f][t][r] * acc[f][t][r];
-          ss = sum_xor32(ss);
-          inv = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
+              for (int r = 0; r < 4; ++r) ss += acc[f][t][r] * acc[f][t][r];
+            ss = sum_xor32(sum_xor16(ss));
+            inv[tt] = 1.0f / __builtin_sqrtf(ss * (1.0f / 128.0f) + a.eps);
+          }
         }
         if (kind == 2) {
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              u32x2 w;
-              w.x = pack_bf16x2(acc[f][t][4 * j + 0], acc[f][t][4 * j + 1]);
-              w.y = pack_bf16x2(acc[f][t][4 * j + 2], acc[f][t][4 * j + 3]);
-              put8(l32, 32 * f + 8 * j + 4 * hh, w);
-            }
+            for (int f = 0; f < FB; ++f) put8(16 * tt + l16, 16 * f + 4 * q4, pack4(acc[f][2 * p + tt]));
         } else {
-          // Rotate-half RoPE over the first `rot` features: feature i <
-          // rot/2 pairs with i + rot/2 (rot 128: block f with f + 2; rot
-          // 64: block 0 with block 1, blocks 2 and 3 pass through).  Each
-          // rope_pair call needs the (cos, sin) of features i0 .. i0+3,
-          // i0 = 32 f1 + 8 j + 4 hh: two 16-byte loads, issued four calls
-          // ahead so that the table's latency is paid about once per block.
+          // Rotate-half RoPE over the first `rot` features.  A rope_pair
+          // call rotates block f1 of row tt with its partner block f2 and
+          // needs the (cos, sin) of features 16 f1 + 4 q4 + (0..3): two
+          // 16-byte loads, issued four calls ahead so that the table's
+          // latency is paid about once per chunk.
           floatx4 pre[4][2];
-          auto fetch = [&](int k, int f1, int j) {
-            const int i0 = 32 * f1 + 8 * j + 4 * hh;
-            pre[k & 3][0] = *reinterpret_cast<const floatx4*>(cs + i0);
-            pre[k & 3][1] = *reinterpret_cast<const floatx4*>(cs + i0 + 2);
+          auto fetch = [&](int k, int tt, int f1) {
+            const int i0 = 16 * f1 + 4 * q4;
+            pre[k & 3][0] = *reinterpret_cast<const floatx4*>(cs[tt] + i0);
+            pre[k & 3][1] = *reinterpret_cast<const floatx4*>(cs[tt] + i0 + 2);
           };
-          auto rope_pair = [&](int f1, int f2, int j, const floatx4& c01, const floatx4& c23) {
-            const int i0 = 32 * f1 + 8 * j + 4 * hh;
+          auto rope_pair = [&](int tt, int f1, int f2, const floatx4& c01, const floatx4& c23) {
+            const int t = 2 * p + tt;
+            const int i0 = 16 * f1 + 4 * q4;
             const float cc[4] = {c01[0], c01[2], c23[0], c23[2]};
             const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-            const u32x2 w1 = wpk[f1][j], w2 = wpk[f2][j];
+            const u32x2 w1 = wpk[f1], w2 = wpk[f2];
             const float g1[4] = {lo_bf16(w1.x), hi_bf16(w1.x), lo_bf16(w1.y), hi_bf16(w1.y)};
             const float g2[4] = {lo_bf16(w2.x), hi_bf16(w2.x), lo_bf16(w2.y), hi_bf16(w2.y)};
-            float y1[4], y2[4];
+            floatx4 y1, y2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float x1 = acc[f1][t][4 * j + e] * inv * g1[e];
-              const float x2 = acc[f2][t][4 * j + e] * inv * g2[e];
+              const float x1 = acc[f1][t][e] * inv[tt] * g1[e];
+              const float x2 = acc[f2][t][e] * inv[tt] * g2[e];
               y1[e] = x1 * cc[e] - x2 * sn[e];
               y2[e] = x2 * cc[e] + x1 * sn[e];
             }
-            u32x2 o1, o2;
-            o1.x = pack_bf16x2(y1[0], y1[1]);
-            o1.y = pack_bf16x2(y1[2], y1[3]);
-            o2.x = pack_bf16x2(y2[0], y2[1]);
-            o2.y = pack_bf16x2(y2[2], y2[3]);
-            put8(l32, i0, o1);
-            put8(l32, i0 + half, o2);
+            put8(16 * tt + l16, i0, pack4(y1));
+            put8(16 * tt + l16, i0 + half, pack4(y2));
           };
-          auto norm_only = [&](int f, int j) {
-            const u32x2 w = wpk[f][j];
-            u32x2 o;
-            o.x = pack_bf16x2(acc[f][t][4 * j + 0] * inv * lo_bf16(w.x),
-                              acc[f][t][4 * j + 1] * inv * hi_bf16(w.x));
-            o.y = pack_bf16x2(acc[f][t][4 * j + 2] * inv * lo_bf16(w.y),
-                              acc[f][t][4 * j + 3] * inv * hi_bf16(w.y));
-            put8(l32, 32 * f + 8 * j + 4 * hh, o);
+          auto norm_only = [&](int tt, int f) {
+            const int t = 2 * p + tt;
+            const u32x2 w = wpk[f];
+            const floatx4 y = {acc[f][t][0] * inv[tt] * lo_bf16(w.x), acc[f][t][1] * inv[tt] * hi_bf16(w.x),
+                               acc[f][t][2] * inv[tt] * lo_bf16(w.y), acc[f][t][3] * inv[tt] * hi_bf16(w.y)};
+            put8(16 * tt + l16, 16 * f + 4 * q4, pack4(y));
           };
-          if (a.rot == 128) {  // call k: f1 = k / 4, j = k % 4
+          if (a.rot == 128) {  // call k: row k / 4, block k % 4 with k % 4 + 4
 #pragma unroll
             for (int k = 0; k < 4; ++k) fetch(k, 0, k);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              rope_pair(k / 4, k / 4 + 2, k % 4, pre[k & 3][0], pre[k & 3][1]);
+              rope_pair(k / 4, k % 4, k % 4 + 4, pre[k & 3][0], pre[k & 3][1]);
               if (k + 4 < 8) fetch(k + 4, 1, k % 4);
               __builtin_amdgcn_sched_barrier(0);
             }
-          } else {  // rot == 64: call j pairs block 0 with block 1
+          } else {  // rot == 64: call k: row k / 2, block k % 2 with k % 2 + 2
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fetch(j, 0, j);
+            for (int k = 0; k < 4; ++k) fetch(k, k / 2, k % 2);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              rope_pair(0, 1, j, pre[j][0], pre[j][1]);
-              norm_only(2, j);
-              norm_only(3, j);
-            }
+            for (int k = 0; k < 4; ++k) rope_pair(k / 2, k % 2, k % 2 + 2, pre[k][0], pre[k][1]);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int f = 4; f < FB; ++f) norm_only(tt, f);
           }
         }
         // cache offsets of the (at most two, when L >= 32) sequences the
-        // block's rows belong to, read once per block
+        // chunk's rows belong to, read once per chunk
         int sp0 = 0, sp1 = 0;
         if (kind != 0 && a.start_pos && long_seq) {
           sp0 = a.start_pos[b0];
           if ((b0 + 1) * L < M) sp1 = a.start_pos[b0 + 1];
         }
-        // Store the block: lane l moves chunk l % 16 of row 4 i + l / 16.
+        // Store the chunk: lane l moves chunk l % 16 of row 4 i + l / 16.
         const int c = lane & 15;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -1010,14 +984,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     const u32x4* sw = wring(g % kWSlots);
     const u32x4* sx = xring(g % kXSlots);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int f = 0; f < FB; ++f) fa[0][f] = sw[offa(0, f)];
 #pragma unroll
-      for (int f = 0; f < FB; ++f) fa[u][f] = sw[offa(u, f)];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) fb[u][t] = sx[offb(u, t)];
-    }
+    for (int t = 0; t < TB; ++t) fb[0][t] = sx[offb(0, t)];
   }
 }
+
 
 // cos/sin of position * theta^(-2i/d) for i < d/2, angles in double.
 // Entry idx of the RoPE table: row `row` is token row - b L of sequence b
