@@ -818,9 +818,54 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       }
       const int half = a.rot >> 1;
       const int L = a.L;
+      // RoPE table rows of this lane's two rows of chunk p, and the table
+      // loads of a chunk's first four rope_pair calls.  The loads of chunk
+      // p + 1 go out at the end of chunk p's rotation, so their latency
+      // runs under chunk p's stores and chunk p + 1's norm.
+      const float2* cs[2];
+      auto rope_rows = [&](int p) {
+        const int mb = m0 + wm * WM + 32 * p;
+        const int b0 = mb / L;  // wave-uniform
+        const int tok0 = mb - b0 * L;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int mr = mb + 16 * tt + l16;
+          int tok;
+          if (L >= 32) {
+            tok = tok0 + 16 * tt + l16;
+            if (tok >= L) tok -= L;
+          } else {
+            tok = mr - (mr / L) * L;
+          }
+          cs[tt] = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : tok) * half;
+        }
+      };
+      floatx4 pre[4][2];
+      auto fetch = [&](int k, int tt, int f1) {
+        const int i0 = 16 * f1 + 4 * q4;
+        pre[k & 3][0] = *reinterpret_cast<const floatx4*>(cs[tt] + i0);
+        pre[k & 3][1] = *reinterpret_cast<const floatx4*>(cs[tt] + i0 + 2);
+      };
+      // rot 128: call k rotates row k / 4, block k % 4 with k % 4 + 4;
+      // rot 64: call k rotates row k / 2, block k % 2 with k % 2 + 2
+      auto fetch_first = [&]() {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (half == 64) fetch(k, 0, k);
+          else fetch(k, k / 2, k % 2);
+        }
+      };
+      if (kind != 2) {
+        rope_rows(0);
+        fetch_first();
+      }
 #pragma unroll
       for (int p = 0; p < TB / 2; ++p) {
         pin_from(2 * p);
+        // the weights stay packed between chunks (unpacked, they would
+        // take 16 more registers through the stores)
+#pragma unroll
+        for (int f = 0; f < FB; ++f) asm volatile("" : "+v"(wpk[f]));
         // Token rows mb .. mb + 31 of this chunk: row m is token tok of
         // sequence b (m = b L + tok).  One division per chunk (wave-uniform);
         // a row's (b, tok) follows by carrying over sequence ends, which
@@ -839,8 +884,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             tok = mb + r - b * L;
           }
         };
-        // the lane's two rows: raw projection out, RoPE table rows, norm scales
-        const float2* cs[2];
+        // the lane's two rows: raw projection out and norm scales
         float inv[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -852,9 +896,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int f = 0; f < FB; ++f) *reinterpret_cast<floatx4*>(yr + 16 * f) = acc[f][t];
           }
-          int rb, rtok;
-          locate(row, rb, rtok);
-          cs[tt] = a.rope + (size_t)(a.start_pos ? (mr < M ? mr : 0) : rtok) * half;
           inv[tt] = 1.0f;
           if (do_norm) {
             float ss = 0.f;
@@ -875,14 +916,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           // Rotate-half RoPE over the first `rot` features.  A rope_pair
           // call rotates block f1 of row tt with its partner block f2 and
           // needs the (cos, sin) of features 16 f1 + 4 q4 + (0..3): two
-          // 16-byte loads, issued four calls ahead so that the table's
-          // latency is paid about once per chunk.
-          floatx4 pre[4][2];
-          auto fetch = [&](int k, int tt, int f1) {
-            const int i0 = 16 * f1 + 4 * q4;
-            pre[k & 3][0] = *reinterpret_cast<const floatx4*>(cs[tt] + i0);
-            pre[k & 3][1] = *reinterpret_cast<const floatx4*>(cs[tt] + i0 + 2);
-          };
+          // 16-byte loads, issued four calls ahead.
           auto rope_pair = [&](int tt, int f1, int f2, const floatx4& c01, const floatx4& c23) {
             const int t = 2 * p + tt;
             const int i0 = 16 * f1 + 4 * q4;
@@ -909,24 +943,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
                                acc[f][t][2] * inv[tt] * lo_bf16(w.y), acc[f][t][3] * inv[tt] * hi_bf16(w.y)};
             put8(16 * tt + l16, 16 * f + 4 * q4, pack4(y));
           };
-          if (a.rot == 128) {  // call k: row k / 4, block k % 4 with k % 4 + 4
-#pragma unroll
-            for (int k = 0; k < 4; ++k) fetch(k, 0, k);
+          if (half == 64) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
               rope_pair(k / 4, k % 4, k % 4 + 4, pre[k & 3][0], pre[k & 3][1]);
               if (k + 4 < 8) fetch(k + 4, 1, k % 4);
               __builtin_amdgcn_sched_barrier(0);
             }
-          } else {  // rot == 64: call k: row k / 2, block k % 2 with k % 2 + 2
-#pragma unroll
-            for (int k = 0; k < 4; ++k) fetch(k, k / 2, k % 2);
+          } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) rope_pair(k / 2, k % 2, k % 2 + 2, pre[k][0], pre[k][1]);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
               for (int f = 4; f < FB; ++f) norm_only(tt, f);
+          }
+          if (p + 1 < TB / 2) {
+            rope_rows(p + 1);
+            fetch_first();
           }
         }
         // cache offsets of the (at most two, when L >= 32) sequences the
@@ -957,6 +991,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
             dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
           }
           st16(dst + 8 * c, v);
+          // at most four rows in flight: the next chunk's table loads are
+          // live here
+          if (i == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
