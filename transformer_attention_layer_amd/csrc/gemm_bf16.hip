@@ -972,28 +972,56 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         }
         // Store the chunk: lane l moves chunk l % 16 of row 4 i + l / 16.
         const int c = lane & 15;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          const int m = mb + row;
-          const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
-          if (m >= M) continue;
-          int b, tok;
-          locate(row, b, tok);
-          bf16* dst;
+        if (long_seq) {
+          // The chunk's rows are tokens tok0 + r of sequence b0, then (past
+          // its end) tokens tok0 + r - L of sequence b0 + 1: row r goes to
+          // base0 + (pos0 + r) rows or base1 + (pos1 + r) rows, with
+          // wave-uniform bases and offsets.
+          bf16* base0;
+          ptrdiff_t stride1;  // from sequence b0's rows to b0 + 1's
+          int pos0 = tok0, pos1 = tok0 - L;
           if (kind == 0) {
-            dst = a.q + (((size_t)b * Hq + h) * L + tok) * 128;
+            base0 = a.q + ((size_t)b0 * Hq + h) * L * 128;
+            stride1 = (ptrdiff_t)Hq * L * 128;
           } else {
-            const int base = !a.start_pos ? 0 : long_seq ? (b == b0 ? sp0 : sp1) : a.start_pos[b];
-            const int pos = base + tok;
-            if (pos < 0 || pos >= a.cap) continue;
             bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
-            dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
+            base0 = cache + ((size_t)b0 * Hkv + h) * a.cap * 128;
+            stride1 = (ptrdiff_t)Hkv * a.cap * 128;
+            pos0 += sp0;
+            pos1 += sp1;
           }
-          st16(dst + 8 * c, v);
-          // at most four rows in flight: the next chunk's table loads are
-          // live here
-          if (i == 3) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
+            const bool second = tok0 + row >= L;
+            const int pos = (second ? pos1 : pos0) + row;
+            const bool ok = mb + row < M && (kind == 0 || (pos >= 0 && pos < a.cap));
+            if (ok) st16(base0 + (second ? stride1 : 0) + (ptrdiff_t)pos * 128 + 8 * c, v);
+            // at most four rows in flight: the next chunk's table loads are
+            // live here
+            if (i == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            const int m = mb + row;
+            const u32x4 v = stage[row * 16 + (c ^ (row & 15))];
+            if (m >= M) continue;
+            int b, tok;
+            locate(row, b, tok);
+            bf16* dst;
+            if (kind == 0) {
+              dst = a.q + (((size_t)b * Hq + h) * L + tok) * 128;
+            } else {
+              const int pos = (a.start_pos ? a.start_pos[b] : 0) + tok;
+              if (pos < 0 || pos >= a.cap) continue;
+              bf16* cache = kind == 1 ? a.k_cache : a.v_cache;
+              dst = cache + (((size_t)b * Hkv + h) * a.cap + pos) * 128;
+            }
+            st16(dst + 8 * c, v);
+          }
         }
       }
     }
