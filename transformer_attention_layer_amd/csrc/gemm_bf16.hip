@@ -25,6 +25,8 @@ namespace gqa {
 
 namespace {
 
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 constexpr int kBK = 64;          // K elements per LDS stage: one 128-byte line per row
 constexpr int kStages = 2;       // loads run kStages stages ahead
 constexpr int kWSlots = 3;       // LDS ring slots of W stages
@@ -358,10 +360,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       const bool reads = step == 0 || NEXT;
-      const u32x4* rw = step == 0 ? sw : sw1;
-      const u32x4* rx = step == 0 ? sx : sx1;
       const int ns = step ^ 1;  // the K step whose fragments are read
       const int cb = step, nb = ns;
+      // this lane's fragment bases in the slots read (one VALU op each per
+      // step; the fragments are then constant offsets below 64 KB, which the
+      // reads take as immediates, while offsets from the LDS array's start
+      // would pass 64 KB in the X ring and cost an add per read)
+      lds_u32x4* rw = (lds_u32x4*)((step == 0 ? sw : sw1) + offa(ns, 0));
+      lds_u32x4* rx = (lds_u32x4*)((step == 0 ? sx : sx1) + offb(ns, 0));
+      asm volatile("" : "+v"(rw));
+      asm volatile("" : "+v"(rx));
 #pragma unroll
       for (int i = 0; i < FB * TB; ++i) {
         const int f = i / TB, t = i % TB;
@@ -370,9 +378,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
         if (i < 32 && (i & 1) == 0 && reads) {
           // next step's fragments in the order its MFMAs use them
           const int r = i / 2;
-          if (r == 0) fa[nb][0] = rw[offa(ns, 0)];
-          else if (r <= TB) fb[nb][r - 1] = rx[offb(ns, r - 1)];
-          else fa[nb][r - TB] = rw[offa(ns, r - TB)];
+          if (r == 0) fa[nb][0] = rw[0];
+          else if (r <= TB) fb[nb][r - 1] = rx[16 * (r - 1) * kCPR];
+          else fa[nb][r - TB] = rw[16 * (r - TB) * kCPR];
         }
         if (step == 0 && i >= 32 && (i & 3) == 0) issue(ld, (i - 32) / 4, 0);
         if constexpr (NEXT) {
