@@ -1351,9 +1351,11 @@ hipError_t launch_cvt_bf16_f16(const __bf16* in, void* out, long long n, hipStre
 }
 
 // The 64-aligned kernel: K splits that bring the workgroups (64 x 64
-// output blocks) to at most two per CU (one round: a few workgroups past
-// that would double the time), each with at least two K stages of 64, and
-// no split left short or empty.  Otherwise (the general kernel, 32 features per workgroup) only when
+// output blocks) to about one per CU (one round; two per CU streamed the
+// weights no faster and left more partial products to sum: the 64-token
+// decode layer took 0.2206 ms with 10 splits of its projections, 0.2185
+// with 6 and 5), each with at least two K stages of 64, and no split left
+// short or empty.  Otherwise (the general kernel, 32 features per workgroup) only when
 // the features alone leave more than half of the CUs idle: a decode step's
 // o_proj (2560 features: 80 workgroups) went from 58 to 30 us (+4 us for
 // the sum) with 4 splits, while its QKV projection (4352 features: 136
@@ -1362,7 +1364,7 @@ int skinny_ksplit(int N, int K, int M) {
   if (K % 64 == 0) {
     const int wgs = max(1, ((N + 63) / 64) * ((M + 63) / 64));  // M = 0: an empty call
     const int nst = K / 64;
-    int ks = 512 / wgs;
+    int ks = 256 / wgs;
     if (ks > nst / 2) ks = nst / 2;
     if (ks > 16) ks = 16;
     if (ks <= 1) return 1;
