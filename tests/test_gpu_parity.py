@@ -211,6 +211,41 @@ def test_chunked_prefill_with_ragged_cache():
     assert_close(to_np(out), ref, w.dtype, "out")
 
 
+@pytest.mark.parametrize("seq,cache_lens", [
+    (100, [300, 0, 123]),
+    (17, [(37 * b) % 200 for b in range(20)]),
+    (17, None),
+])
+def test_fused_epilogue_rows(seq, cache_lens):
+    """More than 256 tokens take the persistent GEMM with the head_dim-128
+    norm/RoPE/scatter epilogue, which stores 32-token chunks: with L >= 32 a
+    chunk spans at most two sequences (two cache bases, whose offsets differ
+    here), with L < 32 its rows are placed one by one; with and without
+    caches to continue."""
+    batch = 20 if cache_lens is None else len(cache_lens)
+    cap = 0 if cache_lens is None else max(cache_lens)
+    w = GI.WORKLOADS["prefill_h1024"].with_(batch=batch, seq=seq, cache_len=cap)
+    announce(f"[fused epilogue rows] B={batch} L={seq} caches={cache_lens}")
+    h = GI.host_layer_inputs(w)
+    if cache_lens is None:
+        out, _, _ = run_layer(w, h)
+        ref, _, _ = oracle_layer(w, h)
+    else:
+        cache = GI.host_cache(w)
+        cl = np.array(cache_lens, dtype=np.int64)
+        for b, n in enumerate(cl):
+            cache["k_cache"][b, :, n:] = np.nan
+            cache["v_cache"][b, :, n:] = np.nan
+        out, kc, vc = run_layer(w, h, cache, cl)
+        ref, rk, rv = oracle_layer(w, h, cache, cl)
+        kc, vc = to_np(kc), to_np(vc)
+        for b, n in enumerate(cl):
+            assert_close(kc[b, :, n:n + seq], rk[b, :, n:n + seq], w.dtype, f"k append {b}")
+            assert_close(vc[b, :, n:n + seq], rv[b, :, n:n + seq], w.dtype, f"v append {b}")
+            assert np.array_equal(kc[b, :, :n], cache["k_cache"][b, :, :n])
+    assert_close(to_np(out), ref, w.dtype, "out")
+
+
 @pytest.mark.parametrize("q_len", [2, 4, 8])
 def test_multi_token_decode(q_len):
     """A few new tokens per sequence (group * q_len <= 32 takes the split-KV
