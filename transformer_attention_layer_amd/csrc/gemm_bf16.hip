@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   pw.init(Kw, wave, lane, EPI == kEpiQKV256);
   px.init(K, wave, lane);
   constexpr int kLw = DmaPlan<BN>::kInstr, kLx = DmaPlan<BM>::kInstr;
-  static_assert(kLw == 8 && kLx == 8, "one load per MFMA in a stage's last substep");
+  static_assert(kLw == 8 && kLx == 8, "one load per four MFMAs in the second half of a step");
   const int wrap = a.w_kmod > 0 ? Kw : 0;
   // K offset into W of a tile's stage kt when K is aligned (K <= 2 Kw: X =
   // [hi | lo] reads W at most twice, and Kw is a multiple of kBK)
