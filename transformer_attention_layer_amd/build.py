@@ -1,5 +1,8 @@
-"""Compile the HIP sources of the GQA layer into ``libgqa.so`` (gfx950), and
-the measurement microkernels into ``libgqa_peaks.so``.
+"""Compile the HIP sources of the GQA layer into ``libgqa.so`` (gfx950), the
+measurement microkernels into ``libgqa_peaks.so``, and the same layer
+sources with ``GQA_LDS_POISON`` into ``libgqa_ldspoison.so``: a debug build
+whose kernels first fill their LDS with NaN bits, which a GPU test runs the
+parity checks against (a read of LDS that nothing wrote then shows up).
 
 Run ``python -m transformer_attention_layer_amd.build`` or call ``build()``.
 Every source is compiled with hipcc for gfx950 only; packed fp32 VALU forms
@@ -21,6 +24,8 @@ SOURCES = ["gqa_api.hip", "gemm_bf16.hip", "attn_bf16.hip", "attn_bwd.hip", "bwd
            "normrope_rows.hip", "f32_kernels.hip"]
 PEAKS_LIB = os.path.join(HERE, "libgqa_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
+POISON_LIB = os.path.join(HERE, "libgqa_ldspoison.so")
+POISON_DIR = os.path.join(BUILD_DIR, "ldspoison")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -31,9 +36,11 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, poison = job
+    obj = os.path.join(POISON_DIR if poison else BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *(["-DGQA_LDS_POISON"] if poison else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -50,16 +57,19 @@ def _link(objs, lib: str) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source, link ``libgqa.so`` and ``libgqa_peaks.so``;
-    returns the layer library's path."""
+    """Compile every source, link ``libgqa.so``, ``libgqa_peaks.so`` and
+    ``libgqa_ldspoison.so``; returns the layer library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = SOURCES + PEAKS_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PEAKS_LIB)
+    os.makedirs(POISON_DIR, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES + PEAKS_SOURCES] + [(s, True) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    n, m = len(SOURCES), len(PEAKS_SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + m], PEAKS_LIB)
+    _link(objs[n + m:], POISON_LIB)
     if verbose:
-        print(f"built {LIB} and {PEAKS_LIB}")
+        print(f"built {LIB}, {PEAKS_LIB} and {POISON_LIB}")
     return LIB
 
 

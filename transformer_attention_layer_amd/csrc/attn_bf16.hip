@@ -229,6 +229,7 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
   // current tile wait for the loads of the next.
   __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
   __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  poison_lds(sk0, sk1, sv0, sv1);
   lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
   lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
 
@@ -331,6 +332,7 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   using Plan = TileLoads<KD, NT, TK>;
   __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
   __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  poison_lds(sk0, sk1, sv0, sv1);
   lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
   lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
 
@@ -450,6 +452,7 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_fp8_kernel(AttnArgs a) 
   using L8 = Fp8TileLoads<KD, TK>;
   __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
   __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  poison_lds(sk0, sk1, sv0, sv1);
   lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
   lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
 
@@ -564,6 +567,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   for (int x = 32; x > 0; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x, 64));
   const float muse = mmax == -INFINITY ? 0.f : mmax;
   __shared__ float wsh[64];
+  poison_lds(wsh);
   float lsum = 0.f;
   floatx4 o = {0.f, 0.f, 0.f, 0.f};
   const float* po = a.part_o + base * KD + 4 * e4;

@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kBwdNT, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   using Tile = RowTile<KD, TK, 0>;
   __shared__ u32x4 sk0[TK * G::NCH], sk1[TK * G::NCH];
   __shared__ u32x4 sv0[TK * G::NCH], sv1[TK * G::NCH];
+  poison_lds(sk0, sk1, sv0, sv1);
   lds_u32x4* const sk[2] = {(lds_u32x4*)sk0, (lds_u32x4*)sk1};
   lds_u32x4* const sv[2] = {(lds_u32x4*)sv0, (lds_u32x4*)sv1};
 
@@ -477,6 +478,7 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   __shared__ u32x4 sq0[TQ * G::NCH], sq1[TQ * G::NCH], sq2[TQ * G::NCH];
   __shared__ u32x4 sd0[TQ * G::NCH], sd1[TQ * G::NCH], sd2[TQ * G::NCH];
   __shared__ float sl0[TQ], sl1[TQ], sl2[TQ], sD0[TQ], sD1[TQ], sD2[TQ];
+  poison_lds(sq0, sq1, sq2, sd0, sd1, sd2, sl0, sl1, sl2, sD0, sD1, sD2);
   lds_u32x4* const sq[3] = {(lds_u32x4*)sq0, (lds_u32x4*)sq1, (lds_u32x4*)sq2};
   lds_u32x4* const sd[3] = {(lds_u32x4*)sd0, (lds_u32x4*)sd1, (lds_u32x4*)sd2};
   lds_float* const sl[3] = {(lds_float*)sl0, (lds_float*)sl1, (lds_float*)sl2};

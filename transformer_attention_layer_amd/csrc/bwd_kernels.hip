@@ -16,6 +16,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restr
                                                              int C, int Rc, int rows_out,
                                                              bf16* __restrict__ out) {
   __shared__ unsigned short tile[64][64 + 8];
+  poison_lds(tile);
   const int c0 = blockIdx.x * 64;
   const int r0 = blockIdx.y * 64;
   const int t = threadIdx.x;

@@ -154,3 +154,24 @@ GQA_DEV float sum_xor32(float v) {
 }
 
 GQA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Debug builds (libgqa_ldspoison.so, compiled with GQA_LDS_POISON): every
+// workgroup first fills its LDS arrays with all-ones bits, a NaN both as
+// fp32 and as bf16, and meets at a barrier, so that a read of LDS that
+// nothing in the workgroup wrote shows up as a NaN in the results.  The
+// release library compiles the calls away.
+#ifdef GQA_LDS_POISON
+template <typename T, size_t N>
+GQA_DEV void poison_one(T (&arr)[N]) {
+  unsigned* p = reinterpret_cast<unsigned*>(&arr[0]);
+  for (int i = (int)threadIdx.x; i < (int)(sizeof(arr) / 4); i += (int)blockDim.x) p[i] = ~0u;
+}
+template <typename... A>
+GQA_DEV void poison_lds(A&... arrs) {
+  (poison_one(arrs), ...);
+  __syncthreads();
+}
+#else
+template <typename... A>
+GQA_DEV void poison_lds(A&...) {}
+#endif

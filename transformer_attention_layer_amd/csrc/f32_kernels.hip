@@ -17,6 +17,7 @@ constexpr int kKT = 16;  // K step
 __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Args a) {
   __shared__ float sx[kKT][kT + 1];
   __shared__ float sw[kKT][kT + 1];
+  poison_lds(sx, sw);
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
@@ -57,6 +58,7 @@ template <typename T>
 __global__ __launch_bounds__(128) void normrope_kernel(NormRopeArgs a) {
   __shared__ float red[128];
   __shared__ float xs[256];
+  poison_lds(red, xs);
   const int m = blockIdx.x;       // token
   const int head = blockIdx.y;    // 0 .. Hq + 2 Hkv - 1
   const int j = threadIdx.x;

@@ -201,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int kWStage = BN * kCPR, kXStage = BM * kCPR;  // 16-byte slots per stage
   static_assert((kThreads / 64) * 32 * 16 <= kXStage, "the epilogue stages through an X slot");
   __shared__ u32x4 lds[kWSlots * kWStage + kXSlots * kXStage];
+  poison_lds(lds);
   auto wring = [&](unsigned slot) { return &lds[slot * kWStage]; };
   auto xring = [&](unsigned slot) { return &lds[kWSlots * kWStage + slot * kXStage]; };
 
@@ -1098,6 +1099,7 @@ constexpr int kSkinnyUnroll = 4;
 template <bool F16>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny_kernel(GemmArgs a) {
   __shared__ floatx16 red[kSkinnyWaves - 1][2][64];
+  poison_lds(red);
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
@@ -1203,6 +1205,7 @@ template <bool F16, bool WCVT = false>
 __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs a) {
   static_assert(!WCVT || F16, "W is rounded to fp16 for the fp16 products");
   __shared__ u32x4 lds[kSkR * kSkStage];
+  poison_lds(lds);
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;

@@ -1115,4 +1115,9 @@ const char* gqa_status_string(gqa_status s) {
 
 const char* gqa_last_error(void) { return g_err; }
 
+#ifdef GQA_LDS_POISON
+// Marks the LDS-poisoning debug build (its tests check that they run it).
+int gqa_lds_poison_build(void) { return 1; }
+#endif
+
 }  // extern "C"

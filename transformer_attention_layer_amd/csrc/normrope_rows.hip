@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdA
   static_assert(PASSES * RPW * (kRowsNT / 64) == kBwdTokens, "a block covers kBwdTokens tokens");
   __shared__ floatx4 red[kRowsNT / 64][RPW][R];
   __shared__ u32x2 tile[kBwdTokens][R];  // bf16 dy of the block's tokens
+  poison_lds(red, tile);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % R, e0 = 4 * sub, grp = lane / R;
   const int head = blockIdx.y;
