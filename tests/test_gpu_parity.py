@@ -52,6 +52,12 @@ SMALL = {
                                                              hkv=4, o_fp16=False, o_split=True),
     "bf16_d64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=300, hq=8, hkv=4,
                                                               head_dim=64),
+    # head_dim 256 through the split-KV decode kernel (one wave per SIMD),
+    # a Gemma-shaped group of 4 query heads per KV head
+    "bf16_d256_decode": GI.WORKLOADS["gemma_h640_d256"].with_(batch=3, seq=1, cache_len=1500),
+    # MQA with 2 new tokens: 32 heads x 2 rows pass one wave's 32, so the
+    # prefill kernel runs over the cache (bottom-right causal alignment)
+    "mqa_two_tokens": GI.WORKLOADS["decode_h2560_mqa"].with_(batch=2, seq=2, cache_len=900),
     # the QKV projection's own norm/RoPE epilogue for head_dim 64 and 256
     # (more than 256 tokens): 256 with and without a cache to continue,
     # 64 with rotary 32 and with an odd head count (the last wave of
