@@ -11,12 +11,14 @@
 // memory traffic of the same products, not their result).
 //
 // Layout inside a wave.  A wave owns 32 query rows.  Scores are formed
-// transposed, S^T = K Q^T (keys are MFMA rows, queries MFMA columns), so
-// lane l holds one query (l % 32) and half of each 32-key block; the row max
-// and sum need a single exchange with lane l ^ 32, and the rescale factor is
-// one scalar per lane.  O^T = V^T P^T then takes P^T straight from the score
-// registers; the V^T operand is read from V (stored as in memory) with
-// transposing LDS reads, keys in the order the score registers hold them.
+// transposed, S^T = K Q^T (keys are MFMA rows, queries MFMA columns), so a
+// lane holds whole queries and the rescale factor is one scalar per lane and
+// query.  O^T = V^T P^T then takes P^T straight from the score registers;
+// the V^T operand is read from V (stored as in memory) with transposing LDS
+// reads, keys in the order the score registers hold them.  The decode
+// kernels use 32x32x16 products (lane l holds query l % 32 and half of each
+// 32-key block: one exchange with lane l ^ 32 per row max and sum), the
+// prefill kernel 16x16x32 ones (two 16-query blocks per wave; see below).
 //
 // Softmax bookkeeping per key tile: the tile's row max is taken on the raw
 // scores (the scale is positive), exp2(s * scale*log2(e) - m) is one FMA and
@@ -204,13 +206,242 @@ __device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)
   }
 }
 
+// ---- prefill on 16x16x32 MFMAs ----
+// A wave's 32 query rows are two 16-row blocks (qb): lane l holds queries
+// l16 and 16 + l16 (l16 = l % 16) and, of each 16-key block of the scores
+// S^T = K Q^T, the keys 4 q + 0..3 (q = l / 16).  The row max and sum of a
+// query then span the four lanes l16 + 16 q (two exchanges), the rescale
+// factor is one scalar per lane and query block, and the P^T operand of
+// O^T = V^T P^T comes straight from the score registers: for a 32-key step,
+// lane l holds keys 4 q + 0..3 and 16 + 4 q + 0..3 of the query, which is
+// an MFMA K-group of eight.  The V^T operand is read with transposing LDS
+// reads in that key order.  The matrix cores do the same work per cycle as
+// with 32x32x16 products, for less power (the board's power limit sets the
+// clock): 1-3% faster at 2x16384 than the 32x32x16 version of this kernel.
+template <int KD>
+struct RowState16 {
+  floatx4 o[KD / 16][2];  // O^T: feature 16 db + 4 q + r, query 16 qb + l16
+  float m[2];             // running max per query block (log2 units, scaled scores)
+  float l[2];             // running sum, this lane's keys only
+};
+
+template <int KD>
+__device__ __forceinline__ void init_state16(RowState16<KD>& st) {
+#pragma unroll
+  for (int d = 0; d < KD / 16; ++d)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.o[d][qb][r] = 0.f;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    st.m[qb] = -INFINITY;
+    st.l[qb] = 0.f;
+  }
+}
+
+// Per-lane LDS offsets of the 16x16 fragments, as one base per operand: the
+// swizzles XOR the chunk with a lane term, so the offset of step s (K) or
+// block db (V) is the base XOR a constant (two registers instead of one per
+// step and block, for one VALU op per read).
+template <int KD>
+struct LaneOffsets16 {
+  int k;  // K fragment of feature step 0 (bytes): key row l16, chunk q; step s: k ^ (64 s)
+  int v;  // V^T fragment of feature block 0 (bytes), first read, key group 0; block db: v ^ (32 db)
+  __device__ __forceinline__ int kofs(int s) const { return k ^ (64 * s); }
+  __device__ __forceinline__ int vofs(int db) const { return v ^ (32 * db); }
+};
+
+// K fragment (A operand of a 16-key x 16-query score block, 32 features per
+// step): lane l reads key row l16, features 32 s + 8 q + 0..7.  V^T fragment
+// (A operand of O^T, 16 features x 32 keys): lane l = 16 q + i must hold
+// feature 16 db + i of keys 4 q + 0..3 and 16 + 4 q + 0..3.  A transposing
+// read in which lane j of group q points at row (key) 4 q + j / 4,
+// features 16 db + 4 (j % 4) + 0..3 hands lane i feature 16 db + i of the 4
+// keys 4 q + e; the second read is the same, 16 rows further on.  Both
+// swizzles depend on the row modulo 16 (K) or 8 (V) only, so key block and
+// key step offsets are whole rows.
+//
+// K: chunk 4 s + q of row l16 sits at slot (4 s + q) ^ kswz(l16), whose
+// bits 2 and up are s ^ (kswz / 4) (kswz < 16 for 256-byte rows, < 8 for
+// 128-byte ones; 512-byte rows keep the row's chunk bits 4 and up): byte
+// offset = base ^ 64 s.  V: chunk 2 db + c of row r sits at (2 db + c) ^
+// vswz16(r) = 2 (db ^ vswz16 / 2) + c: byte offset = base ^ 32 db.
+template <int KD>
+__device__ __forceinline__ void lane_offsets16(LaneOffsets16<KD>& o, int lane) {
+  using G = Geo<KD>;
+  const int l16 = lane & 15, q = lane >> 4;
+  o.k = G::kslot(l16, q) * 16;
+  const int row = 4 * q + (l16 >> 2);
+  const int feat = 4 * (l16 & 3);
+  o.v = G::vslot16(row, feat >> 3) * 16 + (feat & 7) * 2;
+}
+
+// Both query blocks' Q fragments (B operands): feature step s of block qb
+// is features 32 s + 8 q + 0..7 of query row 16 qb + l16.
+template <int KD>
+__device__ __forceinline__ void load_q16(u32x4 (&qf)[2][KD / 32], const bf16* q0, const bf16* q1,
+                                         bool v0, bool v1, int q) {
+#pragma unroll
+  for (int s = 0; s < KD / 32; ++s) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qf[0][s] = v0 ? ld16(q0 + 32 * s + 8 * q) : z;
+    qf[1][s] = v1 ? ld16(q1 + 32 * s + 8 * q) : z;
+  }
+}
+
+// One key tile on 16x16x32 products: scores, online softmax, PV.
+// `kend0` = one past the last key the lane's query of block 0 may see, and
+// `kstep1` what block 1's query (16 rows further on) sees beyond it: 16
+// keys with the causal mask, none without;
+// `masked` (wave-uniform) = some key of the tile may be past it for some
+// row of the wave.  `loads` issues the JW K and JW V loads of the next tile
+// during the first QK MFMAs.
+template <int KD, int TK, int JW, typename Loads>
+__device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&qf)[2][KD / 32],
+                                              const lds_u32x4* sk, const lds_u32x4* sv,
+                                              const LaneOffsets16<KD>& lo, int key0,
+                                              int kend0, int kstep1, bool masked, float c_log2,
+                                              int q, const Loads& loads) {
+  using G = Geo<KD>;
+  constexpr int NS = KD / 32;   // feature steps of the QK product
+  constexpr int ND = KD / 16;   // feature blocks of O^T
+  constexpr int KB = TK / 16;   // key blocks
+  constexpr int KS = TK / 32;   // key steps of the PV product
+  constexpr int NF = KB * NS;   // K fragments per tile = V^T fragments per tile
+  static_assert(NF == KS * ND, "as many V^T as K fragments");
+  constexpr int NQK = 2 * NF;   // QK MFMAs per tile
+  constexpr int kPer = (2 * JW + NQK - 1) / NQK;  // loads per leading QK MFMA
+  u32x4 fr[NF];
+  // K fragments in the order the products use them: feature step major
+#pragma unroll
+  for (int m = 0; m < NF; ++m) {
+    const int s = m / KB, kb = m % KB;
+    fr[m] = *reinterpret_cast<const lds_u32x4*>(reinterpret_cast<lds_cchar*>(sk) + 16 * kb * G::RB +
+                                                 lo.kofs(s));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  floatx4 sc[KB][2];
+  // 2 KB independent accumulation chains, interleaved
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    const int m = i / 2, qb = i % 2, s = m / KB, kb = m % KB;
+    const floatx4 z = {};
+    sc[kb][qb] = mfma16x16x32(fr[m], qf[qb][s], s == 0 ? z : sc[kb][qb]);
+    if (i * kPer < 2 * JW) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int idx = i * kPer + u;
+        if (idx < JW) loads.k(idx);
+        else if (idx < 2 * JW) loads.v(idx - JW);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // V^T fragments of key step ks, feature blocks db of one half of the
+  // head (the register budget of three waves per SIMD holds half of them
+  // at a time): the first half is read now and lands while the softmax
+  // runs, the second after the first half's products
+  constexpr int NH = ND / 2;
+  auto read_v = [&](int ks, int half, u32x4(&vf)[NH]) {
+    lds_cchar* vg = reinterpret_cast<lds_cchar*>(sv) + 32 * ks * G::RB;
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const int vo = lo.vofs(half * NH + j);
+      const u32x2 k0 = lds_read_tr16(vg + vo);
+      const u32x2 k1 = lds_read_tr16(vg + vo + 16 * G::RB);
+      vf[j] = u32x4{k0.x, k0.y, k1.x, k1.y};
+    }
+  };
+  u32x4 vf[NH];
+  read_v(0, 0, vf);
+  __builtin_amdgcn_sched_barrier(0);
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + 16 * kb + 4 * q + r >= kend0 + kstep1 * qb) sc[kb][qb][r] = -INFINITY;
+  }
+  float mx[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    mx[qb] = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx[qb] = fmaxf(mx[qb], sc[kb][qb][r]);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) mx[qb] = max_xor32(max_xor16(mx[qb]));  // over lanes l16 + 16 q
+  float mt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) mt[qb] = mx[qb] * c_log2;  // -inf stays -inf (c_log2 > 0)
+  if (__builtin_amdgcn_ballot_w64(mt[0] > st.m[0] + kLazyRescale ||
+                                  mt[1] > st.m[1] + kLazyRescale)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mn = fmaxf(st.m[qb], mt[qb]);
+      const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(st.m[qb] - mn);
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.o[d][qb][r] *= alpha;
+      st.l[qb] *= alpha;
+      st.m[qb] = mn;
+    }
+  }
+  // P^T operands of both query blocks (and the row sums of their bf16
+  // values), then the products, half of the feature blocks at a time
+  u32x4 pf[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mb = st.m[qb] == -INFINITY ? 0.f : st.m[qb];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[e] = fast_exp2(__builtin_fmaf(sc[2 * ks + e / 4][qb][e % 4], c_log2, -mb));
+      u32x4 f;
+      f.x = pack_bf16x2(p[0], p[1]);
+      f.y = pack_bf16x2(p[2], p[3]);
+      f.z = pack_bf16x2(p[4], p[5]);
+      f.w = pack_bf16x2(p[6], p[7]);
+      st.l[qb] = sum_bf16x2(f.x, st.l[qb]);
+      st.l[qb] = sum_bf16x2(f.y, st.l[qb]);
+      st.l[qb] = sum_bf16x2(f.z, st.l[qb]);
+      st.l[qb] = sum_bf16x2(f.w, st.l[qb]);
+      pf[ks][qb] = f;
+    }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (ks + half > 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_v(ks, half, vf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          st.o[half * NH + j][qb] = mfma16x16x32(vf[j], pf[ks][qb], st.o[half * NH + j][qb]);
+    }
+}
+
 // Prefill tile sizes and occupancy: head_dim 128 takes 32-key tiles, whose
-// registers (168) and LDS (32 KB) let three workgroups share a CU, so three
-// waves per SIMD hide each other's softmax and LDS latency (2% faster than
-// 64-key tiles at two waves per SIMD, which in turn beat 32-key tiles at
-// two); head_dim 64 keeps 64-key tiles (three waves per SIMD already);
-// head_dim 256 takes 32 keys at one wave per SIMD (its fragments would not
-// fit otherwise).
+// registers (168, with the V^T fragments read half a head at a time) and LDS
+// (32 KB) let three workgroups share a CU, so three waves per SIMD hide each
+// other's softmax and LDS latency (64-key tiles need two waves per SIMD and
+// were slower); head_dim 64 keeps 64-key tiles (three waves per SIMD
+// already); head_dim 256 takes 32 keys at one wave per SIMD (its fragments
+// would not fit otherwise).
 template <int KD>
 struct PrefillCfg {
   static constexpr int TK = KD == 64 ? 64 : 32;
@@ -223,7 +454,7 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
     AttnArgs a) {
   using G = Geo<KD>;
   constexpr int TK = PrefillCfg<KD>::TK, NT = PrefillCfg<KD>::NT;
-  using Plan = TileLoads<KD, NT, TK>;
+  using Plan = TileLoads<KD, NT, TK, true>;
   // Separate arrays per buffer: the compiler then knows that the loads into
   // one buffer cannot touch the other, and does not make reads of the
   // current tile wait for the loads of the next.
@@ -235,7 +466,7 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, q = lane >> 4;
   const int qt = a.n_qtiles - 1 - (int)blockIdx.z;  // heaviest query tiles first
   const int b = blockIdx.y;
   const int kvh = blockIdx.x / a.n_hsub;
@@ -256,12 +487,21 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
   const int w_tlast = min(t0 + 31, a.Lq - 1);
   const int key_end_w = wave_live ? (a.causal ? min(kvl, off + w_tlast + 1) : kvl) : 0;
   const int kmin_w = a.causal ? min(kvl, off + t0 + 1) : kvl;
-  const int tq = t0 + l32;
-  const bool row_valid = tq < a.Lq;
-  const int kend_row = row_valid ? (a.causal ? min(kvl, off + tq + 1) : kvl) : 0;
+  // The lane's two query rows: tq and tq + 16.  Masking needs only the
+  // first row's key end: the second one's is 16 keys later.  The masked
+  // tiles are those that reach past kmin_w, where every row of the wave
+  // that exists sees all keys before it; rows past the end of the
+  // sequence take part in the products but are never stored.
+  const int tq = t0 + l16;
+  const int kend0 = a.causal ? off + tq + 1 : kvl;
 
-  u32x4 qf[G::NC];
-  load_q<KD>(qf, a.q + (((size_t)b * a.Hq + hq) * a.Lq + (row_valid ? tq : 0)) * KD, row_valid, hh);
+  u32x4 qf[2][KD / 32];
+  {
+    const bf16* qhead = a.q + ((size_t)b * a.Hq + hq) * a.Lq * KD;
+    const bool v0 = tq < a.Lq, v1 = tq + 16 < a.Lq;
+    load_q16<KD>(qf, qhead + (size_t)(v0 ? tq : 0) * KD, qhead + (size_t)(v1 ? tq + 16 : 0) * KD,
+                 v0, v1, q);
+  }
 
   const size_t kv_base = ((size_t)b * a.Hkv + kvh) * a.cap * KD;
   const bf16* kb = a.k + kv_base;
@@ -269,14 +509,14 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
   // descriptors of the tile starting at key k0 (keys k0 .. kvl - 1 valid)
   auto rk_at = [&](int k0) { return make_rsrc(kb + (size_t)k0 * KD, (long long)(kvl - k0) * G::RB); };
   auto rv_at = [&](int k0) { return make_rsrc(vb + (size_t)k0 * KD, (long long)(kvl - k0) * G::RB); };
-  LaneOffsets<KD> lo;
-  lane_offsets<KD>(lo, lane);
+  LaneOffsets16<KD> lo;
+  lane_offsets16<KD>(lo, lane);
 
-  RowState<KD> st;
-  init_state<KD>(st);
+  RowState16<KD> st;
+  init_state16<KD>(st);
   Plan plan;
   plan.init(wave, lane);
-  const TileDst<KD, NT, TK> first{&plan, rk_at(0), rv_at(0), sk[0], sv[0], n_tiles > 0};
+  const TileDst<KD, NT, TK, true> first{&plan, rk_at(0), rv_at(0), sk[0], sv[0], n_tiles > 0};
   first.all();
   __syncthreads();
   // two tiles per trip, so each buffer's LDS addresses are constants
@@ -284,13 +524,13 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
     constexpr int B = decltype(bufc)::value;
     // the next tile goes to the other buffer, last read before the barrier
     // that ended the previous trip
-    const TileDst<KD, NT, TK> next{&plan, rk_at((it + 1) * TK), rv_at((it + 1) * TK), sk[B ^ 1],
-                                   sv[B ^ 1], it + 1 < n_tiles};
+    const TileDst<KD, NT, TK, true> next{&plan, rk_at((it + 1) * TK), rv_at((it + 1) * TK),
+                                         sk[B ^ 1], sv[B ^ 1], it + 1 < n_tiles};
     const int key0 = it * TK;
     if (key0 < key_end_w) {
       const bool masked = key0 + TK > kmin_w;
-      attend_tile<KD, TK, Plan::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked,
-                                    a.scale_log2, hh, next);
+      attend_tile16<KD, TK, Plan::JW>(st, qf, sk[B], sv[B], lo, key0, kend0, a.causal ? 16 : 0,
+                                      masked, a.scale_log2, q, next);
     } else {
       next.all();  // the other waves still need this wave's share
     }
@@ -301,25 +541,27 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
     if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  const float lt = sum_xor32(st.l);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (!row_valid) return;
-  if (a.lse && hh == 0) {
-    // log sum_j exp(s_j * scale) = (m + log2(l)) * ln 2, m in log2 units
-    a.lse[((size_t)b * a.Hq + hq) * a.Lq + tq] =
-        lt > 0.f ? (st.m + log2f(lt)) * 0.69314718055994531f : -INFINITY;
-  }
   const size_t width = (size_t)a.Hq * KD;
-  bf16* orow = a.o + ((size_t)b * a.Lq + tq) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
 #pragma unroll
-  for (int d = 0; d < G::NB; ++d)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = sum_xor32(sum_xor16(st.l[qb]));
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int t = tq + 16 * qb;
+    if (t >= a.Lq) continue;
+    if (a.lse && q == 0) {
+      // log sum_j exp(s_j * scale) = (m + log2(l)) * ln 2, m in log2 units
+      a.lse[((size_t)b * a.Hq + hq) * a.Lq + t] =
+          lt > 0.f ? (st.m[qb] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    }
+    bf16* orow = a.o + ((size_t)b * a.Lq + t) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int d = 0; d < KD / 16; ++d) {
       float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = st.o[d][4 * j + i] * inv;
-      store_o4(orow + 32 * d + 8 * j + 4 * hh, width, v, a.o_split, a.o_f16);
+      for (int i = 0; i < 4; ++i) v[i] = st.o[d][qb][i] * inv;
+      store_o4(orow + 16 * d + 4 * q, width, v, a.o_split, a.o_f16);
     }
+  }
 }
 
 constexpr int kDecodeTK = 32;

@@ -43,6 +43,16 @@ struct Geo {
   __device__ static __forceinline__ int vswz(int row) {
     return KD == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
   }
+  // V tile read by the 16x16 kernels: a transposing read by 32 lanes touches
+  // 8 consecutive rows x 2 aligned chunks; chunk c of row r sits at slot
+  // c ^ vswz16(r), an even term, so the 16 chunks land on 16 distinct bank
+  // groups (with 128-byte rows, the 4 rows of each parity take 4 terms).
+  __device__ static __forceinline__ int vswz16(int row) {
+    return KD == 64 ? 2 * ((row >> 1) & 3) : 2 * (row & 7);
+  }
+  __device__ static __forceinline__ int vslot16(int row, int chunk) {
+    return row * NCH + (chunk ^ vswz16(row));
+  }
   // Tiles read both as MFMA rows and transposed (the backward kernels): a
   // row fragment read wants the 16 rows of a 16-row run on 16 distinct
   // 16-byte bank slots, a transposing read by 32 lanes wants 4 aligned rows
@@ -75,7 +85,8 @@ struct Geo {
 // descriptors based at its first key, so that the hardware range check
 // (which covers the per-lane offset only, not a scalar offset) still
 // zero-fills the keys past the end.
-template <int KD, int NT, int TK>
+// V16: the V tile takes the swizzle of the 16x16 kernels.
+template <int KD, int NT, int TK, bool V16 = false>
 struct TileLoads {
   using G = Geo<KD>;
   static constexpr int JW = TK / G::RPI / (NT / 64);
@@ -89,7 +100,7 @@ struct TileLoads {
       const int row = (wave * JW + j) * G::RPI + lane / G::NCH;
       const int slot = lane % G::NCH;
       ko[j] = (unsigned)(row * G::RB + ((slot ^ G::kswz(row)) << 4));
-      vo[j] = (unsigned)(row * G::RB + ((slot ^ G::vswz(row)) << 4));
+      vo[j] = (unsigned)(row * G::RB + ((slot ^ (V16 ? G::vswz16(row) : G::vswz(row))) << 4));
     }
     slot0 = wave * JW * 64;
   }
@@ -97,9 +108,9 @@ struct TileLoads {
 
 // The loads of one tile into one buffer; rk / rv start at the tile's first
 // key and end at the last valid key.
-template <int KD, int NT, int TK>
+template <int KD, int NT, int TK, bool V16 = false>
 struct TileDst {
-  const TileLoads<KD, NT, TK>* plan;
+  const TileLoads<KD, NT, TK, V16>* plan;
   __amdgpu_buffer_rsrc_t rk, rv;
   lds_u32x4* sk;
   lds_u32x4* sv;
@@ -116,9 +127,9 @@ struct TileDst {
   }
   __device__ __forceinline__ void all() const {
 #pragma unroll
-    for (int j = 0; j < TileLoads<KD, NT, TK>::JW; ++j) k(j);
+    for (int j = 0; j < TileLoads<KD, NT, TK, V16>::JW; ++j) k(j);
 #pragma unroll
-    for (int j = 0; j < TileLoads<KD, NT, TK>::JW; ++j) v(j);
+    for (int j = 0; j < TileLoads<KD, NT, TK, V16>::JW; ++j) v(j);
   }
 };
 

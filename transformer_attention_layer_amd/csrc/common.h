@@ -147,6 +147,11 @@ GQA_DEV float sum_xor16(float v) {
                                                   __builtin_bit_cast(unsigned, v), false, false);
   return __builtin_bit_cast(float, (unsigned)q[0]) + __builtin_bit_cast(float, (unsigned)q[1]);
 }
+GQA_DEV float max_xor16(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
+}
 GQA_DEV float sum_xor32(float v) {
   const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
                                                   __builtin_bit_cast(unsigned, v), false, false);
