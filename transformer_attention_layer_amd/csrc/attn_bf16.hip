@@ -321,6 +321,10 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
                                                  lo.kofs(s));
   }
   __builtin_amdgcn_sched_barrier(0);
+  // The products run at a raised wave priority, so that a wave whose
+  // MFMAs are ready issues them ahead of the softmax work of the other
+  // waves on its SIMD, which then fills the matrix core's cycles.
+  __builtin_amdgcn_s_setprio(1);
   floatx4 sc[KB][2];
   // 2 KB independent accumulation chains, interleaved
 #pragma unroll
@@ -339,6 +343,7 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
   // V^T fragments of key step ks, feature blocks db of one half of the
   // head (the register budget of three waves per SIMD holds half of them
@@ -367,6 +372,7 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
         for (int r = 0; r < 4; ++r)
           if (key0 + 16 * kb + 4 * q + r >= kend0 + kstep1 * qb) sc[kb][qb][r] = -INFINITY;
   }
+  // this lane's share of each row max (a row spans lanes l16 + 16 q)
   float mx[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -376,16 +382,15 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx[qb] = fmaxf(mx[qb], sc[kb][qb][r]);
   }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) mx[qb] = max_xor32(max_xor16(mx[qb]));  // over lanes l16 + 16 q
-  float mt[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) mt[qb] = mx[qb] * c_log2;  // -inf stays -inf (c_log2 > 0)
-  if (__builtin_amdgcn_ballot_w64(mt[0] > st.m[0] + kLazyRescale ||
-                                  mt[1] > st.m[1] + kLazyRescale)) {
+  // A row max passes its threshold exactly when one of its four shares
+  // does (c_log2 > 0), so the wave tests the shares and exchanges them only
+  // when it rescales.  An unset max (-inf) takes any finite share.
+  if (__builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[0], c_log2, -st.m[0]) > kLazyRescale ||
+                                  __builtin_fmaf(mx[1], c_log2, -st.m[1]) > kLazyRescale)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mn = fmaxf(st.m[qb], mt[qb]);
+      const float mt = max_xor32(max_xor16(mx[qb])) * c_log2;
+      const float mn = fmaxf(st.m[qb], mt);
       const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(st.m[qb] - mn);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
@@ -396,17 +401,18 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
     }
   }
   // P^T operands of both query blocks (and the row sums of their bf16
-  // values), then the products, half of the feature blocks at a time
+  // values), then the products, half of the feature blocks at a time.  The
+  // running max is finite here: key 0 is visible to every row (causal or
+  // not), so the first tile sets it.
   u32x4 pf[KS][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mb = st.m[qb] == -INFINITY ? 0.f : st.m[qb];
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        p[e] = fast_exp2(__builtin_fmaf(sc[2 * ks + e / 4][qb][e % 4], c_log2, -mb));
+        p[e] = fast_exp2(__builtin_fmaf(sc[2 * ks + e / 4][qb][e % 4], c_log2, -st.m[qb]));
       u32x4 f;
       f.x = pack_bf16x2(p[0], p[1]);
       f.y = pack_bf16x2(p[2], p[3]);
@@ -427,12 +433,14 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
         read_v(ks, half, vf);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (ks + half == 0) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < NH; ++j)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           st.o[half * NH + j][qb] = mfma16x16x32(vf[j], pf[ks][qb], st.o[half * NH + j][qb]);
     }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Prefill tile sizes and occupancy: head_dim 128 takes 32-key tiles, whose
