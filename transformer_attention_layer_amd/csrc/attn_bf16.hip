@@ -221,7 +221,8 @@ __device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)
 template <int KD>
 struct RowState16 {
   floatx4 o[KD / 16][2];  // O^T: feature 16 db + 4 q + r, query 16 qb + l16
-  float m[2];             // running max per query block (log2 units, scaled scores)
+  float nm[2];            // minus the running max per query block (log2 units, scaled
+                          // scores), kept negated: it enters every exp offset as is
   float l[2];             // running sum, this lane's keys only
 };
 
@@ -235,7 +236,7 @@ __device__ __forceinline__ void init_state16(RowState16<KD>& st) {
       for (int r = 0; r < 4; ++r) st.o[d][qb][r] = 0.f;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    st.m[qb] = -INFINITY;
+    st.nm[qb] = INFINITY;
     st.l[qb] = 0.f;
   }
 }
@@ -385,19 +386,19 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
   // A row max passes its threshold exactly when one of its four shares
   // does (c_log2 > 0), so the wave tests the shares and exchanges them only
   // when it rescales.  An unset max (-inf) takes any finite share.
-  if (__builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[0], c_log2, -st.m[0]) > kLazyRescale ||
-                                  __builtin_fmaf(mx[1], c_log2, -st.m[1]) > kLazyRescale)) {
+  if (__builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[0], c_log2, st.nm[0]) > kLazyRescale ||
+                                  __builtin_fmaf(mx[1], c_log2, st.nm[1]) > kLazyRescale)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mt = max_xor32(max_xor16(mx[qb])) * c_log2;
-      const float mn = fmaxf(st.m[qb], mt);
-      const float alpha = mn == -INFINITY ? 1.0f : fast_exp2(st.m[qb] - mn);
+      const float nmn = fminf(st.nm[qb], -mt);  // minus the new max
+      const float alpha = nmn == INFINITY ? 1.0f : fast_exp2(nmn - st.nm[qb]);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int r = 0; r < 4; ++r) st.o[d][qb][r] *= alpha;
       st.l[qb] *= alpha;
-      st.m[qb] = mn;
+      st.nm[qb] = nmn;
     }
   }
   // P^T operands of both query blocks (and the row sums of their bf16
@@ -412,7 +413,7 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        p[e] = fast_exp2(__builtin_fmaf(sc[2 * ks + e / 4][qb][e % 4], c_log2, -st.m[qb]));
+        p[e] = fast_exp2(__builtin_fmaf(sc[2 * ks + e / 4][qb][e % 4], c_log2, st.nm[qb]));
       u32x4 f;
       f.x = pack_bf16x2(p[0], p[1]);
       f.y = pack_bf16x2(p[2], p[3]);
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(PrefillCfg<KD>::NT, PrefillCfg<KD>::MIN_BLOCKS) voi
     if (a.lse && q == 0) {
       // log sum_j exp(s_j * scale) = (m + log2(l)) * ln 2, m in log2 units
       a.lse[((size_t)b * a.Hq + hq) * a.Lq + t] =
-          lt > 0.f ? (st.m[qb] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+          lt > 0.f ? (log2f(lt) - st.nm[qb]) * 0.69314718055994531f : -INFINITY;
     }
     bf16* orow = a.o + ((size_t)b * a.Lq + t) * width * (a.o_split ? 2 : 1) + (size_t)hq * KD;
 #pragma unroll
