@@ -297,7 +297,7 @@ __device__ __forceinline__ void load_q16(u32x4 (&qf)[2][KD / 32], const bf16* q0
 // keys with the causal mask, none without;
 // `masked` (wave-uniform) = some key of the tile may be past it for some
 // row of the wave.  `loads` issues the JW K and JW V loads of the next tile
-// during the first QK MFMAs.
+// right after this tile's K fragment reads.
 template <int KD, int TK, int JW, typename Loads>
 __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&qf)[2][KD / 32],
                                               const lds_u32x4* sk, const lds_u32x4* sv,
@@ -312,7 +312,6 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
   constexpr int NF = KB * NS;   // K fragments per tile = V^T fragments per tile
   static_assert(NF == KS * ND, "as many V^T as K fragments");
   constexpr int NQK = 2 * NF;   // QK MFMAs per tile
-  constexpr int kPer = (2 * JW + NQK - 1) / NQK;  // loads per leading QK MFMA
   u32x4 fr[NF];
   // K fragments in the order the products use them: feature step major
 #pragma unroll
@@ -321,6 +320,12 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
     fr[m] = *reinterpret_cast<const lds_u32x4*>(reinterpret_cast<lds_cchar*>(sk) + 16 * kb * G::RB +
                                                  lo.kofs(s));
   }
+  // the next tile's loads, all at once (interleaving them with the
+  // products was slower)
+#pragma unroll
+  for (int j = 0; j < JW; ++j) loads.k(j);
+#pragma unroll
+  for (int j = 0; j < JW; ++j) loads.v(j);
   __builtin_amdgcn_sched_barrier(0);
   // The products run at a raised wave priority, so that a wave whose
   // MFMAs are ready issues them ahead of the softmax work of the other
@@ -333,16 +338,6 @@ __device__ __forceinline__ void attend_tile16(RowState16<KD>& st, const u32x4 (&
     const int m = i / 2, qb = i % 2, s = m / KB, kb = m % KB;
     const floatx4 z = {};
     sc[kb][qb] = mfma16x16x32(fr[m], qf[qb][s], s == 0 ? z : sc[kb][qb]);
-    if (i * kPer < 2 * JW) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int idx = i * kPer + u;
-        if (idx < JW) loads.k(idx);
-        else if (idx < 2 * JW) loads.v(idx - JW);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
