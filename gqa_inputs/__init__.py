@@ -167,6 +167,30 @@ def host_cache(w: Workload, seed: Optional[int] = None,
     return {"k_cache": k, "v_cache": v}
 
 
+def host_ramp_attention(w: Workload, seed: Optional[int] = None,
+                        log2_per_key: float = 0.3, spike_log2: float = 40.0,
+                        spike_key: Optional[int] = None) -> dict:
+    """Attention inputs q [B, Hq, L, d], k, v [B, Hkv, L, d] whose scores
+    grow along the keys: per KV head a unit direction u; q rows are u (the
+    group's direction) plus N(0, 0.1^2) noise, key j is u times a ramp that
+    raises q.k by ``log2_per_key`` / (log2(e) / sqrt(d)) per key (that many
+    log2 units of the softmax) plus the same noise, and in the last sequence
+    key ``spike_key`` (default 2 L / 3) is raised by ``spike_log2`` more.  v
+    ~ N(0, 1).  Rounded once to the workload's dtype."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 2000)
+    B, L, d, hq, hkv = w.batch, w.seq, w.d, w.hq, w.hkv
+    per_unit = np.sqrt(d) / np.log2(np.e)  # raw q.k per log2 unit of the softmax
+    u = rng.standard_normal((hkv, d))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    ramp = log2_per_key * per_unit * np.arange(L)
+    k = u[None, :, None, :] * ramp[None, None, :, None] + 0.1 * rng.standard_normal((B, hkv, L, d))
+    sk = 2 * L // 3 if spike_key is None else spike_key
+    k[B - 1, :, sk] += spike_log2 * per_unit * u
+    q = np.repeat(u, hq // hkv, axis=0)[None, :, None, :] + 0.1 * rng.standard_normal((B, hq, L, d))
+    v = rng.standard_normal((B, hkv, L, d))
+    return {n: _finish(a.astype(np.float32), w.dtype) for n, a in (("q", q), ("k", k), ("v", v))}
+
+
 def torch_dtype(w: Workload):
     import torch
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32

@@ -166,6 +166,27 @@ def test_entry_points_parity(name):
                  w.dtype, "o_proj")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_rescales_in_later_tiles(causal):
+    """Scores that grow by 0.3 log2 units per key (about 10 per 32-key
+    tile) and one late key 40 units above the ramp: each row's running max
+    passes the lazy-rescale threshold in most of its tiles, not only the
+    first, and the spike forces one large rescale late in the row.  The
+    attention core against the oracle on the same rounded q, k, v."""
+    T = T_()
+    w = GI.WORKLOADS["prefill_h1024"].with_(batch=2, seq=300, causal=causal)
+    announce(f"[rescale ramp] causal={causal}")
+    res = resolved(w)
+    a = GI.host_ramp_attention(w)
+    d = GI.to_device(a, w)
+    o = T.gqa_attn_core(cfg_of(w), d["q"], d["k"], d["v"])
+    pos = np.tile(np.arange(w.seq), (w.batch, 1))
+    ro = O.merge_heads(O.grouped_attention(a["q"].astype(np.float64), a["k"].astype(np.float64),
+                                           a["v"].astype(np.float64), pos,
+                                           np.full(w.batch, w.seq), res.scale, causal))
+    assert_close(to_np(o), ro, w.dtype, "attention")
+
+
 @pytest.mark.parametrize("variant", [
     dict(hq=16, hkv=16),            # plain MHA (group 1)
     dict(hq=12, hkv=4),             # group 3
