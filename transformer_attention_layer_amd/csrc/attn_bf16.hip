@@ -31,7 +31,8 @@
 //   prefill: a workgroup of 4 waves covers up to 4 query heads of one KV
 //            group at the same 32 positions (or 2 heads x 64 positions, or
 //            1 head x 128), so every wave walks the same causal key range and
-//            each K/V tile is staged in LDS once for the whole group.
+//            each K/V tile is staged in LDS once per workgroup: once per KV
+//            group for groups of up to 4 query heads, twice for 8.
 //   decode : one wave per (sequence, KV head, key split); its 32 rows are the
 //            group's query heads (x the few new tokens).  Partial (max, sum,
 //            unnormalised output) per split are merged by a second kernel.
@@ -210,7 +211,8 @@ __device__ __forceinline__ void store_o4(bf16* p, size_t width, const float (&v)
 // A wave's 32 query rows are two 16-row blocks (qb): lane l holds queries
 // l16 and 16 + l16 (l16 = l % 16) and, of each 16-key block of the scores
 // S^T = K Q^T, the keys 4 q + 0..3 (q = l / 16).  The row max and sum of a
-// query then span the four lanes l16 + 16 q (two exchanges), the rescale
+// query then span the four lanes l16 + 16 q (two exchanges, for the max only
+// when the wave rescales), the rescale
 // factor is one scalar per lane and query block, and the P^T operand of
 // O^T = V^T P^T comes straight from the score registers: for a 32-key step,
 // lane l holds keys 4 q + 0..3 and 16 + 4 q + 0..3 of the query, which is
