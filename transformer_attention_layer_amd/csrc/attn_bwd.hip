@@ -489,12 +489,15 @@ __global__ __launch_bounds__(kBwdNT) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   // XCD-aware order: workgroup i runs on XCD i % 8; the key blocks of one
   // (sequence, KV head) all go to the same XCD, so that they share its L2
-  // for the query tiles they all read (in the same, descending order)
+  // for the query tiles they all read (in the same, descending order).  On
+  // an XCD the key blocks go out block-index major: with the causal mask
+  // block 0 sees every query tile and the last one the fewest, so the
+  // heaviest workgroups start first and the lightest fill the end.
   const int L = a.L;
-  const int nkb = (L + kBwdKeysWG - 1) / kBwdKeysWG;
+  const int gpx = (a.B * a.Hkv + 7) / 8;  // (sequence, KV head) pairs per XCD
   const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
-  const int grp = xcd + 8 * (slot / nkb);  // (sequence, KV head) pair
-  const int kblk = slot - (slot / nkb) * nkb;
+  const int kblk = slot / gpx;
+  const int grp = xcd + 8 * (slot - kblk * gpx);  // (sequence, KV head) pair
   if (grp >= a.B * a.Hkv) return;  // padding of the grid to a multiple of 8 groups
   const int b = grp / a.Hkv, kvh = grp - b * a.Hkv;
   const int kwg0 = kblk * kBwdKeysWG;
