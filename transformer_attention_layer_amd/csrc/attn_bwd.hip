@@ -257,8 +257,11 @@ __global__ __launch_bounds__(kBwdNT, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int qt = a.n_qtiles - 1 - (int)blockIdx.z;  // heaviest query tiles first
   const int b = blockIdx.y;
-  const int kvh = blockIdx.x / a.n_hsub;
-  const int hsub = blockIdx.x - kvh * a.n_hsub;
+  // the n_hsub workgroups of one KV group's heads are Hkv apart in x, so
+  // with Hkv a multiple of 8 they run on one XCD and share its L2 for the
+  // group's K/V tiles
+  const int kvh = blockIdx.x % a.Hkv;
+  const int hsub = blockIdx.x / a.Hkv;
   const int head_local = wave % a.hpw;
   const int pblk = wave / a.hpw;
   const int hq = kvh * a.G + hsub * a.hpw + head_local;
