@@ -230,8 +230,12 @@ __global__ __launch_bounds__(kRowsNT) void normrope_bwd_rows_kernel(NormRopeBwdA
 
 // Sum of the per-block partials [blocks][2][d] in two fixed-order stages:
 // stage 1 block j sums partial rows j, j + S1, j + 2 S1, ... (one thread per
-// column of the 2 d columns) into stage[j][2][d]; stage 2 sums the S1 rows.
+// column, eight loads in flight); stage 2 (one block of 1024 threads) gives
+// each column 1024 / (2 d) threads, thread u summing stage rows u, u + TPC,
+// ... (sixteen loads in flight), and adds their sums in u order.  Both
+// orders are fixed, so the result does not depend on the schedule.
 constexpr int kReduceS1 = 256;
+constexpr int kReduceS2NT = 1024;
 
 __global__ __launch_bounds__(256) void dgamma_stage1_kernel(const float* __restrict__ part,
                                                             int blocks, int d,
@@ -239,19 +243,30 @@ __global__ __launch_bounds__(256) void dgamma_stage1_kernel(const float* __restr
   const int j = blockIdx.x;
   for (int col = threadIdx.x; col < 2 * d; col += 256) {
     float s = 0.f;
+#pragma unroll 8
     for (int i = j; i < blocks; i += kReduceS1) s += part[(size_t)i * 2 * d + col];
     stage[(size_t)j * 2 * d + col] = s;
   }
 }
 
-__global__ __launch_bounds__(256) void dgamma_stage2_kernel(const float* __restrict__ stage, int d,
-                                                            float* dq_w, float* dk_w) {
-  for (int col = threadIdx.x; col < 2 * d; col += 256) {
-    float s = 0.f;
-    for (int j = 0; j < kReduceS1; ++j) s += stage[(size_t)j * 2 * d + col];
-    if (col < d) dq_w[col] = s;
-    else dk_w[col - d] = s;
-  }
+__global__ __launch_bounds__(kReduceS2NT) void dgamma_stage2_kernel(const float* __restrict__ stage,
+                                                                   int d, float* dq_w,
+                                                                   float* dk_w) {
+  __shared__ float red[kReduceS2NT];
+  poison_lds(red);
+  const int cols = 2 * d;  // 128, 256 or 512: divides kReduceS2NT
+  const int tpc = kReduceS2NT / cols;
+  const int col = threadIdx.x % cols, u = threadIdx.x / cols;
+  float s = 0.f;
+#pragma unroll 16
+  for (int j = u; j < kReduceS1; j += tpc) s += stage[(size_t)j * cols + col];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (u != 0) return;
+  float t = 0.f;
+  for (int v = 0; v < tpc; ++v) t += red[v * cols + col];
+  if (col < d) dq_w[col] = t;
+  else dk_w[col - d] = t;
 }
 
 // Rows per lane group and block: kRowsIter for large row counts, fewer
@@ -326,7 +341,8 @@ hipError_t launch_dgamma_reduce(const float* part, int blocks, int d, float* sta
   dgamma_stage1_kernel<<<kReduceS1, 256, 0, stream>>>(part, blocks, d, stage);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dgamma_stage2_kernel<<<1, 256, 0, stream>>>(stage, d, dq_w, dk_w);
+  if (kReduceS2NT % (2 * d) != 0) return hipErrorInvalidValue;
+  dgamma_stage2_kernel<<<1, kReduceS2NT, 0, stream>>>(stage, d, dq_w, dk_w);
   return hipGetLastError();
 }
 
