@@ -65,6 +65,8 @@ def _decode_twice(w, kv_fp8=False):
     ("mqa_69_splits", GI.WORKLOADS["decode_h2560_mqa"].with_(batch=1, cache_len=70000)),
     ("gqa_8seq_8k", GI.WORKLOADS["decode_h2560_gqa"].with_(batch=8, cache_len=8191)),
     ("gqa_q4", GI.WORKLOADS["decode_h2560_gqa"].with_(batch=3, seq=4, cache_len=3000)),
+    ("gqa_rotated_d64", GI.WORKLOADS["decode_h2560_gqa"].with_(batch=96, cache_len=3500, hq=8,
+                                                               hkv=4, head_dim=64)),
 ])
 def test_decode_repeat_bitwise(name, w):
     announce(f"[repeat] decode {name}")

@@ -52,6 +52,11 @@ SMALL = {
                                                              hkv=4, o_fp16=False, o_split=True),
     "bf16_d64_decode": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=2, cache_len=300, hq=8, hkv=4,
                                                               head_dim=64),
+    # more decode waves than the GPU holds at once (384 streams x 4 splits of
+    # 896 keys, the last one ragged): each wave starts its chunk at its own
+    # tile and wraps round, so partial tiles fall mid-walk
+    "decode_rotated_d64": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=96, cache_len=3500, hq=8,
+                                                                 hkv=4, head_dim=64),
     # head_dim 256 through the split-KV decode kernel (one wave per SIMD),
     # a Gemma-shaped group of 4 query heads per KV head
     "bf16_d256_decode": GI.WORKLOADS["gemma_h640_d256"].with_(batch=3, seq=1, cache_len=1500),

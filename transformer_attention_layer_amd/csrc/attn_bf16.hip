@@ -621,13 +621,27 @@ __global__ __launch_bounds__(kDecodeNT) void attn_decode_kernel(AttnArgs a) {
   init_state<KD>(st);
   Plan plan;
   plan.init(0, lane);
-  const TileDst<KD, NT, TK> first{&plan, rk_at(ks), rv_at(ks), sk[0], sv[0], n_tiles > 0};
+  // With `rotate` the wave walks its chunk's tiles starting at tile
+  // 13 * (wave index) mod n_tiles, wrapping round, so that the waves resident
+  // at one time do not all read the same offset of their chunks.
+  const int rot = a.rotate && n_tiles > 0
+                      ? (int)(((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 13u %
+                              (unsigned)n_tiles)
+                      : 0;
+  auto key_of = [&](int it) {
+    int j = it + rot;
+    if (j >= n_tiles) j -= n_tiles;
+    return ks + j * TK;
+  };
+  const TileDst<KD, NT, TK> first{&plan, rk_at(key_of(0)), rv_at(key_of(0)), sk[0], sv[0],
+                                  n_tiles > 0};
   first.all();
   __syncthreads();
   auto step = [&](auto bufc, int it) {
     constexpr int B = decltype(bufc)::value;
-    const int key0 = ks + it * TK;
-    const TileDst<KD, NT, TK> next{&plan, rk_at(key0 + TK), rv_at(key0 + TK), sk[B ^ 1],
+    const int key0 = key_of(it);
+    const int key1 = key_of(it + 1 < n_tiles ? it + 1 : it);
+    const TileDst<KD, NT, TK> next{&plan, rk_at(key1), rv_at(key1), sk[B ^ 1],
                                    sv[B ^ 1], it + 1 < n_tiles};
     const bool masked = key0 + TK > kmin;
     attend_tile<KD, TK, Plan::JW>(st, qf, sk[B], sv[B], lo, key0, kend_row, masked, a.scale_log2,

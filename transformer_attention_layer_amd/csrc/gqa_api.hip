@@ -171,6 +171,7 @@ bool use_decode(const Shape& s, int q_len) { return s.mfma && s.G * q_len <= 32;
 constexpr int kDecodeMinChunk = 1024;
 constexpr long long kDecodeRoundBf16 = 512;
 constexpr long long kDecodeRoundFp8 = 1024;
+constexpr long long kDecodeResident = 1280;
 void decode_split(const Shape& s, int batch, int cap, int* n_splits, int* chunk) {
   const long long streams = (long long)batch * s.Hkv;
   long long want = (4096 + streams - 1) / (streams > 0 ? streams : 1);
@@ -503,6 +504,11 @@ gqa_status run_attn(const gqa_config& c, const Shape& s, int batch, int q_len, c
   a.lse = lse;
   if (!lse && use_decode(s, q_len)) {
     decode_split(s, batch, cap, &a.n_splits, &a.chunk);
+    // Launches of more waves than the GPU holds at once (about 1280: five
+    // per CU, by LDS) over a bf16 cache start each wave at its own tile:
+    // 64 x 8 streams of 32768 keys 5.75 -> 5.88 TB/s.  One round of waves
+    // (MQA) was 1-4% slower rotated, and the FP8 kernel did not gain.
+    a.rotate = !s.kv_fp8 && (long long)batch * s.Hkv * a.n_splits > kDecodeResident;
     const size_t parts = (size_t)batch * s.Hkv * a.n_splits * s.G * q_len;
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(parts * s.d * sizeof(float)));

@@ -84,6 +84,7 @@ struct AttnArgs {
   float* part_o;       // [B, Hkv, n_splits, G * Lq, d]
   float2* part_ml;     // [B, Hkv, n_splits, G * Lq] (running max in log2 units, sum)
   int n_splits, chunk;
+  int rotate;          // bf16 decode: each wave starts its chunk at a tile of its own
   float* lse;          // prefill, optional: [B, Hq, Lq] natural log of each row's softmax denominator
 };
 
