@@ -256,7 +256,9 @@ gqa_status gqa_layer_forward_noalloc(const gqa_config* cfg, int32_t batch, int32
  */
 typedef struct {
   float* qkv;  /* [batch, q_len, (Hq + 2*Hkv) * d]: the fused projection output
-                  before QK-norm and RoPE */
+                  before QK-norm and RoPE, kept for the norm backward: only
+                  the Q and K columns, and only with QK-norm on, are read,
+                  and the other columns may be left unwritten */
   void* q;     /* [batch, Hq, q_len, d] after QK-norm and RoPE */
   void* k;     /* [batch, Hkv, q_len, d] after QK-norm and RoPE */
   void* v;     /* [batch, Hkv, q_len, d] */

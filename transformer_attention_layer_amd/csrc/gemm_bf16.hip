@@ -554,7 +554,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
               float* yr = a.y_raw + (size_t)mr * N + nw + 4 * q4;
 #pragma unroll
               for (int f = 0; f < FB; ++f) {
-                if (!live[f >> 2]) continue;
+                // only the normalised heads' rows are kept (the norm backward)
+                if (!live[f >> 2] || kind[f >> 2] == 2 || !a.qk_norm) continue;
                 *reinterpret_cast<floatx4*>(yr + 16 * f) = acc[f][t];
               }
             }
@@ -706,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           const int t = 2 * p + tt;
           const int row = 16 * tt + l16;
           const int mr = mb + row;
-          if (a.y_raw && mr < M) {
+          if (a.y_raw && do_norm && mr < M) {  // kept for the norm backward only
             float* yr = a.y_raw + (size_t)mr * N + n0;
 #pragma unroll
             for (int f = 0; f < FB; ++f)
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
           const int t = 2 * p + tt;
           const int row = 16 * tt + l16;
           const int mr = mb + row;
-          if (a.y_raw && mr < M) {  // a.y_raw is wave-uniform
+          if (a.y_raw && do_norm && mr < M) {  // wave-uniform; kept for the norm backward only
             float* yr = a.y_raw + (size_t)mr * N + nw + 4 * q4;
 #pragma unroll
             for (int f = 0; f < FB; ++f) *reinterpret_cast<floatx4*>(yr + 16 * f) = acc[f][t];

@@ -39,7 +39,8 @@ struct GemmArgs {
   int rot;                // rotary width: head_dim 128: 128 or 64; 64: 64 or 32; 256: 256
   int hd;                 // head_dim of the QKV epilogue: 128 (0 counts as 128), 64 or 256
   float eps;
-  float* y_raw;           // optional: [M, N] fp32 projection before norm and RoPE
+  float* y_raw;           // optional: [M, N] fp32 projection before norm and RoPE (QKV
+                          // epilogues: the columns of the normalised heads only)
   // few-token GEMM only: K split over ksplit workgroups (<= 1: none), whose
   // fp32 partial products go to part [ksplit][M][N] and are then summed into out
   int ksplit;
