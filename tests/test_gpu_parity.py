@@ -57,6 +57,10 @@ SMALL = {
     # tile and wraps round, so partial tiles fall mid-walk
     "decode_rotated_d64": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=96, cache_len=3500, hq=8,
                                                                  hkv=4, head_dim=64),
+    # ... with 4 new tokens per sequence, so causally masked keys sit in
+    # tiles that the rotated walks reach mid-way
+    "decode_rotated_q4_d64": GI.WORKLOADS["decode_h2560_gqa"].with_(batch=96, seq=4, cache_len=3500,
+                                                                    hq=8, hkv=4, head_dim=64),
     # head_dim 256 through the split-KV decode kernel (one wave per SIMD),
     # a Gemma-shaped group of 4 query heads per KV head
     "bf16_d256_decode": GI.WORKLOADS["gemma_h640_d256"].with_(batch=3, seq=1, cache_len=1500),
